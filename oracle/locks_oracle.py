@@ -1,0 +1,308 @@
+"""Locks decode path, written out plainly in fp64 (numpy).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py``; never by the product path.  It
+shares no code, constants or helpers with the HIP library.
+
+Source: "Locks: Page-Local Compact Key Summaries for Efficient Long-Context
+Decoding" (arXiv 2607.24555), cited below as [Locks] with its section,
+equation or lemma.  The technical-review blog post of the same paper is cited
+as [Review] (its restatement of the method as Algorithms 1-2 and its toy
+example in 5.1); where the two differ, [Locks] decides.
+
+Locks is an approximation (reconstructed LSE, then a heuristic shared
+selection), so this module runs the method's steps in the paper's order and
+notation; beside them sit the plain definitions the method is checked against
+(exact page log-mass, exact-mass selection, dense softmax attention).
+Library primitives used as steps: ``numpy.linalg.eigh`` (the small symmetric
+eigendecomposition of the build), matrix products, sorting.
+
+Readings taken where the pages leave a step open (each is listed in the design doc):
+  * the most-recent page is the page holding the newest token (possibly
+    partial); pages before it are complete, summarized and scored; page 0
+    (the sink) is scored but never a candidate;
+  * the page-mass share of a query head is normalized over all scored pages,
+    the sink included;
+  * ties at the top-k cut go to the lower page index;
+  * a mode is a zero mode when its Gram eigenvalue is <= ZERO_MODE_RTOL times
+    the largest one, or <= ZERO_MODE_FLOOR times the page's uncentred key
+    energy sum_i ||k_i||^2 (centering rounding noise of a constant page is not a
+    mode); zero modes get a zero basis column and zero coefficients;
+  * each basis column is signed so that its largest-magnitude entry is
+    positive (scores depend only on V V^T, so this only fixes a representative);
+  * the stored summary (centroid, basis, coefficients) is rounded to the
+    storage dtype with round-to-nearest-even, because that is what is stored.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+__all__ = [
+    "ZERO_MODE_RTOL",
+    "ZERO_MODE_FLOOR",
+    "bf16_round",
+    "storage_round",
+    "PageSummary",
+    "build_page_summaries",
+    "reconstructed_page_lse",
+    "exact_page_lse",
+    "share_average",
+    "select_pages",
+    "page_budget",
+    "most_recent_page",
+    "gather_tokens",
+    "attend",
+    "decode_head",
+    "HeadStep",
+    "summary_bytes",
+    "record_elements",
+]
+
+# Eigenvalue thresholds of the zero-mode rule ([Locks] §4 "Build" states the
+# rule, not the constants): relative to the largest eigenvalue, and relative to
+# the page's uncentred key energy.
+ZERO_MODE_RTOL = 1e-5
+ZERO_MODE_FLOOR = 1e-10
+
+
+# ----------------------------------------------------------------------------
+# storage rounding
+# ----------------------------------------------------------------------------
+def bf16_round(x) -> np.ndarray:
+    """Round fp64 values to the nearest bfloat16 (ties to even), returned as fp64.
+
+    bfloat16 keeps 8 significant bits (7 stored); an fp64 significand has 53,
+    so the 45 low bits are rounded away in one step (no double rounding).
+    Values beyond the bf16 range are not expected here and are not handled.
+    """
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    bits = x.view(np.uint64)
+    drop = np.uint64(45)
+    half = np.uint64((1 << 44) - 1)
+    lsb = (bits >> drop) & np.uint64(1)
+    rounded = (bits + half + lsb) & ~np.uint64((1 << 45) - 1)
+    return rounded.view(np.float64)
+
+
+def storage_round(x, dtype: str) -> np.ndarray:
+    """Round to what a ``dtype`` ("f32" or "bf16") buffer holds, back in fp64."""
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return bf16_round(x)
+    if dtype == "f64":
+        return np.asarray(x, dtype=np.float64)
+    raise ValueError(f"unknown storage dtype {dtype!r}")
+
+
+# ----------------------------------------------------------------------------
+# build: [Locks] §4 "Build (once, when a page completes)"; [Review] Alg. 1
+# ----------------------------------------------------------------------------
+@dataclass
+class PageSummary:
+    """Per-page summary arrays for n pages (leading axis)."""
+
+    centroid: np.ndarray  # [n, d]      mu_j
+    basis: np.ndarray     # [n, r, d]   row k is the basis vector v_{j,k} (columns of V_j)
+    coeffs: np.ndarray    # [n, B, r]   row i is c_i (rows of C_j = U_{j,r} Sigma_{j,r})
+    eigvals: np.ndarray   # [n, B]      Gram eigenvalues sigma^2, descending
+    r_eff: np.ndarray     # [n]         retained nonzero modes
+
+
+def build_page_summaries(keys, rank: int, dtype: str = "f64",
+                         zero_mode_rtol: float = ZERO_MODE_RTOL,
+                         zero_mode_floor: float = ZERO_MODE_FLOOR) -> PageSummary:
+    """Build the rank-``rank`` spectral summary of every page in ``keys`` [n, B, d].
+
+    Steps, in [Locks] §4 order: centre the page (k_i = mu + delta_i); stack the
+    deviations as rows of D; eigendecompose the B x B Gram D D^T = U Sigma^2 U^T
+    with eigenvalues sorted descending; keep r components with
+    C = U_r Sigma_r and V = D^T U_r Sigma_r^{-1}; zero modes are dropped (zero
+    column, zero coefficients) so Sigma^{-1} only meets nonzero values.
+    Centroid, basis and coefficients are then rounded to ``dtype``.
+    """
+    keys = np.asarray(keys, dtype=np.float64)
+    if keys.ndim == 2:
+        keys = keys[None]
+    n, B, d = keys.shape
+    mu = keys.mean(axis=1)                                   # [n, d]
+    D = keys - mu[:, None, :]                                # [n, B, d]
+    gram = D @ np.swapaxes(D, 1, 2)                          # [n, B, B]
+    lam, U = np.linalg.eigh(gram)                            # ascending
+    lam = lam[:, ::-1].copy()                                # descending
+    U = U[:, :, ::-1].copy()
+
+    kept = min(rank, B)
+    lam1 = lam[:, :1]                                        # [n, 1]
+    energy = (keys ** 2).sum(axis=(1, 2))[:, None]           # [n, 1]
+    thresh = np.maximum(zero_mode_rtol * lam1, zero_mode_floor * energy)
+    nonzero = (lam[:, :kept] > thresh) & (lam1 > 0)
+    sigma = np.sqrt(np.where(nonzero, lam[:, :kept], 1.0))   # placeholder 1 on zero modes
+    Ur = U[:, :, :kept]                                      # [n, B, kept]
+    V = np.swapaxes(D, 1, 2) @ Ur / sigma[:, None, :]        # [n, d, kept]
+    C = Ur * sigma[:, None, :]                               # [n, B, kept]
+    V = np.where(nonzero[:, None, :], V, 0.0)
+    C = np.where(nonzero[:, None, :], C, 0.0)
+
+    # sign representative: largest-magnitude entry of each basis column positive
+    idx = np.argmax(np.abs(V), axis=1)                       # [n, kept]
+    lead = np.take_along_axis(V, idx[:, None, :], axis=1)[:, 0, :]
+    flip = np.where(lead < 0, -1.0, 1.0)
+    V = V * flip[:, None, :]
+    C = C * flip[:, None, :]
+
+    basis = np.zeros((n, rank, d))
+    coeffs = np.zeros((n, B, rank))
+    basis[:, :kept, :] = np.swapaxes(V, 1, 2)
+    coeffs[:, :, :kept] = C
+    return PageSummary(
+        centroid=storage_round(mu, dtype),
+        basis=storage_round(basis, dtype),
+        coeffs=storage_round(coeffs, dtype),
+        eigvals=np.clip(lam, 0.0, None),
+        r_eff=nonzero.sum(axis=1),
+    )
+
+
+# ----------------------------------------------------------------------------
+# score: [Locks] §4 "Score", Eq. (1)
+# ----------------------------------------------------------------------------
+def _logsumexp(z, axis=-1):
+    m = np.max(z, axis=axis, keepdims=True)
+    return (m + np.log(np.sum(np.exp(z - m), axis=axis, keepdims=True))).squeeze(axis)
+
+
+def reconstructed_page_lse(q, summary: PageSummary, scale: float) -> np.ndarray:
+    """Eq. (1): s_hat_j(q) = log sum_i exp((q^T mu_j + (V_j^T q)^T c_i) * scale).
+
+    ``q`` is [G, d] (one row per query head of the group); returns [G, n].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    a = q @ summary.centroid.T                               # [G, n]   q^T mu_j
+    proj = np.einsum("nrd,gd->gnr", summary.basis, q)        # [G, n, r] V_j^T q
+    recon = np.einsum("nbr,gnr->gnb", summary.coeffs, proj)  # [G, n, B] (V_j^T q)^T c_i
+    z = scale * (a[:, :, None] + recon)
+    return _logsumexp(z, axis=-1)
+
+
+def exact_page_lse(q, keys, scale: float) -> np.ndarray:
+    """Exact page log-mass s_j(q) = log sum_{i in P_j} exp(q^T k_i * scale)
+    ([Locks] Lemma 1(ii)); ``keys`` [n, B, d] -> [G, n]."""
+    q = np.asarray(q, dtype=np.float64)
+    z = scale * np.einsum("gd,nbd->gnb", q, np.asarray(keys, dtype=np.float64))
+    return _logsumexp(z, axis=-1)
+
+
+# ----------------------------------------------------------------------------
+# share-average and selection: [Locks] §4 (after Eq. (1)), Cor. 3
+# ----------------------------------------------------------------------------
+def share_average(page_lse) -> np.ndarray:
+    """m_hat_g(j) = exp(s_hat_j(q_g)) / sum_j' exp(s_hat_j'(q_g)); returns the
+    group average m_bar_j = (1/G) sum_g m_hat_g(j) over the pages given."""
+    s = np.asarray(page_lse, dtype=np.float64)
+    norm = _logsumexp(s, axis=1)                             # [G]
+    shares = np.exp(s - norm[:, None])                       # [G, n]
+    return shares.mean(axis=0)
+
+
+def page_budget(token_budget: int, page_size: int) -> int:
+    """k = ceil(b / B) pages ([Locks] §2)."""
+    return -(-token_budget // page_size)
+
+
+def most_recent_page(seq_len: int, page_size: int) -> int:
+    """Index of the page that holds the newest token."""
+    return (seq_len - 1) // page_size
+
+
+def select_pages(m_bar, n_mr: int, k: int) -> np.ndarray:
+    """Sink page 0, the most recent page n_mr, and the top-(k-2) candidates
+    1..n_mr-1 by m_bar (ties to the lower index); ascending page indices."""
+    if n_mr == 0:
+        return np.array([0], dtype=np.int64)
+    m_bar = np.asarray(m_bar, dtype=np.float64)
+    cand = list(range(1, n_mr))
+    n_top = min(k - 2, len(cand))
+    ranked = sorted(cand, key=lambda j: (-m_bar[j], j))[:n_top]
+    return np.array(sorted({0, n_mr, *ranked}), dtype=np.int64)
+
+
+# ----------------------------------------------------------------------------
+# attention: [Locks] §2 "Decode-time attention"
+# ----------------------------------------------------------------------------
+def gather_tokens(pages_kv, pages, seq_len: int, page_size: int) -> np.ndarray:
+    """Tokens of the listed logical pages, in page order; the page holding the
+    newest token contributes only its filled slots.  ``pages_kv`` [n, B, d]."""
+    out = []
+    for j in pages:
+        filled = min(page_size, seq_len - j * page_size)
+        out.append(np.asarray(pages_kv[j, :filled], dtype=np.float64))
+    return np.concatenate(out, axis=0)
+
+
+def attend(q, keys, values, scale: float):
+    """o = sum_i alpha_i v_i with alpha = softmax(q^T k * scale); also the
+    log-sum-exp of the logits.  ``q`` [G, d], ``keys``/``values`` [T, d]."""
+    q = np.asarray(q, dtype=np.float64)
+    z = scale * (q @ np.asarray(keys, dtype=np.float64).T)   # [G, T]
+    m = z.max(axis=1, keepdims=True)
+    w = np.exp(z - m)
+    l = w.sum(axis=1, keepdims=True)
+    o = (w @ np.asarray(values, dtype=np.float64)) / l
+    return o, (m + np.log(l))[:, 0]
+
+
+# ----------------------------------------------------------------------------
+# one decode step for one (sequence, KV head)
+# ----------------------------------------------------------------------------
+@dataclass
+class HeadStep:
+    page_lse: np.ndarray   # [G, n_mr] reconstructed scores of the scored pages
+    m_bar: np.ndarray      # [n_mr] group-averaged shares
+    selected: np.ndarray   # ascending logical page indices
+    out: np.ndarray        # [G, d]
+    lse: np.ndarray        # [G]
+
+
+def decode_head(q, keys_pages, values_pages, seq_len: int, summary: PageSummary,
+                token_budget: int, scale: float) -> HeadStep:
+    """Score -> share-average -> select -> attend for one KV head's group.
+
+    ``keys_pages``/``values_pages`` [n_pages, B, d] hold the head's cache in
+    logical page order; ``summary`` covers at least pages 0..n_mr-1.
+    """
+    B = keys_pages.shape[1]
+    n_mr = most_recent_page(seq_len, B)
+    k = page_budget(token_budget, B)
+    if n_mr > 0:
+        sub = PageSummary(summary.centroid[:n_mr], summary.basis[:n_mr],
+                          summary.coeffs[:n_mr], summary.eigvals[:n_mr], summary.r_eff[:n_mr])
+        s_hat = reconstructed_page_lse(q, sub, scale)
+        m_bar = share_average(s_hat)
+    else:
+        s_hat = np.zeros((np.asarray(q).shape[0], 0))
+        m_bar = np.zeros(0)
+    sel = select_pages(m_bar, n_mr, k)
+    K = gather_tokens(keys_pages, sel, seq_len, B)
+    Vv = gather_tokens(values_pages, sel, seq_len, B)
+    out, lse = attend(q, K, Vv, scale)
+    return HeadStep(s_hat, m_bar, sel, out, lse)
+
+
+# ----------------------------------------------------------------------------
+# byte accounting: [Locks] App. D "State accounting", Table D.10
+# ----------------------------------------------------------------------------
+def record_elements(head_dim: int, page_size: int, rank: int) -> dict:
+    """Elements of one page summary: basis d*r, coefficients B*r, centroid d."""
+    return {"basis": head_dim * rank, "coeffs": page_size * rank, "centroid": head_dim}
+
+
+def summary_bytes(head_dim: int, page_size: int, rank: int,
+                  basis_bits: float, coeff_bits: float, centroid_bits: float) -> float:
+    """Logical payload bytes of one page summary (quantization scales excluded)."""
+    e = record_elements(head_dim, page_size, rank)
+    return (e["basis"] * basis_bits + e["coeffs"] * coeff_bits
+            + e["centroid"] * centroid_bits) / 8.0
