@@ -1,0 +1,304 @@
+// C ABI of the Locks decode path (declared in include/locks.h): argument
+// validation, workspace carving and kernel launches.  Host code only; every
+// entry point enqueues on the caller's stream and returns without waiting.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/locks.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr int kPagesPerSplitSparse = 1;
+constexpr int kPagesPerSplitDense = 16;
+constexpr int kMaxPagesPerSeq = 1024 * 64;   // selection keeps 64 candidates per thread
+constexpr int kMaxPageBudget = 1024;
+constexpr size_t kAlign = 256;
+
+lk_status fail(lk_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+lk_status fail(lk_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+lk_status ok() {
+  g_last_error.clear();
+  return LK_OK;
+}
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Shape {
+  int d, B, r, hq, hkv, G, k;
+  lk::DType dt;
+  size_t elem;
+};
+
+lk_status check_config(const lk_config* cfg, Shape* sh) {
+  if (!cfg) return fail(LK_ERR_INVALID_ARG, "config is null");
+  if (cfg->head_dim <= 0 || cfg->page_size <= 0 || cfg->rank <= 0 || cfg->num_q_heads <= 0 ||
+      cfg->num_kv_heads <= 0 || cfg->token_budget <= 0)
+    return fail(LK_ERR_INVALID_ARG, "config sizes must be positive (d=%d B=%d r=%d Hq=%d Hkv=%d b=%d)",
+                cfg->head_dim, cfg->page_size, cfg->rank, cfg->num_q_heads, cfg->num_kv_heads,
+                cfg->token_budget);
+  if (cfg->num_q_heads % cfg->num_kv_heads != 0)
+    return fail(LK_ERR_INVALID_ARG, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                cfg->num_q_heads, cfg->num_kv_heads);
+  if (cfg->kv_dtype != LK_F32 && cfg->kv_dtype != LK_BF16)
+    return fail(LK_ERR_INVALID_ARG, "kv_dtype %d is not LK_F32 or LK_BF16", cfg->kv_dtype);
+  if (!std::isfinite(cfg->scale)) return fail(LK_ERR_INVALID_ARG, "scale is not finite");
+  const int k = (cfg->token_budget + cfg->page_size - 1) / cfg->page_size;
+  if (k < 2)
+    return fail(LK_ERR_INVALID_ARG, "page budget ceil(b/B) = %d < 2 (the sink and the most recent page need two slots)", k);
+  if (cfg->head_dim != 128) return fail(LK_ERR_UNSUPPORTED, "head_dim %d: only 128 is built", cfg->head_dim);
+  if (cfg->page_size != 64) return fail(LK_ERR_UNSUPPORTED, "page_size %d: only 64 is built", cfg->page_size);
+  const int r = cfg->rank;
+  if (r != 1 && r != 2 && r != 4 && r != 8 && r != 16)
+    return fail(LK_ERR_UNSUPPORTED, "rank %d: built ranks are 1, 2, 4, 8, 16", r);
+  const int G = cfg->num_q_heads / cfg->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(LK_ERR_UNSUPPORTED, "GQA group %d: built groups are 1, 2, 4, 8", G);
+  if (k > kMaxPageBudget) return fail(LK_ERR_UNSUPPORTED, "page budget %d exceeds %d", k, kMaxPageBudget);
+  sh->d = cfg->head_dim;
+  sh->B = cfg->page_size;
+  sh->r = r;
+  sh->hq = cfg->num_q_heads;
+  sh->hkv = cfg->num_kv_heads;
+  sh->G = G;
+  sh->k = k;
+  sh->dt = cfg->kv_dtype == LK_BF16 ? lk::kBF16 : lk::kF32;
+  sh->elem = cfg->kv_dtype == LK_BF16 ? 2 : 4;
+  return LK_OK;
+}
+
+lk_status check_cache(const lk_cache* c, bool need_kv, bool need_summary) {
+  if (!c) return fail(LK_ERR_INVALID_ARG, "cache is null");
+  if (need_kv && (!c->k_pool || !c->v_pool)) return fail(LK_ERR_INVALID_ARG, "k_pool / v_pool is null");
+  if (need_summary && !c->summary_pool) return fail(LK_ERR_INVALID_ARG, "summary_pool is null");
+  if (c->num_phys_pages <= 0) return fail(LK_ERR_INVALID_ARG, "num_phys_pages %d <= 0", c->num_phys_pages);
+  return LK_OK;
+}
+
+lk_status check_table(const lk_cache* c) {
+  if (!c->block_table || !c->seq_lens) return fail(LK_ERR_INVALID_ARG, "block_table / seq_lens is null");
+  if (c->max_pages_per_seq <= 0) return fail(LK_ERR_INVALID_ARG, "max_pages_per_seq %d <= 0", c->max_pages_per_seq);
+  if (c->max_pages_per_seq > kMaxPagesPerSeq)
+    return fail(LK_ERR_UNSUPPORTED, "max_pages_per_seq %d exceeds %d", c->max_pages_per_seq, kMaxPagesPerSeq);
+  return LK_OK;
+}
+
+// Workspace regions.
+struct Layout {
+  size_t page_lse, sel_pages, sel_count, part_o, part_ml, build_list, total;
+  int n_splits;
+};
+
+Layout layout(const Shape& sh, int batch, int max_pages) {
+  Layout L{};
+  const int ns_sparse = (sh.k + kPagesPerSplitSparse - 1) / kPagesPerSplitSparse;
+  const int ns_dense = (max_pages + kPagesPerSplitDense - 1) / kPagesPerSplitDense;
+  L.n_splits = ns_sparse > ns_dense ? ns_sparse : ns_dense;
+  size_t off = 0;
+  L.page_lse = off; off = align_up(off + sizeof(float) * (size_t)batch * sh.hq * max_pages);
+  L.sel_pages = off; off = align_up(off + sizeof(int32_t) * (size_t)batch * sh.hkv * sh.k);
+  L.sel_count = off; off = align_up(off + sizeof(int32_t) * (size_t)batch * sh.hkv);
+  L.part_o = off; off = align_up(off + sizeof(float) * (size_t)batch * sh.hkv * L.n_splits * sh.G * sh.d);
+  L.part_ml = off; off = align_up(off + sizeof(float) * (size_t)batch * sh.hkv * L.n_splits * sh.G * 2);
+  L.build_list = off; off = align_up(off + sizeof(int32_t) * (size_t)batch);
+  L.total = off;
+  return L;
+}
+
+lk_status check_ws(const Layout& L, void* ws, size_t ws_bytes) {
+  if (ws_bytes < L.total) return fail(LK_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, L.total);
+  if (!ws) return fail(LK_ERR_WORKSPACE, "workspace pointer is null");
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return fail(LK_ERR_WORKSPACE, "workspace is not %zu-byte aligned", kAlign);
+  return LK_OK;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+lk_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(LK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+lk_status enqueue_score_select(const Shape& sh, const lk_config* cfg, const lk_cache* c, int batch,
+                               const void* q, float* page_lse, float* share_out, int32_t* sel,
+                               int32_t* cnt, hipStream_t s) {
+  lk::ScoreArgs sa{q, c->summary_pool, c->block_table, c->seq_lens, page_lse,
+                   batch, c->max_pages_per_seq, c->num_phys_pages, sh.hkv, sh.hq, cfg->scale};
+  hipError_t e = lk::launch_score(sh.dt, sh.r, sh.G, sa, s);
+  if (e != hipSuccess) return hip_status(e, "score launch");
+  lk::SelectArgs se{page_lse, share_out, sel, cnt, c->seq_lens, batch, c->max_pages_per_seq,
+                    sh.hkv, sh.G, sh.B, sh.k};
+  return hip_status(lk::launch_select(se, s), "select launch");
+}
+
+lk_status enqueue_attn(const Shape& sh, const lk_config* cfg, const lk_cache* c, int batch,
+                       const void* q, const int32_t* sel, const int32_t* cnt, void* out,
+                       float* lse_out, void* ws, const Layout& L, hipStream_t s) {
+  const bool dense = sel == nullptr;
+  const int pps = dense ? kPagesPerSplitDense : kPagesPerSplitSparse;
+  const int n_splits = dense ? (c->max_pages_per_seq + pps - 1) / pps : (sh.k + pps - 1) / pps;
+  lk::AttnArgs aa{q, c->k_pool, c->v_pool, c->block_table, c->seq_lens, sel, cnt,
+                  at<float>(ws, L.part_o), at<float>(ws, L.part_ml), out, lse_out,
+                  batch, c->max_pages_per_seq, c->num_phys_pages, sh.hkv, sh.hq, sh.k,
+                  n_splits, pps, cfg->scale};
+  return hip_status(lk::launch_attn(sh.dt, sh.G, aa, s), "attention launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lk_summary_record_bytes(const lk_config* cfg) {
+  if (!cfg || cfg->head_dim <= 0 || cfg->page_size <= 0 || cfg->rank <= 0) return 0;
+  const size_t e = cfg->kv_dtype == LK_BF16 ? 2 : (cfg->kv_dtype == LK_F32 ? 4 : 0);
+  const size_t d = cfg->head_dim, B = cfg->page_size, r = cfg->rank;
+  return (d + r * d + B * r) * e;
+}
+
+int32_t lk_page_budget(const lk_config* cfg) {
+  if (!cfg || cfg->page_size <= 0 || cfg->token_budget <= 0) return 0;
+  return (cfg->token_budget + cfg->page_size - 1) / cfg->page_size;
+}
+
+lk_status lk_workspace_size(const lk_config* cfg, int32_t batch, int32_t max_pages_per_seq, size_t* bytes) {
+  Shape sh;
+  lk_status st = check_config(cfg, &sh);
+  if (st != LK_OK) return st;
+  if (!bytes) return fail(LK_ERR_INVALID_ARG, "bytes is null");
+  if (batch <= 0) return fail(LK_ERR_INVALID_ARG, "batch %d <= 0", batch);
+  if (max_pages_per_seq <= 0) return fail(LK_ERR_INVALID_ARG, "max_pages_per_seq %d <= 0", max_pages_per_seq);
+  if (max_pages_per_seq > kMaxPagesPerSeq)
+    return fail(LK_ERR_UNSUPPORTED, "max_pages_per_seq %d exceeds %d", max_pages_per_seq, kMaxPagesPerSeq);
+  *bytes = layout(sh, batch, max_pages_per_seq).total;
+  return ok();
+}
+
+lk_status lk_build_page_summary(const lk_config* cfg, const lk_cache* cache, const int32_t* phys_page_ids,
+                                int32_t n_pages, float* eigvals_out, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  Shape sh;
+  lk_status st = check_config(cfg, &sh);
+  if (st != LK_OK) return st;
+  if (!cache) return fail(LK_ERR_INVALID_ARG, "cache is null");
+  if (!cache->k_pool || !cache->summary_pool) return fail(LK_ERR_INVALID_ARG, "k_pool / summary_pool is null");
+  if (cache->num_phys_pages <= 0) return fail(LK_ERR_INVALID_ARG, "num_phys_pages %d <= 0", cache->num_phys_pages);
+  if (n_pages < 0) return fail(LK_ERR_INVALID_ARG, "n_pages %d < 0", n_pages);
+  if (n_pages > 0 && !phys_page_ids) return fail(LK_ERR_INVALID_ARG, "phys_page_ids is null");
+  if (n_pages == 0) return ok();
+  lk::BuildArgs ba{cache->k_pool, cache->summary_pool, phys_page_ids, eigvals_out, n_pages,
+                   cache->num_phys_pages, sh.hkv};
+  return hip_status(lk::launch_build(sh.dt, sh.r, ba, static_cast<hipStream_t>(stream)), "build launch");
+}
+
+lk_status lk_score_select(const lk_config* cfg, const lk_cache* cache, int32_t batch, const void* q,
+                          float* page_lse_out, float* share_out, int32_t* sel_pages, int32_t* sel_count,
+                          void* ws, size_t ws_bytes, void* stream) {
+  Shape sh;
+  lk_status st = check_config(cfg, &sh);
+  if (st != LK_OK) return st;
+  if ((st = check_cache(cache, false, true)) != LK_OK) return st;
+  if ((st = check_table(cache)) != LK_OK) return st;
+  if (batch <= 0) return fail(LK_ERR_INVALID_ARG, "batch %d <= 0", batch);
+  if (!q || !sel_pages || !sel_count) return fail(LK_ERR_INVALID_ARG, "q / sel_pages / sel_count is null");
+  const Layout L = layout(sh, batch, cache->max_pages_per_seq);
+  if ((st = check_ws(L, ws, ws_bytes)) != LK_OK) return st;
+  float* lse = page_lse_out ? page_lse_out : at<float>(ws, L.page_lse);
+  return enqueue_score_select(sh, cfg, cache, batch, q, lse, share_out, sel_pages, sel_count,
+                              static_cast<hipStream_t>(stream));
+}
+
+lk_status lk_sparse_decode_attn(const lk_config* cfg, const lk_cache* cache, int32_t batch, const void* q,
+                                const int32_t* sel_pages, const int32_t* sel_count, void* out,
+                                float* lse_out, void* ws, size_t ws_bytes, void* stream) {
+  Shape sh;
+  lk_status st = check_config(cfg, &sh);
+  if (st != LK_OK) return st;
+  if ((st = check_cache(cache, true, false)) != LK_OK) return st;
+  if ((st = check_table(cache)) != LK_OK) return st;
+  if (batch <= 0) return fail(LK_ERR_INVALID_ARG, "batch %d <= 0", batch);
+  if (!q || !out || !sel_pages || !sel_count) return fail(LK_ERR_INVALID_ARG, "q / out / sel_pages / sel_count is null");
+  const Layout L = layout(sh, batch, cache->max_pages_per_seq);
+  if ((st = check_ws(L, ws, ws_bytes)) != LK_OK) return st;
+  return enqueue_attn(sh, cfg, cache, batch, q, sel_pages, sel_count, out, lse_out, ws, L,
+                      static_cast<hipStream_t>(stream));
+}
+
+lk_status lk_dense_decode_attn(const lk_config* cfg, const lk_cache* cache, int32_t batch, const void* q,
+                               void* out, float* lse_out, void* ws, size_t ws_bytes, void* stream) {
+  Shape sh;
+  lk_status st = check_config(cfg, &sh);
+  if (st != LK_OK) return st;
+  if ((st = check_cache(cache, true, false)) != LK_OK) return st;
+  if ((st = check_table(cache)) != LK_OK) return st;
+  if (batch <= 0) return fail(LK_ERR_INVALID_ARG, "batch %d <= 0", batch);
+  if (!q || !out) return fail(LK_ERR_INVALID_ARG, "q / out is null");
+  const Layout L = layout(sh, batch, cache->max_pages_per_seq);
+  if ((st = check_ws(L, ws, ws_bytes)) != LK_OK) return st;
+  return enqueue_attn(sh, cfg, cache, batch, q, nullptr, nullptr, out, lse_out, ws, L,
+                      static_cast<hipStream_t>(stream));
+}
+
+lk_status lk_decode_step(const lk_config* cfg, const lk_cache* cache, int32_t batch, const void* q,
+                         const void* k_new, const void* v_new, void* out, float* lse_out,
+                         int32_t* sel_pages, int32_t* sel_count, void* ws, size_t ws_bytes, void* stream) {
+  Shape sh;
+  lk_status st = check_config(cfg, &sh);
+  if (st != LK_OK) return st;
+  if ((st = check_cache(cache, true, true)) != LK_OK) return st;
+  if ((st = check_table(cache)) != LK_OK) return st;
+  if (batch <= 0) return fail(LK_ERR_INVALID_ARG, "batch %d <= 0", batch);
+  if (!q || !k_new || !v_new || !out) return fail(LK_ERR_INVALID_ARG, "q / k_new / v_new / out is null");
+  if ((sel_pages == nullptr) != (sel_count == nullptr))
+    return fail(LK_ERR_INVALID_ARG, "sel_pages and sel_count must both be given or both be null");
+  const Layout L = layout(sh, batch, cache->max_pages_per_seq);
+  if ((st = check_ws(L, ws, ws_bytes)) != LK_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* build_list = at<int32_t>(ws, L.build_list);
+  int32_t* sel = sel_pages ? sel_pages : at<int32_t>(ws, L.sel_pages);
+  int32_t* cnt = sel_count ? sel_count : at<int32_t>(ws, L.sel_count);
+
+  lk::AppendArgs ap{cache->k_pool, cache->v_pool, k_new, v_new, cache->block_table, cache->seq_lens,
+                    build_list, batch, cache->max_pages_per_seq, cache->num_phys_pages, sh.hkv};
+  hipError_t e = lk::launch_append(sh.dt, ap, s);
+  if (e != hipSuccess) return hip_status(e, "append launch");
+  st = enqueue_score_select(sh, cfg, cache, batch, q, at<float>(ws, L.page_lse), nullptr, sel, cnt, s);
+  if (st != LK_OK) return st;
+  st = enqueue_attn(sh, cfg, cache, batch, q, sel, cnt, out, lse_out, ws, L, s);
+  if (st != LK_OK) return st;
+  lk::BuildArgs ba{cache->k_pool, cache->summary_pool, build_list, nullptr, batch,
+                   cache->num_phys_pages, sh.hkv};
+  return hip_status(lk::launch_build(sh.dt, sh.r, ba, s), "build launch");
+}
+
+const char* lk_status_string(lk_status status) {
+  switch (status) {
+    case LK_OK: return "ok";
+    case LK_ERR_INVALID_ARG: return "invalid argument";
+    case LK_ERR_UNSUPPORTED: return "unsupported configuration";
+    case LK_ERR_WORKSPACE: return "workspace missing or too small";
+    case LK_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* lk_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -148,17 +148,17 @@ def keys_values(w: Workload, seq: int, kv_head: int, bases: np.ndarray | None = 
         bases = page_bases(w, seq, kv_head)
     gb = global_basis(w, kv_head)
     n_pages = -(-T // B)
+    f32 = np.float32
     rk = _rng(w.wid, _P_KEYS, seq, kv_head)
-    a = rk.standard_normal((n_pages * B, LOCAL_RANK))
-    b = rk.standard_normal((n_pages * B, GLOBAL_RANK))
-    noise = rk.standard_normal((n_pages * B, d))
-    local = a.reshape(n_pages, B, LOCAL_RANK) @ bases[:n_pages]
-    keys = LOCAL_SCALE * local.reshape(n_pages * B, d)
-    keys += GLOBAL_SCALE * (b @ gb)
-    keys += KEY_NOISE * noise
-    keys = keys[:T]
-    values = _rng(w.wid, _P_VALUES, seq, kv_head).standard_normal((T, d))
-    return keys.astype(np.float32), values.astype(np.float32)
+    a = rk.standard_normal((n_pages * B, LOCAL_RANK), dtype=f32)
+    b = rk.standard_normal((n_pages * B, GLOBAL_RANK), dtype=f32)
+    keys = rk.standard_normal((n_pages * B, d), dtype=f32)
+    keys *= f32(KEY_NOISE)
+    local = a.reshape(n_pages, B, LOCAL_RANK) @ bases[:n_pages].astype(f32)
+    keys += f32(LOCAL_SCALE) * local.reshape(n_pages * B, d)
+    keys += f32(GLOBAL_SCALE) * (b @ gb.astype(f32))
+    values = _rng(w.wid, _P_VALUES, seq, kv_head).standard_normal((T, d), dtype=f32)
+    return keys[:T], values
 
 
 def queries(w: Workload, step: int, seq: int, kv_head: int, seq_len: int,

@@ -16,3 +16,21 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+def _ensure_library():
+    lib = os.path.join(ROOT, "long_context_sparse_page_amd", "liblocks.so")
+    if not os.path.exists(lib):
+        from long_context_sparse_page_amd import build_lib
+        build_lib.build()
+
+
+_ensure_library()
+
+
+@pytest.fixture(scope="session")
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("a GPU test ran without a visible GPU")
+    return torch.device("cuda:0")

@@ -1,0 +1,88 @@
+"""Oracle-side helpers for the parity tests: regenerate one (sequence, KV head)
+from the seeded generator, run the fp64 oracle on it, and the matching rules
+of the decode path (selection sets, page LSE, attention output)."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from long_context_sparse_page_amd import synth
+from long_context_sparse_page_amd.paged import to_storage
+from oracle import locks_oracle as lo
+
+
+def stored(x: np.ndarray, dtype: str) -> np.ndarray:
+    """What a buffer of ``dtype`` holds for fp32 draws ``x``, widened to fp64."""
+    return to_storage(x, dtype).to(torch.float64).numpy()
+
+
+def host_pages(w: synth.Workload, seq: int, kvh: int, T: int):
+    """K, V of one (sequence, KV head) holding T tokens, as stored, in logical
+    page order: fp64 [n_pages, B, d] with unwritten slots zero."""
+    B, d = w.page_size, w.head_dim
+    k, v = synth.keys_values(w, seq, kvh)
+    n_pages = w.pages_needed(seq)
+    K = np.zeros((n_pages * B, d))
+    V = np.zeros((n_pages * B, d))
+    K[:T] = stored(k[:T], w.dtype)
+    V[:T] = stored(v[:T], w.dtype)
+    return K.reshape(n_pages, B, d), V.reshape(n_pages, B, d)
+
+
+def host_queries(w: synth.Workload, step: int, seq_lens) -> np.ndarray:
+    """Queries [batch][Hq][d] as stored (fp64)."""
+    q = np.zeros((w.batch, w.num_q_heads, w.head_dim), dtype=np.float32)
+    for s in range(w.batch):
+        for h in range(w.num_kv_heads):
+            qq, _ = synth.queries(w, step, s, h, seq_lens[s])
+            q[s, h * w.group:(h + 1) * w.group] = qq
+    return stored(q, w.dtype)
+
+
+def q_device(q64: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    t = torch.from_numpy(q64)
+    return (t.to(torch.bfloat16) if dtype == "bf16" else t.to(torch.float32)).to(device)
+
+
+def oracle_summaries(w, K_pages, n_pages):
+    return lo.build_page_summaries(K_pages[:n_pages], w.rank, w.dtype)
+
+
+def oracle_head(w, q_g, K_pages, V_pages, T, summary=None):
+    n_mr = lo.most_recent_page(T, w.page_size)
+    if summary is None:
+        summary = oracle_summaries(w, K_pages, max(n_mr, 0))
+    return lo.decode_head(q_g, K_pages, V_pages, T, summary, w.token_budget, w.scale), summary
+
+
+def selection_mismatch(gpu_sel, ora_sel, m_bar, n_mr, k, rel=1e-4):
+    """The selection matching rule: same size, sink and most-recent present,
+    and every page in the symmetric difference has an oracle share within
+    ``rel`` (relative) of the oracle's cut value.  Returns None if matched,
+    else a message."""
+    g = sorted(int(x) for x in gpu_sel)
+    o = sorted(int(x) for x in ora_sel)
+    if len(g) != len(o):
+        return f"size {len(g)} != {len(o)}: gpu {g} oracle {o}"
+    if g != sorted(set(g)):
+        return f"duplicate pages {g}"
+    if n_mr >= 0 and (0 not in g or n_mr not in g):
+        return f"sink/recent missing: {g} (n_mr {n_mr})"
+    diff = set(g) ^ set(o)
+    if not diff:
+        return None
+    cand = list(range(1, n_mr))
+    n_top = min(k - 2, len(cand))
+    ranked = sorted(cand, key=lambda j: (-m_bar[j], j))
+    cut = m_bar[ranked[n_top - 1]]
+    bad = [j for j in diff if not (1 <= j < n_mr and abs(m_bar[j] - cut) <= rel * cut)]
+    if bad:
+        return (f"pages {sorted(bad)} differ beyond the near-cut band (cut {cut:.6g}, "
+                f"shares {[float(m_bar[j]) for j in sorted(bad) if 0 <= j < len(m_bar)]})")
+    return None
+
+
+def rel_l2(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Per-row ||a - b|| / ||b||."""
+    return np.linalg.norm(a - b, axis=-1) / np.maximum(np.linalg.norm(b, axis=-1), 1e-30)

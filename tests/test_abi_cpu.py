@@ -1,0 +1,160 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function ``include/locks.h`` declares, sizes records and workspaces, and
+rejects bad arguments with the documented status before enqueuing anything.
+
+Every call below that reaches a compute entry point is invalid, so it returns
+from host validation and never launches a kernel (the fake device addresses
+are never dereferenced)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from long_context_sparse_page_amd import locks as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "locks.h")
+FAKE = 0x10000  # never dereferenced: every call using it fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lk_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_library_agree():
+    names = declared_functions()
+    assert set(names) == set(L.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (lk_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    lib = L.library()
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def cfg(**kw):
+    base = dict(head_dim=128, page_size=64, rank=8, num_q_heads=32, num_kv_heads=8, token_budget=2048,
+                kv_dtype=L.LK_BF16, scale=128 ** -0.5)
+    base.update(kw)
+    return L.make_config(**base)
+
+
+def test_record_bytes_and_budget():
+    assert L.lk_summary_record_bytes(cfg()) == 3328            # (128 + 8*128 + 64*8) * 2
+    assert L.lk_summary_record_bytes(cfg(rank=4)) == 1792
+    assert L.lk_summary_record_bytes(cfg(rank=16)) == 6400
+    assert L.lk_summary_record_bytes(cfg(kv_dtype=L.LK_F32)) == 6656
+    assert L.lk_page_budget(cfg()) == 32
+    assert L.lk_page_budget(cfg(token_budget=2049)) == 33
+    assert L.lk_page_budget(cfg(token_budget=256)) == 4
+
+
+def test_workspace_size_scales():
+    a = L.lk_workspace_size(cfg(), 4, 2049)
+    b = L.lk_workspace_size(cfg(), 8, 2049)
+    assert 0 < a < b
+    assert a % 256 == 0
+    # holds at least the page scores and the dense-attention partials
+    assert a >= 4 * 32 * 2049 * 4 + 4 * 8 * ((2049 + 15) // 16) * 4 * 128 * 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), L.LK_ERR_UNSUPPORTED),
+    (dict(page_size=16), L.LK_ERR_UNSUPPORTED),
+    (dict(rank=3), L.LK_ERR_UNSUPPORTED),
+    (dict(rank=0), L.LK_ERR_INVALID_ARG),
+    (dict(num_q_heads=30), L.LK_ERR_INVALID_ARG),
+    (dict(num_q_heads=24), L.LK_ERR_UNSUPPORTED),      # G = 3
+    (dict(token_budget=64), L.LK_ERR_INVALID_ARG),     # k = 1 < 2
+    (dict(token_budget=64 * 2000), L.LK_ERR_UNSUPPORTED),
+    (dict(kv_dtype=7), L.LK_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), L.LK_ERR_INVALID_ARG),
+])
+def test_config_rejected(kw, status):
+    with pytest.raises(L.LocksError) as e:
+        L.lk_workspace_size(cfg(**kw), 1, 16)
+    assert e.value.status == status
+    assert L.lk_last_error() != ""
+
+
+def test_sizes_rejected_and_error_cleared():
+    for batch, pages, st in [(0, 16, L.LK_ERR_INVALID_ARG), (1, 0, L.LK_ERR_INVALID_ARG),
+                             (1, 70000, L.LK_ERR_UNSUPPORTED)]:
+        with pytest.raises(L.LocksError) as e:
+            L.lk_workspace_size(cfg(), batch, pages)
+        assert e.value.status == st
+    L.lk_workspace_size(cfg(), 1, 16)
+    assert L.lk_last_error() == ""
+
+
+def fake_cache(**kw):
+    base = dict(k_pool=FAKE, v_pool=FAKE, summary_pool=FAKE, block_table=FAKE, seq_lens=FAKE,
+                max_pages_per_seq=16, num_phys_pages=16)
+    base.update(kw)
+    return L.lk_cache(**base)
+
+
+def expect(status, fn, *args):
+    with pytest.raises(L.LocksError) as e:
+        fn(*args)
+    assert e.value.status == status, L.lk_last_error()
+
+
+def test_entry_points_reject_bad_arguments():
+    c = cfg()
+    ws_need = L.lk_workspace_size(c, 2, 16)
+    ws = 0x100000  # 256-aligned fake address
+    # null pointers
+    expect(L.LK_ERR_INVALID_ARG, L.lk_score_select, c, fake_cache(), 2, None, None, None, FAKE, FAKE, ws, ws_need, 0)
+    expect(L.LK_ERR_INVALID_ARG, L.lk_score_select, c, fake_cache(summary_pool=None), 2, FAKE, None, None, FAKE,
+           FAKE, ws, ws_need, 0)
+    expect(L.LK_ERR_INVALID_ARG, L.lk_sparse_decode_attn, c, fake_cache(k_pool=None), 2, FAKE, FAKE, FAKE, FAKE,
+           None, ws, ws_need, 0)
+    expect(L.LK_ERR_INVALID_ARG, L.lk_dense_decode_attn, c, fake_cache(block_table=None), 2, FAKE, FAKE, None, ws,
+           ws_need, 0)
+    expect(L.LK_ERR_INVALID_ARG, L.lk_decode_step, c, fake_cache(), 2, FAKE, None, FAKE, FAKE, None, None, None,
+           ws, ws_need, 0)
+    # sel_pages without sel_count
+    expect(L.LK_ERR_INVALID_ARG, L.lk_decode_step, c, fake_cache(), 2, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
+           ws, ws_need, 0)
+    # batch, table sizes
+    expect(L.LK_ERR_INVALID_ARG, L.lk_score_select, c, fake_cache(), 0, FAKE, None, None, FAKE, FAKE, ws, ws_need, 0)
+    expect(L.LK_ERR_INVALID_ARG, L.lk_score_select, c, fake_cache(num_phys_pages=0), 2, FAKE, None, None, FAKE,
+           FAKE, ws, ws_need, 0)
+    # workspace too small / missing / misaligned
+    expect(L.LK_ERR_WORKSPACE, L.lk_score_select, c, fake_cache(), 2, FAKE, None, None, FAKE, FAKE, ws,
+           ws_need - 1, 0)
+    expect(L.LK_ERR_WORKSPACE, L.lk_sparse_decode_attn, c, fake_cache(), 2, FAKE, FAKE, FAKE, FAKE, None, None,
+           ws_need, 0)
+    expect(L.LK_ERR_WORKSPACE, L.lk_dense_decode_attn, c, fake_cache(), 2, FAKE, FAKE, None, ws + 4, ws_need, 0)
+    expect(L.LK_ERR_WORKSPACE, L.lk_decode_step, c, fake_cache(), 2, FAKE, FAKE, FAKE, FAKE, None, None, None,
+           ws, 16, 0)
+    # unsupported config through a compute entry point
+    expect(L.LK_ERR_UNSUPPORTED, L.lk_score_select, cfg(head_dim=96), fake_cache(), 2, FAKE, None, None, FAKE,
+           FAKE, ws, ws_need, 0)
+    # build: negative count, null ids
+    expect(L.LK_ERR_INVALID_ARG, L.lk_build_page_summary, c, fake_cache(), FAKE, -1, None, None, 0, 0)
+    expect(L.LK_ERR_INVALID_ARG, L.lk_build_page_summary, c, fake_cache(), None, 3, None, None, 0, 0)
+    expect(L.LK_ERR_INVALID_ARG, L.lk_build_page_summary, c, fake_cache(summary_pool=None), FAKE, 3, None, None, 0, 0)
+    # null config / cache
+    lib = L.library()
+    assert lib.lk_workspace_size(None, 1, 1, ctypes.byref(ctypes.c_size_t())) == L.LK_ERR_INVALID_ARG
+    assert lib.lk_score_select(ctypes.byref(c), None, 1, FAKE, None, None, FAKE, FAKE, ws, ws_need, 0) == \
+        L.LK_ERR_INVALID_ARG
+
+
+def test_build_with_no_pages_is_a_no_op():
+    # n_pages == 0 is valid and enqueues nothing
+    L.lk_build_page_summary(cfg(), fake_cache(), None, 0, None, None, 0, 0)
+
+
+def test_status_strings():
+    for st in range(5):
+        assert L.lk_status_string(st)
+    assert L.lk_status_string(99) == "unknown status"

@@ -1,0 +1,339 @@
+"""Parity of the HIP decode path with the fp64 oracle (needs an MI355X).
+
+Every case prints its name and shapes before touching the GPU."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_sparse_page_amd import locks as L
+from long_context_sparse_page_amd import synth
+from long_context_sparse_page_amd.paged import DeviceCache, to_storage
+from oracle import locks_oracle as lo
+
+import reference as ref
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def small_bf16(batch=2, ctx=(4096 + 32, 64 * 9 + 17), hq=32, hkv=8, rank=8, budget=512, steps=0):
+    w = synth.workload(1, rank=rank, budget=budget, steps=steps)
+    w.name = "small-bf16"
+    w.batch = batch
+    w.context = list(ctx)[:batch]
+    w.num_q_heads, w.num_kv_heads = hq, hkv
+    return w
+
+
+def run_oracle_all(w, seq_lens, q64, summaries=None):
+    """Oracle decode_head for every (sequence, KV head): dict[(s, h)] ->
+    (HeadStep, summary, K_pages, V_pages)."""
+    res = {}
+    for s in range(w.batch):
+        for h in range(w.num_kv_heads):
+            K, V = ref.host_pages(w, s, h, seq_lens[s])
+            summ = None if summaries is None else summaries[(s, h)]
+            hs, summ = ref.oracle_head(w, q64[s, h * w.group:(h + 1) * w.group], K, V, seq_lens[s], summ)
+            res[(s, h)] = (hs, summ, K, V)
+    return res
+
+
+def upload_oracle_records(dc: DeviceCache, w, summaries):
+    """Write oracle-built summaries into the device summary pool."""
+    for (s, h), summ in summaries.items():
+        n = summ.centroid.shape[0]
+        recs = np.concatenate([summ.centroid, summ.basis.reshape(n, -1), summ.coeffs.reshape(n, -1)], axis=1)
+        phys = torch.from_numpy(dc.block_table_host[s, :n].astype(np.int64)).cuda()
+        dc.summary_pool[phys, h] = to_storage(recs.astype(np.float32), w.dtype).cuda()
+
+
+def check_scores(w, dc, o, res, seq_lens, atol):
+    page_lse = o["page_lse"].cpu().numpy()
+    share = o["share"].cpu().numpy()
+    sel = o["sel"].cpu().numpy()
+    cnt = o["cnt"].cpu().numpy()
+    worst = 0.0
+    for (s, h), (hs, _, _, _) in res.items():
+        n_mr = lo.most_recent_page(seq_lens[s], w.page_size)
+        G = w.group
+        got = page_lse[s, h * G:(h + 1) * G, :n_mr]
+        if n_mr:
+            err = np.abs(got - hs.page_lse).max()
+            worst = max(worst, err)
+            assert err <= atol, f"seq {s} head {h}: page LSE err {err:.3g} > {atol}"
+            np.testing.assert_allclose(share[s, h, :n_mr], hs.m_bar, rtol=5e-3, atol=1e-7)
+        gsel = sel[s, h, :cnt[s, h]]
+        msg = ref.selection_mismatch(gsel, hs.selected, hs.m_bar, n_mr, lo.page_budget(w.token_budget, w.page_size))
+        assert msg is None, f"seq {s} head {h}: {msg}"
+        assert (sel[s, h, cnt[s, h]:] == -1).all()
+    return worst
+
+
+# ----------------------------------------------------------------------------
+def test_build_matches_oracle_fp32(gpu):
+    w = synth.workload(0)
+    say("build fp32 tiny", w.context, "r", w.rank)
+    dc = DeviceCache(w, poison=True)
+    dc.fill_from_synth()
+    ids, ev = dc.build_all(eigvals=True)
+    torch.cuda.synchronize()
+    K, _ = ref.host_pages(w, 0, 0, w.context[0])
+    n = len(ids)
+    summ = lo.build_page_summaries(K[:n], w.rank, "f32")
+    ev = ev.cpu().numpy()[:, 0]
+    lam1 = summ.eigvals[:, :1]
+    assert np.abs(ev - summ.eigvals).max() <= 1e-5 * lam1.max()
+    assert (np.abs(ev - summ.eigvals) <= 1e-5 * lam1).all()
+    recs = dc.summary_pool[torch.tensor(ids, dtype=torch.long, device="cuda"), 0].cpu().numpy().astype(np.float64)
+    d, r, B = w.head_dim, w.rank, w.page_size
+    cen, bas, co = recs[:, :d], recs[:, d:d + r * d].reshape(n, r, d), recs[:, d + r * d:].reshape(n, B, r)
+    np.testing.assert_allclose(cen, summ.centroid, rtol=1e-6, atol=1e-6)
+    gap = (summ.eigvals[:, r - 1] - summ.eigvals[:, r]) / summ.eigvals[:, 0]
+    ok = gap >= 1e-2
+    assert ok.sum() > n // 2
+    sgn = np.sign((bas * summ.basis).sum(axis=2))  # per-mode sign alignment
+    assert (sgn[ok] > 0).all(), "sign convention differs"
+    np.testing.assert_allclose(bas[ok], summ.basis[ok], atol=2e-4)
+    np.testing.assert_allclose(co[ok], summ.coeffs[ok], atol=2e-4 * np.abs(summ.coeffs).max())
+    # invariants on every page: orthonormal basis, captured energy
+    gram = bas @ np.swapaxes(bas, 1, 2)
+    assert np.abs(gram - np.eye(r)).max() < 1e-4
+
+
+def test_score_select_on_oracle_records_fp32(gpu):
+    w = synth.workload(0)
+    say("score/select on oracle records, fp32 tiny")
+    dc = DeviceCache(w, poison=True)
+    dc.fill_from_synth()
+    T = w.context
+    q64 = ref.host_queries(w, 0, T)
+    res = run_oracle_all(w, T, q64)
+    upload_oracle_records(dc, w, {k: v[1] for k, v in res.items()})
+    o = dc.outputs()
+    dc.score_select(ref.q_device(q64, w.dtype), o)
+    torch.cuda.synchronize()
+    worst = check_scores(w, dc, o, res, T, atol=1e-3)
+    say("max page LSE error", worst)
+    assert worst < 1e-4
+
+
+def test_end_to_end_fp32(gpu):
+    w = synth.workload(0)
+    say("end-to-end fp32 tiny")
+    dc = DeviceCache(w, poison=True)
+    dc.fill_from_synth()
+    dc.build_all()
+    T = w.context
+    q64 = ref.host_queries(w, 0, T)
+    qd = ref.q_device(q64, w.dtype)
+    res = run_oracle_all(w, T, q64)
+    o = dc.outputs()
+    dc.score_select(qd, o)
+    dc.sparse_attn(qd, o["sel"], o["cnt"], o)
+    torch.cuda.synchronize()
+    worst = check_scores(w, dc, o, res, T, atol=1e-3)
+    say("max page LSE error", worst)
+    hs, _, K, V = res[(0, 0)]
+    out = o["out"].cpu().numpy().astype(np.float64)[0]
+    assert list(o["sel"][0, 0, :o["cnt"][0, 0]].cpu().numpy()) == list(hs.selected)
+    assert ref.rel_l2(out, hs.out).max() < 1e-5
+    np.testing.assert_allclose(o["lse"].cpu().numpy()[0], hs.lse, atol=1e-5)
+
+
+@pytest.mark.parametrize("dense", [False, True])
+def test_attention_on_oracle_selection_bf16(gpu, dense):
+    w = small_bf16()
+    say("attention bf16 dense" if dense else "attention bf16 on oracle selection", w.context)
+    dc = DeviceCache(w, poison=True)
+    dc.fill_from_synth()
+    T = w.context
+    q64 = ref.host_queries(w, 0, T)
+    qd = ref.q_device(q64, w.dtype)
+    k = lo.page_budget(w.token_budget, w.page_size)
+    sel = np.full((w.batch, w.num_kv_heads, k), -1, dtype=np.int32)
+    cnt = np.zeros((w.batch, w.num_kv_heads), dtype=np.int32)
+    rng = np.random.default_rng(5)
+    expect = {}
+    for s in range(w.batch):
+        n_mr = lo.most_recent_page(T[s], w.page_size)
+        for h in range(w.num_kv_heads):
+            K, V = ref.host_pages(w, s, h, T[s])
+            if dense:
+                pages = np.arange(n_mr + 1)
+            else:
+                top = rng.choice(np.arange(1, n_mr), size=min(k - 2, n_mr - 1), replace=False)
+                pages = np.array(sorted({0, n_mr, *top.tolist()}))
+                sel[s, h, :len(pages)] = pages
+                cnt[s, h] = len(pages)
+            qg = q64[s, h * w.group:(h + 1) * w.group]
+            expect[(s, h)] = lo.attend(qg, lo.gather_tokens(K, pages, T[s], w.page_size),
+                                       lo.gather_tokens(V, pages, T[s], w.page_size), w.scale)
+    o = dc.outputs()
+    if dense:
+        dc.dense_attn(qd, o)
+    else:
+        dc.sparse_attn(qd, torch.from_numpy(sel).cuda(), torch.from_numpy(cnt).cuda(), o)
+    torch.cuda.synchronize()
+    out = o["out"].float().cpu().numpy().astype(np.float64)
+    lse = o["lse"].cpu().numpy()
+    worst = 0.0
+    for (s, h), (eo, el) in expect.items():
+        G = w.group
+        e = ref.rel_l2(out[s, h * G:(h + 1) * G], eo).max()
+        worst = max(worst, e)
+        assert e <= 2e-2
+        np.testing.assert_allclose(lse[s, h * G:(h + 1) * G], el, atol=1e-3)
+    say("max relative L2", worst)
+    assert worst < 5e-3  # bf16 output rounding dominates
+
+
+def test_build_and_score_bf16(gpu):
+    w = small_bf16()
+    say("build + score bf16", w.context, w.num_q_heads, w.num_kv_heads)
+    dc = DeviceCache(w, poison=True)
+    dc.fill_from_synth()
+    T = w.context
+    q64 = ref.host_queries(w, 0, T)
+    qd = ref.q_device(q64, w.dtype)
+    res = run_oracle_all(w, T, q64)
+    # scorer isolation on oracle records
+    upload_oracle_records(dc, w, {k: v[1] for k, v in res.items()})
+    o = dc.outputs()
+    dc.score_select(qd, o)
+    torch.cuda.synchronize()
+    worst_iso = check_scores(w, dc, o, res, T, atol=1e-3)
+    say("scorer isolation: max page LSE error", worst_iso)
+    # end to end: GPU-built records
+    dc.build_all()
+    o = dc.outputs()
+    dc.score_select(qd, o)
+    dc.sparse_attn(qd, o["sel"], o["cnt"], o)
+    torch.cuda.synchronize()
+    page_lse = o["page_lse"].cpu().numpy()
+    errs = []
+    for (s, h), (hs, _, _, _) in res.items():
+        n_mr = lo.most_recent_page(T[s], w.page_size)
+        errs.append(np.abs(page_lse[s, h * w.group:(h + 1) * w.group, :n_mr] - hs.page_lse).ravel())
+    errs = np.concatenate(errs)
+    say("end-to-end bf16 page LSE error: max", errs.max(), "p99.9", np.quantile(errs, 0.999),
+        "frac>1e-3", (errs > 1e-3).mean())
+    assert errs.max() < 1e-2
+
+
+def test_decode_steps_bf16(gpu):
+    """lk_decode_step over many steps (pages complete and are built in-stream)."""
+    w = small_bf16(batch=3, ctx=(64 * 3 - 5, 64 * 7 + 60, 1), steps=70, budget=256)
+    say("decode steps bf16", w.context, "steps", w.steps)
+    dc = DeviceCache(w, poison=True)
+    dc.fill_from_synth()
+    dc.build_all()
+    lens = list(w.context)
+    summaries = {}
+    kvs = {(s, h): synth.keys_values(w, s, h) for s in range(w.batch) for h in range(w.num_kv_heads)}
+    for step in range(w.steps):
+        new_lens = [t + 1 for t in lens]
+        q64 = ref.host_queries(w, step, new_lens)
+        kn = np.stack([np.stack([kvs[(s, h)][0][lens[s]] for h in range(w.num_kv_heads)]) for s in range(w.batch)])
+        vn = np.stack([np.stack([kvs[(s, h)][1][lens[s]] for h in range(w.num_kv_heads)]) for s in range(w.batch)])
+        o = dc.outputs()
+        dc.decode_step(ref.q_device(q64, w.dtype), to_storage(kn, w.dtype).cuda(), to_storage(vn, w.dtype).cuda(), o)
+        torch.cuda.synchronize()
+        assert dc.seq_lens.cpu().tolist() == new_lens
+        lens = new_lens
+        if step % 7 != 0 and step != w.steps - 1:
+            continue
+        say("check step", step, lens)
+        res = run_oracle_all(w, lens, q64)
+        out = o["out"].float().cpu().numpy().astype(np.float64)
+        sel = o["sel"].cpu().numpy()
+        cnt = o["cnt"].cpu().numpy()
+        k = lo.page_budget(w.token_budget, w.page_size)
+        for (s, h), (hs, _, K, V) in res.items():
+            n_mr = lo.most_recent_page(lens[s], w.page_size)
+            gsel = sel[s, h, :cnt[s, h]]
+            msg = ref.selection_mismatch(gsel, hs.selected, hs.m_bar, n_mr, k, rel=2e-2)
+            assert msg is None, f"step {step} seq {s} head {h}: {msg}"
+            pages = hs.selected if sorted(gsel) == sorted(hs.selected) else gsel
+            qg = q64[s, h * w.group:(h + 1) * w.group]
+            eo, _ = lo.attend(qg, lo.gather_tokens(K, pages, lens[s], w.page_size),
+                              lo.gather_tokens(V, pages, lens[s], w.page_size), w.scale)
+            e = ref.rel_l2(out[s, h * w.group:(h + 1) * w.group], eo).max()
+            assert e <= 2e-2, f"step {step} seq {s} head {h}: rel L2 {e}"
+
+
+def test_determinism_bf16(gpu):
+    w = small_bf16()
+    say("bitwise determinism bf16")
+    dc = DeviceCache(w)
+    dc.fill_from_synth()
+    dc.build_all()
+    q64 = ref.host_queries(w, 0, w.context)
+    qd = ref.q_device(q64, w.dtype)
+    outs = []
+    for _ in range(2):
+        o = dc.outputs()
+        dc.score_select(qd, o)
+        dc.sparse_attn(qd, o["sel"], o["cnt"], o)
+        torch.cuda.synchronize()
+        outs.append({k: v.clone() for k, v in o.items()})
+    for key in ("page_lse", "sel", "cnt", "out", "lse"):
+        a, b = outs[0][key], outs[1][key]
+        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.uint8) if b.dtype == torch.bfloat16 else b) or \
+            torch.equal(torch.nan_to_num(a.float()), torch.nan_to_num(b.float())), key
+
+
+@pytest.mark.parametrize("ctx,budget", [((1,), 512), ((64,), 512), ((65,), 512), ((64 * 5 + 3,), 4096),
+                                        ((64 * 4,), 128)])
+def test_edge_lengths_fp32(gpu, ctx, budget):
+    w = synth.workload(0, budget=budget)
+    w.context = list(ctx)
+    say("edge lengths", ctx, "budget", budget)
+    dc = DeviceCache(w, poison=True)
+    dc.fill_from_synth()
+    dc.build_all()
+    T = w.context
+    q64 = np.random.default_rng(3).standard_normal((1, w.num_q_heads, w.head_dim))
+    q64 = ref.stored(q64.astype(np.float32), "f32")
+    qd = ref.q_device(q64, w.dtype)
+    res = run_oracle_all(w, T, q64)
+    o = dc.outputs()
+    dc.score_select(qd, o)
+    dc.sparse_attn(qd, o["sel"], o["cnt"], o)
+    torch.cuda.synchronize()
+    check_scores(w, dc, o, res, T, atol=1e-3)
+    hs = res[(0, 0)][0]
+    out = o["out"].cpu().numpy().astype(np.float64)[0]
+    assert ref.rel_l2(out, hs.out).max() < 1e-5
+
+
+@pytest.mark.parametrize("group,rank", [(1, 4), (2, 16), (8, 1), (4, 2)])
+def test_group_and_rank_variants_fp32(gpu, group, rank):
+    w = synth.workload(0, rank=rank)
+    w.num_q_heads = group
+    w.context = [64 * 20 + 11]
+    say("variant G", group, "r", rank)
+    dc = DeviceCache(w, poison=True)
+    dc.fill_from_synth()
+    dc.build_all()
+    T = w.context
+    q64 = ref.stored(np.random.default_rng(group * 10 + rank).standard_normal((1, group, 128)).astype(np.float32) * 2, "f32")
+    qd = ref.q_device(q64, w.dtype)
+    res = run_oracle_all(w, T, q64)
+    o = dc.outputs()
+    dc.score_select(qd, o)
+    dc.sparse_attn(qd, o["sel"], o["cnt"], o)
+    torch.cuda.synchronize()
+    check_scores(w, dc, o, res, T, atol=1e-3)
+    hs = res[(0, 0)][0]
+    out = o["out"].cpu().numpy().astype(np.float64)[0]
+    assert ref.rel_l2(out, hs.out).max() < 1e-5
