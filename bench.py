@@ -1,0 +1,244 @@
+"""Decode-step throughput of the Locks decode path on one MI355X.
+
+One step = lk_decode_step on one layer's cache: append the new token, score
+every complete page from its summary, share-average and select, attend over
+the selection, merge, and build the summary of a page the append completed.
+Workload: Llama-3.1-8B attention shape (32 query / 8 KV heads, d=128), bf16,
+page 64, rank 8, budget 2048 tokens, 4 sequences at 131,072 tokens.
+
+Several identical layer copies are rotated so that consecutive steps touch
+cold addresses (the per-step working set would otherwise fit the 256 MB
+last-level cache).  Inputs (queries, new keys/values) are resident in HBM
+before timing.  Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=512)
+    p.add_argument("--warmup", type=int, default=64)
+    p.add_argument("--layers", type=int, default=4, help="layer copies rotated across steps")
+    p.add_argument("--kernel-reps", type=int, default=200, help="timed launches of the scorer alone")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_context_sparse_page_amd import locks as L
+    from long_context_sparse_page_amd import synth
+    from long_context_sparse_page_amd.paged import DeviceCache, to_storage
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    total_steps = args.warmup + args.steps
+    per_layer = -(-total_steps // args.layers)
+    w = synth.workload(2, steps=per_layer + 1)
+    B, d, G, hkv, hq = w.page_size, w.head_dim, w.group, w.num_kv_heads, w.num_q_heads
+    e = 2  # bf16
+    t0 = time.time()
+    base = DeviceCache(w)
+    base.fill_from_synth(threads=min(16, os.cpu_count() or 4))
+    base.build_all()
+    torch.cuda.synchronize()
+    print(f"[bench] layer 0 filled and summarized in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    layers = [base]
+    for _ in range(1, args.layers):
+        c = DeviceCache.__new__(DeviceCache)
+        c.__dict__.update(base.__dict__)
+        c.k_pool = base.k_pool.clone()
+        c.v_pool = base.v_pool.clone()
+        c.summary_pool = base.summary_pool.clone()
+        c.seq_lens = base.seq_lens.clone()
+        c.block_table = base.block_table.clone()
+        c.cache = L.make_cache(c.k_pool, c.v_pool, c.summary_pool, c.block_table, c.seq_lens)
+        layers.append(c)
+    ws, ws_bytes = base.ws, base.ws_bytes
+
+    # resident inputs for every step
+    n_var = 16
+    qs, kns, vns = [], [], []
+    for i in range(n_var):
+        lens = [t + 1 + i for t in w.context]
+        q = np.zeros((w.batch, hq, d), np.float32)
+        for s in range(w.batch):
+            for h in range(hkv):
+                q[s, h * G:(h + 1) * G] = synth.queries(w, i, s, h, lens[s])[0]
+        qs.append(to_storage(q, w.dtype).to(dev))
+    rng = np.random.default_rng(7)
+    for i in range(n_var):
+        kns.append(to_storage(rng.standard_normal((w.batch, hkv, d)).astype(np.float32), w.dtype).to(dev))
+        vns.append(to_storage(rng.standard_normal((w.batch, hkv, d)).astype(np.float32), w.dtype).to(dev))
+    out = torch.empty((w.batch, hq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.batch, hq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step(i):
+        c = layers[i % len(layers)]
+        L.lk_decode_step(c.cfg, c.cache, w.batch, qs[i % n_var], kns[i % n_var], vns[i % n_var], out, lse,
+                         None, None, ws, ws_bytes, sp)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.warmup, total_steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+
+    # algorithmic bytes of one step at the lengths reached
+    rec = L.lk_summary_record_bytes(base.cfg)
+    k_pages = L.lk_page_budget(base.cfg)
+    lens_now = [int(x) for x in layers[0].seq_lens.cpu().tolist()]
+
+    def step_bytes(lens):
+        tot = 0
+        for T in lens:
+            n_mr = (T - 1) // B
+            tail = T - n_mr * B
+            n_sel = min(k_pages, n_mr + 1)
+            toks = (n_sel - 1) * B + tail
+            tot += hkv * (n_mr * (rec + 4 * G) + toks * 2 * d * e)
+        tot += w.batch * (2 * hq * d * e + 2 * hkv * d * e * 2)  # q + out, k_new/v_new read + write
+        return tot
+
+    bytes_step = step_bytes(lens_now)
+
+    # dominant kernel: the scorer, timed alone on the same layers (score-only calls)
+    page_lse = torch.empty((w.batch, hq, base.max_pages), dtype=torch.float32, device=dev)
+    def score(i):
+        c = layers[i % len(layers)]
+        L.lk_score_select(c.cfg, c.cache, w.batch, qs[i % n_var], page_lse, None, None, None, ws, ws_bytes, sp)
+    for i in range(8):
+        score(i)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_reps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_reps)]
+    for i in range(args.kernel_reps):
+        starts[i].record(stream)
+        score(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    score_ms = float(np.mean([s.elapsed_time(t) for s, t in zip(starts, ends)]))
+    units = sum(hkv * ((T - 1) // B) for T in lens_now)
+    score_bytes = units * (rec + 4 * G)
+    score_gbs = score_bytes / (score_ms * 1e-3) / 1e9
+
+    # same-GPU dense decode attention over every token
+    def dense(i):
+        c = layers[i % len(layers)]
+        L.lk_dense_decode_attn(c.cfg, c.cache, w.batch, qs[i % n_var], out, lse, ws, ws_bytes, sp)
+    for i in range(4):
+        dense(i)
+    torch.cuda.synchronize()
+    reps = 40
+    ev0.record(stream)
+    for i in range(reps):
+        dense(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    dense_ms = ev0.elapsed_time(ev1) / reps
+    dense_bytes = sum(hkv * T * 2 * d * e for T in lens_now) + w.batch * 2 * hq * d * e
+
+    result = {
+        "metric": "decode-attn steps/s and achieved HBM GB/s at 128K ctx, budget 2048 tok",
+        "value": 1e3 / ms_per_step,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "128K-context decode, batch 4, Llama-3.1-8B attention shape (32 q / 8 KV heads, d=128), "
+                        "bf16 KV, page 64, rank 8, budget 2048 tokens; one step = lk_decode_step on one layer",
+            "global_batch": w.batch, "seq_len": w.context[0], "page_size": B, "rank": w.rank,
+            "token_budget": w.token_budget, "num_q_heads": hq, "num_kv_heads": hkv, "layers_rotated": args.layers,
+            "parallelism": "single GPU",
+        },
+        "achieved_GBps": bytes_step / (ms_per_step * 1e-3) / 1e9,
+        "algorithmic_bytes_per_step": bytes_step,
+        "hbm_frac": bytes_step / (ms_per_step * 1e-3) / 8e12,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "score_kernel (reconstructed page LSE)",
+            "achieved": score_gbs,
+            "peak": 8000.0,
+            "unit": "GB/s",
+            "frac": score_gbs / 8000.0,
+            "traffic": None,
+            "launch_us": score_ms * 1e3,
+            "bytes_per_launch": score_bytes,
+        },
+        "dense_baseline": {"ms": dense_ms, "GBps": dense_bytes / (dense_ms * 1e-3) / 1e9,
+                           "speedup_of_locks_step": dense_ms / ms_per_step},
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, lens_now, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, lens_now, seconds):
+    """The fp64 oracle, single-threaded, on a bounded sample: one (sequence, KV
+    head) pair of the same workload at the same length, its score + share +
+    select + attend timed over repeated steps and scaled to a whole step
+    (batch x KV heads pairs).  Its summary build is not timed."""
+    from threadpoolctl import threadpool_limits
+
+    from long_context_sparse_page_amd import synth
+    from oracle import locks_oracle as lo
+
+    sys.path.insert(0, os.path.join(os.path.dirname(os.path.abspath(__file__)), "tests"))
+    import reference as ref
+
+    T = lens_now[0]
+    with threadpool_limits(limits=1):
+        K, V = ref.host_pages(w, 0, 0, T)
+        n_mr = lo.most_recent_page(T, w.page_size)
+        summ = lo.build_page_summaries(K[:n_mr], w.rank, w.dtype)
+        q64 = ref.host_queries(w, 0, [T] * w.batch)[0, :w.group]
+        n, t0 = 0, time.perf_counter()
+        while True:
+            lo.decode_head(q64, K, V, T, summ, w.token_budget, w.scale)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or n >= 200:
+                break
+    per_pair = el / n
+    pairs = w.batch * w.num_kv_heads
+    return {"value": 1.0 / (per_pair * pairs), "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"1 of {pairs} (sequence, KV head) pairs at {T} tokens, {n} steps of score+share+select+"
+                      f"attend in fp64 ({el:.1f}s), scaled x{pairs} to one step; host has {os.cpu_count()} cores"}
+
+
+if __name__ == "__main__":
+    main()

@@ -79,8 +79,9 @@ typedef enum { LK_F32 = 0, LK_BF16 = 1 } lk_dtype;
  * GQA grouping, per-head token budget b, storage dtype and logit scale. */
 typedef struct {
   int32_t head_dim;      /* d; 128 is supported                              */
-  int32_t page_size;     /* B; 16, 32 or 64                                  */
-  int32_t rank;          /* r; 1 .. 16 (clamped to the page's nonzero modes) */
+  int32_t page_size;     /* B; 64 is supported                               */
+  int32_t rank;          /* r in {1, 2, 4, 8, 16}; modes beyond the page's
+                          * nonzero modes are stored as zeros              */
   int32_t num_q_heads;   /* Hq                                               */
   int32_t num_kv_heads;  /* Hkv; G = Hq / Hkv in {1, 2, 4, 8}                */
   int32_t token_budget;  /* b; k = ceil(b / B) must be >= 2                  */
@@ -139,7 +140,9 @@ lk_status lk_build_page_summary(const lk_config* cfg, const lk_cache* cache,
  * to the lower index), in ascending page order; sel_count = min(k, n_mr + 1)
  * (0 for an empty sequence).  Unused sel_pages slots are set to -1.
  *   page_lse_out  optional; s_hat for j < n_mr (other entries untouched).
- *   share_out     optional; m_bar for j < n_mr (other entries untouched). */
+ *   share_out     optional; m_bar for j < n_mr (other entries untouched).
+ * Score only: with sel_pages and sel_count both NULL, only the page scores are
+ * computed (page_lse_out is then required and share_out must be NULL). */
 lk_status lk_score_select(const lk_config* cfg, const lk_cache* cache,
                           int32_t batch, const void* q, float* page_lse_out,
                           float* share_out, int32_t* sel_pages,

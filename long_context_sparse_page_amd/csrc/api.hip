@@ -217,12 +217,24 @@ lk_status lk_score_select(const lk_config* cfg, const lk_cache* cache, int32_t b
   if ((st = check_cache(cache, false, true)) != LK_OK) return st;
   if ((st = check_table(cache)) != LK_OK) return st;
   if (batch <= 0) return fail(LK_ERR_INVALID_ARG, "batch %d <= 0", batch);
-  if (!q || !sel_pages || !sel_count) return fail(LK_ERR_INVALID_ARG, "q / sel_pages / sel_count is null");
+  if (!q) return fail(LK_ERR_INVALID_ARG, "q is null");
+  const bool score_only = sel_pages == nullptr && sel_count == nullptr;
+  if (score_only && !page_lse_out)
+    return fail(LK_ERR_INVALID_ARG, "score-only call (no sel_pages / sel_count) needs page_lse_out");
+  if (!score_only && (!sel_pages || !sel_count))
+    return fail(LK_ERR_INVALID_ARG, "sel_pages and sel_count must both be given or both be null");
+  if (score_only && share_out)
+    return fail(LK_ERR_INVALID_ARG, "share_out needs the selection outputs");
   const Layout L = layout(sh, batch, cache->max_pages_per_seq);
   if ((st = check_ws(L, ws, ws_bytes)) != LK_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (score_only) {
+    lk::ScoreArgs sa{q, cache->summary_pool, cache->block_table, cache->seq_lens, page_lse_out, batch,
+                     cache->max_pages_per_seq, cache->num_phys_pages, sh.hkv, sh.hq, cfg->scale};
+    return hip_status(lk::launch_score(sh.dt, sh.r, sh.G, sa, s), "score launch");
+  }
   float* lse = page_lse_out ? page_lse_out : at<float>(ws, L.page_lse);
-  return enqueue_score_select(sh, cfg, cache, batch, q, lse, share_out, sel_pages, sel_count,
-                              static_cast<hipStream_t>(stream));
+  return enqueue_score_select(sh, cfg, cache, batch, q, lse, share_out, sel_pages, sel_count, s);
 }
 
 lk_status lk_sparse_decode_attn(const lk_config* cfg, const lk_cache* cache, int32_t batch, const void* q,

@@ -11,6 +11,12 @@ from __future__ import annotations
 import ctypes
 import os
 
+# The library must run on the same HIP runtime as torch (whose allocations and
+# streams it is handed).  torch loads its own libamdhip64 (SONAME
+# libamdhip64.so.7); importing torch first makes liblocks.so bind to that copy
+# instead of loading a second runtime.
+import torch  # noqa: F401
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblocks.so")
 
@@ -105,7 +111,6 @@ def _ptr(x) -> int | None:
 
 def _stream(stream) -> int | None:
     if stream is None:
-        import torch
         return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, int):
         return stream

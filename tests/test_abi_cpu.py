@@ -158,3 +158,11 @@ def test_status_strings():
     for st in range(5):
         assert L.lk_status_string(st)
     assert L.lk_status_string(99) == "unknown status"
+
+
+def test_single_hip_runtime_in_process():
+    """liblocks.so binds to the HIP runtime torch loaded (one libamdhip64 mapped),
+    so torch's streams and allocations are valid in its calls."""
+    maps = open("/proc/self/maps").read()
+    libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(libs) == 1, libs
