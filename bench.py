@@ -33,6 +33,8 @@ def parse():
     p.add_argument("--kernel-reps", type=int, default=200, help="timed launches of the scorer alone")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--copy-bytes", type=int, default=0,
+                   help="also run a plain device copy of this size (counter calibration)")
     return p.parse_args()
 
 
@@ -201,6 +203,16 @@ def main():
         "dense_baseline": {"ms": dense_ms, "GBps": dense_bytes / (dense_ms * 1e-3) / 1e9,
                            "speedup_of_locks_step": dense_ms / ms_per_step},
     }
+
+    if args.copy_bytes:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters scale
+        # the scorer's counters to bytes
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = args.copy_bytes
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, lens_now, args.cpu_seconds)

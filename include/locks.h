@@ -111,7 +111,8 @@ int32_t lk_page_budget(const lk_config* cfg);
 /* Workspace bytes that every entry point below needs for `batch` sequences of
  * up to `max_pages_per_seq` pages.  One workspace of this size serves all of
  * them; it holds intermediate scores, selections and attention partials, and
- * its contents need no initialization. */
+ * its contents need no initialization.  Calls that share a workspace must be
+ * ordered on one stream (concurrent calls on one workspace race). */
 lk_status lk_workspace_size(const lk_config* cfg, int32_t batch,
                             int32_t max_pages_per_seq, size_t* bytes);
 
@@ -171,13 +172,18 @@ lk_status lk_dense_decode_attn(const lk_config* cfg, const lk_cache* cache,
                                void* stream);
 
 /* One whole decode step on `stream` ([Locks] App. E, Fig. E.1):
- *   1. append k_new / v_new at slot T mod B of page T / B, T += 1;
- *   2. score every complete page, share-average, select (as lk_score_select);
+ *   1. append k_new / v_new at slot T mod B of page T / B, so the sequence
+ *      holds T + 1 tokens (done by the scoring kernel before it scores);
+ *   2. score every complete page, share-average, select (as lk_score_select,
+ *      with T + 1 tokens);
  *   3. attend over the selection (as lk_sparse_decode_attn);
  *   4. if the append completed a page, build its summary for every KV head
  *      (as lk_build_page_summary).  That page is this step's most recent page,
  *      so it is attended, not scored, and its summary is first scored by the
- *      next step; the result does not depend on when the build runs.
+ *      next step; the result does not depend on when the build runs.  This
+ *      last kernel also stores seq_lens[seq] = T + 1.
+ * An append whose page is outside the block table (T / B >= max_pages_per_seq
+ * or an invalid entry) writes nothing and leaves seq_lens unchanged.
  * sel_pages / sel_count are optional outputs of step 2. */
 lk_status lk_decode_step(const lk_config* cfg, const lk_cache* cache,
                          int32_t batch, const void* q, const void* k_new,

@@ -14,9 +14,15 @@ namespace {
 
 thread_local std::string g_last_error;
 
-constexpr int kPagesPerSplitSparse = 1;
-constexpr int kPagesPerSplitDense = 16;
-constexpr int kMaxPagesPerSeq = 1024 * 64;   // selection keeps 64 candidates per thread
+// attention: a split is a workgroup of 4 waves; each wave takes this many
+// half pages (32-token units)
+constexpr int kAttnWavesPerSplit = 4;
+constexpr int kUnitsPerWaveSparse = 1;
+constexpr int kUnitsPerWaveDense = 32;
+// the selector holds every page's G scores in registers: 1024 threads x up to
+// 96 / G values (24 pages per thread for G <= 4, 12 for G = 8)
+constexpr int kMaxPagesPerSeq = 1024 * 24;
+int max_pages_for_group(int G) { return G == 8 ? 1024 * 12 : kMaxPagesPerSeq; }
 constexpr int kMaxPageBudget = 1024;
 constexpr size_t kAlign = 256;
 
@@ -89,29 +95,33 @@ lk_status check_cache(const lk_cache* c, bool need_kv, bool need_summary) {
   return LK_OK;
 }
 
-lk_status check_table(const lk_cache* c) {
+lk_status check_table(const lk_cache* c, const Shape& sh) {
   if (!c->block_table || !c->seq_lens) return fail(LK_ERR_INVALID_ARG, "block_table / seq_lens is null");
   if (c->max_pages_per_seq <= 0) return fail(LK_ERR_INVALID_ARG, "max_pages_per_seq %d <= 0", c->max_pages_per_seq);
-  if (c->max_pages_per_seq > kMaxPagesPerSeq)
-    return fail(LK_ERR_UNSUPPORTED, "max_pages_per_seq %d exceeds %d", c->max_pages_per_seq, kMaxPagesPerSeq);
+  const int lim = max_pages_for_group(sh.G);
+  if (c->max_pages_per_seq > lim)
+    return fail(LK_ERR_UNSUPPORTED, "max_pages_per_seq %d exceeds %d (GQA group %d)", c->max_pages_per_seq, lim, sh.G);
   return LK_OK;
 }
 
 // Workspace regions.
 struct Layout {
-  size_t page_lse, sel_pages, sel_count, part_o, part_ml, build_list, total;
+  size_t page_lse, sel_pages, sel_count, sel_phys, part_o, part_ml, build_list, total;
   int n_splits;
 };
 
 Layout layout(const Shape& sh, int batch, int max_pages) {
   Layout L{};
-  const int ns_sparse = (sh.k + kPagesPerSplitSparse - 1) / kPagesPerSplitSparse;
-  const int ns_dense = (max_pages + kPagesPerSplitDense - 1) / kPagesPerSplitDense;
+  const int per_sparse = kAttnWavesPerSplit * kUnitsPerWaveSparse;
+  const int per_dense = kAttnWavesPerSplit * kUnitsPerWaveDense;
+  const int ns_sparse = (2 * sh.k + per_sparse - 1) / per_sparse;
+  const int ns_dense = (2 * max_pages + per_dense - 1) / per_dense;
   L.n_splits = ns_sparse > ns_dense ? ns_sparse : ns_dense;
   size_t off = 0;
   L.page_lse = off; off = align_up(off + sizeof(float) * (size_t)batch * sh.hq * max_pages);
   L.sel_pages = off; off = align_up(off + sizeof(int32_t) * (size_t)batch * sh.hkv * sh.k);
   L.sel_count = off; off = align_up(off + sizeof(int32_t) * (size_t)batch * sh.hkv);
+  L.sel_phys = off; off = align_up(off + sizeof(int32_t) * (size_t)batch * sh.hkv * sh.k);
   L.part_o = off; off = align_up(off + sizeof(float) * (size_t)batch * sh.hkv * L.n_splits * sh.G * sh.d);
   L.part_ml = off; off = align_up(off + sizeof(float) * (size_t)batch * sh.hkv * L.n_splits * sh.G * 2);
   L.build_list = off; off = align_up(off + sizeof(int32_t) * (size_t)batch);
@@ -136,28 +146,31 @@ lk_status hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// Score (+ the decode step's append when app.k_new is set) and select.
 lk_status enqueue_score_select(const Shape& sh, const lk_config* cfg, const lk_cache* c, int batch,
                                const void* q, float* page_lse, float* share_out, int32_t* sel,
-                               int32_t* cnt, hipStream_t s) {
+                               int32_t* cnt, int32_t* sel_phys, int len_add, const lk::AppendDuty& app,
+                               hipStream_t s) {
   lk::ScoreArgs sa{q, c->summary_pool, c->block_table, c->seq_lens, page_lse,
-                   batch, c->max_pages_per_seq, c->num_phys_pages, sh.hkv, sh.hq, cfg->scale};
+                   batch, c->max_pages_per_seq, c->num_phys_pages, sh.hkv, sh.hq, cfg->scale, len_add, app};
   hipError_t e = lk::launch_score(sh.dt, sh.r, sh.G, sa, s);
   if (e != hipSuccess) return hip_status(e, "score launch");
   lk::SelectArgs se{page_lse, share_out, sel, cnt, c->seq_lens, batch, c->max_pages_per_seq,
-                    sh.hkv, sh.G, sh.B, sh.k};
+                    sh.hkv, sh.G, sh.B, sh.k, len_add, c->block_table, sel_phys, c->num_phys_pages};
   return hip_status(lk::launch_select(se, s), "select launch");
 }
 
 lk_status enqueue_attn(const Shape& sh, const lk_config* cfg, const lk_cache* c, int batch,
-                       const void* q, const int32_t* sel, const int32_t* cnt, void* out,
-                       float* lse_out, void* ws, const Layout& L, hipStream_t s) {
+                       const void* q, const int32_t* sel, const int32_t* cnt, const int32_t* sel_phys,
+                       void* out, float* lse_out, void* ws, const Layout& L, int len_add, hipStream_t s) {
   const bool dense = sel == nullptr;
-  const int pps = dense ? kPagesPerSplitDense : kPagesPerSplitSparse;
-  const int n_splits = dense ? (c->max_pages_per_seq + pps - 1) / pps : (sh.k + pps - 1) / pps;
-  lk::AttnArgs aa{q, c->k_pool, c->v_pool, c->block_table, c->seq_lens, sel, cnt,
+  const int ups = dense ? kUnitsPerWaveDense : kUnitsPerWaveSparse;
+  const int per = kAttnWavesPerSplit * ups;
+  const int n_splits = dense ? (2 * c->max_pages_per_seq + per - 1) / per : (2 * sh.k + per - 1) / per;
+  lk::AttnArgs aa{q, c->k_pool, c->v_pool, c->block_table, c->seq_lens, sel, cnt, sel_phys,
                   at<float>(ws, L.part_o), at<float>(ws, L.part_ml), out, lse_out,
                   batch, c->max_pages_per_seq, c->num_phys_pages, sh.hkv, sh.hq, sh.k,
-                  n_splits, pps, cfg->scale};
+                  n_splits, ups, cfg->scale, len_add};
   return hip_status(lk::launch_attn(sh.dt, sh.G, aa, s), "attention launch");
 }
 
@@ -184,8 +197,9 @@ lk_status lk_workspace_size(const lk_config* cfg, int32_t batch, int32_t max_pag
   if (!bytes) return fail(LK_ERR_INVALID_ARG, "bytes is null");
   if (batch <= 0) return fail(LK_ERR_INVALID_ARG, "batch %d <= 0", batch);
   if (max_pages_per_seq <= 0) return fail(LK_ERR_INVALID_ARG, "max_pages_per_seq %d <= 0", max_pages_per_seq);
-  if (max_pages_per_seq > kMaxPagesPerSeq)
-    return fail(LK_ERR_UNSUPPORTED, "max_pages_per_seq %d exceeds %d", max_pages_per_seq, kMaxPagesPerSeq);
+  if (max_pages_per_seq > max_pages_for_group(sh.G))
+    return fail(LK_ERR_UNSUPPORTED, "max_pages_per_seq %d exceeds %d (GQA group %d)", max_pages_per_seq,
+                max_pages_for_group(sh.G), sh.G);
   *bytes = layout(sh, batch, max_pages_per_seq).total;
   return ok();
 }
@@ -204,7 +218,7 @@ lk_status lk_build_page_summary(const lk_config* cfg, const lk_cache* cache, con
   if (n_pages > 0 && !phys_page_ids) return fail(LK_ERR_INVALID_ARG, "phys_page_ids is null");
   if (n_pages == 0) return ok();
   lk::BuildArgs ba{cache->k_pool, cache->summary_pool, phys_page_ids, eigvals_out, n_pages,
-                   cache->num_phys_pages, sh.hkv};
+                   cache->num_phys_pages, sh.hkv, nullptr, nullptr, 0};
   return hip_status(lk::launch_build(sh.dt, sh.r, ba, static_cast<hipStream_t>(stream)), "build launch");
 }
 
@@ -215,7 +229,7 @@ lk_status lk_score_select(const lk_config* cfg, const lk_cache* cache, int32_t b
   lk_status st = check_config(cfg, &sh);
   if (st != LK_OK) return st;
   if ((st = check_cache(cache, false, true)) != LK_OK) return st;
-  if ((st = check_table(cache)) != LK_OK) return st;
+  if ((st = check_table(cache, sh)) != LK_OK) return st;
   if (batch <= 0) return fail(LK_ERR_INVALID_ARG, "batch %d <= 0", batch);
   if (!q) return fail(LK_ERR_INVALID_ARG, "q is null");
   const bool score_only = sel_pages == nullptr && sel_count == nullptr;
@@ -230,11 +244,13 @@ lk_status lk_score_select(const lk_config* cfg, const lk_cache* cache, int32_t b
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (score_only) {
     lk::ScoreArgs sa{q, cache->summary_pool, cache->block_table, cache->seq_lens, page_lse_out, batch,
-                     cache->max_pages_per_seq, cache->num_phys_pages, sh.hkv, sh.hq, cfg->scale};
+                     cache->max_pages_per_seq, cache->num_phys_pages, sh.hkv, sh.hq, cfg->scale, 0,
+                     lk::AppendDuty{}};
     return hip_status(lk::launch_score(sh.dt, sh.r, sh.G, sa, s), "score launch");
   }
   float* lse = page_lse_out ? page_lse_out : at<float>(ws, L.page_lse);
-  return enqueue_score_select(sh, cfg, cache, batch, q, lse, share_out, sel_pages, sel_count, s);
+  return enqueue_score_select(sh, cfg, cache, batch, q, lse, share_out, sel_pages, sel_count, nullptr, 0,
+                              lk::AppendDuty{}, s);
 }
 
 lk_status lk_sparse_decode_attn(const lk_config* cfg, const lk_cache* cache, int32_t batch, const void* q,
@@ -244,12 +260,12 @@ lk_status lk_sparse_decode_attn(const lk_config* cfg, const lk_cache* cache, int
   lk_status st = check_config(cfg, &sh);
   if (st != LK_OK) return st;
   if ((st = check_cache(cache, true, false)) != LK_OK) return st;
-  if ((st = check_table(cache)) != LK_OK) return st;
+  if ((st = check_table(cache, sh)) != LK_OK) return st;
   if (batch <= 0) return fail(LK_ERR_INVALID_ARG, "batch %d <= 0", batch);
   if (!q || !out || !sel_pages || !sel_count) return fail(LK_ERR_INVALID_ARG, "q / out / sel_pages / sel_count is null");
   const Layout L = layout(sh, batch, cache->max_pages_per_seq);
   if ((st = check_ws(L, ws, ws_bytes)) != LK_OK) return st;
-  return enqueue_attn(sh, cfg, cache, batch, q, sel_pages, sel_count, out, lse_out, ws, L,
+  return enqueue_attn(sh, cfg, cache, batch, q, sel_pages, sel_count, nullptr, out, lse_out, ws, L, 0,
                       static_cast<hipStream_t>(stream));
 }
 
@@ -259,12 +275,12 @@ lk_status lk_dense_decode_attn(const lk_config* cfg, const lk_cache* cache, int3
   lk_status st = check_config(cfg, &sh);
   if (st != LK_OK) return st;
   if ((st = check_cache(cache, true, false)) != LK_OK) return st;
-  if ((st = check_table(cache)) != LK_OK) return st;
+  if ((st = check_table(cache, sh)) != LK_OK) return st;
   if (batch <= 0) return fail(LK_ERR_INVALID_ARG, "batch %d <= 0", batch);
   if (!q || !out) return fail(LK_ERR_INVALID_ARG, "q / out is null");
   const Layout L = layout(sh, batch, cache->max_pages_per_seq);
   if ((st = check_ws(L, ws, ws_bytes)) != LK_OK) return st;
-  return enqueue_attn(sh, cfg, cache, batch, q, nullptr, nullptr, out, lse_out, ws, L,
+  return enqueue_attn(sh, cfg, cache, batch, q, nullptr, nullptr, nullptr, out, lse_out, ws, L, 0,
                       static_cast<hipStream_t>(stream));
 }
 
@@ -275,7 +291,7 @@ lk_status lk_decode_step(const lk_config* cfg, const lk_cache* cache, int32_t ba
   lk_status st = check_config(cfg, &sh);
   if (st != LK_OK) return st;
   if ((st = check_cache(cache, true, true)) != LK_OK) return st;
-  if ((st = check_table(cache)) != LK_OK) return st;
+  if ((st = check_table(cache, sh)) != LK_OK) return st;
   if (batch <= 0) return fail(LK_ERR_INVALID_ARG, "batch %d <= 0", batch);
   if (!q || !k_new || !v_new || !out) return fail(LK_ERR_INVALID_ARG, "q / k_new / v_new / out is null");
   if ((sel_pages == nullptr) != (sel_count == nullptr))
@@ -287,16 +303,19 @@ lk_status lk_decode_step(const lk_config* cfg, const lk_cache* cache, int32_t ba
   int32_t* sel = sel_pages ? sel_pages : at<int32_t>(ws, L.sel_pages);
   int32_t* cnt = sel_count ? sel_count : at<int32_t>(ws, L.sel_count);
 
-  lk::AppendArgs ap{cache->k_pool, cache->v_pool, k_new, v_new, cache->block_table, cache->seq_lens,
-                    build_list, batch, cache->max_pages_per_seq, cache->num_phys_pages, sh.hkv};
-  hipError_t e = lk::launch_append(sh.dt, ap, s);
-  if (e != hipSuccess) return hip_status(e, "append launch");
-  st = enqueue_score_select(sh, cfg, cache, batch, q, at<float>(ws, L.page_lse), nullptr, sel, cnt, s);
+  // 1-2) append (done by the scorer's prologue) + score + select, all with T + 1
+  lk::AppendDuty app{cache->k_pool, cache->v_pool, k_new, v_new, build_list};
+  int32_t* sel_phys = at<int32_t>(ws, L.sel_phys);
+  st = enqueue_score_select(sh, cfg, cache, batch, q, at<float>(ws, L.page_lse), nullptr, sel, cnt, sel_phys, 1,
+                            app, s);
   if (st != LK_OK) return st;
-  st = enqueue_attn(sh, cfg, cache, batch, q, sel, cnt, out, lse_out, ws, L, s);
+  // 3) attention over the selection (split + merge)
+  st = enqueue_attn(sh, cfg, cache, batch, q, sel, cnt, sel_phys, out, lse_out, ws, L, 1, s);
   if (st != LK_OK) return st;
+  // 4) summaries of pages the append completed; the stored lengths advance here
   lk::BuildArgs ba{cache->k_pool, cache->summary_pool, build_list, nullptr, batch,
-                   cache->num_phys_pages, sh.hkv};
+                   cache->num_phys_pages, sh.hkv, cache->seq_lens, cache->block_table,
+                   cache->max_pages_per_seq};
   return hip_status(lk::launch_build(sh.dt, sh.r, ba, s), "build launch");
 }
 

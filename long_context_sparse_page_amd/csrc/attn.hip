@@ -6,15 +6,18 @@
 // only (the most recent page contributes its filled slots); App. E, Stage B.
 // All G query heads of a KV head read each K/V page once.
 //
-// Split kernel: one wave per (sequence, KV head, split); a split is a run of
-// consecutive entries of the page list.  Lane (sg = lane / 8, e = lane % 8)
-// owns dims 16e..16e+15 of tokens sg, sg+8, ..., so K and V are read with
-// coalesced 16-byte loads (eight tokens x 256 bytes per instruction).  q . k is
+// Split kernel: a workgroup of 4 waves per (sequence, KV head, split); each
+// wave takes a run of consecutive half pages of the page list (32 tokens each).  Lane
+// (sg = lane / 8, e = lane % 8) owns dims 16e..16e+15 of tokens sg, sg+8, ...,
+// so K and V are read with coalesced 16-byte loads (eight tokens x 256 bytes
+// per instruction), both issued before any arithmetic.  q . k is
 // summed over the 8 lanes of a token group with DPP; every lane then runs its
 // own online softmax over its tokens (running max m, sum l, output o), and
 // the 8 token groups are combined at the end of the split.
-// Merge kernel: per (sequence, query head), o = sum_s e^{m_s - M} o_s /
-// sum_s e^{m_s - M} l_s and lse = M + log sum_s e^{m_s - M} l_s.
+// The 4 waves' results are combined in LDS into one partial per workgroup;
+// a merge kernel then combines a (sequence, KV head)'s partials for all G
+// heads: o = sum_s e^{m_s - M} o_s / sum_s e^{m_s - M} l_s and
+// lse = M + log sum_s e^{m_s - M} l_s.
 
 #include "common.cuh"
 #include "kernels.h"
@@ -72,36 +75,47 @@ template <> struct KV16<float> {
   }
 };
 
+constexpr int kAttnWaves = 4;
+
 template <typename T, int G>
-__global__ __launch_bounds__(kWave) void attn_split_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs a) {
   constexpr int B = 64;
   constexpr int D = kHeadDim;
   constexpr int TG = 8;               // token groups per wave
-  constexpr int TPG = B / TG;         // tokens per group per page
-  const int lane = threadIdx.x;
+  constexpr int HALF = B / 2;         // tokens per unit (half a page)
+  constexpr int TPG = HALF / TG;      // tokens per group per unit
+  __shared__ float s_m[kAttnWaves][G], s_l[kAttnWaves][G];
+  __shared__ float s_o[kAttnWaves][G][D];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
   const int sg = lane >> 3;
   const int e = lane & 7;
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
   const int seq = blockIdx.z;
 
-  const int len = a.seq_lens[seq];
+  const int len = a.seq_lens[seq] + a.len_add;
   int n_mr = len > 0 ? (len - 1) / B : -1;
   if (n_mr > a.max_pages - 1) n_mr = a.max_pages - 1;
   int n_list;
   const int32_t* list = nullptr;
+  const int32_t* plist = nullptr;  // physical pages of list (else looked up)
   if (len <= 0) {
     n_list = 0;
   } else if (a.sel_pages) {
     list = a.sel_pages + ((size_t)seq * a.hkv + kvh) * a.k;
+    if (a.sel_phys) plist = a.sel_phys + ((size_t)seq * a.hkv + kvh) * a.k;
     n_list = min(a.sel_count[(size_t)seq * a.hkv + kvh], a.k);
   } else {
     n_list = n_mr + 1;
   }
-  const int i0 = split * a.pages_per_split;
-  const int i1 = min(i0 + a.pages_per_split, n_list);
+  // units are half pages: unit u is half (u & 1) of list entry u >> 1; wave w
+  // of split s takes units [(4 s + w) * ups, +ups)
+  const int ups = a.pages_per_split;
+  const int u0 = (split * kAttnWaves + wave) * ups;
+  const int u1 = min(u0 + ups, 2 * n_list);
 
-  // query slices (dims 16e..16e+15) of the group's G heads
   const T* qp = reinterpret_cast<const T*>(a.q) + ((size_t)seq * a.hq + (size_t)kvh * G) * D + e * 16;
   QSliceBF16 qb[G];
   float qf[G][16];
@@ -126,163 +140,209 @@ __global__ __launch_bounds__(kWave) void attn_split_kernel(AttnArgs a) {
   const float zscale = a.scale * kLog2e;
   const int32_t* bt = a.block_table + (size_t)seq * a.max_pages;
 
-  for (int i = i0; i < i1; ++i) {
-    const int pg = list ? list[i] : i;
+  for (int u = u0; u < u1; ++u) {
+    const int pg = list ? list[u >> 1] : (u >> 1);
     if (pg < 0 || pg > n_mr) continue;
-    const int phys = bt[pg];
+    const int phys = plist ? plist[u >> 1] : bt[pg];
     if (phys < 0 || phys >= a.num_phys) continue;
-    const int n_tok = (pg == n_mr) ? len - n_mr * B : B;
-    const size_t base = (((size_t)phys * a.hkv + kvh) * B) * D + e * 16;
+    const int t_base = (u & 1) * HALF;
+    const int n_tok = ((pg == n_mr) ? len - n_mr * B : B) - t_base;  // tokens from t_base on
+    if (n_tok <= 0) continue;
+    const size_t base = (((size_t)phys * a.hkv + kvh) * B + t_base) * D + e * 16;
     const T* Kp = reinterpret_cast<const T*>(a.k_pool) + base;
     const T* Vp = reinterpret_cast<const T*>(a.v_pool) + base;
 
-    KV16<T> kr[TPG];
+    KV16<T> kr[TPG], vr[TPG];
 #pragma unroll
-    for (int u = 0; u < TPG; ++u) {
-      const int t = sg + TG * u;
-      if (t < n_tok) kr[u].load(Kp + (size_t)t * D); else kr[u].zero();
+    for (int x = 0; x < TPG; ++x) {
+      const int t = sg + TG * x;
+      if (t < n_tok) { kr[x].load(Kp + (size_t)t * D); vr[x].load(Vp + (size_t)t * D); }
+      else { kr[x].zero(); vr[x].zero(); }
     }
     float z[TPG][G];
 #pragma unroll
-    for (int u = 0; u < TPG; ++u) {
+    for (int x = 0; x < TPG; ++x) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float acc;
         if constexpr (sizeof(T) == 2) {
-          acc = qb[g].dot(kr[u].a, kr[u].b);
+          acc = qb[g].dot(kr[x].a, kr[x].b);
         } else {
           float kx[16];
-          kr[u].to_f32(kx);
+          kr[x].to_f32(kx);
           acc = 0.f;
 #pragma unroll
-          for (int x = 0; x < 16; ++x) acc = fmaf(qf[g][x], kx[x], acc);
+          for (int y = 0; y < 16; ++y) acc = fmaf(qf[g][y], kx[y], acc);
         }
-        z[u][g] = acc;
+        z[x][g] = acc;
       }
     }
 #pragma unroll
-    for (int u = 0; u < TPG; ++u)
+    for (int x = 0; x < TPG; ++x)
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float full = group_sum<8>(z[u][g]);
-        z[u][g] = (sg + TG * u < n_tok) ? full * zscale : -INFINITY;
+        const float full = group_sum<8>(z[x][g]);
+        z[x][g] = (sg + TG * x < n_tok) ? full * zscale : -INFINITY;
       }
-
-    KV16<T> vr[TPG];
-#pragma unroll
-    for (int u = 0; u < TPG; ++u) {
-      const int t = sg + TG * u;
-      if (t < n_tok) vr[u].load(Vp + (size_t)t * D); else vr[u].zero();
-    }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float pm = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < TPG; ++u) pm = fmaxf(pm, z[u][g]);
+      for (int x = 0; x < TPG; ++x) pm = fmaxf(pm, z[x][g]);
       const float m_new = fmaxf(m[g], pm);
       if (m_new == -INFINITY) continue;  // no token of this lane yet
       const float corr = fast_exp2(m[g] - m_new);
       m[g] = m_new;
       l[g] *= corr;
 #pragma unroll
-      for (int x = 0; x < 16; ++x) o[g][x] *= corr;
+      for (int y = 0; y < 16; ++y) o[g][y] *= corr;
 #pragma unroll
-      for (int u = 0; u < TPG; ++u) {
-        const float p = fast_exp2(z[u][g] - m_new);
+      for (int x = 0; x < TPG; ++x) {
+        const float p = fast_exp2(z[x][g] - m_new);
         l[g] += p;
         float vx[16];
-        vr[u].to_f32(vx);
+        vr[x].to_f32(vx);
 #pragma unroll
-        for (int x = 0; x < 16; ++x) o[g][x] = fmaf(p, vx[x], o[g][x]);
+        for (int y = 0; y < 16; ++y) o[g][y] = fmaf(p, vx[y], o[g][y]);
       }
     }
   }
 
-  // combine the 8 token groups (lanes e, e+8, ..., e+56)
+  // combine the 8 token groups of this wave (lanes e, e+8, ..., e+56)
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     float M = fmaxf(m[g], dpp<kDppRor8>(m[g]));
-    M = fmaxf(M, __shfl_xor(M, 16));
-    M = fmaxf(M, __shfl_xor(M, 32));
+    M = xor32_max(xor16_max(M));
     const float f = (M == -INFINITY) ? 0.f : fast_exp2(m[g] - M);
     float lg = l[g] * f;
     lg += dpp<kDppRor8>(lg);
-    lg += __shfl_xor(lg, 16);
-    lg += __shfl_xor(lg, 32);
+    lg = xor32_sum(xor16_sum(lg));
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      float v = o[g][x] * f;
+    for (int y = 0; y < 16; ++y) {
+      float v = o[g][y] * f;
       v += dpp<kDppRor8>(v);
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      o[g][x] = v;
+      o[g][y] = xor32_sum(xor16_sum(v));
     }
     m[g] = M;
     l[g] = lg;
   }
-  const size_t pidx = ((size_t)seq * a.hkv + kvh) * a.n_splits + split;
+  // combine the workgroup's waves through LDS into one partial per workgroup
   if (sg == 0) {
-    float* po = a.part_o + pidx * G * D + e * 16;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float4* dst = reinterpret_cast<float4*>(po + (size_t)g * D);
+    for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int x = 0; x < 4; ++x) dst[x] = make_float4(o[g][4 * x], o[g][4 * x + 1], o[g][4 * x + 2], o[g][4 * x + 3]);
-    }
-    if (e == 0) {
+      for (int y = 0; y < 16; ++y) s_o[wave][g][e * 16 + y] = o[g][y];
+  }
+  if (lane == 0) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        a.part_ml[(pidx * G + g) * 2 + 0] = m[g];
-        a.part_ml[(pidx * G + g) * 2 + 1] = l[g];
+    for (int g = 0; g < G; ++g) { s_m[wave][g] = m[g]; s_l[wave][g] = l[g]; }
+  }
+  __syncthreads();
+  const size_t pidx = ((size_t)seq * a.hkv + kvh) * a.n_splits + split;
+  for (int x = threadIdx.x; x < G * D; x += kAttnWaves * kWave) {
+    const int g = x / D, dim = x % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, s_m[w][g]);
+    float ov = 0.f, lv = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w) {
+        const float f = s_m[w][g] == -INFINITY ? 0.f : fast_exp2(s_m[w][g] - M);
+        ov = fmaf(f, s_o[w][g][dim], ov);
+        lv = fmaf(f, s_l[w][g], lv);
       }
     }
-  }
-}
-
-template <typename T>
-__global__ __launch_bounds__(kWave) void attn_merge_kernel(AttnArgs a, int group) {
-  constexpr int D = kHeadDim;
-  const int h = blockIdx.x;
-  const int seq = blockIdx.y;
-  const int kvh = h / group;
-  const int g = h % group;
-  const int lane = threadIdx.x;
-  const size_t pbase = ((size_t)seq * a.hkv + kvh) * a.n_splits;
-  float M = -INFINITY;
-  for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, a.part_ml[((pbase + s) * group + g) * 2]);
-  float L = 0.f, o0 = 0.f, o1 = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < a.n_splits; ++s) {
-      const float ms = a.part_ml[((pbase + s) * group + g) * 2];
-      if (ms == -INFINITY) continue;
-      const float w = fast_exp2(ms - M);
-      L = fmaf(w, a.part_ml[((pbase + s) * group + g) * 2 + 1], L);
-      const float2 ov = reinterpret_cast<const float2*>(a.part_o + ((pbase + s) * group + g) * D)[lane];
-      o0 = fmaf(w, ov.x, o0);
-      o1 = fmaf(w, ov.y, o1);
+    a.part_o[(pidx * G + g) * D + dim] = ov;
+    if (dim == 0) {
+      a.part_ml[(pidx * G + g) * 2 + 0] = M;
+      a.part_ml[(pidx * G + g) * 2 + 1] = lv;
     }
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  T* out = reinterpret_cast<T*>(a.out) + ((size_t)seq * a.hq + h) * D + 2 * lane;
-  Elem<T>::store(out, o0 * inv);
-  Elem<T>::store(out + 1, o1 * inv);
-  if (a.lse_out && lane == 0)
-    a.lse_out[(size_t)seq * a.hq + h] = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+
+}
+
+// Merge: one workgroup per (sequence, KV head) combines the split partials of
+// all G heads: o = sum_s e^{m_s - M} o_s / sum_s e^{m_s - M} l_s and
+// lse = M + log sum_s e^{m_s - M} l_s.
+template <typename T, int G>
+__global__ __launch_bounds__(kAttnWaves * kWave) void attn_merge_kernel(AttnArgs a) {
+  constexpr int D = kHeadDim;
+  constexpr int MAXS = 256;  // splits whose weights fit in LDS per pass
+  __shared__ float s_w[MAXS][G];
+  __shared__ float s_M[G], s_L[G];
+  const int kvh = blockIdx.x;
+  const int seq = blockIdx.y;
+  const float* ml = a.part_ml + ((size_t)seq * a.hkv + kvh) * a.n_splits * G * 2;
+  const float* ob = a.part_o + ((size_t)seq * a.hkv + kvh) * a.n_splits * G * D;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid & (kWave - 1);
+  // per-head maximum over the splits (wave g reduces head g; G <= 8 heads in 4 waves)
+  for (int g = wave; g < G; g += kAttnWaves) {
+    float mx = -INFINITY;
+    for (int s0 = lane; s0 < a.n_splits; s0 += kWave) mx = fmaxf(mx, ml[((size_t)s0 * G + g) * 2]);
+    mx = group_max<kWave>(mx);
+    if (lane == 0) { s_M[g] = mx; s_L[g] = 0.f; }
+  }
+  __syncthreads();
+  constexpr int NSLOT = (G * D + kAttnWaves * kWave - 1) / (kAttnWaves * kWave);
+  float acc[NSLOT], lacc[NSLOT];
+#pragma unroll
+  for (int x = 0; x < NSLOT; ++x) acc[x] = lacc[x] = 0.f;
+  for (int base = 0; base < a.n_splits; base += MAXS) {
+    const int n = min(MAXS, a.n_splits - base);
+    // weights e^{m_s - M} of this pass's splits
+    for (int x = tid; x < n * G; x += kAttnWaves * kWave) {
+      const int s0 = x / G, g = x % G;
+      const float ms = ml[((size_t)(base + s0) * G + g) * 2];
+      s_w[s0][g] = (ms == -INFINITY || s_M[g] == -INFINITY) ? 0.f : fast_exp2(ms - s_M[g]);
+    }
+    __syncthreads();
+    for (int x = tid, slot = 0; x < G * D; x += kAttnWaves * kWave, ++slot) {
+      const int g = x / D, dim = x % D;
+      float ov = 0.f, lv = 0.f;
+#pragma unroll 16
+      for (int s0 = 0; s0 < n; ++s0) {
+        const float w = s_w[s0][g];
+        ov = fmaf(w, ob[((size_t)(base + s0) * G + g) * D + dim], ov);
+        if (dim == 0) lv = fmaf(w, ml[((size_t)(base + s0) * G + g) * 2 + 1], lv);
+      }
+      acc[slot] += ov;
+      lacc[slot] += lv;
+    }
+    __syncthreads();
+  }
+  for (int x = tid, slot = 0; x < G * D; x += kAttnWaves * kWave, ++slot) {
+    const int dim = x % D;
+    if (dim == 0) s_L[x / D] = lacc[slot];
+  }
+  __syncthreads();
+  for (int x = tid, slot = 0; x < G * D; x += kAttnWaves * kWave, ++slot) {
+    const int g = x / D, dim = x % D;
+    const float L = s_L[g];
+    const int h = kvh * G + g;
+    Elem<T>::store(reinterpret_cast<T*>(a.out) + ((size_t)seq * a.hq + h) * D + dim, L > 0.f ? acc[slot] / L : 0.f);
+    if (a.lse_out && dim == 0)
+      a.lse_out[(size_t)seq * a.hq + h] = L > 0.f ? (s_M[g] + fast_log2(L)) * kLn2 : -INFINITY;
+  }
 }
 
 template <typename T>
 static hipError_t launch_attn_t(int group, const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.n_splits, a.hkv, a.batch);
+  dim3 block(kAttnWaves * kWave);
+  dim3 mgrid(a.hkv, a.batch);
   switch (group) {
-    case 1: hipLaunchKernelGGL((attn_split_kernel<T, 1>), grid, dim3(kWave), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((attn_split_kernel<T, 2>), grid, dim3(kWave), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((attn_split_kernel<T, 4>), grid, dim3(kWave), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((attn_split_kernel<T, 8>), grid, dim3(kWave), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((attn_split_kernel<T, 1>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((attn_merge_kernel<T, 1>), mgrid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((attn_split_kernel<T, 2>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((attn_merge_kernel<T, 2>), mgrid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((attn_split_kernel<T, 4>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((attn_merge_kernel<T, 4>), mgrid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((attn_split_kernel<T, 8>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((attn_merge_kernel<T, 8>), mgrid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(attn_merge_kernel<T>, dim3(a.hq, a.batch), dim3(kWave), 0, s, a, group);
   return hipGetLastError();
 }
 

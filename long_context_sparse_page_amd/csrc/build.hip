@@ -1,4 +1,4 @@
-// Page summary builder: one workgroup per (page, KV head).
+// Page summary builder: one workgroup of 1024 threads per (page, KV head).
 //
 // [Locks] §4 "Build (once, when a page completes)": centre the page,
 // k_i = mu + delta_i; stack the deviations as rows of D (B x d); eigendecompose
@@ -7,14 +7,16 @@
 // orthonormal basis V = D^T U_r Sigma_r^{-1}; zero modes are dropped with
 // zero coefficients.
 //
-// Device plan: the K tile is widened to fp32 in LDS and centred; the Gram is
-// formed in fp32 from LDS; the eigendecomposition is a cyclic parallel Jacobi
+// Device plan: the K tile is widened to fp32 and centred in LDS (stored
+// transposed, D^T, so the Gram and basis reads are bank-conflict free); the
+// Gram is formed in fp32; the eigendecomposition is a cyclic parallel Jacobi
 // method held in LDS: each round rotates 32 disjoint index pairs chosen by the
 // circle (round-robin) ordering, with the symmetric Schur rotation of Golub &
-// Van Loan (Matrix Computations, sym.schur2), applied as 2 x 2 block updates
-// of the upper block triangle (mirrored, so A stays exactly symmetric) and to
-// the accumulated eigenvector matrix U.  Sweeps stop when the off-diagonal
-// energy falls below 1e-13 of the total.
+// Van Loan (Matrix Computations, sym.schur2).  A round is one 2 x 2 block
+// update of the upper block triangle per thread (mirrored, so A stays exactly
+// symmetric; the rotated pair is set exactly: a_pp - t a_pq, a_qq + t a_pq, 0)
+// plus two column-pair updates of the accumulated eigenvector matrix U.
+// Sweeps stop when the off-diagonal energy is below 1e-10 of the total.
 //
 // Zero-mode rule: eigenvalue <= 1e-5 * lambda_1 or <= 1e-10 * sum_i ||k_i||^2.
 // Sign rule: each basis vector's largest-magnitude entry is made positive.
@@ -24,8 +26,10 @@
 
 namespace lk {
 
-constexpr int kBuildThreads = 256;
-constexpr int kBuildMaxSweeps = 12;
+constexpr int kBuildThreads = 1024;
+constexpr int kBuildWaves = kBuildThreads / kWave;
+constexpr int kBuildMaxSweeps = 15;
+constexpr float kJacobiTol = 1e-10f;
 constexpr float kZeroModeRtol = 1e-5f;
 constexpr float kZeroModeFloor = 1e-10f;
 
@@ -34,100 +38,94 @@ __global__ __launch_bounds__(kBuildThreads) void build_kernel(BuildArgs a) {
   constexpr int B = 64;
   constexpr int D = kHeadDim;
   constexpr int NP = B / 2;                 // pairs per round
-  constexpr int NBLK = NP * (NP + 1) / 2;   // upper 2x2 blocks
+  constexpr int NBLK = NP * (NP + 1) / 2;   // upper 2x2 blocks (528)
   constexpr int KEPT = R < B ? R : B;
   constexpr int LDA = B + 1;
 
-  __shared__ float sD[B][D + 4];
-  __shared__ float sA[B][LDA];              // Gram -> eigenvalues; later the basis
+  __shared__ float sDT[D][LDA];             // D^T: sDT[c][i] = delta_i[c]
+  __shared__ float sA[B][LDA];              // Gram -> diagonal; later the basis
   __shared__ float sU[B][LDA];
   __shared__ float sMu[D];
-  __shared__ float sRc[NP], sRs[NP], sRt[NP];
-  __shared__ int sRp[NP], sRq[NP];
-  __shared__ unsigned short sBlk[NBLK];
+  __shared__ float4 sPar[NP];               // c, s, t, (p | q << 8) as bits
   __shared__ float sLam[B];
   __shared__ int sOrder[B];
-  __shared__ float sRed[2][kBuildThreads / kWave];
+  __shared__ float sRed[2][kBuildWaves];
   __shared__ float sSigma[KEPT], sSign[KEPT];
   __shared__ int sCol[KEPT], sNz[KEPT];
-  __shared__ float sEnergy;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int idx = blockIdx.x;
   const int kvh = blockIdx.y;
+  if (a.commit_seq_lens && kvh == 0 && tid == 0) {
+    // decode step: the append of sequence idx was valid -> advance its length
+    const int len = a.commit_seq_lens[idx];
+    const int page = len / B;
+    int ph = -1;
+    if (len >= 0 && page < a.max_pages) ph = a.block_table[(size_t)idx * a.max_pages + page];
+    if (ph >= 0 && ph < a.num_phys) a.commit_seq_lens[idx] = len + 1;
+  }
   const int phys = a.phys_ids[idx];
   if (phys < 0 || phys >= a.num_phys) return;
 
-  // upper block table (k1 <= k2)
-  for (int b = tid; b < NBLK; b += kBuildThreads) {
-    int k1 = 0, rem = b;
+  // this thread's upper block (k1 <= k2), if any
+  int k1 = -1, k2 = -1;
+  if (tid < NBLK) {
+    int rem = tid;
+    k1 = 0;
     while (rem >= NP - k1) { rem -= NP - k1; ++k1; }
-    sBlk[b] = (unsigned short)((k1 << 8) | (k1 + rem));
+    k2 = k1 + rem;
   }
 
-  // 1) load K (fp32 in LDS), page energy
+  // 1) load K (8 elements per thread), energy, transpose into LDS
   const T* K = reinterpret_cast<const T*>(a.k_pool) + (((size_t)phys * a.hkv + kvh) * B) * D;
   float en = 0.f;
   {
-    const int row = tid >> 2;
-    const int c0 = (tid & 3) * 32;
+    const int row = tid >> 4;
+    const int c0 = (tid & 15) * 8;
+    float v[8];
+    load8(K + (size_t)row * D + c0, v);
 #pragma unroll
-    for (int x = 0; x < 32; x += 8) {
-      float v[8];
-      load8(K + (size_t)row * D + c0 + x, v);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) { sD[row][c0 + x + t] = v[t]; en = fmaf(v[t], v[t], en); }
-    }
+    for (int t = 0; t < 8; ++t) { sDT[c0 + t][row] = v[t]; en = fmaf(v[t], v[t], en); }
   }
   en = group_sum<kWave>(en);
   if (lane == 0) sRed[0][wave] = en;
   __syncthreads();
-  if (tid == 0) {
-    float e = 0.f;
-    for (int w = 0; w < kBuildThreads / kWave; ++w) e += sRed[0][w];
-    sEnergy = e;
-  }
+  float energy = 0.f;
+#pragma unroll
+  for (int w = 0; w < kBuildWaves; ++w) energy += sRed[0][w];
   // 2) centroid and centring
   if (tid < D) {
     float s = 0.f;
-    for (int i = 0; i < B; ++i) s += sD[i][tid];
+    for (int i = 0; i < B; ++i) s += sDT[tid][i];
     sMu[tid] = s * (1.0f / B);
   }
   __syncthreads();
   {
-    const int row = tid >> 2;
-    const int c0 = (tid & 3) * 32;
+    const int row = tid >> 4;
+    const int c0 = (tid & 15) * 8;
 #pragma unroll
-    for (int x = 0; x < 32; ++x) sD[row][c0 + x] -= sMu[c0 + x];
+    for (int t = 0; t < 8; ++t) sDT[c0 + t][row] -= sMu[c0 + t];
   }
   __syncthreads();
 
-  // 3) Gram A = D D^T (each thread a 4 x 4 tile), U = I
+  // 3) Gram A = D D^T (2 x 2 tile per thread), U = I
   {
-    const int bi = tid >> 4, bj = tid & 15;
-    float acc[4][4];
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int y = 0; y < 4; ++y) acc[x][y] = 0.f;
+    const int bi = tid >> 5, bj = tid & 31;
+    float a00 = 0.f, a01 = 0.f, a10 = 0.f, a11 = 0.f;
     for (int c = 0; c < D; ++c) {
-      float av[4], bv[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) { av[x] = sD[4 * bi + x][c]; bv[x] = sD[4 * bj + x][c]; }
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(av[x], bv[y], acc[x][y]);
+      const float x0 = sDT[c][2 * bi], x1 = sDT[c][2 * bi + 1];
+      const float y0 = sDT[c][2 * bj], y1 = sDT[c][2 * bj + 1];
+      a00 = fmaf(x0, y0, a00); a01 = fmaf(x0, y1, a01);
+      a10 = fmaf(x1, y0, a10); a11 = fmaf(x1, y1, a11);
     }
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        sA[4 * bi + x][4 * bj + y] = acc[x][y];
-        sU[4 * bi + x][4 * bj + y] = (4 * bi + x == 4 * bj + y) ? 1.f : 0.f;
-      }
+    sA[2 * bi][2 * bj] = a00; sA[2 * bi][2 * bj + 1] = a01;
+    sA[2 * bi + 1][2 * bj] = a10; sA[2 * bi + 1][2 * bj + 1] = a11;
+    sU[2 * bi][2 * bj] = (bi == bj) ? 1.f : 0.f;
+    sU[2 * bi][2 * bj + 1] = 0.f;
+    sU[2 * bi + 1][2 * bj] = 0.f;
+    sU[2 * bi + 1][2 * bj + 1] = (bi == bj) ? 1.f : 0.f;
   }
   __syncthreads();
 
@@ -146,47 +144,52 @@ __global__ __launch_bounds__(kBuildThreads) void build_kernel(BuildArgs a) {
           c = 1.f / sqrtf(1.f + t * t);
           s = t * c;
         }
-        sRp[k] = p; sRq[k] = q; sRc[k] = c; sRs[k] = s; sRt[k] = t;
+        sPar[k] = make_float4(c, s, t, __int_as_float(p | (q << 8)));
       }
       __syncthreads();
-      for (int b = tid; b < NBLK; b += kBuildThreads) {
-        const int k1 = sBlk[b] >> 8, k2 = sBlk[b] & 0xff;
-        const int p1 = sRp[k1], q1 = sRq[k1];
+      if (k1 >= 0) {
+        const float4 P1 = sPar[k1];
+        const int p1 = __float_as_int(P1.w) & 0xff, q1 = __float_as_int(P1.w) >> 8;
         if (k1 == k2) {
-          const float apq = sA[p1][q1], t1 = sRt[k1];
-          sA[p1][p1] -= t1 * apq;
-          sA[q1][q1] += t1 * apq;
+          const float apq = sA[p1][q1];
+          sA[p1][p1] -= P1.z * apq;
+          sA[q1][q1] += P1.z * apq;
           sA[p1][q1] = 0.f;
           sA[q1][p1] = 0.f;
-          continue;
+        } else {
+          const float4 P2 = sPar[k2];
+          const int p2 = __float_as_int(P2.w) & 0xff, q2 = __float_as_int(P2.w) >> 8;
+          const float c1 = P1.x, s1 = P1.y, c2 = P2.x, s2 = P2.y;
+          const float x00 = sA[p1][p2], x01 = sA[p1][q2], x10 = sA[q1][p2], x11 = sA[q1][q2];
+          const float y00 = c1 * x00 - s1 * x10, y01 = c1 * x01 - s1 * x11;
+          const float y10 = s1 * x00 + c1 * x10, y11 = s1 * x01 + c1 * x11;
+          const float z00 = c2 * y00 - s2 * y01, z01 = s2 * y00 + c2 * y01;
+          const float z10 = c2 * y10 - s2 * y11, z11 = s2 * y10 + c2 * y11;
+          sA[p1][p2] = z00; sA[p2][p1] = z00;
+          sA[p1][q2] = z01; sA[q2][p1] = z01;
+          sA[q1][p2] = z10; sA[p2][q1] = z10;
+          sA[q1][q2] = z11; sA[q2][q1] = z11;
         }
-        const int p2 = sRp[k2], q2 = sRq[k2];
-        const float c1 = sRc[k1], s1 = sRs[k1], c2 = sRc[k2], s2 = sRs[k2];
-        const float x00 = sA[p1][p2], x01 = sA[p1][q2], x10 = sA[q1][p2], x11 = sA[q1][q2];
-        const float y00 = c1 * x00 - s1 * x10, y01 = c1 * x01 - s1 * x11;
-        const float y10 = s1 * x00 + c1 * x10, y11 = s1 * x01 + c1 * x11;
-        const float z00 = c2 * y00 - s2 * y01, z01 = s2 * y00 + c2 * y01;
-        const float z10 = c2 * y10 - s2 * y11, z11 = s2 * y10 + c2 * y11;
-        sA[p1][p2] = z00; sA[p2][p1] = z00;
-        sA[p1][q2] = z01; sA[q2][p1] = z01;
-        sA[q1][p2] = z10; sA[p2][q1] = z10;
-        sA[q1][q2] = z11; sA[q2][q1] = z11;
       }
-      // U <- U J (columns p, q of every row)
-      for (int w = tid; w < B * NP; w += kBuildThreads) {
-        const int i = w / NP, k = w % NP;
-        const int p = sRp[k], q = sRq[k];
-        const float c = sRc[k], s = sRs[k];
+      // U <- U J: columns p, q of rows i (two (row, pair) items per thread)
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int w = tid + x * kBuildThreads;
+        const int i = w >> 5, k = w & 31;
+        const float4 P = sPar[k];
+        const int p = __float_as_int(P.w) & 0xff, q = __float_as_int(P.w) >> 8;
         const float up = sU[i][p], uq = sU[i][q];
-        sU[i][p] = c * up - s * uq;
-        sU[i][q] = s * up + c * uq;
+        sU[i][p] = P.x * up - P.y * uq;
+        sU[i][q] = P.y * up + P.x * uq;
       }
       __syncthreads();
     }
-    // convergence: off-diagonal energy vs total
+    // convergence: off-diagonal energy vs total (4 entries per thread)
     float off = 0.f, tot = 0.f;
-    for (int w = tid; w < B * B; w += kBuildThreads) {
-      const int i = w / B, j = w % B;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int w = tid + x * kBuildThreads;
+      const int i = w >> 6, j = w & 63;
       const float v = sA[i][j];
       tot = fmaf(v, v, tot);
       if (i != j) off = fmaf(v, v, off);
@@ -197,9 +200,9 @@ __global__ __launch_bounds__(kBuildThreads) void build_kernel(BuildArgs a) {
     __syncthreads();
     float o = 0.f, tt = 0.f;
 #pragma unroll
-    for (int w = 0; w < kBuildThreads / kWave; ++w) { o += sRed[0][w]; tt += sRed[1][w]; }
+    for (int w = 0; w < kBuildWaves; ++w) { o += sRed[0][w]; tt += sRed[1][w]; }
     __syncthreads();
-    if (o <= 1e-13f * tt) break;
+    if (o <= kJacobiTol * tt) break;
   }
 
   // 5) eigenvalues sorted descending (ties to the lower index)
@@ -219,7 +222,7 @@ __global__ __launch_bounds__(kBuildThreads) void build_kernel(BuildArgs a) {
     const float lam1 = sLam[sOrder[0]];
     const int col = sOrder[tid];
     const float lam = sLam[col];
-    const float thresh = fmaxf(kZeroModeRtol * lam1, kZeroModeFloor * sEnergy);
+    const float thresh = fmaxf(kZeroModeRtol * lam1, kZeroModeFloor * energy);
     const int nz = (lam1 > 0.f && lam > thresh) ? 1 : 0;
     sCol[tid] = col;
     sNz[tid] = nz;
@@ -232,21 +235,19 @@ __global__ __launch_bounds__(kBuildThreads) void build_kernel(BuildArgs a) {
 
   // 6) basis V[k][c] = sum_i D[i][c] U[i][col_k] / sigma_k  (stored in sA)
   float* sV = &sA[0][0];
-  {
-    const int c = tid & (D - 1);
-    for (int k = tid / D; k < KEPT; k += kBuildThreads / D) {
-      float v = 0.f;
-      if (sNz[k]) {
-        const int col = sCol[k];
-        for (int i = 0; i < B; ++i) v = fmaf(sD[i][c], sU[i][col], v);
-        v /= sSigma[k];
-      }
-      sV[k * D + c] = v;
+  for (int w = tid; w < KEPT * D; w += kBuildThreads) {
+    const int k = w / D, c = w % D;
+    float v = 0.f;
+    if (sNz[k]) {
+      const int col = sCol[k];
+      for (int i = 0; i < B; ++i) v = fmaf(sDT[c][i], sU[i][col], v);
+      v /= sSigma[k];
     }
+    sV[k * D + c] = v;
   }
   __syncthreads();
   // sign: largest |entry| positive (ties to the lower dim)
-  for (int k = wave; k < KEPT; k += kBuildThreads / kWave) {
+  for (int k = wave; k < KEPT; k += kBuildWaves) {
     float best = -1.f, val = 0.f;
     int bidx = D;
 #pragma unroll

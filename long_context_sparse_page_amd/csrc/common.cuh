@@ -70,6 +70,26 @@ __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
 
+// Exchange with lane ^ 16 / lane ^ 32 on the VALU (gfx950 permlane swaps):
+// swapping a value with itself leaves x in one result and its partner in the
+// other, so their sum (or max) is the pairwise combine for every lane.
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
 // Sum / max over aligned groups of N lanes (N in {1,2,4,8,16,32,64}); every
 // lane of the group receives the result.
 template <int N>
@@ -78,8 +98,8 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (N >= 4) x += dpp<kDppXor2>(x);
   if constexpr (N >= 8) x += dpp<kDppHalfMirror>(x);
   if constexpr (N >= 16) x += dpp<kDppMirror>(x);
-  if constexpr (N >= 32) x += __shfl_xor(x, 16);
-  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  if constexpr (N >= 32) x = xor16_sum(x);
+  if constexpr (N >= 64) x = xor32_sum(x);
   return x;
 }
 template <int N>
@@ -88,8 +108,8 @@ __device__ __forceinline__ float group_max(float x) {
   if constexpr (N >= 4) x = fmaxf(x, dpp<kDppXor2>(x));
   if constexpr (N >= 8) x = fmaxf(x, dpp<kDppHalfMirror>(x));
   if constexpr (N >= 16) x = fmaxf(x, dpp<kDppMirror>(x));
-  if constexpr (N >= 32) x = fmaxf(x, __shfl_xor(x, 16));
-  if constexpr (N >= 64) x = fmaxf(x, __shfl_xor(x, 32));
+  if constexpr (N >= 32) x = xor16_max(x);
+  if constexpr (N >= 64) x = xor32_max(x);
   return x;
 }
 

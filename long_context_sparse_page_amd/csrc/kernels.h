@@ -8,6 +8,21 @@ namespace lk {
 
 enum DType : int { kF32 = 0, kBF16 = 1 };
 
+// The cache append of a decode step, carried out by the scorer's first
+// workgroup of every (sequence, KV head): the new key and value go to slot
+// T mod B of logical page T / B (T = seq_lens[seq] before the step), and the
+// physical page an append completes is recorded in build_list[seq] (else -1).
+struct AppendDuty {
+  void* k_pool;
+  void* v_pool;
+  const void* k_new;           // [batch][Hkv][d]; nullptr: no append
+  const void* v_new;
+  int32_t* build_list;         // [batch]
+};
+
+// In a decode step every kernel sees T = seq_lens[seq] + len_add (len_add = 1:
+// the token appended by this step); the stored length is advanced by the
+// step's last kernel.
 struct ScoreArgs {
   const void* q;               // [batch][Hq][d]
   const void* summary;         // [num_phys][Hkv][record]
@@ -16,6 +31,8 @@ struct ScoreArgs {
   float* page_lse;             // [batch][Hq][max_pages]
   int32_t batch, max_pages, num_phys, hkv, hq;
   float scale;
+  int32_t len_add;
+  AppendDuty app;
 };
 
 struct SelectArgs {
@@ -25,6 +42,10 @@ struct SelectArgs {
   int32_t* sel_count;          // [batch][Hkv]
   const int32_t* seq_lens;
   int32_t batch, max_pages, hkv, group, page_size, k;
+  int32_t len_add;
+  const int32_t* block_table;  // with sel_phys: physical page of every selected page
+  int32_t* sel_phys;           // optional [batch][Hkv][k]
+  int32_t num_phys;
 };
 
 struct AttnArgs {
@@ -35,12 +56,15 @@ struct AttnArgs {
   const int32_t* seq_lens;
   const int32_t* sel_pages;    // null: every page of the sequence (dense)
   const int32_t* sel_count;
+  const int32_t* sel_phys;     // optional: physical pages of sel_pages
   float* part_o;               // [batch][Hkv][n_splits][G][d]
   float* part_ml;              // [batch][Hkv][n_splits][G][2]  (max in log2 units, sum)
   void* out;                   // [batch][Hq][d]
   float* lse_out;              // optional [batch][Hq]
-  int32_t batch, max_pages, num_phys, hkv, hq, k, n_splits, pages_per_split;
+  int32_t batch, max_pages, num_phys, hkv, hq, k, n_splits;
+  int32_t pages_per_split;     // half-page units per wave (4 waves per split)
   float scale;
+  int32_t len_add;
 };
 
 struct BuildArgs {
@@ -49,23 +73,16 @@ struct BuildArgs {
   const int32_t* phys_ids;     // [n]; entries < 0 are skipped
   float* eigvals_out;          // optional [n][Hkv][B]
   int32_t n, num_phys, hkv;
-};
-
-struct AppendArgs {
-  void* k_pool;
-  void* v_pool;
-  const void* k_new;           // [batch][Hkv][d]
-  const void* v_new;
+  // decode step: workgroup (seq, 0) advances seq_lens[seq] by one when the
+  // step's append was valid (phys_ids is then the build list, n = batch)
+  int32_t* commit_seq_lens;
   const int32_t* block_table;
-  int32_t* seq_lens;
-  int32_t* build_list;         // [batch]: physical page completed by this append, else -1
-  int32_t batch, max_pages, num_phys, hkv;
+  int32_t max_pages;
 };
 
 hipError_t launch_score(DType dt, int rank, int group, const ScoreArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_attn(DType dt, int group, const AttnArgs& a, hipStream_t s);
 hipError_t launch_build(DType dt, int rank, const BuildArgs& a, hipStream_t s);
-hipError_t launch_append(DType dt, const AppendArgs& a, hipStream_t s);
 
 }  // namespace lk

@@ -6,7 +6,7 @@
 // The record stores centroid | basis rows | coeffs, so rows 0..r of the
 // record form W = [mu; v_1; ...; v_r] and the projection is P = W q_g.
 //
-// Layout of the work (one wave per page at a time, pages of one
+// fp32 records (below, VALU; one wave per page at a time, pages of one
 // (sequence, KV head) per workgroup):
 //   projection: lane (s = lane / 16, e = lane % 16) owns dims 8e..8e+7 of rows
 //     s, s+4, s+8, ...; partial dots are summed over the 16 lanes of a row
@@ -23,6 +23,10 @@
 namespace lk {
 
 constexpr int kScoreWaves = 4;
+#ifndef LK_SCORE_PIPELINE
+#define LK_SCORE_PIPELINE 1
+#endif
+constexpr bool kScorePipeline = LK_SCORE_PIPELINE;
 constexpr int kScorePagesPerWave = 8;
 constexpr int kScorePagesPerBlock = kScoreWaves * kScorePagesPerWave;
 
@@ -42,6 +46,33 @@ __device__ __forceinline__ void load_coeffs(const T* p, float (&c)[R]) {
   }
 }
 
+// Decode-step cache append (AppendDuty), done by workgroup x = 0 of every
+// (sequence, KV head) before anything else: 16-byte copies of the new key and
+// value rows into slot T mod B of page T / B, and the build-list entry.
+template <typename T>
+__device__ __forceinline__ void append_duty(const ScoreArgs& a, int seq, int kvh) {
+  if (a.app.k_new == nullptr || blockIdx.x != 0) return;
+  constexpr int B = 64;
+  constexpr int D = kHeadDim;
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int CH = D / VEC;  // 16-byte chunks per row
+  const int len = a.seq_lens[seq];
+  const int page = len / B, slot = len % B;
+  int phys = -1;
+  if (len >= 0 && page < a.max_pages) phys = a.block_table[(size_t)seq * a.max_pages + page];
+  const bool ok = phys >= 0 && phys < a.num_phys;
+  const int t = threadIdx.x;
+  if (ok && t < 2 * CH) {
+    const int which = t / CH, ch = t % CH;
+    const T* src = reinterpret_cast<const T*>(which ? a.app.v_new : a.app.k_new) +
+                   ((size_t)seq * a.hkv + kvh) * D + ch * VEC;
+    T* dst = reinterpret_cast<T*>(which ? a.app.v_pool : a.app.k_pool) +
+             (((size_t)phys * a.hkv + kvh) * B + slot) * D + ch * VEC;
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+  }
+  if (kvh == 0 && t == 0) a.app.build_list[seq] = (ok && slot == B - 1) ? phys : -1;
+}
+
 template <typename T, int R, int G>
 __global__ __launch_bounds__(kScoreWaves * kWave) void score_kernel(ScoreArgs a) {
   constexpr int B = 64;
@@ -59,7 +90,8 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_kernel(ScoreArgs a)
   const int wave = threadIdx.x / kWave;
   const int seq = blockIdx.z;
   const int kvh = blockIdx.y;
-  const int len = a.seq_lens[seq];
+  append_duty<T>(a, seq, kvh);
+  const int len = a.seq_lens[seq] + a.len_add;
   if (len <= 0) return;
   int n_scored = (len - 1) / B;
   if (n_scored > a.max_pages - 1) n_scored = a.max_pages - 1;
@@ -157,6 +189,226 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_kernel(ScoreArgs a)
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 records: the projection on the matrix cores.
+//
+// A wave takes NR records at a time.  Their (r + 1) rows (centroid, basis)
+// are the 16-wide columns of B in v_mfma_f32_16x16x32_bf16 (row slot
+// s = record * (r + 1) + row), the group's G queries are the rows of A (rows
+// >= G are zero), and four K-steps of 32 cover d = 128: the product holds
+// P[slot][g] = W_slot . q_g.  Lane l of B supplies column l % 16 and 8
+// consecutive dims of K-step t at group l / 16, i.e. one 16-byte load; lane l
+// of A supplies the same dims of query l % 16.  The accumulator of lane l
+// holds rows 4 (l / 16) .. +3 of column l % 16.  All of a group's record rows
+// and coefficients are loaded before any arithmetic.
+template <int R> struct ScoreGroup {
+  static constexpr int NR = R >= 16 ? 2 : (R >= 8 ? 4 : (R >= 4 ? 8 : 16));  // records per group
+  static constexpr int SLOTS = NR * (R + 1);
+  static constexpr int TILES = (SLOTS + 15) / 16;
+  static constexpr int CW = (R + 1) / 2;        // 32-bit words of one token's coefficients
+  static constexpr int GROUPS_PER_WAVE = 4;
+};
+
+// One group's loads, held in registers until the group is computed.
+template <int R> struct GroupLoads {
+  uint4 wb[ScoreGroup<R>::TILES][4];             // B operand tiles
+  uint32_t cw[ScoreGroup<R>::NR][ScoreGroup<R>::CW];  // this lane's token coefficients (bf16 pairs)
+  const bf16_t* recp[ScoreGroup<R>::NR];         // record bases (nullptr: none)
+};
+
+template <int R>
+__device__ __forceinline__ void load_group(GroupLoads<R>& L, const bf16_t* summ, const int* phys_g, int g0,
+                                           int n_scored, int num_phys, int hkv, int kvh, int col, int kg,
+                                           int lane) {
+  constexpr int D = kHeadDim;
+  constexpr int B = 64;
+  constexpr int ROWS = R + 1;
+  constexpr int NR = ScoreGroup<R>::NR;
+  constexpr int SLOTS = ScoreGroup<R>::SLOTS;
+  constexpr int TILES = ScoreGroup<R>::TILES;
+  constexpr int CW = ScoreGroup<R>::CW;
+  constexpr size_t REC = (size_t)ROWS * D + (size_t)B * R;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int j = g0 + r;
+    const int phys = j < n_scored ? phys_g[r] : -1;
+    L.recp[r] = (phys >= 0 && phys < num_phys) ? summ + ((size_t)phys * hkv + kvh) * REC : nullptr;
+  }
+#pragma unroll
+  for (int tau = 0; tau < TILES; ++tau) {
+    const int slot = 16 * tau + col;
+    const int r = slot / ROWS, m = slot % ROWS;
+    const bf16_t* rp = nullptr;
+#pragma unroll
+    for (int x = 0; x < NR; ++x) if (x == r) rp = L.recp[x];
+    const bool ok = slot < SLOTS && rp != nullptr;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      L.wb[tau][t] = ok ? *reinterpret_cast<const uint4*>(rp + (size_t)m * D + 32 * t + 8 * kg)
+                        : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const bf16_t* cp = L.recp[r] ? L.recp[r] + (size_t)ROWS * D + (size_t)lane * R : nullptr;
+    if constexpr (R % 8 == 0) {
+#pragma unroll
+      for (int x = 0; x < CW; x += 4) {
+        const uint4 v = cp ? *reinterpret_cast<const uint4*>(cp + 2 * x) : make_uint4(0, 0, 0, 0);
+        L.cw[r][x] = v.x; L.cw[r][x + 1] = v.y; L.cw[r][x + 2] = v.z; L.cw[r][x + 3] = v.w;
+      }
+    } else if constexpr (R == 4) {
+      const uint2 v = cp ? *reinterpret_cast<const uint2*>(cp) : make_uint2(0, 0);
+      L.cw[r][0] = v.x; L.cw[r][1] = v.y;
+    } else if constexpr (R == 2) {
+      L.cw[r][0] = cp ? *reinterpret_cast<const uint32_t*>(cp) : 0u;
+    } else {
+      L.cw[r][0] = cp ? (uint32_t)*cp : 0u;
+    }
+  }
+}
+
+template <int R, int G>
+__global__ __launch_bounds__(kScoreWaves * kWave) void score_mfma_kernel(ScoreArgs a) {
+  constexpr int B = 64;
+  constexpr int D = kHeadDim;
+  constexpr int ROWS = R + 1;
+  constexpr int NR = ScoreGroup<R>::NR;
+  constexpr int SLOTS = ScoreGroup<R>::SLOTS;
+  constexpr int TILES = ScoreGroup<R>::TILES;
+  constexpr int LPH = kWave / G;
+  constexpr int TPL = B / LPH;
+  constexpr int PAGES_PER_WAVE = ScoreGroup<R>::GROUPS_PER_WAVE * NR;
+  static_assert(G <= 8, "at most 8 query heads per KV head");
+
+  __shared__ float sP[kScoreWaves][SLOTS * G];
+  __shared__ float sZ[kScoreWaves][G * B];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int seq = blockIdx.z;
+  const int kvh = blockIdx.y;
+  append_duty<bf16_t>(a, seq, kvh);
+  const int j0 = (blockIdx.x * kScoreWaves + wave) * PAGES_PER_WAVE;
+  if (j0 >= a.max_pages) return;
+  const int col = lane & 15;       // B column / A row of this lane
+  const int kg = lane >> 4;        // K group (8 dims) within a K-step
+  const bf16_t* summ = reinterpret_cast<const bf16_t*>(a.summary);
+  const int32_t* bt = a.block_table + (size_t)seq * a.max_pages;
+
+  // Loads that do not depend on the sequence length go out first: the
+  // wave's block-table slice (clamped in bounds), the group's queries, and
+  // then the first group's records (pages past the sequence end are masked
+  // when results are written).
+  int phys_all[PAGES_PER_WAVE];
+#pragma unroll
+  for (int x = 0; x < PAGES_PER_WAVE; ++x) phys_all[x] = bt[min(j0 + x, a.max_pages - 1)];
+  const int len_raw = a.seq_lens[seq] + a.len_add;
+  bf16x8_t qa[4];  // A operand: query `col` (zero rows beyond G), 4 K-steps
+  {
+    const bf16_t* q = reinterpret_cast<const bf16_t*>(a.q) + ((size_t)seq * a.hq + (size_t)kvh * G) * D;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (col < G) w = *reinterpret_cast<const uint4*>(q + (size_t)col * D + 32 * t + 8 * kg);
+      qa[t] = __builtin_bit_cast(bf16x8_t, w);
+    }
+  }
+  GroupLoads<R> cur, nxt;
+  load_group<R>(cur, summ, phys_all, j0, a.max_pages, a.num_phys, a.hkv, kvh, col, kg, lane);
+
+  if (len_raw <= 0) return;
+  int n_scored = (len_raw - 1) / B;
+  if (n_scored > a.max_pages - 1) n_scored = a.max_pages - 1;
+  if (j0 >= n_scored) return;
+  const int j_end = min(j0 + PAGES_PER_WAVE, n_scored);
+
+  const float zscale = a.scale * kLog2e;
+  float* out = a.page_lse + ((size_t)seq * a.hq + (size_t)kvh * G) * a.max_pages;
+  float* P = sP[wave];
+  float* Z = sZ[wave];
+
+#pragma unroll
+  for (int gi = 0; gi < ScoreGroup<R>::GROUPS_PER_WAVE; ++gi) {
+    const int g0 = j0 + gi * NR;
+    if (g0 >= j_end) break;
+    // software pipeline: the next group's loads are in flight while this one computes
+    if (kScorePipeline && gi + 1 < ScoreGroup<R>::GROUPS_PER_WAVE && g0 + NR < j_end)
+      load_group<R>(nxt, summ, phys_all + (gi + 1) * NR, g0 + NR, a.max_pages, a.num_phys, a.hkv, kvh, col, kg, lane);
+    if (!kScorePipeline && gi > 0)
+      load_group<R>(cur, summ, phys_all + gi * NR, g0, a.max_pages, a.num_phys, a.hkv, kvh, col, kg, lane);
+
+    // projection on the matrix cores
+#pragma unroll
+    for (int tau = 0; tau < TILES; ++tau) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], __builtin_bit_cast(bf16x8_t, cur.wb[tau][t]), acc, 0, 0, 0);
+      const int slot = 16 * tau + col;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int g = 4 * kg + i;
+        if (g < G && slot < SLOTS) P[slot * G + g] = acc[i];
+      }
+    }
+    wave_lds_fence();
+    // reconstruction and per-head LSE, record by record (lane = token)
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int j = g0 + r;
+      if (j >= j_end) break;
+      if (!cur.recp[r]) {
+        if (lane < G) out[(size_t)lane * a.max_pages + j] = -INFINITY;
+        continue;
+      }
+      float c[R];
+#pragma unroll
+      for (int m = 0; m < R; ++m) c[m] = (m & 1) ? bf16_hi(cur.cw[r][m >> 1]) : bf16_lo(cur.cw[r][m >> 1]);
+      const float* Pr = P + r * ROWS * G;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float z = Pr[g];
+#pragma unroll
+        for (int m = 0; m < R; ++m) z = fmaf(c[m], Pr[(m + 1) * G + g], z);
+        Z[g * B + lane] = z * zscale;
+      }
+      wave_lds_fence();
+      const int hg = lane / LPH;
+      const int t0 = (lane % LPH) * TPL;
+      float v[TPL];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < TPL; ++t) {
+        v[t] = Z[hg * B + t0 + t];
+        mx = fmaxf(mx, v[t]);
+      }
+      mx = group_max<LPH>(mx);
+      float sum = 0.f;
+#pragma unroll
+      for (int t = 0; t < TPL; ++t) sum += fast_exp2(v[t] - mx);
+      sum = group_sum<LPH>(sum);
+      if (lane % LPH == 0) out[(size_t)hg * a.max_pages + j] = (mx + fast_log2(sum)) * kLn2;
+      wave_lds_fence();
+    }
+    if (kScorePipeline) cur = nxt;
+  }
+}
+
+template <int R>
+static hipError_t launch_score_mfma(int group, const ScoreArgs& a, hipStream_t s) {
+  constexpr int per_block = kScoreWaves * ScoreGroup<R>::GROUPS_PER_WAVE * ScoreGroup<R>::NR;
+  dim3 grid((a.max_pages + per_block - 1) / per_block, a.hkv, a.batch);
+  dim3 block(kScoreWaves * kWave);
+  switch (group) {
+    case 1: hipLaunchKernelGGL((score_mfma_kernel<R, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((score_mfma_kernel<R, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((score_mfma_kernel<R, 4>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((score_mfma_kernel<R, 8>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <typename T, int R>
 static hipError_t launch_score_rg(int group, const ScoreArgs& a, hipStream_t s) {
   dim3 grid((a.max_pages + kScorePagesPerBlock - 1) / kScorePagesPerBlock, a.hkv, a.batch);
@@ -184,8 +436,17 @@ static hipError_t launch_score_t(int rank, int group, const ScoreArgs& a, hipStr
 }
 
 hipError_t launch_score(DType dt, int rank, int group, const ScoreArgs& a, hipStream_t s) {
-  return dt == kBF16 ? launch_score_t<bf16_t>(rank, group, a, s)
-                     : launch_score_t<float>(rank, group, a, s);
+  if (dt == kBF16) {
+    switch (rank) {
+      case 1: return launch_score_mfma<1>(group, a, s);
+      case 2: return launch_score_mfma<2>(group, a, s);
+      case 4: return launch_score_mfma<4>(group, a, s);
+      case 8: return launch_score_mfma<8>(group, a, s);
+      case 16: return launch_score_mfma<16>(group, a, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return launch_score_t<float>(rank, group, a, s);
 }
 
 }  // namespace lk

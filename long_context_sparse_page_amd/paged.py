@@ -3,8 +3,8 @@
 ``DeviceCache`` owns the paged K/V pools, the summary pool, the block table,
 the sequence lengths and the workspace of one attention layer, allocated with
 torch on the GPU and described to the C ABI by ``lk_cache``.  Physical pages
-are handed out in a seeded random order so every kernel exercises the block
-table.  It performs no step of the method: K/V come from ``synth`` (or the
+are handed out in a seeded random order (``perm_seed``; None hands them out in
+order) so every kernel exercises the block table.  It performs no step of the method: K/V come from ``synth`` (or the
 caller), summaries from ``lk_build_page_summary``.
 """
 
@@ -28,7 +28,7 @@ def to_storage(x: np.ndarray, dtype: str) -> torch.Tensor:
 
 
 class DeviceCache:
-    def __init__(self, w: synth.Workload, device: str = "cuda", perm_seed: int = 1,
+    def __init__(self, w: synth.Workload, device: str = "cuda", perm_seed: int | None = 1,
                  poison: bool = False, capacity_pages: list | None = None):
         self.w = w
         self.device = device
@@ -38,7 +38,8 @@ class DeviceCache:
         pages = capacity_pages or [w.pages_needed(s) for s in range(w.batch)]
         self.max_pages = max(pages)
         total = int(sum(pages))
-        perm = np.random.default_rng(perm_seed).permutation(total)
+        perm = (np.arange(total) if perm_seed is None
+                else np.random.default_rng(perm_seed).permutation(total))
         bt = np.full((w.batch, self.max_pages), -1, dtype=np.int32)
         off = 0
         for s, n in enumerate(pages):
@@ -56,7 +57,7 @@ class DeviceCache:
         self.block_table = torch.from_numpy(bt).to(device)
         self.seq_lens = torch.tensor(w.context, dtype=torch.int32, device=device)
         self.ws_bytes = L.lk_workspace_size(self.cfg, w.batch, self.max_pages)
-        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=device)  # zero once (arrival counters)
         self.cache = L.make_cache(self.k_pool, self.v_pool, self.summary_pool, self.block_table,
                                   self.seq_lens)
 
