@@ -162,7 +162,8 @@ lk_status enqueue_score_select(const Shape& sh, const lk_config* cfg, const lk_c
 
 lk_status enqueue_attn(const Shape& sh, const lk_config* cfg, const lk_cache* c, int batch,
                        const void* q, const int32_t* sel, const int32_t* cnt, const int32_t* sel_phys,
-                       void* out, float* lse_out, void* ws, const Layout& L, int len_add, hipStream_t s) {
+                       void* out, float* lse_out, void* ws, const Layout& L, int len_add, bool merge,
+                       hipStream_t s, int* n_splits_out = nullptr) {
   const bool dense = sel == nullptr;
   const int ups = dense ? kUnitsPerWaveDense : kUnitsPerWaveSparse;
   const int per = kAttnWavesPerSplit * ups;
@@ -171,7 +172,8 @@ lk_status enqueue_attn(const Shape& sh, const lk_config* cfg, const lk_cache* c,
                   at<float>(ws, L.part_o), at<float>(ws, L.part_ml), out, lse_out,
                   batch, c->max_pages_per_seq, c->num_phys_pages, sh.hkv, sh.hq, sh.k,
                   n_splits, ups, cfg->scale, len_add};
-  return hip_status(lk::launch_attn(sh.dt, sh.G, aa, s), "attention launch");
+  if (n_splits_out) *n_splits_out = n_splits;
+  return hip_status(lk::launch_attn(sh.dt, sh.G, aa, merge, s), "attention launch");
 }
 
 }  // namespace
@@ -218,7 +220,7 @@ lk_status lk_build_page_summary(const lk_config* cfg, const lk_cache* cache, con
   if (n_pages > 0 && !phys_page_ids) return fail(LK_ERR_INVALID_ARG, "phys_page_ids is null");
   if (n_pages == 0) return ok();
   lk::BuildArgs ba{cache->k_pool, cache->summary_pool, phys_page_ids, eigvals_out, n_pages,
-                   cache->num_phys_pages, sh.hkv, nullptr, nullptr, 0};
+                   cache->num_phys_pages, sh.hkv, nullptr, nullptr, 0, {}};
   return hip_status(lk::launch_build(sh.dt, sh.r, ba, static_cast<hipStream_t>(stream)), "build launch");
 }
 
@@ -265,7 +267,7 @@ lk_status lk_sparse_decode_attn(const lk_config* cfg, const lk_cache* cache, int
   if (!q || !out || !sel_pages || !sel_count) return fail(LK_ERR_INVALID_ARG, "q / out / sel_pages / sel_count is null");
   const Layout L = layout(sh, batch, cache->max_pages_per_seq);
   if ((st = check_ws(L, ws, ws_bytes)) != LK_OK) return st;
-  return enqueue_attn(sh, cfg, cache, batch, q, sel_pages, sel_count, nullptr, out, lse_out, ws, L, 0,
+  return enqueue_attn(sh, cfg, cache, batch, q, sel_pages, sel_count, nullptr, out, lse_out, ws, L, 0, true,
                       static_cast<hipStream_t>(stream));
 }
 
@@ -280,7 +282,7 @@ lk_status lk_dense_decode_attn(const lk_config* cfg, const lk_cache* cache, int3
   if (!q || !out) return fail(LK_ERR_INVALID_ARG, "q / out is null");
   const Layout L = layout(sh, batch, cache->max_pages_per_seq);
   if ((st = check_ws(L, ws, ws_bytes)) != LK_OK) return st;
-  return enqueue_attn(sh, cfg, cache, batch, q, nullptr, nullptr, nullptr, out, lse_out, ws, L, 0,
+  return enqueue_attn(sh, cfg, cache, batch, q, nullptr, nullptr, nullptr, out, lse_out, ws, L, 0, true,
                       static_cast<hipStream_t>(stream));
 }
 
@@ -309,13 +311,17 @@ lk_status lk_decode_step(const lk_config* cfg, const lk_cache* cache, int32_t ba
   st = enqueue_score_select(sh, cfg, cache, batch, q, at<float>(ws, L.page_lse), nullptr, sel, cnt, sel_phys, 1,
                             app, s);
   if (st != LK_OK) return st;
-  // 3) attention over the selection (split + merge)
-  st = enqueue_attn(sh, cfg, cache, batch, q, sel, cnt, sel_phys, out, lse_out, ws, L, 1, s);
+  // 3) attention over the selection (split partials)
+  int n_splits = 0;
+  st = enqueue_attn(sh, cfg, cache, batch, q, sel, cnt, sel_phys, out, lse_out, ws, L, 1, false, s, &n_splits);
   if (st != LK_OK) return st;
-  // 4) summaries of pages the append completed; the stored lengths advance here
+  // 4) one launch of (sequence, KV head) workgroups: merge the attention
+  //    partials, advance the stored lengths, and summarize pages the append
+  //    completed
   lk::BuildArgs ba{cache->k_pool, cache->summary_pool, build_list, nullptr, batch,
                    cache->num_phys_pages, sh.hkv, cache->seq_lens, cache->block_table,
-                   cache->max_pages_per_seq};
+                   cache->max_pages_per_seq,
+                   {at<float>(ws, L.part_o), at<float>(ws, L.part_ml), out, lse_out, n_splits, sh.G, sh.hq}};
   return hip_status(lk::launch_build(sh.dt, sh.r, ba, s), "build launch");
 }
 

@@ -15,8 +15,8 @@
 // own online softmax over its tokens (running max m, sum l, output o), and
 // the 8 token groups are combined at the end of the split.
 // The 4 waves' results are combined in LDS into one partial per workgroup;
-// a merge kernel then combines a (sequence, KV head)'s partials for all G
-// heads: o = sum_s e^{m_s - M} o_s / sum_s e^{m_s - M} l_s and
+// the partials of a (sequence, KV head) are then combined for all G heads
+// (by the merge kernel below, or in the decode step's build launch): o = sum_s e^{m_s - M} o_s / sum_s e^{m_s - M} l_s and
 // lse = M + log sum_s e^{m_s - M} l_s.
 
 #include "common.cuh"
@@ -265,89 +265,83 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs
 // Merge: one workgroup per (sequence, KV head) combines the split partials of
 // all G heads: o = sum_s e^{m_s - M} o_s / sum_s e^{m_s - M} l_s and
 // lse = M + log sum_s e^{m_s - M} l_s.
+// Merge for the standalone attention entry points: one workgroup of 4 waves
+// per (sequence, query head); wave w takes splits w, w+4, ...; lane owns dims
+// 2 lane, 2 lane + 1.  (The decode step merges inside its build launch.)
 template <typename T, int G>
 __global__ __launch_bounds__(kAttnWaves * kWave) void attn_merge_kernel(AttnArgs a) {
   constexpr int D = kHeadDim;
-  constexpr int MAXS = 256;  // splits whose weights fit in LDS per pass
-  __shared__ float s_w[MAXS][G];
-  __shared__ float s_M[G], s_L[G];
-  const int kvh = blockIdx.x;
+  __shared__ float s_m[kAttnWaves], s_o[kAttnWaves][D], s_l[kAttnWaves];
+  const int h = blockIdx.x;
   const int seq = blockIdx.y;
-  const float* ml = a.part_ml + ((size_t)seq * a.hkv + kvh) * a.n_splits * G * 2;
-  const float* ob = a.part_o + ((size_t)seq * a.hkv + kvh) * a.n_splits * G * D;
-  const int tid = threadIdx.x;
-  const int wave = tid / kWave, lane = tid & (kWave - 1);
-  // per-head maximum over the splits (wave g reduces head g; G <= 8 heads in 4 waves)
-  for (int g = wave; g < G; g += kAttnWaves) {
-    float mx = -INFINITY;
-    for (int s0 = lane; s0 < a.n_splits; s0 += kWave) mx = fmaxf(mx, ml[((size_t)s0 * G + g) * 2]);
-    mx = group_max<kWave>(mx);
-    if (lane == 0) { s_M[g] = mx; s_L[g] = 0.f; }
-  }
+  const int kvh = h / G;
+  const int g = h % G;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const size_t pbase = ((size_t)seq * a.hkv + kvh) * a.n_splits;
+  const float* ml = a.part_ml;
+  float M = -INFINITY;
+  for (int s0 = threadIdx.x; s0 < a.n_splits; s0 += kAttnWaves * kWave)
+    M = fmaxf(M, ml[((pbase + s0) * G + g) * 2]);
+  M = group_max<kWave>(M);
+  if (lane == 0) s_m[wave] = M;
   __syncthreads();
-  constexpr int NSLOT = (G * D + kAttnWaves * kWave - 1) / (kAttnWaves * kWave);
-  float acc[NSLOT], lacc[NSLOT];
+  M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  float L = 0.f, o0 = 0.f, o1 = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll 4
+    for (int s0 = wave; s0 < a.n_splits; s0 += kAttnWaves) {
+      const float ms = ml[((pbase + s0) * G + g) * 2];
+      const float ls = ml[((pbase + s0) * G + g) * 2 + 1];
+      const float2 ov = reinterpret_cast<const float2*>(a.part_o + ((pbase + s0) * G + g) * D)[lane];
+      const float w = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
+      L = fmaf(w, ls, L);
+      o0 = fmaf(w, ov.x, o0);
+      o1 = fmaf(w, ov.y, o1);
+    }
+  }
+  s_o[wave][2 * lane] = o0;
+  s_o[wave][2 * lane + 1] = o1;
+  if (lane == 0) s_l[wave] = L;
+  __syncthreads();
+  if (wave == 0) {
+    float Lt = 0.f, x0 = 0.f, x1 = 0.f;
 #pragma unroll
-  for (int x = 0; x < NSLOT; ++x) acc[x] = lacc[x] = 0.f;
-  for (int base = 0; base < a.n_splits; base += MAXS) {
-    const int n = min(MAXS, a.n_splits - base);
-    // weights e^{m_s - M} of this pass's splits
-    for (int x = tid; x < n * G; x += kAttnWaves * kWave) {
-      const int s0 = x / G, g = x % G;
-      const float ms = ml[((size_t)(base + s0) * G + g) * 2];
-      s_w[s0][g] = (ms == -INFINITY || s_M[g] == -INFINITY) ? 0.f : fast_exp2(ms - s_M[g]);
+    for (int w = 0; w < kAttnWaves; ++w) {
+      Lt += s_l[w];
+      x0 += s_o[w][2 * lane];
+      x1 += s_o[w][2 * lane + 1];
     }
-    __syncthreads();
-    for (int x = tid, slot = 0; x < G * D; x += kAttnWaves * kWave, ++slot) {
-      const int g = x / D, dim = x % D;
-      float ov = 0.f, lv = 0.f;
-#pragma unroll 16
-      for (int s0 = 0; s0 < n; ++s0) {
-        const float w = s_w[s0][g];
-        ov = fmaf(w, ob[((size_t)(base + s0) * G + g) * D + dim], ov);
-        if (dim == 0) lv = fmaf(w, ml[((size_t)(base + s0) * G + g) * 2 + 1], lv);
-      }
-      acc[slot] += ov;
-      lacc[slot] += lv;
-    }
-    __syncthreads();
-  }
-  for (int x = tid, slot = 0; x < G * D; x += kAttnWaves * kWave, ++slot) {
-    const int dim = x % D;
-    if (dim == 0) s_L[x / D] = lacc[slot];
-  }
-  __syncthreads();
-  for (int x = tid, slot = 0; x < G * D; x += kAttnWaves * kWave, ++slot) {
-    const int g = x / D, dim = x % D;
-    const float L = s_L[g];
-    const int h = kvh * G + g;
-    Elem<T>::store(reinterpret_cast<T*>(a.out) + ((size_t)seq * a.hq + h) * D + dim, L > 0.f ? acc[slot] / L : 0.f);
-    if (a.lse_out && dim == 0)
-      a.lse_out[(size_t)seq * a.hq + h] = L > 0.f ? (s_M[g] + fast_log2(L)) * kLn2 : -INFINITY;
+    const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+    T* out = reinterpret_cast<T*>(a.out) + ((size_t)seq * a.hq + h) * D + 2 * lane;
+    Elem<T>::store(out, x0 * inv);
+    Elem<T>::store(out + 1, x1 * inv);
+    if (a.lse_out && lane == 0)
+      a.lse_out[(size_t)seq * a.hq + h] = Lt > 0.f ? (M + fast_log2(Lt)) * kLn2 : -INFINITY;
   }
 }
 
 template <typename T>
-static hipError_t launch_attn_t(int group, const AttnArgs& a, hipStream_t s) {
+static hipError_t launch_attn_t(int group, const AttnArgs& a, bool merge, hipStream_t s) {
   dim3 grid(a.n_splits, a.hkv, a.batch);
   dim3 block(kAttnWaves * kWave);
-  dim3 mgrid(a.hkv, a.batch);
+  dim3 mgrid(a.hq, a.batch);
   switch (group) {
     case 1: hipLaunchKernelGGL((attn_split_kernel<T, 1>), grid, block, 0, s, a);
-            hipLaunchKernelGGL((attn_merge_kernel<T, 1>), mgrid, block, 0, s, a); break;
+            if (merge) hipLaunchKernelGGL((attn_merge_kernel<T, 1>), mgrid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((attn_split_kernel<T, 2>), grid, block, 0, s, a);
-            hipLaunchKernelGGL((attn_merge_kernel<T, 2>), mgrid, block, 0, s, a); break;
+            if (merge) hipLaunchKernelGGL((attn_merge_kernel<T, 2>), mgrid, block, 0, s, a); break;
     case 4: hipLaunchKernelGGL((attn_split_kernel<T, 4>), grid, block, 0, s, a);
-            hipLaunchKernelGGL((attn_merge_kernel<T, 4>), mgrid, block, 0, s, a); break;
+            if (merge) hipLaunchKernelGGL((attn_merge_kernel<T, 4>), mgrid, block, 0, s, a); break;
     case 8: hipLaunchKernelGGL((attn_split_kernel<T, 8>), grid, block, 0, s, a);
-            hipLaunchKernelGGL((attn_merge_kernel<T, 8>), mgrid, block, 0, s, a); break;
+            if (merge) hipLaunchKernelGGL((attn_merge_kernel<T, 8>), mgrid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_attn(DType dt, int group, const AttnArgs& a, hipStream_t s) {
-  return dt == kBF16 ? launch_attn_t<bf16_t>(group, a, s) : launch_attn_t<float>(group, a, s);
+hipError_t launch_attn(DType dt, int group, const AttnArgs& a, bool merge, hipStream_t s) {
+  return dt == kBF16 ? launch_attn_t<bf16_t>(group, a, merge, s) : launch_attn_t<float>(group, a, merge, s);
 }
 
 }  // namespace lk

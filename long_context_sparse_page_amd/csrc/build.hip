@@ -33,6 +33,39 @@ constexpr float kJacobiTol = 1e-10f;
 constexpr float kZeroModeRtol = 1e-5f;
 constexpr float kZeroModeFloor = 1e-10f;
 
+// Decode step: combine the attention split partials of (seq, kvh) for its G
+// heads, o = sum_s e^{m_s - M} o_s / sum_s e^{m_s - M} l_s and
+// lse = M + log sum_s e^{m_s - M} l_s (max in log2 units); one output per thread.
+template <typename T>
+__device__ __forceinline__ void merge_partials(const BuildArgs& a, int seq, int kvh) {
+  constexpr int D = kHeadDim;
+  const int G = a.merge.group;
+  const int x = threadIdx.x;
+  if (x >= G * D) return;
+  const int g = x / D, dim = x % D;
+  const int ns = a.merge.n_splits;
+  const float* ml = a.merge.part_ml + ((size_t)seq * a.hkv + kvh) * ns * G * 2;
+  const float* ob = a.merge.part_o + ((size_t)seq * a.hkv + kvh) * ns * G * D;
+  float M = -INFINITY;
+  for (int s0 = 0; s0 < ns; ++s0) M = fmaxf(M, ml[((size_t)s0 * G + g) * 2]);
+  float ov = 0.f, lv = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll 8
+    for (int s0 = 0; s0 < ns; ++s0) {
+      const float ms = ml[((size_t)s0 * G + g) * 2];
+      const float f = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+      ov = fmaf(f, ob[((size_t)s0 * G + g) * D + dim], ov);
+      lv = fmaf(f, ml[((size_t)s0 * G + g) * 2 + 1], lv);
+    }
+  }
+  const int h = kvh * G + g;
+  Elem<T>::store(reinterpret_cast<T*>(a.merge.out) + ((size_t)seq * a.merge.hq + h) * D + dim,
+                 lv > 0.f ? ov / lv : 0.f);
+  if (a.merge.lse_out && dim == 0)
+    a.merge.lse_out[(size_t)seq * a.merge.hq + h] =
+        lv > 0.f ? (M + __builtin_amdgcn_logf(lv)) * kLn2 : -INFINITY;
+}
+
 template <typename T, int R>
 __global__ __launch_bounds__(kBuildThreads) void build_kernel(BuildArgs a) {
   constexpr int B = 64;
@@ -66,6 +99,7 @@ __global__ __launch_bounds__(kBuildThreads) void build_kernel(BuildArgs a) {
     if (len >= 0 && page < a.max_pages) ph = a.block_table[(size_t)idx * a.max_pages + page];
     if (ph >= 0 && ph < a.num_phys) a.commit_seq_lens[idx] = len + 1;
   }
+  if (a.merge.part_o) merge_partials<T>(a, idx, kvh);
   const int phys = a.phys_ids[idx];
   if (phys < 0 || phys >= a.num_phys) return;
 

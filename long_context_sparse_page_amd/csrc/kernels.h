@@ -78,11 +78,21 @@ struct BuildArgs {
   int32_t* commit_seq_lens;
   const int32_t* block_table;
   int32_t max_pages;
+  // decode step: workgroup (seq, kvh) first merges the attention partials of
+  // (seq, kvh) for its G heads into out / lse_out (merge.part_o == nullptr: no merge)
+  struct {
+    const float* part_o;
+    const float* part_ml;
+    void* out;
+    float* lse_out;
+    int32_t n_splits, group, hq;
+  } merge;
 };
 
 hipError_t launch_score(DType dt, int rank, int group, const ScoreArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
-hipError_t launch_attn(DType dt, int group, const AttnArgs& a, hipStream_t s);
+// merge = false leaves the split partials for the decode step's build launch
+hipError_t launch_attn(DType dt, int group, const AttnArgs& a, bool merge, hipStream_t s);
 hipError_t launch_build(DType dt, int rank, const BuildArgs& a, hipStream_t s);
 
 }  // namespace lk
