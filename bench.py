@@ -191,12 +191,12 @@ def main():
         "hbm_frac": bytes_step / (ms_per_step * 1e-3) / 8e12,
         "roofline": {
             "bound": "hbm",
-            "kernel": "score_kernel (reconstructed page LSE)",
+            "kernel": "score_mfma_kernel (reconstructed page LSE)",
             "achieved": score_gbs,
             "peak": 8000.0,
             "unit": "GB/s",
             "frac": score_gbs / 8000.0,
-            "traffic": None,
+            "traffic": recorded_traffic(),
             "launch_us": score_ms * 1e3,
             "bytes_per_launch": score_bytes,
         },
@@ -217,6 +217,30 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, lens_now, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+TRAFFIC_PROFILE = "profiles/score_mfma_128K_b4_hbm_traffic.txt"
+
+
+def recorded_traffic():
+    """HBM bytes per scorer launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or None when the scorer's
+    sources have changed since the counters were taken."""
+    import hashlib
+
+    root = os.path.dirname(os.path.abspath(__file__))
+    try:
+        fields = dict(line.strip().split("=", 1) for line in open(os.path.join(root, TRAFFIC_PROFILE))
+                      if "=" in line and not line.startswith(" "))
+        h = hashlib.sha256()
+        for f in fields["kernel_sources"].split():
+            with open(os.path.join(root, f), "rb") as fh:
+                h.update(fh.read())
+        if h.hexdigest() != fields["kernel_sources_sha256"]:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, lens_now, seconds):
