@@ -10,13 +10,16 @@
 // wave takes a run of consecutive half pages of the page list (32 tokens each).  Lane
 // (sg = lane / 8, e = lane % 8) owns dims 16e..16e+15 of tokens sg, sg+8, ...,
 // so K and V are read with coalesced 16-byte loads (eight tokens x 256 bytes
-// per instruction), both issued before any arithmetic.  q . k is
-// summed over the 8 lanes of a token group with DPP; every lane then runs its
-// own online softmax over its tokens (running max m, sum l, output o), and
-// the 8 token groups are combined at the end of the split.
-// The 4 waves' results are combined in LDS into one partial per workgroup;
-// the partials of a (sequence, KV head) are then combined for all G heads
-// (by the merge kernel below, or in the decode step's build launch): o = sum_s e^{m_s - M} o_s / sum_s e^{m_s - M} l_s and
+// per instruction), all issued before any arithmetic; the first half page's
+// loads go out together with the sequence length and the selection count.
+// q . k is summed over the 8 lanes of a token group with DPP; every lane then
+// runs its own online softmax over its tokens (running max m, sum l, output o).
+// At the end every lane is rescaled to its wave's maximum, token groups are
+// added in pairs (or fours) on the VALU, and the workgroup's partials are
+// combined in LDS into one partial per workgroup; the partials of a
+// (sequence, KV head) are then combined for all G heads (by the merge kernel
+// below, or in the decode step's build launch):
+// o = sum_s e^{m_s - M} o_s / sum_s e^{m_s - M} l_s and
 // lse = M + log sum_s e^{m_s - M} l_s.
 
 #include "common.cuh"
@@ -77,6 +80,14 @@ template <> struct KV16<float> {
 
 constexpr int kAttnWaves = 4;
 
+// Partials per workgroup combined through LDS: the 8 token groups of a wave
+// are first paired (G <= 4) or grouped by four (G = 8) on the VALU.
+template <int G> struct AttnCombine {
+  static constexpr int kGroupsPerPartial = G <= 4 ? 2 : 4;
+  static constexpr int kPartialsPerWave = 8 / kGroupsPerPartial;
+  static constexpr int kPartials = kAttnWaves * kPartialsPerWave;
+};
+
 template <typename T, int G>
 __global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs a) {
   constexpr int B = 64;
@@ -84,37 +95,41 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs
   constexpr int TG = 8;               // token groups per wave
   constexpr int HALF = B / 2;         // tokens per unit (half a page)
   constexpr int TPG = HALF / TG;      // tokens per group per unit
-  __shared__ float s_m[kAttnWaves][G], s_l[kAttnWaves][G];
-  __shared__ float s_o[kAttnWaves][G][D];
+  constexpr int NP = AttnCombine<G>::kPartials;
+  constexpr int PPW = AttnCombine<G>::kPartialsPerWave;
+  constexpr int GPP = AttnCombine<G>::kGroupsPerPartial;
+  __shared__ float4 s_o[NP][G][D / 4];
+  __shared__ float s_l[NP][G];
+  __shared__ float s_m[kAttnWaves][G];
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar page-list loads
   const int sg = lane >> 3;
   const int e = lane & 7;
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
   const int seq = blockIdx.z;
+  const int32_t* bt = a.block_table + (size_t)seq * a.max_pages;
 
-  const int len = a.seq_lens[seq] + a.len_add;
-  int n_mr = len > 0 ? (len - 1) / B : -1;
-  if (n_mr > a.max_pages - 1) n_mr = a.max_pages - 1;
-  int n_list;
-  const int32_t* list = nullptr;
-  const int32_t* plist = nullptr;  // physical pages of list (else looked up)
-  if (len <= 0) {
-    n_list = 0;
-  } else if (a.sel_pages) {
-    list = a.sel_pages + ((size_t)seq * a.hkv + kvh) * a.k;
-    if (a.sel_phys) plist = a.sel_phys + ((size_t)seq * a.hkv + kvh) * a.k;
-    n_list = min(a.sel_count[(size_t)seq * a.hkv + kvh], a.k);
-  } else {
-    n_list = n_mr + 1;
-  }
   // units are half pages: unit u is half (u & 1) of list entry u >> 1; wave w
   // of split s takes units [(4 s + w) * ups, +ups)
   const int ups = a.pages_per_split;
   const int u0 = (split * kAttnWaves + wave) * ups;
-  const int u1 = min(u0 + ups, 2 * n_list);
+  const int32_t* list = a.sel_pages ? a.sel_pages + ((size_t)seq * a.hkv + kvh) * a.k : nullptr;
+  const int32_t* plist = (list && a.sel_phys) ? a.sel_phys + ((size_t)seq * a.hkv + kvh) * a.k : nullptr;
+  const int n_entries = list ? a.k : a.max_pages;  // list entries that exist in memory
+
+  // The first unit's page and physical page are fetched together with the
+  // lengths; its K/V loads are issued before the lengths are used (every
+  // address is inside the physical page, tokens past the end are masked).
+  int pg_first = -1, phys_first = -1;
+  if (u0 < 2 * n_entries) {
+    const int x = u0 >> 1;
+    pg_first = list ? list[x] : x;
+    phys_first = plist ? plist[x] : -2;  // -2: look up through the block table
+  }
+  const int len = a.seq_lens[seq] + a.len_add;
+  const int cnt = list ? a.sel_count[(size_t)seq * a.hkv + kvh] : 0;
 
   const T* qp = reinterpret_cast<const T*>(a.q) + ((size_t)seq * a.hq + (size_t)kvh * G) * D + e * 16;
   QSliceBF16 qb[G];
@@ -138,27 +153,46 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs
     for (int i = 0; i < 16; ++i) o[g][i] = 0.f;
   }
   const float zscale = a.scale * kLog2e;
-  const int32_t* bt = a.block_table + (size_t)seq * a.max_pages;
 
-  for (int u = u0; u < u1; ++u) {
-    const int pg = list ? list[u >> 1] : (u >> 1);
-    if (pg < 0 || pg > n_mr) continue;
-    const int phys = plist ? plist[u >> 1] : bt[pg];
-    if (phys < 0 || phys >= a.num_phys) continue;
+  int u = u0;
+  int pg = pg_first, phys = phys_first;
+  if (phys == -2) phys = (pg >= 0 && pg < a.max_pages) ? bt[pg] : -1;
+  KV16<T> kr[TPG], vr[TPG];
+  auto issue = [&](int ph, int unit) {
+    const size_t base = (((size_t)ph * a.hkv + kvh) * B + (unit & 1) * HALF) * D + e * 16;
+    const T* Kp = reinterpret_cast<const T*>(a.k_pool) + base;
+    const T* Vp = reinterpret_cast<const T*>(a.v_pool) + base;
+#pragma unroll
+    for (int x = 0; x < TPG; ++x) {
+      kr[x].load(Kp + (size_t)(sg + TG * x) * D);
+      vr[x].load(Vp + (size_t)(sg + TG * x) * D);
+    }
+  };
+  bool loaded = false;
+  if (len > 0 && phys >= 0 && phys < a.num_phys) { issue(phys, u); loaded = true; }
+
+  int n_mr = len > 0 ? (len - 1) / B : -1;
+  if (n_mr > a.max_pages - 1) n_mr = a.max_pages - 1;
+  const int n_list = len <= 0 ? 0 : (list ? min(cnt, a.k) : n_mr + 1);
+  const int u1 = min(u0 + ups, 2 * n_list);
+
+  for (; u < u1; ++u) {
+    if (u != u0) {
+      pg = list ? list[u >> 1] : (u >> 1);
+      phys = plist ? plist[u >> 1] : ((pg >= 0 && pg < a.max_pages) ? bt[pg] : -1);
+      loaded = phys >= 0 && phys < a.num_phys;
+      if (loaded) issue(phys, u);
+    }
+    if (!loaded || pg < 0 || pg > n_mr) continue;
     const int t_base = (u & 1) * HALF;
     const int n_tok = ((pg == n_mr) ? len - n_mr * B : B) - t_base;  // tokens from t_base on
     if (n_tok <= 0) continue;
-    const size_t base = (((size_t)phys * a.hkv + kvh) * B + t_base) * D + e * 16;
-    const T* Kp = reinterpret_cast<const T*>(a.k_pool) + base;
-    const T* Vp = reinterpret_cast<const T*>(a.v_pool) + base;
-
-    KV16<T> kr[TPG], vr[TPG];
+    if (n_tok < HALF) {  // the filled part of the most recent page only
 #pragma unroll
-    for (int x = 0; x < TPG; ++x) {
-      const int t = sg + TG * x;
-      if (t < n_tok) { kr[x].load(Kp + (size_t)t * D); vr[x].load(Vp + (size_t)t * D); }
-      else { kr[x].zero(); vr[x].zero(); }
+      for (int x = 0; x < TPG; ++x)
+        if (sg + TG * x >= n_tok) { kr[x].zero(); vr[x].zero(); }
     }
+
     float z[TPG][G];
 #pragma unroll
     for (int x = 0; x < TPG; ++x) {
@@ -184,31 +218,41 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs
         const float full = group_sum<8>(z[x][g]);
         z[x][g] = (sg + TG * x < n_tok) ? full * zscale : -INFINITY;
       }
+    // running max, rescale and probabilities per head (a head with no token
+    // yet keeps m = -inf and gets p = 0), then P V one token at a time
+    float p[TPG][G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float pm = -INFINITY;
 #pragma unroll
       for (int x = 0; x < TPG; ++x) pm = fmaxf(pm, z[x][g]);
       const float m_new = fmaxf(m[g], pm);
-      if (m_new == -INFINITY) continue;  // no token of this lane yet
-      const float corr = fast_exp2(m[g] - m_new);
+      const float mref = (m_new == -INFINITY) ? 0.f : m_new;
+      const float corr = fast_exp2(m[g] - mref);
       m[g] = m_new;
       l[g] *= corr;
 #pragma unroll
       for (int y = 0; y < 16; ++y) o[g][y] *= corr;
 #pragma unroll
       for (int x = 0; x < TPG; ++x) {
-        const float p = fast_exp2(z[x][g] - m_new);
-        l[g] += p;
-        float vx[16];
-        vr[x].to_f32(vx);
-#pragma unroll
-        for (int y = 0; y < 16; ++y) o[g][y] = fmaf(p, vx[y], o[g][y]);
+        p[x][g] = fast_exp2(z[x][g] - mref);
+        l[g] += p[x][g];
       }
+    }
+#pragma unroll
+    for (int x = 0; x < TPG; ++x) {
+      float vx[16];
+      vr[x].to_f32(vx);
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int y = 0; y < 16; ++y) o[g][y] = fmaf(p[x][g], vx[y], o[g][y]);
     }
   }
 
-  // combine the 8 token groups of this wave (lanes e, e+8, ..., e+56)
+  // Combine: rescale every lane to its wave's running max, add token groups
+  // pairwise (G <= 4) or by four (G = 8) on the VALU, then the workgroup's
+  // NP partials in LDS with the waves' weights e^{M_w - M}.
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     float M = fmaxf(m[g], dpp<kDppRor8>(m[g]));
@@ -216,50 +260,59 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs
     const float f = (M == -INFINITY) ? 0.f : fast_exp2(m[g] - M);
     float lg = l[g] * f;
     lg += dpp<kDppRor8>(lg);
-    lg = xor32_sum(xor16_sum(lg));
+    if constexpr (GPP == 4) lg = xor16_sum(lg);
+    l[g] = lg;
 #pragma unroll
     for (int y = 0; y < 16; ++y) {
       float v = o[g][y] * f;
       v += dpp<kDppRor8>(v);
-      o[g][y] = xor32_sum(xor16_sum(v));
+      if constexpr (GPP == 4) v = xor16_sum(v);
+      o[g][y] = v;
     }
     m[g] = M;
-    l[g] = lg;
   }
-  // combine the workgroup's waves through LDS into one partial per workgroup
-  if (sg == 0) {
+  if (sg % GPP == 0) {
+    const int p = wave * PPW + sg / GPP;
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G; ++g) {
 #pragma unroll
-      for (int y = 0; y < 16; ++y) s_o[wave][g][e * 16 + y] = o[g][y];
+      for (int y = 0; y < 4; ++y)
+        s_o[p][g][e * 4 + y] = make_float4(o[g][4 * y], o[g][4 * y + 1], o[g][4 * y + 2], o[g][4 * y + 3]);
+      if (e == 0) s_l[p][g] = l[g];
+    }
   }
   if (lane == 0) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) { s_m[wave][g] = m[g]; s_l[wave][g] = l[g]; }
+    for (int g = 0; g < G; ++g) s_m[wave][g] = m[g];
   }
   __syncthreads();
   const size_t pidx = ((size_t)seq * a.hkv + kvh) * a.n_splits + split;
-  for (int x = threadIdx.x; x < G * D; x += kAttnWaves * kWave) {
-    const int g = x / D, dim = x % D;
+  for (int x = threadIdx.x; x < G * (D / 4); x += kAttnWaves * kWave) {
+    const int g = x / (D / 4), d4 = x % (D / 4);
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, s_m[w][g]);
-    float ov = 0.f, lv = 0.f;
+    float4 ov = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lv = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kAttnWaves; ++w) {
         const float f = s_m[w][g] == -INFINITY ? 0.f : fast_exp2(s_m[w][g] - M);
-        ov = fmaf(f, s_o[w][g][dim], ov);
-        lv = fmaf(f, s_l[w][g], lv);
+#pragma unroll
+        for (int q = 0; q < PPW; ++q) {
+          const float4 v = s_o[w * PPW + q][g][d4];
+          ov.x = fmaf(f, v.x, ov.x); ov.y = fmaf(f, v.y, ov.y);
+          ov.z = fmaf(f, v.z, ov.z); ov.w = fmaf(f, v.w, ov.w);
+          lv = fmaf(f, s_l[w * PPW + q][g], lv);
+        }
       }
     }
-    a.part_o[(pidx * G + g) * D + dim] = ov;
-    if (dim == 0) {
+    reinterpret_cast<float4*>(a.part_o + (pidx * G + g) * D)[d4] = ov;
+    if (d4 == 0) {
       a.part_ml[(pidx * G + g) * 2 + 0] = M;
       a.part_ml[(pidx * G + g) * 2 + 1] = lv;
     }
   }
-
 }
 
 // Merge: one workgroup per (sequence, KV head) combines the split partials of
