@@ -337,3 +337,100 @@ def test_group_and_rank_variants_fp32(gpu, group, rank):
     hs = res[(0, 0)][0]
     out = o["out"].cpu().numpy().astype(np.float64)[0]
     assert ref.rel_l2(out, hs.out).max() < 1e-5
+
+
+# ----------------------------------------------------------------------------
+# Selector paths: a pivot short list in registers, every candidate when few
+# threads hold one, the block-wide fallback when ties overflow the list, and
+# the large-table tiers (scores loaded twice).
+
+def _selector_case(T, budget, capacity=None, group=4, layout=None):
+    """fp32 single-sequence cache holding T tokens whose keys may be rearranged
+    by ``layout(keys)`` (page copies make exact ties); returns the workload,
+    cache, host K/V pages and fp64 queries."""
+    w = synth.workload(0, budget=budget)
+    w.context = [T]
+    w.num_q_heads = group
+    dc = DeviceCache(w, poison=True, capacity_pages=[capacity] if capacity else None)
+    kk, vv = synth.keys_values(w, 0, 0)
+    kk, vv = kk[:T].copy(), vv[:T].copy()
+    q = np.random.default_rng(T).standard_normal((1, group, w.head_dim)).astype(np.float32)
+    if layout is not None:
+        q = layout(kk, q)
+    dc.write_tokens(0, 0, 0, to_storage(kk, w.dtype), to_storage(vv, w.dtype))
+    dc.build_all()
+    B, d = w.page_size, w.head_dim
+    n_pages = -(-T // B)
+    K = np.zeros((n_pages * B, d))
+    V = np.zeros((n_pages * B, d))
+    K[:T] = ref.stored(kk, w.dtype)
+    V[:T] = ref.stored(vv, w.dtype)
+    return w, dc, K.reshape(n_pages, B, d), V.reshape(n_pages, B, d), ref.stored(q, w.dtype)
+
+
+def _run_selector(w, dc, K, V, q64):
+    T = w.context
+    hs, _ = ref.oracle_head(w, q64[0], K, V, T[0])
+    o = dc.outputs()
+    dc.score_select(ref.q_device(q64, w.dtype), o)
+    torch.cuda.synchronize()
+    check_scores(w, dc, o, {(0, 0): (hs, None, K, V)}, T, atol=1e-3)
+    sel = o["sel"].cpu().numpy()[0, 0, :o["cnt"].cpu().numpy()[0, 0]]
+    return [int(x) for x in sel], hs
+
+
+def test_selector_ties_overflow_list(gpu):
+    """Every candidate page is a copy of page 1: all shares tie, more than the
+    short list holds, so the block-wide path must pick the lowest indices."""
+    T = 64 * 400 + 10
+
+    def layout(kk, q):
+        for p in range(2, T // 64):
+            kk[p * 64:(p + 1) * 64] = kk[64:128]
+        return q
+
+    say("selector: ties over", T // 64 - 1, "candidates, budget 2048")
+    w, dc, K, V, q64 = _selector_case(T, 2048, layout=layout)
+    sel, hs = _run_selector(w, dc, K, V, q64)
+    n_mr = lo.most_recent_page(T, w.page_size)
+    expect = [0] + list(range(1, 31)) + [n_mr]
+    assert list(hs.selected) == expect
+    assert sel == expect
+
+
+def test_selector_ties_at_cut(gpu):
+    """41 copies of one page dominate the shares; the 30 selected must be the
+    30 lowest-index copies (the list holds all candidates above the pivot)."""
+    T = 64 * 150 + 5
+    hot = sorted(np.random.default_rng(11).choice(np.arange(2, 149), size=40, replace=False).tolist())
+
+    def layout(kk, q):
+        u = np.random.default_rng(12).standard_normal(kk.shape[1])
+        u /= np.linalg.norm(u)
+        base = kk[64:128] + 2.0 * u  # every token of a hot page leans along u
+        for p in [1] + hot:
+            kk[p * 64:(p + 1) * 64] = base
+        return (q * 0.1 + 3.0 * np.sqrt(kk.shape[1]) * u).astype(np.float32)
+
+    say("selector: 41 tied pages at the cut, budget 2048")
+    w, dc, K, V, q64 = _selector_case(T, 2048, layout=layout)
+    sel, hs = _run_selector(w, dc, K, V, q64)
+    n_mr = lo.most_recent_page(T, w.page_size)
+    tied = sorted([1] + hot)
+    assert min(hs.m_bar[j] for j in tied) > max(hs.m_bar[j] for j in range(1, n_mr) if j not in tied)
+    expect = sorted([0, n_mr] + tied[:30])
+    assert list(hs.selected) == expect
+    assert sel == expect
+
+
+@pytest.mark.parametrize("T,budget,capacity,group", [
+    (64 * 101 + 3, 4096, None, 4),     # fewer threads hold candidates than the budget needs
+    (64 * 300 + 7, 2048, 3300, 4),     # 1024-thread tier, scores loaded twice
+    (64 * 700 + 40, 1024, 13000, 4),   # largest-table tier at G = 4
+    (64 * 500 + 1, 2048, 9000, 8),     # 1024-thread tier at G = 8
+])
+def test_selector_tiers(gpu, T, budget, capacity, group):
+    say("selector tier: T", T, "budget", budget, "capacity", capacity, "G", group)
+    w, dc, K, V, q64 = _selector_case(T, budget, capacity=capacity, group=group)
+    sel, hs = _run_selector(w, dc, K, V, q64)
+    assert len(sel) == len(hs.selected)
