@@ -154,9 +154,28 @@ def keys_values(w: Workload, seq: int, kv_head: int, bases: np.ndarray | None = 
     b = rk.standard_normal((n_pages * B, GLOBAL_RANK), dtype=f32)
     keys = rk.standard_normal((n_pages * B, d), dtype=f32)
     keys *= f32(KEY_NOISE)
-    local = a.reshape(n_pages, B, LOCAL_RANK) @ bases[:n_pages].astype(f32)
-    keys += f32(LOCAL_SCALE) * local.reshape(n_pages * B, d)
-    keys += f32(GLOBAL_SCALE) * (b @ gb.astype(f32))
+    # Components as fixed-order elementwise sums (no BLAS): a float32 matrix
+    # product may round differently with the library's thread partitioning,
+    # and every caller, in any thread, must get the same bits.
+    a3 = a.reshape(n_pages, B, LOCAL_RANK)
+    b32 = bases[:n_pages].astype(f32)
+    acc = np.empty((n_pages, B, d), dtype=f32)
+    tmp = np.empty_like(acc)
+    np.multiply(a3[:, :, 0, None], b32[:, None, 0, :], out=acc)
+    for m in range(1, LOCAL_RANK):
+        np.multiply(a3[:, :, m, None], b32[:, None, m, :], out=tmp)
+        acc += tmp
+    acc *= f32(LOCAL_SCALE)
+    keys += acc.reshape(n_pages * B, d)
+    g32 = gb.astype(f32)
+    acc2 = acc.reshape(n_pages * B, d)
+    tmp2 = tmp.reshape(n_pages * B, d)
+    np.multiply(b[:, 0, None], g32[0], out=acc2)
+    for m in range(1, GLOBAL_RANK):
+        np.multiply(b[:, m, None], g32[m], out=tmp2)
+        acc2 += tmp2
+    acc2 *= f32(GLOBAL_SCALE)
+    keys += acc2
     values = _rng(w.wid, _P_VALUES, seq, kv_head).standard_normal((T, d), dtype=f32)
     return keys[:T], values
 
