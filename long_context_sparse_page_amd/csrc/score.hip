@@ -23,10 +23,9 @@
 namespace lk {
 
 constexpr int kScoreWaves = 4;
-#ifndef LK_SCORE_PIPELINE
-#define LK_SCORE_PIPELINE 1
+#ifndef LK_SCORE_GPW
+#define LK_SCORE_GPW 1
 #endif
-constexpr bool kScorePipeline = LK_SCORE_PIPELINE;
 constexpr int kScorePagesPerWave = 8;
 constexpr int kScorePagesPerBlock = kScoreWaves * kScorePagesPerWave;
 
@@ -199,14 +198,19 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_kernel(ScoreArgs a)
 // P[slot][g] = W_slot . q_g.  Lane l of B supplies column l % 16 and 8
 // consecutive dims of K-step t at group l / 16, i.e. one 16-byte load; lane l
 // of A supplies the same dims of query l % 16.  The accumulator of lane l
-// holds rows 4 (l / 16) .. +3 of column l % 16.  All of a group's record rows
-// and coefficients are loaded before any arithmetic.
+// holds rows 4 (l / 16) .. +3 of column l % 16.
+//
+// Every record byte a wave needs is requested in its prologue, before any
+// arithmetic, and waves are short (one group of NR records by default): on
+// this part a scattered read of many short-lived waves, each with one batch
+// of loads in flight, streams faster than fewer waves that loop over several
+// batches.
 template <int R> struct ScoreGroup {
   static constexpr int NR = R >= 16 ? 2 : (R >= 8 ? 4 : (R >= 4 ? 8 : 16));  // records per group
   static constexpr int SLOTS = NR * (R + 1);
   static constexpr int TILES = (SLOTS + 15) / 16;
   static constexpr int CW = (R + 1) / 2;        // 32-bit words of one token's coefficients
-  static constexpr int GROUPS_PER_WAVE = 4;
+  static constexpr int GROUPS_PER_WAVE = LK_SCORE_GPW;
 };
 
 // One group's loads, held in registers until the group is computed.
@@ -284,7 +288,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_mfma_kernel(ScoreAr
   __shared__ float sZ[kScoreWaves][G * B];
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar table loads
   const int seq = blockIdx.z;
   const int kvh = blockIdx.y;
   append_duty<bf16_t>(a, seq, kvh);
@@ -297,7 +301,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_mfma_kernel(ScoreAr
 
   // Loads that do not depend on the sequence length go out first: the
   // wave's block-table slice (clamped in bounds), the group's queries, and
-  // then the first group's records (pages past the sequence end are masked
+  // then every record of the wave (pages past the sequence end are masked
   // when results are written).
   int phys_all[PAGES_PER_WAVE];
 #pragma unroll
@@ -313,8 +317,12 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_mfma_kernel(ScoreAr
       qa[t] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
-  GroupLoads<R> cur, nxt;
-  load_group<R>(cur, summ, phys_all, j0, a.max_pages, a.num_phys, a.hkv, kvh, col, kg, lane);
+  constexpr int GPW = ScoreGroup<R>::GROUPS_PER_WAVE;
+  GroupLoads<R> grp[GPW];
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi)
+    load_group<R>(grp[gi], summ, phys_all + gi * NR, j0 + gi * NR, a.max_pages, a.num_phys, a.hkv, kvh, col, kg,
+                  lane);
 
   if (len_raw <= 0) return;
   int n_scored = (len_raw - 1) / B;
@@ -328,15 +336,10 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_mfma_kernel(ScoreAr
   float* Z = sZ[wave];
 
 #pragma unroll
-  for (int gi = 0; gi < ScoreGroup<R>::GROUPS_PER_WAVE; ++gi) {
+  for (int gi = 0; gi < GPW; ++gi) {
+    const GroupLoads<R>& cur = grp[gi];
     const int g0 = j0 + gi * NR;
     if (g0 >= j_end) break;
-    // software pipeline: the next group's loads are in flight while this one computes
-    if (kScorePipeline && gi + 1 < ScoreGroup<R>::GROUPS_PER_WAVE && g0 + NR < j_end)
-      load_group<R>(nxt, summ, phys_all + (gi + 1) * NR, g0 + NR, a.max_pages, a.num_phys, a.hkv, kvh, col, kg, lane);
-    if (!kScorePipeline && gi > 0)
-      load_group<R>(cur, summ, phys_all + gi * NR, g0, a.max_pages, a.num_phys, a.hkv, kvh, col, kg, lane);
-
     // projection on the matrix cores
 #pragma unroll
     for (int tau = 0; tau < TILES; ++tau) {
@@ -390,7 +393,6 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_mfma_kernel(ScoreAr
       if (lane % LPH == 0) out[(size_t)hg * a.max_pages + j] = (mx + fast_log2(sum)) * kLn2;
       wave_lds_fence();
     }
-    if (kScorePipeline) cur = nxt;
   }
 }
 
