@@ -1,4 +1,4 @@
-// Page summary builder: one workgroup of 1024 threads per (page, KV head).
+// Page summary builder: one workgroup of 256 threads per (page, KV head).
 //
 // [Locks] §4 "Build (once, when a page completes)": centre the page,
 // k_i = mu + delta_i; stack the deviations as rows of D (B x d); eigendecompose
@@ -7,16 +7,20 @@
 // orthonormal basis V = D^T U_r Sigma_r^{-1}; zero modes are dropped with
 // zero coefficients.
 //
-// Device plan: the K tile is widened to fp32 and centred in LDS (stored
-// transposed, D^T, so the Gram and basis reads are bank-conflict free); the
-// Gram is formed in fp32; the eigendecomposition is a cyclic parallel Jacobi
-// method held in LDS: each round rotates 32 disjoint index pairs chosen by the
-// circle (round-robin) ordering, with the symmetric Schur rotation of Golub &
-// Van Loan (Matrix Computations, sym.schur2).  A round is one 2 x 2 block
-// update of the upper block triangle per thread (mirrored, so A stays exactly
-// symmetric; the rotated pair is set exactly: a_pp - t a_pq, a_qq + t a_pq, 0)
-// plus two column-pair updates of the accumulated eigenvector matrix U.
-// Sweeps stop when the off-diagonal energy is below 1e-10 of the total.
+// Only the top r eigenpairs of the Gram are needed, so the symmetric
+// eigenproblem is solved the way one computes a few eigenpairs of a dense
+// symmetric matrix (Golub & Van Loan, Matrix Computations, ch. 8):
+//   1. Householder reduction to tridiagonal form T = Q^T A Q (62 reflections;
+//      the reflector vectors are kept in the strict lower part of A);
+//   2. the r largest eigenvalues of T by Sturm-sequence multisection (each of
+//      a wave's 64 lanes counts the eigenvalues below its own shift, so an
+//      interval shrinks 65-fold per pass);
+//   3. their eigenvectors of T by inverse iteration with partial pivoting,
+//      re-orthogonalized within clusters of close eigenvalues;
+//   4. back-transformation by the reflectors.
+// All B eigenvalues (for the optional eigenvalue output) are found by plain
+// bisection, one lane per eigenvalue.  The K tile is widened to fp32 and
+// centred in LDS, stored transposed (D^T) for the Gram and the basis.
 //
 // Zero-mode rule: eigenvalue <= 1e-5 * lambda_1 or <= 1e-10 * sum_i ||k_i||^2.
 // Sign rule: each basis vector's largest-magnitude entry is made positive.
@@ -26,69 +30,91 @@
 
 namespace lk {
 
-constexpr int kBuildThreads = 1024;
+constexpr int kBuildThreads = 256;
+constexpr int kMergeThreads = 512;      // decode-step launch: one merged output per thread for G <= 4
 constexpr int kBuildWaves = kBuildThreads / kWave;
-constexpr int kBuildMaxSweeps = 15;
-constexpr float kJacobiTol = 1e-10f;
 constexpr float kZeroModeRtol = 1e-5f;
 constexpr float kZeroModeFloor = 1e-10f;
+constexpr int kInvIters = 3;         // inverse-iteration passes per eigenvector
+constexpr float kClusterTol = 1e-3f; // eigenvalues this close (relative to lambda_1) are re-orthogonalized
 
 // Decode step: combine the attention split partials of (seq, kvh) for its G
 // heads, o = sum_s e^{m_s - M} o_s / sum_s e^{m_s - M} l_s and
-// lse = M + log sum_s e^{m_s - M} l_s (max in log2 units); one output per thread.
+// lse = M + log sum_s e^{m_s - M} l_s (max in log2 units).
 template <typename T>
 __device__ __forceinline__ void merge_partials(const BuildArgs& a, int seq, int kvh) {
   constexpr int D = kHeadDim;
   const int G = a.merge.group;
-  const int x = threadIdx.x;
-  if (x >= G * D) return;
-  const int g = x / D, dim = x % D;
   const int ns = a.merge.n_splits;
   const float* ml = a.merge.part_ml + ((size_t)seq * a.hkv + kvh) * ns * G * 2;
   const float* ob = a.merge.part_o + ((size_t)seq * a.hkv + kvh) * ns * G * D;
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < ns; ++s0) M = fmaxf(M, ml[((size_t)s0 * G + g) * 2]);
-  float ov = 0.f, lv = 0.f;
-  if (M != -INFINITY) {
+  for (int x = threadIdx.x; x < G * D; x += blockDim.x) {
+    const int g = x / D, dim = x % D;
+    float M = -INFINITY;
+    for (int s0 = 0; s0 < ns; ++s0) M = fmaxf(M, ml[((size_t)s0 * G + g) * 2]);
+    float ov = 0.f, lv = 0.f;
+    if (M != -INFINITY) {
 #pragma unroll 8
-    for (int s0 = 0; s0 < ns; ++s0) {
-      const float ms = ml[((size_t)s0 * G + g) * 2];
-      const float f = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-      ov = fmaf(f, ob[((size_t)s0 * G + g) * D + dim], ov);
-      lv = fmaf(f, ml[((size_t)s0 * G + g) * 2 + 1], lv);
+      for (int s0 = 0; s0 < ns; ++s0) {
+        const float ms = ml[((size_t)s0 * G + g) * 2];
+        const float f = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+        ov = fmaf(f, ob[((size_t)s0 * G + g) * D + dim], ov);
+        lv = fmaf(f, ml[((size_t)s0 * G + g) * 2 + 1], lv);
+      }
     }
+    const int h = kvh * G + g;
+    Elem<T>::store(reinterpret_cast<T*>(a.merge.out) + ((size_t)seq * a.merge.hq + h) * D + dim,
+                   lv > 0.f ? ov / lv : 0.f);
+    if (a.merge.lse_out && dim == 0)
+      a.merge.lse_out[(size_t)seq * a.merge.hq + h] =
+          lv > 0.f ? (M + __builtin_amdgcn_logf(lv)) * kLn2 : -INFINITY;
   }
-  const int h = kvh * G + g;
-  Elem<T>::store(reinterpret_cast<T*>(a.merge.out) + ((size_t)seq * a.merge.hq + h) * D + dim,
-                 lv > 0.f ? ov / lv : 0.f);
-  if (a.merge.lse_out && dim == 0)
-    a.merge.lse_out[(size_t)seq * a.merge.hq + h] =
-        lv > 0.f ? (M + __builtin_amdgcn_logf(lv)) * kLn2 : -INFINITY;
+}
+
+// Number of eigenvalues of the symmetric tridiagonal (d, e) below sigma: the
+// negative pivots of the LDL^T factorization of T - sigma I (Sturm count).
+// e2[i] = e[i]^2; pivots smaller than pivmin are replaced by -pivmin.
+__device__ __forceinline__ int sturm_count(const float* sd, const float* se2, float sigma, float pivmin) {
+  constexpr int B = 64;
+  float q = sd[0] - sigma;
+  if (fabsf(q) < pivmin) q = -pivmin;
+  int c = q < 0.f ? 1 : 0;
+#pragma unroll 8
+  for (int i = 1; i < B; ++i) {
+    q = (sd[i] - sigma) - se2[i - 1] * __builtin_amdgcn_rcpf(q);
+    if (fabsf(q) < pivmin) q = -pivmin;
+    c += q < 0.f ? 1 : 0;
+  }
+  return c;
 }
 
 template <typename T, int R>
-__global__ __launch_bounds__(kBuildThreads) void build_kernel(BuildArgs a) {
+__global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
   constexpr int B = 64;
   constexpr int D = kHeadDim;
-  constexpr int NP = B / 2;                 // pairs per round
-  constexpr int NBLK = NP * (NP + 1) / 2;   // upper 2x2 blocks (528)
   constexpr int KEPT = R < B ? R : B;
-  constexpr int LDA = B + 1;
+  constexpr int KW = (KEPT + kBuildWaves - 1) / kBuildWaves;  // eigenvectors per wave
+  constexpr int LDT = 68;                  // D^T row stride (16-byte aligned rows)
+  constexpr int LA = B + 1;
+  static_assert(KEPT <= 16, "rank above 16");
 
-  __shared__ float sDT[D][LDA];             // D^T: sDT[c][i] = delta_i[c]
-  __shared__ float sA[B][LDA];              // Gram -> diagonal; later the basis
-  __shared__ float sU[B][LDA];
+  __shared__ float sDT[D][LDT];            // D^T: sDT[c][i] = delta_i[c]
+  __shared__ float sA[B + 1][LA];          // Gram (+ a zero pad row); reflectors below the diagonal; later the basis
   __shared__ float sMu[D];
-  __shared__ float4 sPar[NP];               // c, s, t, (p | q << 8) as bits
-  __shared__ float sLam[B];
-  __shared__ int sOrder[B];
+  __shared__ float sd[B], se[B], se2[B];   // tridiagonal T (e[i] couples i, i + 1)
+  __shared__ float su[2][B], sp[B];        // reflectors (double-buffered) and p = 2 A22 u
   __shared__ float sRed[2][kBuildWaves];
+  __shared__ float sLam[KEPT];             // top eigenvalues, descending
+  __shared__ float sZ[B][KEPT];            // eigenvectors (of T, then of A)
+  __shared__ float sRP[B][KEPT], sDU[B][KEPT], sDU2[B][KEPT], sML[B][KEPT], sZZ[B][KEPT];  // inverse-iteration factors
+  __shared__ int sSW[B][KEPT];
   __shared__ float sSigma[KEPT], sSign[KEPT];
-  __shared__ int sCol[KEPT], sNz[KEPT];
+  __shared__ int sNz[KEPT];
+  __shared__ float sBound[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int idx = blockIdx.x;
   const int kvh = blockIdx.y;
   if (a.commit_seq_lens && kvh == 0 && tid == 0) {
@@ -100,24 +126,21 @@ __global__ __launch_bounds__(kBuildThreads) void build_kernel(BuildArgs a) {
     if (ph >= 0 && ph < a.num_phys) a.commit_seq_lens[idx] = len + 1;
   }
   if (a.merge.part_o) merge_partials<T>(a, idx, kvh);
+  // The decode step launches kMergeThreads threads for the merge; the build
+  // below runs on the first kBuildThreads (a barrier waits only for waves
+  // that have not ended).
+  if (tid >= kBuildThreads) return;
   const int phys = a.phys_ids[idx];
   if (phys < 0 || phys >= a.num_phys) return;
 
-  // this thread's upper block (k1 <= k2), if any
-  int k1 = -1, k2 = -1;
-  if (tid < NBLK) {
-    int rem = tid;
-    k1 = 0;
-    while (rem >= NP - k1) { rem -= NP - k1; ++k1; }
-    k2 = k1 + rem;
-  }
-
-  // 1) load K (8 elements per thread), energy, transpose into LDS
+  // 1) load K (32 elements per thread), energy sum ||k_i||^2, transpose into LDS
   const T* K = reinterpret_cast<const T*>(a.k_pool) + (((size_t)phys * a.hkv + kvh) * B) * D;
   float en = 0.f;
-  {
-    const int row = tid >> 4;
-    const int c0 = (tid & 15) * 8;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int x = tid + kBuildThreads * it;
+    const int row = x >> 4;
+    const int c0 = (x & 15) * 8;
     float v[8];
     load8(K + (size_t)row * D + c0, v);
 #pragma unroll
@@ -129,6 +152,7 @@ __global__ __launch_bounds__(kBuildThreads) void build_kernel(BuildArgs a) {
   float energy = 0.f;
 #pragma unroll
   for (int w = 0; w < kBuildWaves; ++w) energy += sRed[0][w];
+
   // 2) centroid and centring
   if (tid < D) {
     float s = 0.f;
@@ -137,144 +161,308 @@ __global__ __launch_bounds__(kBuildThreads) void build_kernel(BuildArgs a) {
   }
   __syncthreads();
   {
-    const int row = tid >> 4;
-    const int c0 = (tid & 15) * 8;
+    const int c = tid >> 1;
+    const int i0 = (tid & 1) * (B / 2);
+    const float mu = sMu[c];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) sDT[c0 + t][row] -= sMu[c0 + t];
+    for (int i = 0; i < B / 2; ++i) sDT[c][i0 + i] -= mu;
   }
   __syncthreads();
 
-  // 3) Gram A = D D^T (2 x 2 tile per thread), U = I
+  // 3) Gram A = D D^T, a 4 x 4 tile per thread (both halves: exactly symmetric)
   {
-    const int bi = tid >> 5, bj = tid & 31;
-    float a00 = 0.f, a01 = 0.f, a10 = 0.f, a11 = 0.f;
+    const int ti = tid >> 4, tj = tid & 15;
+    float acc[4][4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) acc[x][y] = 0.f;
     for (int c = 0; c < D; ++c) {
-      const float x0 = sDT[c][2 * bi], x1 = sDT[c][2 * bi + 1];
-      const float y0 = sDT[c][2 * bj], y1 = sDT[c][2 * bj + 1];
-      a00 = fmaf(x0, y0, a00); a01 = fmaf(x0, y1, a01);
-      a10 = fmaf(x1, y0, a10); a11 = fmaf(x1, y1, a11);
+      const float4 xi = *reinterpret_cast<const float4*>(&sDT[c][4 * ti]);
+      const float4 yj = *reinterpret_cast<const float4*>(&sDT[c][4 * tj]);
+      const float xa[4] = {xi.x, xi.y, xi.z, xi.w};
+      const float ya[4] = {yj.x, yj.y, yj.z, yj.w};
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(xa[x], ya[y], acc[x][y]);
     }
-    sA[2 * bi][2 * bj] = a00; sA[2 * bi][2 * bj + 1] = a01;
-    sA[2 * bi + 1][2 * bj] = a10; sA[2 * bi + 1][2 * bj + 1] = a11;
-    sU[2 * bi][2 * bj] = (bi == bj) ? 1.f : 0.f;
-    sU[2 * bi][2 * bj + 1] = 0.f;
-    sU[2 * bi + 1][2 * bj] = 0.f;
-    sU[2 * bi + 1][2 * bj + 1] = (bi == bj) ? 1.f : 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y) sA[4 * ti + x][4 * tj + y] = acc[x][y];
   }
   __syncthreads();
 
-  // 4) cyclic parallel Jacobi
-  for (int sweep = 0; sweep < kBuildMaxSweeps; ++sweep) {
-    for (int r = 0; r < B - 1; ++r) {
-      if (tid < NP) {
-        const int k = tid;
-        const int p = k == 0 ? B - 1 : (r + k) % (B - 1);
-        const int q = k == 0 ? r : (r - k + (B - 1)) % (B - 1);
-        const float app = sA[p][p], aqq = sA[q][q], apq = sA[p][q];
-        float c = 1.f, s = 0.f, t = 0.f;
-        if (apq != 0.f) {
-          const float tau = (aqq - app) / (2.f * apq);
-          t = (tau >= 0.f ? 1.f : -1.f) / (fabsf(tau) + sqrtf(1.f + tau * tau));
-          c = 1.f / sqrtf(1.f + t * t);
-          s = t * c;
-        }
-        sPar[k] = make_float4(c, s, t, __int_as_float(p | (q << 8)));
+  // 4) Householder tridiagonalization.  Step k zeroes column k below the
+  //    subdiagonal with H = I - 2 u u^T (||u|| = 1), u stored in A[k+1.., k];
+  //    with p = 2 A22 u and w = p - (u.p) u, A22 <- A22 - u w^T - w u^T.
+  //    Two barriers per step: wave 0 updates column 0 of A22 itself and
+  //    derives the next reflector from it before the step's closing barrier.
+  auto reflector = [&](int k, float x, int buf) {  // wave 0; x = A[k+1+lane][k] (0 past the end)
+    const int m = B - 1 - k;
+    const float nrm2 = group_sum<kWave>(x * x);
+    const float x0 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+    float u = 0.f, alpha = 0.f;
+    if (nrm2 > 0.f) {
+      const float nrm = sqrtf(nrm2);
+      alpha = x0 >= 0.f ? -nrm : nrm;
+      const float inv = __builtin_amdgcn_rsqf(2.f * (nrm2 + nrm * fabsf(x0)));  // 1 / ||x - alpha e_1||
+      u = (lane == 0 ? x - alpha : x) * inv;
+    }
+    su[buf][lane] = lane < m ? u : 0.f;  // zero tail: row blocks may run past column m
+    if (lane < m) sA[k + 1 + lane][k] = u;
+    if (lane == 0) se[k] = alpha;
+  };
+  if (tid < LA) sA[B][tid] = 0.f;  // pad row and pad column, read by the blocks of the last rows
+  if (tid < B) sA[tid][B] = 0.f;
+  if (wave == 0) {
+    if (lane == 0) sd[0] = sA[0][0];
+    reflector(0, lane < B - 1 ? sA[1 + lane][0] : 0.f, 0);
+  }
+  __syncthreads();
+  const int mrow = tid >> 2, mq = tid & 3;   // matvec / update: row and column quarter
+  for (int k = 0; k < B - 2; ++k) {
+    const int m = B - 1 - k;
+    const int buf = k & 1;
+    const float* uu = su[buf];
+    // p = 2 A22 u: row mrow, columns mq + 4 s (clamped loads, masked terms);
+    // the four quarters are summed over lanes
+    // (columns 16 mq .. 16 mq + 15; entries past m meet zero reflector entries
+    // and stay inside sA thanks to the pad row)
+    float pp = 0.f;
+    if (mrow < m) {
+      const float* Ar = &sA[k + 1 + mrow][k + 1 + 16 * mq];
+      const float* ub = uu + 16 * mq;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) pp = fmaf(Ar[t], ub[t], pp);
+    }
+    pp += dpp<kDppXor1>(pp);
+    pp += dpp<kDppXor2>(pp);
+    pp *= 2.f;
+    float up = (mq == 0 && mrow < m) ? pp * uu[mrow] : 0.f;
+    up = group_sum<kWave>(up);
+    if (mq == 0 && mrow < m) sp[mrow] = pp;
+    if (lane == 0) sRed[1][wave] = up;
+    __syncthreads();
+    float Kup = 0.f;
+#pragma unroll
+    for (int w = 0; w < kBuildWaves; ++w) Kup += sRed[1][w];
+    if (mrow < m) {  // columns 1 .. m-1 of A22
+      const float ui = uu[mrow], wi = sp[mrow] - Kup * ui;
+      float* Ar = &sA[k + 1 + mrow][k + 1 + 16 * mq];
+      const float* ub = uu + 16 * mq;
+      const float* pb = sp + 16 * mq;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int j = 16 * mq + t;
+        const float uj = ub[t], wj = pb[t] - Kup * uj;
+        const float nv = Ar[t] - (ui * wj + wi * uj);
+        if (j >= 1 && j < m) Ar[t] = nv;
       }
-      __syncthreads();
-      if (k1 >= 0) {
-        const float4 P1 = sPar[k1];
-        const int p1 = __float_as_int(P1.w) & 0xff, q1 = __float_as_int(P1.w) >> 8;
-        if (k1 == k2) {
-          const float apq = sA[p1][q1];
-          sA[p1][p1] -= P1.z * apq;
-          sA[q1][q1] += P1.z * apq;
-          sA[p1][q1] = 0.f;
-          sA[q1][p1] = 0.f;
+    }
+    if (wave == 0) {  // column 0 of A22 (= column k + 1 of A), then the next reflector
+      const float u0 = uu[0], w0 = sp[0] - Kup * u0;
+      float a0 = 0.f;
+      if (lane < m) {
+        const float ul = uu[lane], wl = sp[lane] - Kup * ul;
+        a0 = sA[k + 1 + lane][k + 1] - (ul * w0 + wl * u0);
+        sA[k + 1 + lane][k + 1] = a0;
+      }
+      if (lane == 0) sd[k + 1] = a0;
+      wave_lds_fence();
+      if (k + 1 < B - 2) reflector(k + 1, lane < m - 1 ? sA[k + 2 + lane][k + 1] : 0.f, buf ^ 1);
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    sd[B - 1] = sA[B - 1][B - 1];
+    se[B - 2] = sA[B - 1][B - 2];
+    se[B - 1] = 0.f;
+  }
+  __syncthreads();
+  if (tid < B) se2[tid] = se[tid] * se[tid];
+  // Gershgorin interval of T
+  if (wave == 0) {
+    const float em = lane > 0 ? fabsf(se[lane - 1]) : 0.f;
+    const float ep = fabsf(se[lane]);
+    float lo = sd[lane] - em - ep, hi = sd[lane] + em + ep;
+    lo = -group_max<kWave>(-lo);
+    hi = group_max<kWave>(hi);
+    if (lane == 0) { sBound[0] = lo; sBound[1] = hi; }
+  }
+  __syncthreads();
+  const float glo = sBound[0], ghi = sBound[1];
+  const float tnorm = fmaxf(fabsf(glo), fabsf(ghi));
+  const float pivmin = fmaxf(tnorm * 1e-30f, 1e-30f);
+  const float tol = 2.f * 1.19209290e-7f * tnorm;
+
+  // 5) the KEPT largest eigenvalues: wave w takes the w-th, (w+4)-th, ...;
+  //    each pass counts below 64 shifts spread over the current interval
+#pragma unroll
+  for (int s = 0; s < KW; ++s) {
+    const int kk = wave + kBuildWaves * s;
+    if (kk >= KEPT) break;
+    const int target = B - 1 - kk;          // ascending index of the kk-th largest
+    float lo = glo, hi = ghi;
+    for (int it = 0; it < 12 && hi - lo > tol; ++it) {
+      const float width = hi - lo;
+      const float sig = lo + width * (float)(lane + 1) * (1.f / 65.f);
+      const int cnt = sturm_count(sd, se2, sig, pivmin);
+      const uint64_t below = __ballot(cnt <= target);   // shifts at or below the eigenvalue
+      const int nl = below ? 64 - __clzll(below) : 0;   // highest such lane + 1
+      const float nlo = nl > 0 ? lo + width * (float)nl * (1.f / 65.f) : lo;
+      const float nhi = nl < 64 ? lo + width * (float)(nl + 1) * (1.f / 65.f) : hi;
+      if (nlo == lo && nhi == hi) break;  // below the resolution of fp32
+      lo = nlo;
+      hi = nhi;
+    }
+    if (lane == 0) sLam[kk] = 0.5f * (lo + hi);
+  }
+  __syncthreads();
+
+  // 6) inverse iteration on T: lane kk of wave 0 factors T - lambda_kk I once
+  //    with partial pivoting (row i swaps with row i + 1 when |e_i| > |pivot|),
+  //    then solves kInvIters times from a fixed varied start
+  if (wave == 0 && lane < KEPT) {
+    const int kk = lane;
+    const float lam = sLam[kk];
+    {
+      float ddc = sd[0] - lam, duc = se[0];
+#pragma unroll
+      for (int i = 0; i < B - 1; ++i) {
+        const float dl = se[i];
+        const float ddn = sd[i + 1] - lam;
+        const float dun = i + 1 < B - 1 ? se[i + 1] : 0.f;
+        if (fabsf(ddc) >= fabsf(dl)) {
+          const float rp = __builtin_amdgcn_rcpf(fabsf(ddc) < pivmin ? pivmin : ddc);
+          const float mlt = dl * rp;
+          sRP[i][kk] = rp; sDU[i][kk] = duc; sDU2[i][kk] = 0.f; sML[i][kk] = mlt; sSW[i][kk] = 0;
+          ddc = ddn - mlt * duc;
+          duc = dun;
         } else {
-          const float4 P2 = sPar[k2];
-          const int p2 = __float_as_int(P2.w) & 0xff, q2 = __float_as_int(P2.w) >> 8;
-          const float c1 = P1.x, s1 = P1.y, c2 = P2.x, s2 = P2.y;
-          const float x00 = sA[p1][p2], x01 = sA[p1][q2], x10 = sA[q1][p2], x11 = sA[q1][q2];
-          const float y00 = c1 * x00 - s1 * x10, y01 = c1 * x01 - s1 * x11;
-          const float y10 = s1 * x00 + c1 * x10, y11 = s1 * x01 + c1 * x11;
-          const float z00 = c2 * y00 - s2 * y01, z01 = s2 * y00 + c2 * y01;
-          const float z10 = c2 * y10 - s2 * y11, z11 = s2 * y10 + c2 * y11;
-          sA[p1][p2] = z00; sA[p2][p1] = z00;
-          sA[p1][q2] = z01; sA[q2][p1] = z01;
-          sA[q1][p2] = z10; sA[p2][q1] = z10;
-          sA[q1][q2] = z11; sA[q2][q1] = z11;
+          const float mlt = ddc * __builtin_amdgcn_rcpf(dl);
+          sRP[i][kk] = __builtin_amdgcn_rcpf(dl); sDU[i][kk] = ddn; sDU2[i][kk] = dun; sML[i][kk] = mlt;
+          sSW[i][kk] = 1;
+          ddc = duc - mlt * ddn;
+          duc = -mlt * dun;
         }
       }
-      // U <- U J: columns p, q of rows i (two (row, pair) items per thread)
+      sRP[B - 1][kk] = __builtin_amdgcn_rcpf(fabsf(ddc) < pivmin ? pivmin : ddc);
+    }
+    float nrm2 = 0.f;
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int w = tid + x * kBuildThreads;
-        const int i = w >> 5, k = w & 31;
-        const float4 P = sPar[k];
-        const int p = __float_as_int(P.w) & 0xff, q = __float_as_int(P.w) >> 8;
-        const float up = sU[i][p], uq = sU[i][q];
-        sU[i][p] = P.x * up - P.y * uq;
-        sU[i][q] = P.y * up + P.x * uq;
+    for (int i = 0; i < B; ++i) {
+      const uint32_t hsh = (uint32_t)(i * 2654435761u) ^ (uint32_t)((kk + 1) * 40503u);
+      const float b = 0.5f + (float)((hsh >> 9) & 1023) * (1.f / 1024.f);
+      sZZ[i][kk] = b;
+      nrm2 = fmaf(b, b, nrm2);
+    }
+    float scale = __builtin_amdgcn_rsqf(nrm2);
+    for (int itr = 0; itr < kInvIters; ++itr) {
+      // forward: apply the row swaps and multipliers to the right-hand side
+      float zc = sZZ[0][kk] * scale;
+#pragma unroll
+      for (int i = 0; i < B - 1; ++i) {
+        const float zn = sZZ[i + 1][kk] * scale;
+        const float mlt = sML[i][kk];
+        if (sSW[i][kk]) { sZ[i][kk] = zn; zc = zc - mlt * zn; }
+        else { sZ[i][kk] = zc; zc = zn - mlt * zc; }
       }
-      __syncthreads();
-    }
-    // convergence: off-diagonal energy vs total (4 entries per thread)
-    float off = 0.f, tot = 0.f;
+      // back substitution, the solution written over the right-hand side
+      float x1 = zc * sRP[B - 1][kk], x2 = 0.f;
+      sZZ[B - 1][kk] = x1;
+      nrm2 = x1 * x1;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int w = tid + x * kBuildThreads;
-      const int i = w >> 6, j = w & 63;
-      const float v = sA[i][j];
-      tot = fmaf(v, v, tot);
-      if (i != j) off = fmaf(v, v, off);
+      for (int i = B - 2; i >= 0; --i) {
+        const float x = (sZ[i][kk] - sDU[i][kk] * x1 - sDU2[i][kk] * x2) * sRP[i][kk];
+        sZZ[i][kk] = x;
+        nrm2 = fmaf(x, x, nrm2);
+        x2 = x1;
+        x1 = x;
+      }
+      scale = __builtin_amdgcn_rsqf(nrm2);
     }
-    off = group_sum<kWave>(off);
-    tot = group_sum<kWave>(tot);
-    if (lane == 0) { sRed[0][wave] = off; sRed[1][wave] = tot; }
-    __syncthreads();
-    float o = 0.f, tt = 0.f;
 #pragma unroll
-    for (int w = 0; w < kBuildWaves; ++w) { o += sRed[0][w]; tt += sRed[1][w]; }
-    __syncthreads();
-    if (o <= kJacobiTol * tt) break;
+    for (int i = 0; i < B; ++i) sZ[i][kk] = sZZ[i][kk] * scale;
+  }
+  __syncthreads();
+  // re-orthogonalize within clusters of close eigenvalues (wave 0, lane = row)
+  if (wave == 0) {
+    const float ctol = kClusterTol * fabsf(sLam[0]);
+    for (int kk = 1; kk < KEPT; ++kk) {
+      bool touched = false;
+      float zk = sZ[lane][kk];
+      for (int j = 0; j < kk; ++j) {
+        if (fabsf(sLam[j] - sLam[kk]) > ctol) continue;
+        const float zj = sZ[lane][j];
+        zk -= group_sum<kWave>(zj * zk) * zj;
+        touched = true;
+      }
+      if (touched) {
+        zk *= __builtin_amdgcn_rsqf(group_sum<kWave>(zk * zk));
+        sZ[lane][kk] = zk;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 7) back-transformation y = H_0 H_1 ... H_{B-3} z (lane = row; wave w
+  //    takes eigenvectors w, w + 4, ...)
+  {
+    float y[KW];
+#pragma unroll
+    for (int s = 0; s < KW; ++s) {
+      const int kk = wave + kBuildWaves * s;
+      y[s] = kk < KEPT ? sZ[lane][kk] : 0.f;
+    }
+    for (int k = B - 3; k >= 0; --k) {
+      const float u = lane > k ? sA[lane][k] : 0.f;
+#pragma unroll
+      for (int s = 0; s < KW; ++s) {
+        const float dot = group_sum<kWave>(u * y[s]);
+        y[s] = fmaf(-2.f * dot, u, y[s]);
+      }
+    }
+    __syncthreads();  // every wave is done with the reflectors and sZ
+#pragma unroll
+    for (int s = 0; s < KW; ++s) {
+      const int kk = wave + kBuildWaves * s;
+      if (kk < KEPT) sZ[lane][kk] = y[s];
+    }
   }
 
-  // 5) eigenvalues sorted descending (ties to the lower index)
-  if (tid < B) sLam[tid] = sA[tid][tid];
-  __syncthreads();
-  if (tid < B) {
-    const float li = sLam[tid];
-    int rank = 0;
-    for (int j = 0; j < B; ++j) {
-      const float lj = sLam[j];
-      rank += (lj > li || (lj == li && j < tid)) ? 1 : 0;
-    }
-    sOrder[rank] = tid;
-  }
-  __syncthreads();
+  // zero modes, sigma
   if (tid < KEPT) {
-    const float lam1 = sLam[sOrder[0]];
-    const int col = sOrder[tid];
-    const float lam = sLam[col];
+    const float lam1 = sLam[0];
+    const float lam = sLam[tid];
     const float thresh = fmaxf(kZeroModeRtol * lam1, kZeroModeFloor * energy);
     const int nz = (lam1 > 0.f && lam > thresh) ? 1 : 0;
-    sCol[tid] = col;
     sNz[tid] = nz;
     sSigma[tid] = nz ? sqrtf(lam) : 1.f;
   }
-  if (a.eigvals_out && tid < B) {
-    a.eigvals_out[((size_t)idx * a.hkv + kvh) * B + tid] = fmaxf(sLam[sOrder[tid]], 0.f);
+  // optional: every eigenvalue (descending), bisection with one lane per eigenvalue
+  if (a.eigvals_out && wave == kBuildWaves - 1) {
+    const int target = B - 1 - lane;
+    float lo = glo, hi = ghi;
+    for (int it = 0; it < 64 && hi - lo > tol; ++it) {
+      const float mid = 0.5f * (lo + hi);
+      if (mid == lo || mid == hi) break;
+      if (sturm_count(sd, se2, mid, pivmin) <= target) lo = mid;
+      else hi = mid;
+    }
+    const float lam = lane < KEPT ? sLam[lane] : 0.5f * (lo + hi);
+    a.eigvals_out[((size_t)idx * a.hkv + kvh) * B + lane] = fmaxf(lam, 0.f);
   }
   __syncthreads();
 
-  // 6) basis V[k][c] = sum_i D[i][c] U[i][col_k] / sigma_k  (stored in sA)
+  // 8) basis V[k][c] = sum_i D[i][c] Y[i][k] / sigma_k  (stored in sA)
   float* sV = &sA[0][0];
   for (int w = tid; w < KEPT * D; w += kBuildThreads) {
     const int k = w / D, c = w % D;
     float v = 0.f;
     if (sNz[k]) {
-      const int col = sCol[k];
-      for (int i = 0; i < B; ++i) v = fmaf(sDT[c][i], sU[i][col], v);
+      for (int i = 0; i < B; ++i) v = fmaf(sDT[c][i], sZ[i][k], v);
       v /= sSigma[k];
     }
     sV[k * D + c] = v;
@@ -301,7 +489,7 @@ __global__ __launch_bounds__(kBuildThreads) void build_kernel(BuildArgs a) {
   }
   __syncthreads();
 
-  // 7) write the record: centroid | basis rows | coefficients
+  // 9) write the record: centroid | basis rows | coefficients
   constexpr int REC = D + R * D + B * R;
   T* rec = reinterpret_cast<T*>(a.summary) + ((size_t)phys * a.hkv + kvh) * REC;
   for (int x = tid; x < REC; x += kBuildThreads) {
@@ -313,7 +501,7 @@ __global__ __launch_bounds__(kBuildThreads) void build_kernel(BuildArgs a) {
       v = (k < KEPT) ? sV[k * D + c] * sSign[k] : 0.f;
     } else {
       const int i = (x - D - R * D) / R, k = (x - D - R * D) % R;
-      v = (k < KEPT && sNz[k]) ? sU[i][sCol[k]] * sSigma[k] * sSign[k] : 0.f;
+      v = (k < KEPT && sNz[k]) ? sZ[i][k] * sSigma[k] * sSign[k] : 0.f;
     }
     Elem<T>::store(rec + x, v);
   }
@@ -323,7 +511,7 @@ template <typename T>
 static hipError_t launch_build_t(int rank, const BuildArgs& a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
   dim3 grid(a.n, a.hkv);
-  dim3 block(kBuildThreads);
+  dim3 block(a.merge.part_o ? kMergeThreads : kBuildThreads);
   switch (rank) {
     case 1: hipLaunchKernelGGL((build_kernel<T, 1>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((build_kernel<T, 2>), grid, block, 0, s, a); break;
