@@ -302,19 +302,40 @@ lk_status lk_decode_step(const lk_config* cfg, const lk_cache* cache, int32_t ba
   if ((st = check_ws(L, ws, ws_bytes)) != LK_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t* build_list = at<int32_t>(ws, L.build_list);
-  int32_t* sel = sel_pages ? sel_pages : at<int32_t>(ws, L.sel_pages);
-  int32_t* cnt = sel_count ? sel_count : at<int32_t>(ws, L.sel_count);
-
-  // 1-2) append (done by the scorer's prologue) + score + select, all with T + 1
-  lk::AppendDuty app{cache->k_pool, cache->v_pool, k_new, v_new, build_list};
   int32_t* sel_phys = at<int32_t>(ws, L.sel_phys);
-  st = enqueue_score_select(sh, cfg, cache, batch, q, at<float>(ws, L.page_lse), nullptr, sel, cnt, sel_phys, 1,
-                            app, s);
+  float* page_lse = at<float>(ws, L.page_lse);
+
+  // 1) append (done by the scorer's prologue) + score, with T + 1
+  lk::AppendDuty app{cache->k_pool, cache->v_pool, k_new, v_new, build_list};
+  lk::ScoreArgs sa{q, cache->summary_pool, cache->block_table, cache->seq_lens, page_lse, batch,
+                   cache->max_pages_per_seq, cache->num_phys_pages, sh.hkv, sh.hq, cfg->scale, 1, app};
+  st = hip_status(lk::launch_score(sh.dt, sh.r, sh.G, sa, s), "score launch");
   if (st != LK_OK) return st;
-  // 3) attention over the selection (split partials)
-  int n_splits = 0;
-  st = enqueue_attn(sh, cfg, cache, batch, q, sel, cnt, sel_phys, out, lse_out, ws, L, 1, false, s, &n_splits);
-  if (st != LK_OK) return st;
+  // 2-3) selection and the attention splits: one fused launch when the table
+  //      fits one workgroup's selection, else a selection then an attention launch
+  const int per = kAttnWavesPerSplit * kUnitsPerWaveSparse;
+  const int n_splits = (2 * sh.k + per - 1) / per;
+  lk::SelectArgs se{page_lse, nullptr, sel_pages, sel_count, cache->seq_lens, batch, cache->max_pages_per_seq,
+                    sh.hkv, sh.G, sh.B, sh.k, 1, cache->block_table, nullptr, cache->num_phys_pages};
+  if (lk::select_attn_fusable(se)) {
+    lk::AttnArgs aa{q, cache->k_pool, cache->v_pool, cache->block_table, cache->seq_lens, nullptr, nullptr, nullptr,
+                    at<float>(ws, L.part_o), at<float>(ws, L.part_ml), out, lse_out,
+                    batch, cache->max_pages_per_seq, cache->num_phys_pages, sh.hkv, sh.hq, sh.k,
+                    n_splits, kUnitsPerWaveSparse, cfg->scale, 1};
+    st = hip_status(lk::launch_select_attn(sh.dt, se, aa, s), "selection + attention launch");
+    if (st != LK_OK) return st;
+  } else {
+    int32_t* sel = sel_pages ? sel_pages : at<int32_t>(ws, L.sel_pages);
+    int32_t* cnt = sel_count ? sel_count : at<int32_t>(ws, L.sel_count);
+    se.sel_pages = sel;
+    se.sel_count = cnt;
+    se.sel_phys = sel_phys;
+    st = hip_status(lk::launch_select(se, s), "select launch");
+    if (st != LK_OK) return st;
+    int ns = 0;
+    st = enqueue_attn(sh, cfg, cache, batch, q, sel, cnt, sel_phys, out, lse_out, ws, L, 1, false, s, &ns);
+    if (st != LK_OK) return st;
+  }
   // 4) one launch of (sequence, KV head) workgroups: merge the attention
   //    partials, advance the stored lengths, and summarize pages the append
   //    completed

@@ -24,6 +24,7 @@
 
 #include "common.cuh"
 #include "kernels.h"
+#include "select_impl.cuh"
 
 namespace lk {
 
@@ -88,8 +89,13 @@ template <int G> struct AttnCombine {
   static constexpr int kPartials = kAttnWaves * kPartialsPerWave;
 };
 
+// One workgroup's split of the attention of (seq, kvh) over the page list
+// `list` (logical pages; nullptr: every page of the sequence), `plist` their
+// physical pages (nullptr: looked up) and `cnt_p` the list length; the lists
+// may live in global memory or LDS.
 template <typename T, int G>
-__global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs a) {
+__device__ __forceinline__ void attn_split_block(const AttnArgs& a, int split, int kvh, int seq, const int32_t* list,
+                                                 const int32_t* plist, const int32_t* cnt_p) {
   constexpr int B = 64;
   constexpr int D = kHeadDim;
   constexpr int TG = 8;               // token groups per wave
@@ -106,17 +112,12 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar page-list loads
   const int sg = lane >> 3;
   const int e = lane & 7;
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int seq = blockIdx.z;
   const int32_t* bt = a.block_table + (size_t)seq * a.max_pages;
 
   // units are half pages: unit u is half (u & 1) of list entry u >> 1; wave w
   // of split s takes units [(4 s + w) * ups, +ups)
   const int ups = a.pages_per_split;
   const int u0 = (split * kAttnWaves + wave) * ups;
-  const int32_t* list = a.sel_pages ? a.sel_pages + ((size_t)seq * a.hkv + kvh) * a.k : nullptr;
-  const int32_t* plist = (list && a.sel_phys) ? a.sel_phys + ((size_t)seq * a.hkv + kvh) * a.k : nullptr;
   const int n_entries = list ? a.k : a.max_pages;  // list entries that exist in memory
 
   // The first unit's page and physical page are fetched together with the
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs
     phys_first = plist ? plist[x] : -2;  // -2: look up through the block table
   }
   const int len = a.seq_lens[seq] + a.len_add;
-  const int cnt = list ? a.sel_count[(size_t)seq * a.hkv + kvh] : 0;
+  const int cnt = list ? *cnt_p : 0;
 
   const T* qp = reinterpret_cast<const T*>(a.q) + ((size_t)seq * a.hq + (size_t)kvh * G) * D + e * 16;
   QSliceBF16 qb[G];
@@ -315,6 +316,35 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs
   }
 }
 
+template <typename T, int G>
+__global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs a) {
+  const int split = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
+  const size_t pair = (size_t)seq * a.hkv + kvh;
+  const int32_t* list = a.sel_pages ? a.sel_pages + pair * a.k : nullptr;
+  const int32_t* plist = (list && a.sel_phys) ? a.sel_phys + pair * a.k : nullptr;
+  attn_split_block<T, G>(a, split, kvh, seq, list, plist, list ? a.sel_count + pair : nullptr);
+}
+
+// Decode step: selection and attention in one launch.  Every workgroup of a
+// (sequence, KV head) runs the (deterministic) selection of that pair itself
+// into LDS, then attends its split of the selected pages; workgroup 0 also
+// writes the selection out when asked.  This trades redundant selection work
+// for one kernel boundary and one dependent global round trip.
+template <typename T, int NPT, int G>
+__global__ __launch_bounds__(kAttnWaves * kWave) void select_attn_kernel(SelectArgs se, AttnArgs a) {
+  __shared__ int32_t s_sel[kMaxSelect], s_selp[kMaxSelect];
+  __shared__ int32_t s_cnt;
+  const int split = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
+  select_block<kAttnWaves * kWave, NPT, G>(se, seq, kvh, s_sel, &s_cnt, s_selp);
+  __syncthreads();
+  if (split == 0 && se.sel_pages) {
+    const size_t pair = (size_t)seq * se.hkv + kvh;
+    for (int i = threadIdx.x; i < se.k; i += kAttnWaves * kWave) se.sel_pages[pair * se.k + i] = s_sel[i];
+    if (threadIdx.x == 0) se.sel_count[pair] = s_cnt;
+  }
+  attn_split_block<T, G>(a, split, kvh, seq, s_sel, s_selp, &s_cnt);
+}
+
 // Merge: one workgroup per (sequence, KV head) combines the split partials of
 // all G heads: o = sum_s e^{m_s - M} o_s / sum_s e^{m_s - M} l_s and
 // lse = M + log sum_s e^{m_s - M} l_s.
@@ -395,6 +425,38 @@ static hipError_t launch_attn_t(int group, const AttnArgs& a, bool merge, hipStr
 
 hipError_t launch_attn(DType dt, int group, const AttnArgs& a, bool merge, hipStream_t s) {
   return dt == kBF16 ? launch_attn_t<bf16_t>(group, a, merge, s) : launch_attn_t<float>(group, a, merge, s);
+}
+
+template <typename T, int NPT>
+static hipError_t launch_select_attn_n(const SelectArgs& se, const AttnArgs& a, hipStream_t s) {
+  dim3 grid(a.n_splits, a.hkv, a.batch);
+  dim3 block(kAttnWaves * kWave);
+  switch (se.group) {
+    case 1: hipLaunchKernelGGL((select_attn_kernel<T, NPT, 1>), grid, block, 0, s, se, a); break;
+    case 2: hipLaunchKernelGGL((select_attn_kernel<T, NPT, 2>), grid, block, 0, s, se, a); break;
+    case 4: hipLaunchKernelGGL((select_attn_kernel<T, NPT, 4>), grid, block, 0, s, se, a); break;
+    case 8: hipLaunchKernelGGL((select_attn_kernel<T, NPT, 8>), grid, block, 0, s, se, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_select_attn_t(const SelectArgs& se, const AttnArgs& a, hipStream_t s) {
+  const int n = se.max_pages;
+  if (n <= kAttnWaves * kWave * 4) return launch_select_attn_n<T, 4>(se, a, s);
+  if (n <= kAttnWaves * kWave * 8) return launch_select_attn_n<T, 8>(se, a, s);
+  if (n <= kAttnWaves * kWave * 12) return launch_select_attn_n<T, 12>(se, a, s);
+  return hipErrorNotSupported;
+}
+
+bool select_attn_fusable(const SelectArgs& se) {
+  return se.max_pages <= kAttnWaves * kWave * 12 && se.k <= kMaxSelect && se.group <= kMaxGroup;
+}
+
+hipError_t launch_select_attn(DType dt, const SelectArgs& se, const AttnArgs& a, hipStream_t s) {
+  if (!select_attn_fusable(se)) return hipErrorNotSupported;
+  return dt == kBF16 ? launch_select_attn_t<bf16_t>(se, a, s) : launch_select_attn_t<float>(se, a, s);
 }
 
 }  // namespace lk

@@ -94,5 +94,9 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 // merge = false leaves the split partials for the decode step's build launch
 hipError_t launch_attn(DType dt, int group, const AttnArgs& a, bool merge, hipStream_t s);
 hipError_t launch_build(DType dt, int rank, const BuildArgs& a, hipStream_t s);
+// Decode step: selection (se) and attention splits (a) in one launch, for
+// tables of up to 3072 pages per sequence (select_attn_fusable).
+bool select_attn_fusable(const SelectArgs& se);
+hipError_t launch_select_attn(DType dt, const SelectArgs& se, const AttnArgs& a, hipStream_t s);
 
 }  // namespace lk
