@@ -317,11 +317,13 @@ lk_status lk_decode_step(const lk_config* cfg, const lk_cache* cache, int32_t ba
   const int n_splits = (2 * sh.k + per - 1) / per;
   lk::SelectArgs se{page_lse, nullptr, sel_pages, sel_count, cache->seq_lens, batch, cache->max_pages_per_seq,
                     sh.hkv, sh.G, sh.B, sh.k, 1, cache->block_table, nullptr, cache->num_phys_pages};
-  if (lk::select_attn_fusable(se)) {
+  const bool fused = lk::select_attn_fusable(se);
+  const int n_merge = fused ? lk::select_attn_splits(sh.k) : n_splits;
+  if (fused) {
     lk::AttnArgs aa{q, cache->k_pool, cache->v_pool, cache->block_table, cache->seq_lens, nullptr, nullptr, nullptr,
                     at<float>(ws, L.part_o), at<float>(ws, L.part_ml), out, lse_out,
                     batch, cache->max_pages_per_seq, cache->num_phys_pages, sh.hkv, sh.hq, sh.k,
-                    n_splits, kUnitsPerWaveSparse, cfg->scale, 1};
+                    n_merge, 1, cfg->scale, 1};
     st = hip_status(lk::launch_select_attn(sh.dt, se, aa, s), "selection + attention launch");
     if (st != LK_OK) return st;
   } else {
@@ -342,7 +344,7 @@ lk_status lk_decode_step(const lk_config* cfg, const lk_cache* cache, int32_t ba
   lk::BuildArgs ba{cache->k_pool, cache->summary_pool, build_list, nullptr, batch,
                    cache->num_phys_pages, sh.hkv, cache->seq_lens, cache->block_table,
                    cache->max_pages_per_seq,
-                   {at<float>(ws, L.part_o), at<float>(ws, L.part_ml), out, lse_out, n_splits, sh.G, sh.hq}};
+                   {at<float>(ws, L.part_o), at<float>(ws, L.part_ml), out, lse_out, n_merge, sh.G, sh.hq}};
   return hip_status(lk::launch_build(sh.dt, sh.r, ba, s), "build launch");
 }
 

@@ -80,180 +80,142 @@ template <> struct KV16<float> {
 };
 
 constexpr int kAttnWaves = 4;
+constexpr int kAttnTG = 8;                     // token groups per wave
+constexpr int kAttnHalf = 32;                  // tokens per unit (half a page)
+constexpr int kAttnTPG = kAttnHalf / kAttnTG;  // tokens per group per unit
 
 // Partials per workgroup combined through LDS: the 8 token groups of a wave
 // are first paired (G <= 4) or grouped by four (G = 8) on the VALU.
-template <int G> struct AttnCombine {
+template <int G, int NWV> struct AttnCombine {
   static constexpr int kGroupsPerPartial = G <= 4 ? 2 : 4;
-  static constexpr int kPartialsPerWave = 8 / kGroupsPerPartial;
-  static constexpr int kPartials = kAttnWaves * kPartialsPerWave;
+  static constexpr int kPartialsPerWave = kAttnTG / kGroupsPerPartial;
+  static constexpr int kPartials = NWV * kPartialsPerWave;
 };
 
-// One workgroup's split of the attention of (seq, kvh) over the page list
-// `list` (logical pages; nullptr: every page of the sequence), `plist` their
-// physical pages (nullptr: looked up) and `cnt_p` the list length; the lists
-// may live in global memory or LDS.
-template <typename T, int G>
-__device__ __forceinline__ void attn_split_block(const AttnArgs& a, int split, int kvh, int seq, const int32_t* list,
-                                                 const int32_t* plist, const int32_t* cnt_p) {
-  constexpr int B = 64;
-  constexpr int D = kHeadDim;
-  constexpr int TG = 8;               // token groups per wave
-  constexpr int HALF = B / 2;         // tokens per unit (half a page)
-  constexpr int TPG = HALF / TG;      // tokens per group per unit
-  constexpr int NP = AttnCombine<G>::kPartials;
-  constexpr int PPW = AttnCombine<G>::kPartialsPerWave;
-  constexpr int GPP = AttnCombine<G>::kGroupsPerPartial;
-  __shared__ float4 s_o[NP][G][D / 4];
-  __shared__ float s_l[NP][G];
-  __shared__ float s_m[kAttnWaves][G];
-
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar page-list loads
-  const int sg = lane >> 3;
-  const int e = lane & 7;
-  const int32_t* bt = a.block_table + (size_t)seq * a.max_pages;
-
-  // units are half pages: unit u is half (u & 1) of list entry u >> 1; wave w
-  // of split s takes units [(4 s + w) * ups, +ups)
-  const int ups = a.pages_per_split;
-  const int u0 = (split * kAttnWaves + wave) * ups;
-  const int n_entries = list ? a.k : a.max_pages;  // list entries that exist in memory
-
-  // The first unit's page and physical page are fetched together with the
-  // lengths; its K/V loads are issued before the lengths are used (every
-  // address is inside the physical page, tokens past the end are masked).
-  int pg_first = -1, phys_first = -1;
-  if (u0 < 2 * n_entries) {
-    const int x = u0 >> 1;
-    pg_first = list ? list[x] : x;
-    phys_first = plist ? plist[x] : -2;  // -2: look up through the block table
-  }
-  const int len = a.seq_lens[seq] + a.len_add;
-  const int cnt = list ? *cnt_p : 0;
-
-  const T* qp = reinterpret_cast<const T*>(a.q) + ((size_t)seq * a.hq + (size_t)kvh * G) * D + e * 16;
+// The lane's query slices (dims 16e..16e+15) of the G heads of a KV head.
+template <typename T, int G> struct QLane {
   QSliceBF16 qb[G];
   float qf[G][16];
-  if constexpr (sizeof(T) == 2) {
+  __device__ __forceinline__ void load(const AttnArgs& a, int seq, int kvh, int e) {
+    constexpr int D = kHeadDim;
+    const T* qp = reinterpret_cast<const T*>(a.q) + ((size_t)seq * a.hq + (size_t)kvh * G) * D + e * 16;
+    if constexpr (sizeof(T) == 2) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) qb[g].load(reinterpret_cast<const bf16_t*>(qp) + (size_t)g * D);
-  } else {
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) qf[g][i] = reinterpret_cast<const float*>(qp)[(size_t)g * D + i];
-  }
-
-  float m[G], l[G], o[G][16];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -INFINITY;
-    l[g] = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[g][i] = 0.f;
-  }
-  const float zscale = a.scale * kLog2e;
-
-  int u = u0;
-  int pg = pg_first, phys = phys_first;
-  if (phys == -2) phys = (pg >= 0 && pg < a.max_pages) ? bt[pg] : -1;
-  KV16<T> kr[TPG], vr[TPG];
-  auto issue = [&](int ph, int unit) {
-    const size_t base = (((size_t)ph * a.hkv + kvh) * B + (unit & 1) * HALF) * D + e * 16;
-    const T* Kp = reinterpret_cast<const T*>(a.k_pool) + base;
-    const T* Vp = reinterpret_cast<const T*>(a.v_pool) + base;
-#pragma unroll
-    for (int x = 0; x < TPG; ++x) {
-      kr[x].load(Kp + (size_t)(sg + TG * x) * D);
-      vr[x].load(Vp + (size_t)(sg + TG * x) * D);
-    }
-  };
-  bool loaded = false;
-  if (len > 0 && phys >= 0 && phys < a.num_phys) { issue(phys, u); loaded = true; }
-
-  int n_mr = len > 0 ? (len - 1) / B : -1;
-  if (n_mr > a.max_pages - 1) n_mr = a.max_pages - 1;
-  const int n_list = len <= 0 ? 0 : (list ? min(cnt, a.k) : n_mr + 1);
-  const int u1 = min(u0 + ups, 2 * n_list);
-
-  for (; u < u1; ++u) {
-    if (u != u0) {
-      pg = list ? list[u >> 1] : (u >> 1);
-      phys = plist ? plist[u >> 1] : ((pg >= 0 && pg < a.max_pages) ? bt[pg] : -1);
-      loaded = phys >= 0 && phys < a.num_phys;
-      if (loaded) issue(phys, u);
-    }
-    if (!loaded || pg < 0 || pg > n_mr) continue;
-    const int t_base = (u & 1) * HALF;
-    const int n_tok = ((pg == n_mr) ? len - n_mr * B : B) - t_base;  // tokens from t_base on
-    if (n_tok <= 0) continue;
-    if (n_tok < HALF) {  // the filled part of the most recent page only
-#pragma unroll
-      for (int x = 0; x < TPG; ++x)
-        if (sg + TG * x >= n_tok) { kr[x].zero(); vr[x].zero(); }
-    }
-
-    float z[TPG][G];
-#pragma unroll
-    for (int x = 0; x < TPG; ++x) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float acc;
-        if constexpr (sizeof(T) == 2) {
-          acc = qb[g].dot(kr[x].a, kr[x].b);
-        } else {
-          float kx[16];
-          kr[x].to_f32(kx);
-          acc = 0.f;
-#pragma unroll
-          for (int y = 0; y < 16; ++y) acc = fmaf(qf[g][y], kx[y], acc);
-        }
-        z[x][g] = acc;
-      }
-    }
-#pragma unroll
-    for (int x = 0; x < TPG; ++x)
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float full = group_sum<8>(z[x][g]);
-        z[x][g] = (sg + TG * x < n_tok) ? full * zscale : -INFINITY;
-      }
-    // running max, rescale and probabilities per head (a head with no token
-    // yet keeps m = -inf and gets p = 0), then P V one token at a time
-    float p[TPG][G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float pm = -INFINITY;
-#pragma unroll
-      for (int x = 0; x < TPG; ++x) pm = fmaxf(pm, z[x][g]);
-      const float m_new = fmaxf(m[g], pm);
-      const float mref = (m_new == -INFINITY) ? 0.f : m_new;
-      const float corr = fast_exp2(m[g] - mref);
-      m[g] = m_new;
-      l[g] *= corr;
-#pragma unroll
-      for (int y = 0; y < 16; ++y) o[g][y] *= corr;
-#pragma unroll
-      for (int x = 0; x < TPG; ++x) {
-        p[x][g] = fast_exp2(z[x][g] - mref);
-        l[g] += p[x][g];
-      }
-    }
-#pragma unroll
-    for (int x = 0; x < TPG; ++x) {
-      float vx[16];
-      vr[x].to_f32(vx);
+      for (int g = 0; g < G; ++g) qb[g].load(reinterpret_cast<const bf16_t*>(qp) + (size_t)g * D);
+    } else {
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int y = 0; y < 16; ++y) o[g][y] = fmaf(p[x][g], vx[y], o[g][y]);
+        for (int i = 0; i < 16; ++i) qf[g][i] = reinterpret_cast<const float*>(qp)[(size_t)g * D + i];
     }
   }
+};
 
-  // Combine: rescale every lane to its wave's running max, add token groups
-  // pairwise (G <= 4) or by four (G = 8) on the VALU, then the workgroup's
-  // NP partials in LDS with the waves' weights e^{M_w - M}.
+// K and V loads of half `half` of physical page ph for this lane: tokens
+// sg, sg + 8, ... of the half, dims 16e..16e+15 (coalesced 16-byte loads).
+template <typename T>
+__device__ __forceinline__ void issue_unit(const AttnArgs& a, int kvh, int ph, int half, int sg, int e,
+                                           KV16<T> (&kr)[kAttnTPG], KV16<T> (&vr)[kAttnTPG]) {
+  constexpr int B = 64;
+  constexpr int D = kHeadDim;
+  const size_t base = (((size_t)ph * a.hkv + kvh) * B + half * kAttnHalf) * D + e * 16;
+  const T* Kp = reinterpret_cast<const T*>(a.k_pool) + base;
+  const T* Vp = reinterpret_cast<const T*>(a.v_pool) + base;
+#pragma unroll
+  for (int x = 0; x < kAttnTPG; ++x) {
+    kr[x].load(Kp + (size_t)(sg + kAttnTG * x) * D);
+    vr[x].load(Vp + (size_t)(sg + kAttnTG * x) * D);
+  }
+}
+
+// Online-softmax update of the lane's (m, l, o) with the first n_tok tokens
+// (0 < n_tok) of a loaded unit: q . k summed over the 8 lanes of a token
+// group with DPP, then running max, rescale and probabilities per head (a
+// head with no token yet keeps m = -inf and gets p = 0), then P V one token
+// at a time.
+template <typename T, int G>
+__device__ __forceinline__ void attend_unit(const QLane<T, G>& q, KV16<T> (&kr)[kAttnTPG], KV16<T> (&vr)[kAttnTPG],
+                                            int n_tok, int sg, float zscale, float (&m)[G], float (&l)[G],
+                                            float (&o)[G][16]) {
+  constexpr int TPG = kAttnTPG;
+  if (n_tok < kAttnHalf) {  // the filled part of the most recent page only
+#pragma unroll
+    for (int x = 0; x < TPG; ++x)
+      if (sg + kAttnTG * x >= n_tok) { kr[x].zero(); vr[x].zero(); }
+  }
+  float z[TPG][G];
+#pragma unroll
+  for (int x = 0; x < TPG; ++x) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float acc;
+      if constexpr (sizeof(T) == 2) {
+        acc = q.qb[g].dot(kr[x].a, kr[x].b);
+      } else {
+        float kx[16];
+        kr[x].to_f32(kx);
+        acc = 0.f;
+#pragma unroll
+        for (int y = 0; y < 16; ++y) acc = fmaf(q.qf[g][y], kx[y], acc);
+      }
+      z[x][g] = acc;
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < TPG; ++x)
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float full = group_sum<8>(z[x][g]);
+      z[x][g] = (sg + kAttnTG * x < n_tok) ? full * zscale : -INFINITY;
+    }
+  float p[TPG][G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float pm = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < TPG; ++x) pm = fmaxf(pm, z[x][g]);
+    const float m_new = fmaxf(m[g], pm);
+    const float mref = (m_new == -INFINITY) ? 0.f : m_new;
+    const float corr = fast_exp2(m[g] - mref);
+    m[g] = m_new;
+    l[g] *= corr;
+#pragma unroll
+    for (int y = 0; y < 16; ++y) o[g][y] *= corr;
+#pragma unroll
+    for (int x = 0; x < TPG; ++x) {
+      p[x][g] = fast_exp2(z[x][g] - mref);
+      l[g] += p[x][g];
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < TPG; ++x) {
+    float vx[16];
+    vr[x].to_f32(vx);
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int y = 0; y < 16; ++y) o[g][y] = fmaf(p[x][g], vx[y], o[g][y]);
+  }
+}
+
+// Combine the (m, l, o) of every lane of NWV waves into the workgroup's
+// partial, written at index pidx of part_o / part_ml: every lane is rescaled
+// to its wave's running max, token groups are added in pairs (or fours) on
+// the VALU, and the workgroup's partials are combined in LDS with the waves'
+// weights e^{M_w - M}.  Every thread of the workgroup must call it.
+template <int G, int NWV>
+__device__ __forceinline__ void combine_write(const AttnArgs& a, size_t pidx, int wave, int lane, float (&m)[G],
+                                              float (&l)[G], float (&o)[G][16]) {
+  constexpr int D = kHeadDim;
+  constexpr int NT = NWV * kWave;
+  constexpr int NP = AttnCombine<G, NWV>::kPartials;
+  constexpr int PPW = AttnCombine<G, NWV>::kPartialsPerWave;
+  constexpr int GPP = AttnCombine<G, NWV>::kGroupsPerPartial;
+  __shared__ float4 s_o[NP][G][D / 4];
+  __shared__ float s_l[NP][G];
+  __shared__ float s_m[NWV][G];
+  const int sg = lane >> 3;
+  const int e = lane & 7;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     float M = fmaxf(m[g], dpp<kDppRor8>(m[g]));
@@ -287,33 +249,131 @@ __device__ __forceinline__ void attn_split_block(const AttnArgs& a, int split, i
     for (int g = 0; g < G; ++g) s_m[wave][g] = m[g];
   }
   __syncthreads();
-  const size_t pidx = ((size_t)seq * a.hkv + kvh) * a.n_splits + split;
-  for (int x = threadIdx.x; x < G * (D / 4); x += kAttnWaves * kWave) {
-    const int g = x / (D / 4), d4 = x % (D / 4);
-    float M = -INFINITY;
+  if constexpr (NWV == kAttnWaves) {  // one float4 of the output per thread
+    for (int x = threadIdx.x; x < G * (D / 4); x += NT) {
+      const int g = x / (D / 4), d4 = x % (D / 4);
+      float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, s_m[w][g]);
-    float4 ov = make_float4(0.f, 0.f, 0.f, 0.f);
-    float lv = 0.f;
-    if (M != -INFINITY) {
+      for (int w = 0; w < NWV; ++w) M = fmaxf(M, s_m[w][g]);
+      float4 ov = make_float4(0.f, 0.f, 0.f, 0.f);
+      float lv = 0.f;
+      if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kAttnWaves; ++w) {
-        const float f = s_m[w][g] == -INFINITY ? 0.f : fast_exp2(s_m[w][g] - M);
+        for (int w = 0; w < NWV; ++w) {
+          const float f = s_m[w][g] == -INFINITY ? 0.f : fast_exp2(s_m[w][g] - M);
 #pragma unroll
-        for (int q = 0; q < PPW; ++q) {
-          const float4 v = s_o[w * PPW + q][g][d4];
-          ov.x = fmaf(f, v.x, ov.x); ov.y = fmaf(f, v.y, ov.y);
-          ov.z = fmaf(f, v.z, ov.z); ov.w = fmaf(f, v.w, ov.w);
-          lv = fmaf(f, s_l[w * PPW + q][g], lv);
+          for (int q = 0; q < PPW; ++q) {
+            const float4 v = s_o[w * PPW + q][g][d4];
+            ov.x = fmaf(f, v.x, ov.x); ov.y = fmaf(f, v.y, ov.y);
+            ov.z = fmaf(f, v.z, ov.z); ov.w = fmaf(f, v.w, ov.w);
+            lv = fmaf(f, s_l[w * PPW + q][g], lv);
+          }
         }
       }
+      reinterpret_cast<float4*>(a.part_o + (pidx * G + g) * D)[d4] = ov;
+      if (d4 == 0) {
+        a.part_ml[(pidx * G + g) * 2 + 0] = M;
+        a.part_ml[(pidx * G + g) * 2 + 1] = lv;
+      }
     }
-    reinterpret_cast<float4*>(a.part_o + (pidx * G + g) * D)[d4] = ov;
-    if (d4 == 0) {
-      a.part_ml[(pidx * G + g) * 2 + 0] = M;
-      a.part_ml[(pidx * G + g) * 2 + 1] = lv;
+  } else {  // one output element per thread
+    const float* so = reinterpret_cast<const float*>(&s_o[0][0][0]);
+    for (int x = threadIdx.x; x < G * D; x += NT) {
+      const int g = x / D, d = x % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) M = fmaxf(M, s_m[w][g]);
+      float ov = 0.f, lv = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) {
+          const float f = s_m[w][g] == -INFINITY ? 0.f : fast_exp2(s_m[w][g] - M);
+#pragma unroll
+          for (int q = 0; q < PPW; ++q) {
+            ov = fmaf(f, so[((size_t)(w * PPW + q) * G + g) * D + d], ov);
+            lv = fmaf(f, s_l[w * PPW + q][g], lv);
+          }
+        }
+      }
+      a.part_o[(pidx * G + g) * D + d] = ov;
+      if (d == 0) {
+        a.part_ml[(pidx * G + g) * 2 + 0] = M;
+        a.part_ml[(pidx * G + g) * 2 + 1] = lv;
+      }
     }
   }
+}
+
+// One workgroup's split of the attention of (seq, kvh) over the page list
+// `list` (logical pages; nullptr: every page of the sequence), `plist` their
+// physical pages (nullptr: looked up) and `cnt_p` the list length; the lists
+// may live in global memory or LDS.  seq_len is a.seq_lens[seq], loaded by
+// the caller.
+template <typename T, int G>
+__device__ __forceinline__ void attn_split_block(const AttnArgs& a, int split, int kvh, int seq, int seq_len,
+                                                 const int32_t* list, const int32_t* plist, const int32_t* cnt_p) {
+  constexpr int B = 64;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar page-list loads
+  const int sg = lane >> 3;
+  const int e = lane & 7;
+  const int32_t* bt = a.block_table + (size_t)seq * a.max_pages;
+
+  // units are half pages: unit u is half (u & 1) of list entry u >> 1; wave w
+  // of split s takes units [(4 s + w) * ups, +ups)
+  const int ups = a.pages_per_split;
+  const int u0 = (split * kAttnWaves + wave) * ups;
+  const int n_entries = list ? a.k : a.max_pages;  // list entries that exist in memory
+
+  // The first unit's page and physical page are fetched together with the
+  // lengths; its K/V loads are issued before the lengths are used (every
+  // address is inside the physical page, tokens past the end are masked).
+  int pg_first = -1, phys_first = -1;
+  if (u0 < 2 * n_entries) {
+    const int x = u0 >> 1;
+    pg_first = list ? list[x] : x;
+    phys_first = plist ? plist[x] : -2;  // -2: look up through the block table
+  }
+  const int len = seq_len + a.len_add;
+  const int cnt = list ? *cnt_p : 0;
+
+  QLane<T, G> q;
+  q.load(a, seq, kvh, e);
+  float m[G], l[G], o[G][16];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[g][i] = 0.f;
+  }
+  const float zscale = a.scale * kLog2e;
+
+  int u = u0;
+  int pg = pg_first, phys = phys_first;
+  if (phys == -2) phys = (pg >= 0 && pg < a.max_pages) ? bt[pg] : -1;
+  KV16<T> kr[kAttnTPG], vr[kAttnTPG];
+  bool loaded = false;
+  if (len > 0 && phys >= 0 && phys < a.num_phys) { issue_unit<T>(a, kvh, phys, u & 1, sg, e, kr, vr); loaded = true; }
+
+  int n_mr = len > 0 ? (len - 1) / B : -1;
+  if (n_mr > a.max_pages - 1) n_mr = a.max_pages - 1;
+  const int n_list = len <= 0 ? 0 : (list ? min(cnt, a.k) : n_mr + 1);
+  const int u1 = min(u0 + ups, 2 * n_list);
+
+  for (; u < u1; ++u) {
+    if (u != u0) {
+      pg = list ? list[u >> 1] : (u >> 1);
+      phys = plist ? plist[u >> 1] : ((pg >= 0 && pg < a.max_pages) ? bt[pg] : -1);
+      loaded = phys >= 0 && phys < a.num_phys;
+      if (loaded) issue_unit<T>(a, kvh, phys, u & 1, sg, e, kr, vr);
+    }
+    if (!loaded || pg < 0 || pg > n_mr) continue;
+    const int n_tok = ((pg == n_mr) ? len - n_mr * B : B) - (u & 1) * kAttnHalf;  // tokens from the unit's start on
+    if (n_tok <= 0) continue;
+    attend_unit<T, G>(q, kr, vr, n_tok, sg, zscale, m, l, o);
+  }
+  combine_write<G, kAttnWaves>(a, ((size_t)seq * a.hkv + kvh) * a.n_splits + split, wave, lane, m, l, o);
 }
 
 template <typename T, int G>
@@ -322,27 +382,316 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs
   const size_t pair = (size_t)seq * a.hkv + kvh;
   const int32_t* list = a.sel_pages ? a.sel_pages + pair * a.k : nullptr;
   const int32_t* plist = (list && a.sel_phys) ? a.sel_phys + pair * a.k : nullptr;
-  attn_split_block<T, G>(a, split, kvh, seq, list, plist, list ? a.sel_count + pair : nullptr);
+  attn_split_block<T, G>(a, split, kvh, seq, a.seq_lens[seq], list, plist, list ? a.sel_count + pair : nullptr);
 }
 
-// Decode step: selection and attention in one launch.  Every workgroup of a
-// (sequence, KV head) runs the (deterministic) selection of that pair itself
-// into LDS, then attends its split of the selected pages; workgroup 0 also
-// writes the selection out when asked.  This trades redundant selection work
-// for one kernel boundary and one dependent global round trip.
+// ---------------------------------------------------------------------------
+// Decode step: selection and attention in one launch.
+//
+// Workgroup = 8 waves per (split, KV head, sequence); wave w of split s
+// attends unit 8 s + w of the selection list (half page (8 s + w) & 1 of list
+// entry (8 s + w) >> 1).  Every workgroup of a (sequence, KV head) computes
+// that pair's selection itself (the same selection as select_block: the
+// sink, the most recent page and the top k - 2 candidates by m_bar, ties to
+// the lower page index, in page order), with three barriers:
+//  1. per-head normalizers (thread t holds pages (8 NPT (t / 64) + 64 i)
+//     + t % 64, i < NPT: each wave owns a contiguous page range);
+//  2. ranking keys; each thread's largest key goes to LDS;
+//  3. every wave finds the same pivot (the (k-2)-th largest of the maxima of
+//     groups of 8 threads; at least k-2 keys reach it) and appends its keys
+//     >= pivot to its own LDS list, in page order.
+// Then every wave reads the concatenated lists (page order), finds the exact
+// cut by bisection on ballot counts (up to 2 keys per lane) and takes its own
+// unit's page from the lane that holds it: no further barrier before the
+// K/V loads.  More than 128 keys at the pivot (massive ties) fall back to
+// select_block over LDS.
+constexpr int kFusedWaves = 8;
+constexpr int kFusedThreads = kFusedWaves * kWave;
+constexpr int kFusedCap = 2 * kWave;  // list entries the exact cut holds in registers
+
 template <typename T, int NPT, int G>
-__global__ __launch_bounds__(kAttnWaves * kWave) void select_attn_kernel(SelectArgs se, AttnArgs a) {
-  __shared__ int32_t s_sel[kMaxSelect], s_selp[kMaxSelect];
+__global__ __launch_bounds__(kFusedThreads) void select_attn_kernel(SelectArgs se, AttnArgs a) {
+  constexpr int B = 64;
+  constexpr int BS = kFusedThreads;
+  constexpr int NW = kFusedWaves;
+  constexpr int TR = BS / kWave;  // threads per pivot group
+  __shared__ float s_pm[G][NW], s_ps[G][NW];
+  __shared__ uint32_t s_tmax[BS];
+  __shared__ uint32_t s_ck[NW][kFusedCap];
+  __shared__ int32_t s_cp[NW][kFusedCap];
+  __shared__ int32_t s_cph[NW][kFusedCap];
+  __shared__ int32_t s_wc[NW];
+  __shared__ int32_t s_fix[2];
+  __shared__ int32_t s_sel[kMaxSelect], s_selp[kMaxSelect];  // fallback selection
   __shared__ int32_t s_cnt;
+
   const int split = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
-  select_block<kAttnWaves * kWave, NPT, G>(se, seq, kvh, s_sel, &s_cnt, s_selp);
-  __syncthreads();
-  if (split == 0 && se.sel_pages) {
-    const size_t pair = (size_t)seq * se.hkv + kvh;
-    for (int i = threadIdx.x; i < se.k; i += kAttnWaves * kWave) se.sel_pages[pair * se.k + i] = s_sel[i];
-    if (threadIdx.x == 0) se.sel_count[pair] = s_cnt;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const size_t pair = (size_t)seq * se.hkv + kvh;
+  const int k = se.k;
+  const int32_t* bt = se.block_table + (size_t)seq * se.max_pages;
+  const float* lse = se.page_lse + ((size_t)seq * se.hkv * G + (size_t)kvh * G) * se.max_pages;
+  auto page = [&](int i) { return (wave * NPT + i) * kWave + lane; };
+  auto valid_phys = [&](int ph) { return (ph >= 0 && ph < se.num_phys) ? ph : -1; };
+
+  // Loads that need no length go out first: the scores and block-table
+  // entries of this thread's pages (clamped in bounds, masked below) and the
+  // lane's query slices.
+  float v[G][NPT];
+  int ph[NPT];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) v[g][i] = lse[(size_t)g * se.max_pages + min(page(i), se.max_pages - 1)];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) ph[i] = bt[min(page(i), se.max_pages - 1)];
+  const int sg = lane >> 3;
+  const int e = lane & 7;
+  QLane<T, G> q;
+  q.load(a, seq, kvh, e);
+  const int seq_len = se.seq_lens[seq];
+
+  const int len = seq_len + se.len_add;
+  int n_mr = len > 0 ? (len - 1) / B : -1;
+  if (n_mr > se.max_pages - 1) n_mr = se.max_pages - 1;
+  const int n_cand = n_mr > 0 ? n_mr - 1 : 0;
+  const int n_top = min(k - 2, n_cand);
+  const int unit = split * NW + wave;  // this wave's unit of the selection list
+  const int x = unit >> 1;             // its list entry
+  int cnt = 0, pg = -1, phys = -1;
+  int mode = 0;  // 0: no page or every page, 1: fixed pages + list in registers, 2: fallback in LDS
+  uint32_t ck[2] = {0u, 0u};
+  int cpg[2] = {-1, -1}, cph[2] = {-1, -1}, slot[2] = {0, 0};
+  bool taken[2] = {false, false};
+
+  if (len > 0 && n_top == n_cand) {  // every page 0 .. n_mr is selected
+    cnt = n_mr + 1;
+    if (x <= n_mr) { pg = x; phys = bt[x]; }
+  } else if (len > 0) {
+    // 1) per-head normalizers M_g, S_g (scores in log2 units)
+    float mg[G], sl[G], E[G][NPT];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      mg[g] = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < NPT; ++i) {
+        v[g][i] = page(i) < n_mr ? v[g][i] * kLog2e : -INFINITY;
+        mg[g] = fmaxf(mg[g], v[g][i]);
+      }
+      sl[g] = 0.f;
+#pragma unroll
+      for (int i = 0; i < NPT; ++i) {
+        E[g][i] = mg[g] == -INFINITY ? 0.f : fast_exp2(v[g][i] - mg[g]);
+        sl[g] += E[g][i];
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float wm = wave_max(mg[g]);
+      const float ws = wave_sum(wm == -INFINITY || mg[g] == -INFINITY ? 0.f : sl[g] * fast_exp2(mg[g] - wm));
+      if (lane == 0) { s_pm[g][wave] = wm; s_ps[g][wave] = ws; }
+    }
+    __syncthreads();
+    float Mg[G], scale[G], log2S[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_pm[g][w]);
+      float S = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float wm = s_pm[g][w];
+        S += wm == -INFINITY ? 0.f : s_ps[g][w] * fast_exp2(wm - M);
+      }
+      Mg[g] = M;
+      log2S[g] = fast_log2(S);
+      scale[g] = (mg[g] == -INFINITY || !(S > 0.f)) ? 0.f : fast_exp2(mg[g] - M) / S;
+    }
+    // 2) ranking keys of the candidates 1 .. n_mr - 1; the fixed pages'
+    //    physical pages for every wave
+    const float invG = 1.f / (float)G;
+    const float log2G = fast_log2((float)G);
+    uint32_t key[NPT];
+    uint32_t tmax = 0u;
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int j = page(i);
+      key[i] = 0u;
+      if (j == 0) s_fix[0] = ph[i];
+      if (j == n_mr) s_fix[1] = ph[i];
+      if (j < 1 || j >= n_mr) continue;
+      float xg[G], eg[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) { xg[g] = v[g][i]; eg[g] = E[g][i]; }
+      float mb;
+      key[i] = order_key(share_log2<G>(xg, eg, scale, Mg, log2S, invG, log2G, mb));
+      tmax = max(tmax, key[i]);
+    }
+    s_tmax[tid] = tmax;
+    __syncthreads();
+    cnt = n_top + 2;
+    if (n_top > 0) {
+      // 3) pivot, found by every wave alike
+      uint32_t piv;
+      {
+        uint32_t gm[1] = {0u};
+#pragma unroll
+        for (int r = 0; r < TR; ++r) gm[0] = max(gm[0], s_tmax[lane * TR + r]);
+        if (__popcll(__ballot(gm[0] != 0u)) >= n_top) {
+          piv = wave_nth_largest<1>(gm, n_top);
+        } else {
+          uint32_t tv[TR];
+          int nz = 0;
+#pragma unroll
+          for (int r = 0; r < TR; ++r) {
+            tv[r] = s_tmax[lane + kWave * r];
+            nz += __popcll(__ballot(tv[r] != 0u));
+          }
+          piv = nz >= n_top ? wave_nth_largest<TR>(tv, n_top) : 1u;
+        }
+      }
+      //    this wave's keys >= pivot, in page order, to its own list
+      int wc = 0;
+#pragma unroll
+      for (int i = 0; i < NPT; ++i) {
+        const bool c = key[i] >= piv && key[i] != 0u;
+        const uint64_t bm = __ballot(c);
+        const int pos = wc + lanes_below(bm);
+        if (c && pos < kFusedCap) {
+          s_ck[wave][pos] = key[i];
+          s_cp[wave][pos] = page(i);
+          s_cph[wave][pos] = ph[i];
+        }
+        wc += __popcll(bm);
+      }
+      if (lane == 0) s_wc[wave] = wc;
+      __syncthreads();
+      int off[NW + 1];
+      off[0] = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) off[w + 1] = off[w] + s_wc[w];
+      const int C = off[NW];
+      if (C <= kFusedCap) {
+        // exact cut over the concatenated lists (entry lane + 64 r)
+        mode = 1;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int en = lane + kWave * r;
+          if (en < C) {
+            int w = 0, base = 0;
+#pragma unroll
+            for (int ww = 1; ww < NW; ++ww)
+              if (en >= off[ww]) { w = ww; base = off[ww]; }
+            ck[r] = s_ck[w][en - base];
+            cpg[r] = s_cp[w][en - base];
+            cph[r] = s_cph[w][en - base];
+          }
+        }
+        const uint32_t t = wave_nth_largest<2>(ck, n_top);
+        int n_gt = 0;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) n_gt += __popcll(__ballot(ck[r] > t));
+        const int take_eq = n_top - n_gt;
+        int eq_before = 0, out_before = 0;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const bool eq = ck[r] == t;
+          const uint64_t be = __ballot(eq);
+          taken[r] = ck[r] > t || (eq && eq_before + lanes_below(be) < take_eq);
+          eq_before += __popcll(be);
+          const uint64_t bs = __ballot(taken[r]);
+          slot[r] = 1 + out_before + lanes_below(bs);
+          out_before += __popcll(bs);
+        }
+        if (x == 0) {
+          pg = 0;
+          phys = s_fix[0];
+        } else if (x <= n_top) {
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            const uint64_t mm = __ballot(taken[r] && slot[r] == x);
+            if (mm) {
+              const int src = __ffsll((unsigned long long)mm) - 1;
+              pg = __builtin_amdgcn_readlane(cpg[r], src);
+              phys = __builtin_amdgcn_readlane(cph[r], src);
+            }
+          }
+        } else if (x == n_top + 1) {
+          pg = n_mr;
+          phys = s_fix[1];
+        }
+      } else {
+        // massive ties at the pivot: the general selection over LDS
+        mode = 2;
+        select_block<BS, NPT, G>(se, seq, kvh, seq_len, s_sel, &s_cnt, s_selp);
+        __syncthreads();
+        cnt = s_cnt;
+        if (x < cnt) { pg = s_sel[x]; phys = s_selp[x]; }
+      }
+    } else {  // k = 2: the sink and the most recent page
+      mode = 1;
+      if (x == 0) { pg = 0; phys = s_fix[0]; }
+      else if (x == 1) { pg = n_mr; phys = s_fix[1]; }
+    }
   }
-  attn_split_block<T, G>(a, split, kvh, seq, s_sel, s_selp, &s_cnt);
+
+  // the selection, when asked for, from split 0
+  if (split == 0 && se.sel_pages) {
+    int32_t* so = se.sel_pages + pair * k;
+    int32_t* sp = se.sel_phys ? se.sel_phys + pair * k : nullptr;
+    if (mode == 0) {
+      for (int sl0 = tid; sl0 < k; sl0 += BS) {
+        const bool in = sl0 < cnt;
+        so[sl0] = in ? sl0 : -1;
+        if (sp) sp[sl0] = in ? valid_phys(bt[sl0]) : -1;
+      }
+    } else if (mode == 2) {
+      for (int sl0 = tid; sl0 < k; sl0 += BS) {
+        so[sl0] = s_sel[sl0];
+        if (sp) sp[sl0] = s_selp[sl0];
+      }
+    } else {
+      if (wave == 0) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+          if (taken[r]) {
+            so[slot[r]] = cpg[r];
+            if (sp) sp[slot[r]] = valid_phys(cph[r]);
+          }
+      }
+      if (tid == 0) {
+        so[0] = 0;
+        so[cnt - 1] = n_mr;
+        if (sp) { sp[0] = valid_phys(s_fix[0]); sp[cnt - 1] = valid_phys(s_fix[1]); }
+      }
+      for (int sl0 = cnt + tid; sl0 < k; sl0 += BS) {
+        so[sl0] = -1;
+        if (sp) sp[sl0] = -1;
+      }
+    }
+    if (tid == 0) se.sel_count[pair] = cnt;
+  }
+
+  // attention over this wave's unit
+  float m[G], l[G], o[G][16];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[g][i] = 0.f;
+  }
+  if (x < cnt && pg >= 0 && pg <= n_mr && phys >= 0 && phys < a.num_phys) {
+    const int half = unit & 1;
+    KV16<T> kr[kAttnTPG], vr[kAttnTPG];
+    issue_unit<T>(a, kvh, phys, half, sg, e, kr, vr);
+    const int n_tok = ((pg == n_mr) ? len - n_mr * B : B) - half * kAttnHalf;
+    if (n_tok > 0) attend_unit<T, G>(q, kr, vr, n_tok, sg, a.scale * kLog2e, m, l, o);
+  }
+  combine_write<G, NW>(a, pair * a.n_splits + split, wave, lane, m, l, o);
 }
 
 // Merge: one workgroup per (sequence, KV head) combines the split partials of
@@ -430,13 +779,12 @@ hipError_t launch_attn(DType dt, int group, const AttnArgs& a, bool merge, hipSt
 template <typename T, int NPT>
 static hipError_t launch_select_attn_n(const SelectArgs& se, const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.n_splits, a.hkv, a.batch);
-  dim3 block(kAttnWaves * kWave);
+  dim3 block(kFusedThreads);
   switch (se.group) {
     case 1: hipLaunchKernelGGL((select_attn_kernel<T, NPT, 1>), grid, block, 0, s, se, a); break;
     case 2: hipLaunchKernelGGL((select_attn_kernel<T, NPT, 2>), grid, block, 0, s, se, a); break;
     case 4: hipLaunchKernelGGL((select_attn_kernel<T, NPT, 4>), grid, block, 0, s, se, a); break;
-    case 8: hipLaunchKernelGGL((select_attn_kernel<T, NPT, 8>), grid, block, 0, s, se, a); break;
-    default: return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;  // G = 8 keeps the two launches (registers)
   }
   return hipGetLastError();
 }
@@ -444,18 +792,23 @@ static hipError_t launch_select_attn_n(const SelectArgs& se, const AttnArgs& a, 
 template <typename T>
 static hipError_t launch_select_attn_t(const SelectArgs& se, const AttnArgs& a, hipStream_t s) {
   const int n = se.max_pages;
-  if (n <= kAttnWaves * kWave * 4) return launch_select_attn_n<T, 4>(se, a, s);
-  if (n <= kAttnWaves * kWave * 8) return launch_select_attn_n<T, 8>(se, a, s);
-  if (n <= kAttnWaves * kWave * 12) return launch_select_attn_n<T, 12>(se, a, s);
+  if (n <= kFusedThreads * 2) return launch_select_attn_n<T, 2>(se, a, s);
+  if (n <= kFusedThreads * 4) return launch_select_attn_n<T, 4>(se, a, s);
+  if (n <= kFusedThreads * 5) return launch_select_attn_n<T, 5>(se, a, s);
+  if (n <= kFusedThreads * 6) return launch_select_attn_n<T, 6>(se, a, s);
   return hipErrorNotSupported;
 }
 
 bool select_attn_fusable(const SelectArgs& se) {
-  return se.max_pages <= kAttnWaves * kWave * 12 && se.k <= kMaxSelect && se.group <= kMaxGroup;
+  return se.max_pages <= kFusedThreads * 6 && se.k <= kMaxSelect && se.group <= 4 && se.page_size == 64 &&
+         se.share_out == nullptr;
 }
+
+int select_attn_splits(int k) { return (2 * k + kFusedWaves - 1) / kFusedWaves; }
 
 hipError_t launch_select_attn(DType dt, const SelectArgs& se, const AttnArgs& a, hipStream_t s) {
   if (!select_attn_fusable(se)) return hipErrorNotSupported;
+  if (se.seq_lens != a.seq_lens || a.n_splits != select_attn_splits(se.k)) return hipErrorInvalidValue;
   return dt == kBF16 ? launch_select_attn_t<bf16_t>(se, a, s) : launch_select_attn_t<float>(se, a, s);
 }
 

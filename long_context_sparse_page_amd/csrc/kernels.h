@@ -97,6 +97,7 @@ hipError_t launch_build(DType dt, int rank, const BuildArgs& a, hipStream_t s);
 // Decode step: selection (se) and attention splits (a) in one launch, for
 // tables of up to 3072 pages per sequence (select_attn_fusable).
 bool select_attn_fusable(const SelectArgs& se);
+int select_attn_splits(int k);  // attention splits of the fused launch
 hipError_t launch_select_attn(DType dt, const SelectArgs& se, const AttnArgs& a, hipStream_t s);
 
 }  // namespace lk

@@ -194,7 +194,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_kernel(ScoreArgs a)
 // A wave takes NR records at a time.  Their (r + 1) rows (centroid, basis)
 // are the 16-wide columns of B in v_mfma_f32_16x16x32_bf16 (row slot
 // s = record * (r + 1) + row), the group's G queries are the rows of A (rows
-// >= G are zero), and four K-steps of 32 cover d = 128: the product holds
+// >= G repeat the last query and are ignored), and four K-steps of 32 cover d = 128: the product holds
 // P[slot][g] = W_slot . q_g.  Lane l of B supplies column l % 16 and 8
 // consecutive dims of K-step t at group l / 16, i.e. one 16-byte load; lane l
 // of A supplies the same dims of query l % 16.  The accumulator of lane l
@@ -217,13 +217,16 @@ template <int R> struct ScoreGroup {
 template <int R> struct GroupLoads {
   uint4 wb[ScoreGroup<R>::TILES][4];             // B operand tiles
   uint32_t cw[ScoreGroup<R>::NR][ScoreGroup<R>::CW];  // this lane's token coefficients (bf16 pairs)
-  const bf16_t* recp[ScoreGroup<R>::NR];         // record bases (nullptr: none)
+  bool valid[ScoreGroup<R>::NR];                 // record present in the pool (else the page scores -inf)
 };
 
+// Every load is unconditional, so the compiler keeps them in one batch with no
+// wait in between: a record that is not in the pool is read from physical
+// page 0 instead (always allocated) and its result discarded, and B columns
+// past the group's slots repeat its last slot (their products are unused).
 template <int R>
-__device__ __forceinline__ void load_group(GroupLoads<R>& L, const bf16_t* summ, const int* phys_g, int g0,
-                                           int n_scored, int num_phys, int hkv, int kvh, int col, int kg,
-                                           int lane) {
+__device__ __forceinline__ void load_group(GroupLoads<R>& L, const bf16_t* summ, const int* phys_g, int num_phys,
+                                           int hkv, int kvh, int col, int kg, int lane) {
   constexpr int D = kHeadDim;
   constexpr int B = 64;
   constexpr int ROWS = R + 1;
@@ -232,41 +235,40 @@ __device__ __forceinline__ void load_group(GroupLoads<R>& L, const bf16_t* summ,
   constexpr int TILES = ScoreGroup<R>::TILES;
   constexpr int CW = ScoreGroup<R>::CW;
   constexpr size_t REC = (size_t)ROWS * D + (size_t)B * R;
+  const bf16_t* recp[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
-    const int j = g0 + r;
-    const int phys = j < n_scored ? phys_g[r] : -1;
-    L.recp[r] = (phys >= 0 && phys < num_phys) ? summ + ((size_t)phys * hkv + kvh) * REC : nullptr;
+    const int phys = phys_g[r];
+    L.valid[r] = phys >= 0 && phys < num_phys;
+    recp[r] = summ + ((size_t)(L.valid[r] ? phys : 0) * hkv + kvh) * REC;
   }
 #pragma unroll
   for (int tau = 0; tau < TILES; ++tau) {
-    const int slot = 16 * tau + col;
+    const int slot = min(16 * tau + col, SLOTS - 1);
     const int r = slot / ROWS, m = slot % ROWS;
-    const bf16_t* rp = nullptr;
+    const bf16_t* rp = recp[0];
 #pragma unroll
-    for (int x = 0; x < NR; ++x) if (x == r) rp = L.recp[x];
-    const bool ok = slot < SLOTS && rp != nullptr;
+    for (int x = 1; x < NR; ++x) if (x == r) rp = recp[x];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      L.wb[tau][t] = ok ? *reinterpret_cast<const uint4*>(rp + (size_t)m * D + 32 * t + 8 * kg)
-                        : make_uint4(0, 0, 0, 0);
+      L.wb[tau][t] = *reinterpret_cast<const uint4*>(rp + (size_t)m * D + 32 * t + 8 * kg);
   }
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
-    const bf16_t* cp = L.recp[r] ? L.recp[r] + (size_t)ROWS * D + (size_t)lane * R : nullptr;
+    const bf16_t* cp = recp[r] + (size_t)ROWS * D + (size_t)lane * R;
     if constexpr (R % 8 == 0) {
 #pragma unroll
       for (int x = 0; x < CW; x += 4) {
-        const uint4 v = cp ? *reinterpret_cast<const uint4*>(cp + 2 * x) : make_uint4(0, 0, 0, 0);
+        const uint4 v = *reinterpret_cast<const uint4*>(cp + 2 * x);
         L.cw[r][x] = v.x; L.cw[r][x + 1] = v.y; L.cw[r][x + 2] = v.z; L.cw[r][x + 3] = v.w;
       }
     } else if constexpr (R == 4) {
-      const uint2 v = cp ? *reinterpret_cast<const uint2*>(cp) : make_uint2(0, 0);
+      const uint2 v = *reinterpret_cast<const uint2*>(cp);
       L.cw[r][0] = v.x; L.cw[r][1] = v.y;
     } else if constexpr (R == 2) {
-      L.cw[r][0] = cp ? *reinterpret_cast<const uint32_t*>(cp) : 0u;
+      L.cw[r][0] = *reinterpret_cast<const uint32_t*>(cp);
     } else {
-      L.cw[r][0] = cp ? (uint32_t)*cp : 0u;
+      L.cw[r][0] = (uint32_t)*cp;
     }
   }
 }
@@ -307,22 +309,24 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_mfma_kernel(ScoreAr
 #pragma unroll
   for (int x = 0; x < PAGES_PER_WAVE; ++x) phys_all[x] = bt[min(j0 + x, a.max_pages - 1)];
   const int len_raw = a.seq_lens[seq] + a.len_add;
-  bf16x8_t qa[4];  // A operand: query `col` (zero rows beyond G), 4 K-steps
+  bf16x8_t qa[4];  // A operand: query `col`, 4 K-steps
   {
     const bf16_t* q = reinterpret_cast<const bf16_t*>(a.q) + ((size_t)seq * a.hq + (size_t)kvh * G) * D;
+    // rows >= G repeat query G-1 (their products are unused)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (col < G) w = *reinterpret_cast<const uint4*>(q + (size_t)col * D + 32 * t + 8 * kg);
-      qa[t] = __builtin_bit_cast(bf16x8_t, w);
-    }
+    for (int t = 0; t < 4; ++t)
+      qa[t] = __builtin_bit_cast(bf16x8_t,
+                                 *reinterpret_cast<const uint4*>(q + (size_t)min(col, G - 1) * D + 32 * t + 8 * kg));
   }
   constexpr int GPW = ScoreGroup<R>::GROUPS_PER_WAVE;
   GroupLoads<R> grp[GPW];
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi)
-    load_group<R>(grp[gi], summ, phys_all + gi * NR, j0 + gi * NR, a.max_pages, a.num_phys, a.hkv, kvh, col, kg,
-                  lane);
+    load_group<R>(grp[gi], summ, phys_all + gi * NR, a.num_phys, a.hkv, kvh, col, kg, lane);
+  // The loads above have no side effects, so without this fence the compiler
+  // would move them below the length checks and between the products (each
+  // move adds a wait for earlier loads before later ones are issued).
+  asm volatile("" ::: "memory");
 
   if (len_raw <= 0) return;
   int n_scored = (len_raw - 1) / B;
@@ -360,7 +364,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_mfma_kernel(ScoreAr
     for (int r = 0; r < NR; ++r) {
       const int j = g0 + r;
       if (j >= j_end) break;
-      if (!cur.recp[r]) {
+      if (!cur.valid[r]) {
         if (lane < G) out[(size_t)lane * a.max_pages + j] = -INFINITY;
         continue;
       }

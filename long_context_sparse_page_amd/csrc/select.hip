@@ -10,7 +10,7 @@ __global__ __launch_bounds__(BS) void select_kernel(SelectArgs a) {
   const int kvh = blockIdx.x;
   const int seq = blockIdx.y;
   const size_t pair = (size_t)seq * a.hkv + kvh;
-  select_block<BS, NPT, G>(a, seq, kvh, a.sel_pages + pair * a.k, a.sel_count + pair,
+  select_block<BS, NPT, G>(a, seq, kvh, a.seq_lens[seq], a.sel_pages + pair * a.k, a.sel_count + pair,
                            a.sel_phys ? a.sel_phys + pair * a.k : nullptr);
 }
 

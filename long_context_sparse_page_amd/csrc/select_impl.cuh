@@ -199,11 +199,43 @@ __device__ __forceinline__ void select_from_list(const uint32_t* s_ckey, const i
   }
 }
 
+// log2 m_bar_j of one page from its G scores in log2 units x[g], with
+// e[g] = 2^(x[g] - m_g) (m_g: the thread's running maximum of head g) and
+// scale[g] = 2^(m_g - M_g) / S_g; m_bar_j itself is returned in mb.  A share
+// below 2^-120 is evaluated in the log domain,
+// log2 m_bar = log2 sum_g 2^(x[g] - M_g - log2 S_g) - log2 G.
+template <int G>
+__device__ __forceinline__ float share_log2(const float (&x)[G], const float (&e)[G], const float (&scale)[G],
+                                           const float (&Mg)[G], const float (&log2S)[G], float invG, float log2G,
+                                           float& mb) {
+  mb = 0.f;
+#pragma unroll
+  for (int g = 0; g < G; ++g) mb = fmaf(e[g], scale[g], mb);
+  mb *= invG;
+  if (mb >= 0x1p-120f) return fast_log2(mb);
+  float d[G], mx = -INFINITY;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    d[g] = (Mg[g] == -INFINITY) ? -INFINITY : x[g] - Mg[g] - log2S[g];
+    mx = fmaxf(mx, d[g]);
+  }
+  float lm = -INFINITY;
+  if (mx != -INFINITY) {
+    float sm = 0.f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) sm += fast_exp2(d[g] - mx);
+    lm = mx + fast_log2(sm) - log2G;
+  }
+  mb = fast_exp2(lm);
+  return lm;
+}
+
 // One workgroup of BS threads selects for (seq, kvh); sel / cnt_out / selp
-// may point to global memory or LDS (selp nullptr: no physical pages).
+// may point to global memory or LDS (selp nullptr: no physical pages);
+// seq_len is a.seq_lens[seq], loaded by the caller.
 template <int BS, int NPT, int G>
-__device__ __forceinline__ void select_block(const SelectArgs& a, int seq, int kvh, int32_t* sel, int32_t* cnt_out,
-                                             int32_t* selp) {
+__device__ __forceinline__ void select_block(const SelectArgs& a, int seq, int kvh, int seq_len, int32_t* sel,
+                                             int32_t* cnt_out, int32_t* selp) {
   constexpr int NW = BS / kWave;
   // Up to 256 threads the scores stay in registers from one early load; larger
   // blocks (128 registers per thread) load them again for the keys (L2 hits).
@@ -256,7 +288,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, int seq, int k
     if (selp) selp[s] = (page >= 0 && phys >= 0 && phys < a.num_phys) ? phys : -1;
   };
 
-  const int len = a.seq_lens[seq] + a.len_add;
+  const int len = seq_len + a.len_add;
   if (len <= 0) {
     for (int s = tid; s < k; s += BS) emit(s, -1, -1);
     if (tid == 0) *cnt_out = 0;
@@ -354,35 +386,14 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, int seq, int k
     float x[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) x[g] = score_at(g, i);
-    float mb = 0.f;
+    float eg[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float eg;
-      if constexpr (kKeepE) eg = E[g][i];
-      else eg = m[g] == -INFINITY ? 0.f : fast_exp2(x[g] - m[g]);
-      mb = fmaf(eg, scale[g], mb);
+      if constexpr (kKeepE) eg[g] = E[g][i];
+      else eg[g] = m[g] == -INFINITY ? 0.f : fast_exp2(x[g] - m[g]);
     }
-    mb *= invG;
-    float lm;
-    if (mb >= 0x1p-120f) {
-      lm = fast_log2(mb);
-    } else {  // tiny share: log2 m_bar = log2 sum_g 2^(s2 - M_g - log2 S_g) - log2 G
-      float d[G], mx = -INFINITY;
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        d[g] = (Mg[g] == -INFINITY) ? -INFINITY : x[g] - Mg[g] - log2S[g];
-        mx = fmaxf(mx, d[g]);
-      }
-      if (mx == -INFINITY) {
-        lm = -INFINITY;
-      } else {
-        float sm = 0.f;
-#pragma unroll
-        for (int g = 0; g < G; ++g) sm += fast_exp2(d[g] - mx);
-        lm = mx + fast_log2(sm) - log2G;
-      }
-      mb = fast_exp2(lm);
-    }
+    float mb;
+    const float lm = share_log2<G>(x, eg, scale, Mg, log2S, invG, log2G, mb);
     if (so) so[j] = mb;
     if (j >= 1) {  // candidates: pages 1 .. n_mr - 1
       key[i] = order_key(lm);

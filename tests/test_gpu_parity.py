@@ -344,10 +344,11 @@ def test_group_and_rank_variants_fp32(gpu, group, rank):
 # threads hold one, the block-wide fallback when ties overflow the list, and
 # the large-table tiers (scores loaded twice).
 
-def _selector_case(T, budget, capacity=None, group=4, layout=None):
+def _selector_case(T, budget, capacity=None, group=4, layout=None, hold_last=False):
     """fp32 single-sequence cache holding T tokens whose keys may be rearranged
     by ``layout(keys)`` (page copies make exact ties); returns the workload,
-    cache, host K/V pages and fp64 queries."""
+    cache, host K/V pages and fp64 queries.  hold_last: the cache holds the
+    first T - 1 tokens only (T % 64 != 0), for a decode step to append the last."""
     w = synth.workload(0, budget=budget)
     w.context = [T]
     w.num_q_heads = group
@@ -357,7 +358,12 @@ def _selector_case(T, budget, capacity=None, group=4, layout=None):
     q = np.random.default_rng(T).standard_normal((1, group, w.head_dim)).astype(np.float32)
     if layout is not None:
         q = layout(kk, q)
-    dc.write_tokens(0, 0, 0, to_storage(kk, w.dtype), to_storage(vv, w.dtype))
+    n_write = T - 1 if hold_last else T
+    assert not hold_last or T % w.page_size != 0
+    dc.write_tokens(0, 0, 0, to_storage(kk[:n_write], w.dtype), to_storage(vv[:n_write], w.dtype))
+    if hold_last:
+        dc.seq_lens.fill_(T - 1)
+        dc.held = (kk[T - 1:T], vv[T - 1:T])
     dc.build_all()
     B, d = w.page_size, w.head_dim
     n_pages = -(-T // B)
@@ -421,6 +427,72 @@ def test_selector_ties_at_cut(gpu):
     expect = sorted([0, n_mr] + tied[:30])
     assert list(hs.selected) == expect
     assert sel == expect
+
+
+def _run_decode_selector(w, dc, K, V, q64):
+    """The held-back last token appended by lk_decode_step (which selects and
+    attends in one launch for these tables); its selection and output against
+    the oracle at T tokens."""
+    T = w.context[0]
+    hs, _ = ref.oracle_head(w, q64[0], K, V, T)
+    o = dc.outputs()
+    kn, vn = dc.held
+    dc.decode_step(ref.q_device(q64, w.dtype), to_storage(kn, w.dtype).cuda()[None],
+                   to_storage(vn, w.dtype).cuda()[None], o)
+    torch.cuda.synchronize()
+    assert dc.seq_lens.cpu().tolist() == [T]
+    sel = [int(x) for x in o["sel"].cpu().numpy()[0, 0, :o["cnt"].cpu().numpy()[0, 0]]]
+    k = lo.page_budget(w.token_budget, w.page_size)
+    assert (o["sel"].cpu().numpy()[0, 0, len(sel):] == -1).all()
+    n_mr = lo.most_recent_page(T, w.page_size)
+    msg = ref.selection_mismatch(sel, hs.selected, hs.m_bar, n_mr, k)
+    assert msg is None, msg
+    eo, else_ = lo.attend(q64[0], lo.gather_tokens(K, sel, T, w.page_size),
+                          lo.gather_tokens(V, sel, T, w.page_size), w.scale)
+    out = o["out"].cpu().numpy().astype(np.float64)[0]
+    assert ref.rel_l2(out, eo).max() < 1e-5
+    np.testing.assert_allclose(o["lse"].cpu().numpy()[0], else_, atol=1e-5)
+    return sel, hs
+
+
+def _copies_of_page1(kk, q):
+    for p in range(2, kk.shape[0] // 64):
+        kk[p * 64:(p + 1) * 64] = kk[64:128]
+    return q
+
+
+def _hot_copies(kk, q):
+    hot = sorted(np.random.default_rng(11).choice(np.arange(2, 149), size=40, replace=False).tolist())
+    u = np.random.default_rng(12).standard_normal(kk.shape[1])
+    u /= np.linalg.norm(u)
+    base = kk[64:128] + 2.0 * u
+    for p in [1] + hot:
+        kk[p * 64:(p + 1) * 64] = base
+    return (q * 0.1 + 3.0 * np.sqrt(kk.shape[1]) * u).astype(np.float32)
+
+
+@pytest.mark.parametrize("T,budget,capacity,group,layout,expect", [
+    (64 * 400 + 10, 2048, None, 4, _copies_of_page1, "lowest"),  # all tie: more keys at the pivot than fit
+    (64 * 150 + 5, 2048, None, 4, _hot_copies, "hot"),           # 41 tied pages across the cut
+    (64 * 101 + 3, 4096, None, 4, None, None),                   # budget 64 pages
+    (64 * 700 + 40, 1024, 2500, 2, None, None),                  # 5 pages per thread, G = 2
+    (64 * 2000 + 7, 2048, 3000, 1, None, None),                  # 6 pages per thread, G = 1
+    (64 * 20 + 9, 128, None, 4, None, None),                     # k = 2: sink and most recent
+    (64 * 20 + 9, 2048, None, 4, None, None),                    # every page selected
+    (64 * 1 + 1, 2048, None, 4, None, None),                     # two pages
+])
+def test_decode_step_selection(gpu, T, budget, capacity, group, layout, expect):
+    say("decode-step selection: T", T, "budget", budget, "capacity", capacity, "G", group,
+        "layout", layout.__name__ if layout else None)
+    w, dc, K, V, q64 = _selector_case(T, budget, capacity=capacity, group=group, layout=layout, hold_last=True)
+    sel, hs = _run_decode_selector(w, dc, K, V, q64)
+    n_mr = lo.most_recent_page(T, w.page_size)
+    if expect == "lowest":
+        assert sel == [0] + list(range(1, 31)) + [n_mr]
+    elif expect == "hot":
+        hot = sorted(np.random.default_rng(11).choice(np.arange(2, 149), size=40, replace=False).tolist())
+        assert sel == sorted([0, n_mr] + sorted([1] + hot)[:30])
+    assert len(sel) == len(hs.selected)
 
 
 @pytest.mark.parametrize("T,budget,capacity,group", [
