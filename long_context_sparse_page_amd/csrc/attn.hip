@@ -494,21 +494,22 @@ __global__ __launch_bounds__(kFusedThreads) void select_attn_kernel(SelectArgs s
       if (lane == 0) { s_pm[g][wave] = wm; s_ps[g][wave] = ws; }
     }
     __syncthreads();
+    // lane g * 8 + w combines wave w's partial of head g; groups of 8 lanes
+    // reduce with DPP and every lane reads the G results
     float Mg[G], scale[G], log2S[G];
+    {
+      static_assert(G * NW <= kWave && NW == 8, "one lane per (head, wave)");
+      const int gl = min(lane / NW, G - 1), wl = lane % NW;
+      const float pm = s_pm[gl][wl], ps = s_ps[gl][wl];
+      const float M = group_max<NW>(pm);
+      const float S = group_sum<NW>(pm == -INFINITY ? 0.f : ps * fast_exp2(pm - M));
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_pm[g][w]);
-      float S = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float wm = s_pm[g][w];
-        S += wm == -INFINITY ? 0.f : s_ps[g][w] * fast_exp2(wm - M);
+      for (int g = 0; g < G; ++g) {
+        Mg[g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(M), g * NW));
+        const float Sg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(S), g * NW));
+        log2S[g] = fast_log2(Sg);
+        scale[g] = (mg[g] == -INFINITY || !(Sg > 0.f)) ? 0.f : fast_exp2(mg[g] - Mg[g]) / Sg;
       }
-      Mg[g] = M;
-      log2S[g] = fast_log2(S);
-      scale[g] = (mg[g] == -INFINITY || !(S > 0.f)) ? 0.f : fast_exp2(mg[g] - M) / S;
     }
     // 2) ranking keys of the candidates 1 .. n_mr - 1; the fixed pages'
     //    physical pages for every wave

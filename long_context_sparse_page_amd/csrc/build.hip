@@ -44,23 +44,40 @@ constexpr float kClusterTol = 1e-3f; // eigenvalues this close (relative to lamb
 template <typename T>
 __device__ __forceinline__ void merge_partials(const BuildArgs& a, int seq, int kvh) {
   constexpr int D = kHeadDim;
+  constexpr int CH = 16;  // splits whose partials are loaded together (one round trip)
   const int G = a.merge.group;
   const int ns = a.merge.n_splits;
   const float* ml = a.merge.part_ml + ((size_t)seq * a.hkv + kvh) * ns * G * 2;
   const float* ob = a.merge.part_o + ((size_t)seq * a.hkv + kvh) * ns * G * D;
   for (int x = threadIdx.x; x < G * D; x += blockDim.x) {
     const int g = x / D, dim = x % D;
-    float M = -INFINITY;
-    for (int s0 = 0; s0 < ns; ++s0) M = fmaxf(M, ml[((size_t)s0 * G + g) * 2]);
-    float ov = 0.f, lv = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll 8
-      for (int s0 = 0; s0 < ns; ++s0) {
-        const float ms = ml[((size_t)s0 * G + g) * 2];
-        const float f = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-        ov = fmaf(f, ob[((size_t)s0 * G + g) * D + dim], ov);
-        lv = fmaf(f, ml[((size_t)s0 * G + g) * 2 + 1], lv);
+    float M = -INFINITY, ov = 0.f, lv = 0.f;
+    for (int c0 = 0; c0 < ns; c0 += CH) {
+      float ms[CH], ls[CH], os[CH];
+#pragma unroll
+      for (int t = 0; t < CH; ++t) {  // clamped, unconditional: no waits between the loads
+        const int s0 = min(c0 + t, ns - 1);
+        const float2 mlv = *reinterpret_cast<const float2*>(ml + ((size_t)s0 * G + g) * 2);
+        ms[t] = mlv.x;
+        ls[t] = mlv.y;
+        os[t] = ob[((size_t)s0 * G + g) * D + dim];
       }
+      float Mc = M;
+#pragma unroll
+      for (int t = 0; t < CH; ++t)
+        if (c0 + t < ns) Mc = fmaxf(Mc, ms[t]);
+      if (Mc == -INFINITY) continue;
+      const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mc);  // earlier chunks to the new max
+      ov *= r;
+      lv *= r;
+#pragma unroll
+      for (int t = 0; t < CH; ++t) {
+        if (c0 + t >= ns) continue;
+        const float f = ms[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms[t] - Mc);
+        ov = fmaf(f, os[t], ov);
+        lv = fmaf(f, ls[t], lv);
+      }
+      M = Mc;
     }
     const int h = kvh * G + g;
     Elem<T>::store(reinterpret_cast<T*>(a.merge.out) + ((size_t)seq * a.merge.hq + h) * D + dim,
