@@ -134,20 +134,18 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int idx = blockIdx.x;
   const int kvh = blockIdx.y;
-  if (a.commit_seq_lens && kvh == 0 && tid == 0) {
-    // decode step: the append of sequence idx was valid -> advance its length
-    const int len = a.commit_seq_lens[idx];
-    const int page = len / B;
-    int ph = -1;
-    if (len >= 0 && page < a.max_pages) ph = a.block_table[(size_t)idx * a.max_pages + page];
-    if (ph >= 0 && ph < a.num_phys) a.commit_seq_lens[idx] = len + 1;
-  }
+  // loaded before the merge's loads and stores, which the compiler may not
+  // move them across
+  const int phys = a.phys_ids[idx];
+  const bool commit = a.commit_seq_lens && kvh == 0 && tid == 0;
+  const int len = commit ? a.commit_seq_lens[idx] : 0;
   if (a.merge.part_o) merge_partials<T>(a, idx, kvh);
+  // decode step: the append of sequence idx was valid -> advance its length
+  if (commit && phys != -2) a.commit_seq_lens[idx] = len + 1;
   // The decode step launches kMergeThreads threads for the merge; the build
   // below runs on the first kBuildThreads (a barrier waits only for waves
   // that have not ended).
   if (tid >= kBuildThreads) return;
-  const int phys = a.phys_ids[idx];
   if (phys < 0 || phys >= a.num_phys) return;
 
   // 1) load K (32 elements per thread), energy sum ||k_i||^2, transpose into LDS

@@ -10,8 +10,10 @@ enum DType : int { kF32 = 0, kBF16 = 1 };
 
 // The cache append of a decode step, carried out by the scorer's first
 // workgroup of every (sequence, KV head): the new key and value go to slot
-// T mod B of logical page T / B (T = seq_lens[seq] before the step), and the
-// physical page an append completes is recorded in build_list[seq] (else -1).
+// T mod B of logical page T / B (T = seq_lens[seq] before the step), and
+// build_list[seq] records the outcome: the physical page when the append
+// completes it, -1 for any other valid append, -2 when page T / B has no
+// physical page (nothing is written and the length is not advanced).
 struct AppendDuty {
   void* k_pool;
   void* v_pool;
@@ -74,7 +76,8 @@ struct BuildArgs {
   float* eigvals_out;          // optional [n][Hkv][B]
   int32_t n, num_phys, hkv;
   // decode step: workgroup (seq, 0) advances seq_lens[seq] by one when the
-  // step's append was valid (phys_ids is then the build list, n = batch)
+  // step's append was valid, i.e. build_list[seq] != -2 (phys_ids is then the
+  // build list, n = batch)
   int32_t* commit_seq_lens;
   const int32_t* block_table;
   int32_t max_pages;

@@ -69,7 +69,7 @@ __device__ __forceinline__ void append_duty(const ScoreArgs& a, int seq, int kvh
              (((size_t)phys * a.hkv + kvh) * B + slot) * D + ch * VEC;
     *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
   }
-  if (kvh == 0 && t == 0) a.app.build_list[seq] = (ok && slot == B - 1) ? phys : -1;
+  if (kvh == 0 && t == 0) a.app.build_list[seq] = !ok ? -2 : (slot == B - 1 ? phys : -1);
 }
 
 template <typename T, int R, int G>

@@ -344,6 +344,36 @@ def test_group_and_rank_variants_fp32(gpu, group, rank):
 # threads hold one, the block-wide fallback when ties overflow the list, and
 # the large-table tiers (scores loaded twice).
 
+def test_decode_step_table_full(gpu):
+    """A sequence whose next token has no page in its block table: nothing is
+    appended and its stored length stays; the other sequence advances and its
+    selection is well formed."""
+    w = synth.workload(0, batch=2)
+    w.context = [64 * 5 + 3, 64 * 4]
+    say("decode step with a full block table: lengths", w.context, "capacities [6, 4]")
+    dc = DeviceCache(w, poison=True, capacity_pages=[6, 4])
+    dc.fill_from_synth()
+    dc.build_all()
+    k_before = dc.k_pool.clone()
+    rng = np.random.default_rng(5)
+    q = dc.queries(0, [t + 1 for t in w.context])
+    kn = to_storage(rng.standard_normal((2, w.num_kv_heads, w.head_dim)).astype(np.float32), w.dtype).cuda()
+    vn = to_storage(rng.standard_normal((2, w.num_kv_heads, w.head_dim)).astype(np.float32), w.dtype).cuda()
+    o = dc.outputs()
+    dc.decode_step(q, kn, vn, o)
+    torch.cuda.synchronize()
+    assert dc.seq_lens.cpu().tolist() == [64 * 5 + 4, 64 * 4]
+    # sequence 0's token landed in slot 3 of its page 5; nothing else changed
+    ph = int(dc.block_table_host[0, 5])
+    changed = (dc.k_pool != k_before) & ~(torch.isnan(dc.k_pool) & torch.isnan(k_before))
+    idx = changed.nonzero().cpu().numpy()
+    assert len(idx) and (idx[:, 0] == ph).all() and (idx[:, 2] == 3).all()
+    c0 = int(o["cnt"][0, 0])
+    sel0 = o["sel"][0, 0, :c0].cpu().numpy()
+    assert sel0[0] == 0 and sel0[-1] == 5 and (np.diff(sel0) > 0).all()
+    assert torch.isfinite(o["out"][0].float()).all()
+
+
 def _selector_case(T, budget, capacity=None, group=4, layout=None, hold_last=False):
     """fp32 single-sequence cache holding T tokens whose keys may be rearranged
     by ``layout(keys)`` (page copies make exact ties); returns the workload,
