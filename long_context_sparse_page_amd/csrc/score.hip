@@ -287,7 +287,8 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_mfma_kernel(ScoreAr
   static_assert(G <= 8, "at most 8 query heads per KV head");
 
   __shared__ float sP[kScoreWaves][SLOTS * G];
-  __shared__ float sZ[kScoreWaves][G * B];
+  constexpr int RC = (16 / G) < NR ? (16 / G) : NR;  // records per LDS transpose (RC * G <= 16)
+  __shared__ float sZ[kScoreWaves][RC * G * B];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar table loads
@@ -359,43 +360,68 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_mfma_kernel(ScoreAr
       }
     }
     wave_lds_fence();
-    // reconstruction and per-head LSE, record by record (lane = token)
+    // Reconstruction and per-head LSE, RC records at a time: every record's
+    // logits (lane = token) in one pass, one transpose through LDS, then the
+    // records' LSEs side by side (independent chains), one store per head.
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const int j = g0 + r;
-      if (j >= j_end) break;
-      if (!cur.valid[r]) {
-        if (lane < G) out[(size_t)lane * a.max_pages + j] = -INFINITY;
-        continue;
+    for (int c0 = 0; c0 < NR; c0 += RC) {
+      float z[RC][G];
+#pragma unroll
+      for (int rr = 0; rr < RC; ++rr) {
+        const int r = c0 + rr;
+        float c[R];
+#pragma unroll
+        for (int m = 0; m < R; ++m) c[m] = (m & 1) ? bf16_hi(cur.cw[r][m >> 1]) : bf16_lo(cur.cw[r][m >> 1]);
+        const float* Pr = P + r * ROWS * G;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float acc = Pr[g];
+#pragma unroll
+          for (int m = 0; m < R; ++m) acc = fmaf(c[m], Pr[(m + 1) * G + g], acc);
+          z[rr][g] = acc * zscale;
+        }
       }
-      float c[R];
 #pragma unroll
-      for (int m = 0; m < R; ++m) c[m] = (m & 1) ? bf16_hi(cur.cw[r][m >> 1]) : bf16_lo(cur.cw[r][m >> 1]);
-      const float* Pr = P + r * ROWS * G;
+      for (int rr = 0; rr < RC; ++rr)
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float z = Pr[g];
-#pragma unroll
-        for (int m = 0; m < R; ++m) z = fmaf(c[m], Pr[(m + 1) * G + g], z);
-        Z[g * B + lane] = z * zscale;
-      }
+        for (int g = 0; g < G; ++g) Z[(rr * G + g) * B + lane] = z[rr][g];
       wave_lds_fence();
       const int hg = lane / LPH;
       const int t0 = (lane % LPH) * TPL;
-      float v[TPL];
-      float mx = -INFINITY;
+      float res[RC];
 #pragma unroll
-      for (int t = 0; t < TPL; ++t) {
-        v[t] = Z[hg * B + t0 + t];
-        mx = fmaxf(mx, v[t]);
+      for (int rr = 0; rr < RC; ++rr) {
+        float v[TPL];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < TPL; ++t) {
+          v[t] = Z[(rr * G + hg) * B + t0 + t];
+          mx = fmaxf(mx, v[t]);
+        }
+        mx = group_max<LPH>(mx);
+        float sum = 0.f;
+#pragma unroll
+        for (int t = 0; t < TPL; ++t) sum += fast_exp2(v[t] - mx);
+        sum = group_sum<LPH>(sum);
+        res[rr] = cur.valid[c0 + rr] ? (mx + fast_log2(sum)) * kLn2 : -INFINITY;
       }
-      mx = group_max<LPH>(mx);
-      float sum = 0.f;
+      // lane hg * LPH + rr of head group hg writes record c0 + rr
+      const int rsel = lane % LPH;
+      if constexpr (RC <= LPH) {
+        float val = res[0];
 #pragma unroll
-      for (int t = 0; t < TPL; ++t) sum += fast_exp2(v[t] - mx);
-      sum = group_sum<LPH>(sum);
-      if (lane % LPH == 0) out[(size_t)hg * a.max_pages + j] = (mx + fast_log2(sum)) * kLn2;
-      wave_lds_fence();
+        for (int rr = 1; rr < RC; ++rr)
+          if (rsel == rr) val = res[rr];
+        const int j = g0 + c0 + rsel;
+        if (rsel < RC && j < j_end) out[(size_t)hg * a.max_pages + j] = val;
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < RC; ++rr) {
+          const int j = g0 + c0 + rr;
+          if (rr % LPH == rsel && j < j_end) out[(size_t)hg * a.max_pages + j] = res[rr];
+        }
+      }
+      if (c0 + RC < NR) wave_lds_fence();  // Z is rewritten by the next records
     }
   }
 }
