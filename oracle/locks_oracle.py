@@ -59,6 +59,13 @@ __all__ = [
     "HeadStep",
     "summary_bytes",
     "record_elements",
+    "fp16_round",
+    "quantize_symmetric",
+    "QuantSummary",
+    "quantize_summary",
+    "dequantize_summary",
+    "QUANT_BASIS_LEVELS",
+    "QUANT_ROW_LEVELS",
 ]
 
 # Eigenvalue thresholds of the zero-mode rule ([Locks] §4 "Build" states the
@@ -164,6 +171,74 @@ def build_page_summaries(keys, rank: int, dtype: str = "f64",
         coeffs=storage_round(coeffs, dtype),
         eigvals=np.clip(lam, 0.0, None),
         r_eff=nonzero.sum(axis=1),
+    )
+
+
+# ----------------------------------------------------------------------------
+# quantized summary: [Locks] §4 "Build" (int4 basis with per-column scales,
+# int8 coefficients and centroid with per-row scales), App. D "State
+# accounting"; [Review] Alg. 1 (the quantization follows the build)
+#
+# The pages name the precisions and where the scales sit, not the scheme.
+# Reading taken: symmetric absmax quantization; int4 codes in [-7, 7], int8
+# codes in [-127, 127]; each scale is rounded to fp16 (the scale overhead that
+# brings the 9.4% payload to "about a tenth" at B = 16) and the codes are
+# computed against that stored scale, rounding half to even; an all-zero row
+# has scale 0 and codes 0.  Scores use the dequantized values code * scale.
+# ----------------------------------------------------------------------------
+QUANT_BASIS_LEVELS = 7
+QUANT_ROW_LEVELS = 127
+
+
+def fp16_round(x) -> np.ndarray:
+    """Round fp64 values to the nearest IEEE half (ties to even), back in fp64."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+def quantize_symmetric(x, levels: int):
+    """Symmetric quantization of the last axis of ``x``: one scale per row,
+    s = fp16(max |x| / levels), codes = clip(rint(x / s), -levels, levels).
+    Returns (codes as int, scales as fp64)."""
+    x = np.asarray(x, dtype=np.float64)
+    s = fp16_round(np.max(np.abs(x), axis=-1) / levels)
+    safe = np.where(s > 0, s, 1.0)[..., None]
+    codes = np.clip(np.rint(x / safe), -levels, levels)
+    codes = np.where(s[..., None] > 0, codes, 0.0)
+    return codes.astype(np.int64), s
+
+
+@dataclass
+class QuantSummary:
+    """Quantized page summaries for n pages: integer codes and their scales."""
+
+    centroid_q: np.ndarray  # [n, d]     int8 codes of mu_j
+    centroid_s: np.ndarray  # [n]        one scale per centroid
+    basis_q: np.ndarray     # [n, r, d]  int4 codes; row k is v_{j,k}
+    basis_s: np.ndarray     # [n, r]     one scale per basis vector (column of V_j)
+    coeffs_q: np.ndarray    # [n, B, r]  int8 codes; row i is c_i
+    coeffs_s: np.ndarray    # [n, B]     one scale per token (row of C_j)
+    eigvals: np.ndarray     # [n, B]     carried over from the unquantized build
+    r_eff: np.ndarray       # [n]
+
+
+def quantize_summary(summary: PageSummary) -> QuantSummary:
+    """int4 basis (per-column scales), int8 coefficients and centroid (per-row
+    scales) of an unrounded (fp64) summary."""
+    bq, bs = quantize_symmetric(summary.basis, QUANT_BASIS_LEVELS)
+    cq, cs = quantize_symmetric(summary.coeffs, QUANT_ROW_LEVELS)
+    mq, ms = quantize_symmetric(summary.centroid, QUANT_ROW_LEVELS)
+    return QuantSummary(centroid_q=mq, centroid_s=ms, basis_q=bq, basis_s=bs, coeffs_q=cq, coeffs_s=cs,
+                        eigvals=summary.eigvals, r_eff=summary.r_eff)
+
+
+def dequantize_summary(qs: QuantSummary) -> PageSummary:
+    """The summary the scorer sees: every code times its scale."""
+    return PageSummary(
+        centroid=qs.centroid_q * qs.centroid_s[..., None],
+        basis=qs.basis_q * qs.basis_s[..., None],
+        coeffs=qs.coeffs_q * qs.coeffs_s[..., None],
+        eigvals=qs.eigvals,
+        r_eff=qs.r_eff,
     )
 
 

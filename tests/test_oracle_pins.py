@@ -328,3 +328,89 @@ def test_table_d10_byte_accounting(golden_dir):
         b = lo.summary_bytes(g["head_dim"], g["page_size"], row["rank"], row["basis_bits"], 8, 8)
         assert b == row["bytes"], row
         assert abs(100 * b / g["kv_bytes"] - row["pct"]) < 0.06
+
+
+# ----------------------------------------------------------------------------
+# quantized summary ([Locks] §4 "Build": int4 basis with per-column scales,
+# int8 coefficients and centroid with per-row scales; App. D)
+# ----------------------------------------------------------------------------
+def test_quantize_symmetric_properties():
+    """Every entry comes back within half a step (the row maximum may lose the
+    sliver by which the fp16 scale was rounded down), the row maximum sits on
+    +-levels, codes are integers in range, the scale is an fp16 value within
+    half an fp16 ulp of max|x| / levels, and a power-of-two rescale of a row
+    only rescales its scale."""
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((200, 128)) * rng.uniform(0.01, 10.0, (200, 1))
+    for levels in (lo.QUANT_BASIS_LEVELS, lo.QUANT_ROW_LEVELS):
+        q, s = lo.quantize_symmetric(x, levels)
+        assert q.dtype.kind == "i" and np.abs(q).max() <= levels
+        amax = np.abs(x).max(axis=1)
+        slack = np.maximum(amax - levels * s, 0.0)
+        assert (np.abs(x - q * s[:, None]) <= (s / 2 + slack)[:, None] + 1e-12).all()
+        big = np.argmax(np.abs(x), axis=1)
+        assert (np.abs(q[np.arange(len(x)), big]) == levels).all()
+        assert (s.astype(np.float16).astype(np.float64) == s).all()
+        assert (np.abs(s - amax / levels) <= (amax / levels) * 2.0 ** -11).all()
+        q8, s8 = lo.quantize_symmetric(x * 8.0, levels)
+        assert (q8 == q).all() and (s8 == 8.0 * s).all()
+    zq, zs = lo.quantize_symmetric(np.zeros((2, 16)), 7)
+    assert (zq == 0).all() and (zs == 0).all()
+
+
+def test_quantized_summary_lossless_case_and_score():
+    """Rows that are exact multiples k * s of an fp16 scale with max |k| = levels
+    are reproduced exactly (codes, scales and dequantized values), so Eq. (1) on
+    the dequantized summary equals Eq. (1) on the original."""
+    rng = np.random.default_rng(22)
+    n, B, d, r = 5, 64, 128, 8
+
+    def exact(shape, levels):
+        k = rng.integers(-levels, levels + 1, size=shape)
+        k[..., 3] = -levels
+        s = lo.fp16_round(rng.uniform(1e-3, 2.0, size=shape[:-1]))
+        return k * s[..., None], k, s
+
+    basis, bk, bsc = exact((n, r, d), lo.QUANT_BASIS_LEVELS)
+    coeffs, ck, csc = exact((n, B, r), lo.QUANT_ROW_LEVELS)
+    mu, mk, msc = exact((n, d), lo.QUANT_ROW_LEVELS)
+    summ = lo.PageSummary(centroid=mu, basis=basis, coeffs=coeffs, eigvals=np.zeros((n, B)),
+                          r_eff=np.full(n, r))
+    qs = lo.quantize_summary(summ)
+    assert (qs.basis_q == bk).all() and (qs.coeffs_q == ck).all() and (qs.centroid_q == mk).all()
+    assert (qs.basis_s == bsc).all() and (qs.coeffs_s == csc).all() and (qs.centroid_s == msc).all()
+    back = lo.dequantize_summary(qs)
+    assert (back.basis == basis).all() and (back.coeffs == coeffs).all() and (back.centroid == mu).all()
+    q = rng.standard_normal((4, d))
+    np.testing.assert_allclose(lo.reconstructed_page_lse(q, back, 0.0884),
+                               lo.reconstructed_page_lse(q, summ, 0.0884), rtol=0, atol=1e-12)
+
+
+def test_quantized_build_zero_modes_and_score_perturbation():
+    """On built pages: zero modes (a page of rank 3 at r = 8) quantize to zero
+    scales and codes; the quantized score moves by at most the largest change of
+    a reconstructed logit (log-sum-exp is 1-Lipschitz in the sup norm, [Locks]
+    Prop. 2 proof), and every dequantized entry is within half a step."""
+    rng = np.random.default_rng(23)
+    d, B, r = 128, 64, 8
+    low = rng.standard_normal((2, B, 3)) @ rng.standard_normal((2, 3, d)) + 0.3
+    pages = np.concatenate([low, rng.standard_normal((4, B, d))], axis=0)
+    summ = lo.build_page_summaries(pages, r, dtype="f64")
+    qs = lo.quantize_summary(summ)
+    assert (qs.basis_s[:2, 3:] == 0).all() and (qs.basis_q[:2, 3:] == 0).all()
+    assert (qs.coeffs_q[:2, :, 3:] == 0).all()
+    back = lo.dequantize_summary(qs)
+    for a, b, sc in ((summ.basis, back.basis, qs.basis_s), (summ.coeffs, back.coeffs, qs.coeffs_s),
+                     (summ.centroid, back.centroid, qs.centroid_s)):
+        assert (np.abs(a - b) <= sc[..., None] / 2 + 1e-12).all()
+    q = rng.standard_normal((4, d)) * 2.0
+    scale = 1 / np.sqrt(d)
+
+    def logits(sm):
+        a = q @ sm.centroid.T
+        proj = np.einsum("nrd,gd->gnr", sm.basis, q)
+        return scale * (a[:, :, None] + np.einsum("nbr,gnr->gnb", sm.coeffs, proj))
+
+    dz = np.abs(logits(back) - logits(summ)).max(axis=-1)
+    ds = np.abs(lo.reconstructed_page_lse(q, back, scale) - lo.reconstructed_page_lse(q, summ, scale))
+    assert (ds <= dz + 1e-12).all() and dz.max() > 0
