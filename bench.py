@@ -33,6 +33,8 @@ def parse():
     p.add_argument("--kernel-reps", type=int, default=200, help="timed launches of the scorer alone")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--summary", choices=("kv", "i4"), default="kv",
+                   help="page summaries in the KV dtype (bf16, the default) or int4 basis / int8 rows")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="also run a plain device copy of this size (counter calibration)")
     return p.parse_args()
@@ -54,7 +56,7 @@ def main():
     dev = "cuda"
     total_steps = args.warmup + args.steps
     per_layer = -(-total_steps // args.layers)
-    w = synth.workload(2, steps=per_layer + 1)
+    w = synth.workload(2, steps=per_layer + 1, summary=args.summary)
     B, d, G, hkv, hq = w.page_size, w.head_dim, w.group, w.num_kv_heads, w.num_q_heads
     e = 2  # bf16
     t0 = time.time()
@@ -181,7 +183,10 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "128K-context decode, batch 4, Llama-3.1-8B attention shape (32 q / 8 KV heads, d=128), "
-                        "bf16 KV, page 64, rank 8, budget 2048 tokens; one step = lk_decode_step on one layer",
+                        "bf16 KV, page 64, rank 8, budget 2048 tokens; one step = lk_decode_step on one layer"
+                        + ("; int4 basis / int8 coefficient and centroid summaries" if args.summary == "i4" else ""),
+            "summary_records": "bf16" if args.summary == "kv" else "int4 basis, int8 coefficients and centroid",
+            "record_bytes": rec,
             "global_batch": w.batch, "seq_len": w.context[0], "page_size": B, "rank": w.rank,
             "token_budget": w.token_budget, "num_q_heads": hq, "num_kv_heads": hkv, "layers_rotated": args.layers,
             "parallelism": "single GPU",
@@ -191,12 +196,12 @@ def main():
         "hbm_frac": bytes_step / (ms_per_step * 1e-3) / 8e12,
         "roofline": {
             "bound": "hbm",
-            "kernel": "score_mfma_kernel (reconstructed page LSE)",
+            "kernel": ("score_mfma_kernel" if args.summary == "kv" else "score_q4_kernel") + " (reconstructed page LSE)",
             "achieved": score_gbs,
             "peak": 8000.0,
             "unit": "GB/s",
             "frac": score_gbs / 8000.0,
-            "traffic": recorded_traffic(),
+            "traffic": recorded_traffic(TRAFFIC_PROFILE[args.summary]),
             "launch_us": score_ms * 1e3,
             "bytes_per_launch": score_bytes,
         },
@@ -219,10 +224,11 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-TRAFFIC_PROFILE = "profiles/score_mfma_128K_b4_hbm_traffic.txt"
+TRAFFIC_PROFILE = {"kv": "profiles/score_mfma_128K_b4_hbm_traffic.txt",
+                   "i4": "profiles/score_q4_128K_b4_hbm_traffic.txt"}
 
 
-def recorded_traffic():
+def recorded_traffic(profile):
     """HBM bytes per scorer launch from the committed rocprofv3 counter summary
     (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or None when the scorer's
     sources have changed since the counters were taken."""
@@ -230,7 +236,7 @@ def recorded_traffic():
 
     root = os.path.dirname(os.path.abspath(__file__))
     try:
-        fields = dict(line.strip().split("=", 1) for line in open(os.path.join(root, TRAFFIC_PROFILE))
+        fields = dict(line.strip().split("=", 1) for line in open(os.path.join(root, profile))
                       if "=" in line and not line.startswith(" "))
         h = hashlib.sha256()
         for f in fields["kernel_sources"].split():
@@ -260,7 +266,7 @@ def cpu_baseline(w, lens_now, seconds):
     with threadpool_limits(limits=1):
         K, V = ref.host_pages(w, 0, 0, T)
         n_mr = lo.most_recent_page(T, w.page_size)
-        summ = lo.build_page_summaries(K[:n_mr], w.rank, w.dtype)
+        summ = ref.oracle_summaries(w, K, n_mr)
         q64 = ref.host_queries(w, 0, [T] * w.batch)[0, :w.group]
         n, t0 = 0, time.perf_counter()
         while True:

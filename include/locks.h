@@ -38,7 +38,14 @@
  *   k_pool, v_pool   [num_phys_pages][num_kv_heads][B][d]
  *   summary_pool     [num_phys_pages][num_kv_heads][record] where one record is
  *                    centroid[d] | basis[r][d] (row m = m-th basis vector) |
- *                    coeffs[B][r] (row i = c_i); lk_summary_record_bytes()
+ *                    coeffs[B][r] (row i = c_i) in kv_dtype; with
+ *                    summary_format = LK_SUMMARY_I4 the record holds bytes:
+ *                    centroid int8[d] | basis int4[r][d/2] (byte c of row m
+ *                    holds dims 2c (low nibble) and 2c+1, two's complement) |
+ *                    coeffs int8[B][r] | coefficient scales fp16[B] | basis
+ *                    scales fp16[r] | centroid scale fp16, zero-padded to a
+ *                    multiple of 16 bytes.  A value is code * scale.
+ *                    lk_summary_record_bytes() gives the record size
  *   block_table      int32 [batch][max_pages_per_seq], logical -> physical page
  *   seq_lens         int32 [batch], tokens held by each sequence
  *   q, out           [batch][num_q_heads][d]; query head h reads KV head h / G,
@@ -75,6 +82,19 @@ typedef enum {
 
 typedef enum { LK_F32 = 0, LK_BF16 = 1 } lk_dtype;
 
+/* Storage of the page summaries ([Locks] §4 "Build", App. D "State
+ * accounting"):
+ *   LK_SUMMARY_KV  centroid, basis and coefficients in kv_dtype;
+ *   LK_SUMMARY_I4  the deployed compact form: int4 basis with one scale per
+ *                  basis vector (a column of V), int8 coefficients with one
+ *                  scale per token (a row of C) and int8 centroid with one
+ *                  scale.  Scales are fp16; the quantization is symmetric,
+ *                  s = fp16(max |x| / L) with L = 7 (int4) or 127 (int8),
+ *                  code = round-half-even(x / s) clamped to [-L, L], and an
+ *                  all-zero row has s = 0.  Needs kv_dtype LK_BF16 and rank
+ *                  4, 8 or 16 (the pages quote r = 8, "r8i4"). */
+typedef enum { LK_SUMMARY_KV = 0, LK_SUMMARY_I4 = 1 } lk_summary_format;
+
 /* Problem parameters ([Locks] §2, §4): head dimension d, page size B, rank r,
  * GQA grouping, per-head token budget b, storage dtype and logit scale. */
 typedef struct {
@@ -87,6 +107,7 @@ typedef struct {
   int32_t token_budget;  /* b; k = ceil(b / B) must be >= 2                  */
   int32_t kv_dtype;      /* lk_dtype of K, V, q, out, k_new, v_new, summary  */
   float scale;           /* logit scale, normally 1 / sqrt(d)                */
+  int32_t summary_format;  /* lk_summary_format                              */
 } lk_config;
 
 /* The paged cache of one attention layer. */
@@ -102,7 +123,9 @@ typedef struct {
 
 /* Bytes of one (page, KV head) summary record: (d + r*d + B*r) elements of
  * kv_dtype ([Locks] App. D "State accounting": basis d*r, coefficients B*r,
- * centroid d).  Returns 0 for an invalid config. */
+ * centroid d), or for LK_SUMMARY_I4 d + r*d/2 + B*r bytes of codes plus
+ * 2*(B + r + 1) bytes of scales, rounded up to 16 (1312 at d = 128, B = 64,
+ * r = 8).  Returns 0 for an invalid config. */
 size_t lk_summary_record_bytes(const lk_config* cfg);
 
 /* Page budget k = ceil(token_budget / page_size) ([Locks] §2); 0 if invalid. */

@@ -48,6 +48,7 @@ struct Shape {
   int d, B, r, hq, hkv, G, k;
   lk::DType dt;
   size_t elem;
+  bool q4;  // LK_SUMMARY_I4 records
 };
 
 lk_status check_config(const lk_config* cfg, Shape* sh) {
@@ -75,6 +76,12 @@ lk_status check_config(const lk_config* cfg, Shape* sh) {
   if (G != 1 && G != 2 && G != 4 && G != 8)
     return fail(LK_ERR_UNSUPPORTED, "GQA group %d: built groups are 1, 2, 4, 8", G);
   if (k > kMaxPageBudget) return fail(LK_ERR_UNSUPPORTED, "page budget %d exceeds %d", k, kMaxPageBudget);
+  if (cfg->summary_format != LK_SUMMARY_KV && cfg->summary_format != LK_SUMMARY_I4)
+    return fail(LK_ERR_INVALID_ARG, "summary_format %d is not LK_SUMMARY_KV or LK_SUMMARY_I4", cfg->summary_format);
+  if (cfg->summary_format == LK_SUMMARY_I4 && cfg->kv_dtype != LK_BF16)
+    return fail(LK_ERR_UNSUPPORTED, "LK_SUMMARY_I4 is built for kv_dtype LK_BF16 only");
+  if (cfg->summary_format == LK_SUMMARY_I4 && r != 4 && r != 8 && r != 16)
+    return fail(LK_ERR_UNSUPPORTED, "LK_SUMMARY_I4 rank %d: built ranks are 4, 8, 16", r);
   sh->d = cfg->head_dim;
   sh->B = cfg->page_size;
   sh->r = r;
@@ -84,6 +91,7 @@ lk_status check_config(const lk_config* cfg, Shape* sh) {
   sh->k = k;
   sh->dt = cfg->kv_dtype == LK_BF16 ? lk::kBF16 : lk::kF32;
   sh->elem = cfg->kv_dtype == LK_BF16 ? 2 : 4;
+  sh->q4 = cfg->summary_format == LK_SUMMARY_I4;
   return LK_OK;
 }
 
@@ -153,7 +161,7 @@ lk_status enqueue_score_select(const Shape& sh, const lk_config* cfg, const lk_c
                                hipStream_t s) {
   lk::ScoreArgs sa{q, c->summary_pool, c->block_table, c->seq_lens, page_lse,
                    batch, c->max_pages_per_seq, c->num_phys_pages, sh.hkv, sh.hq, cfg->scale, len_add, app};
-  hipError_t e = lk::launch_score(sh.dt, sh.r, sh.G, sa, s);
+  hipError_t e = lk::launch_score(sh.dt, sh.r, sh.G, sh.q4, sa, s);
   if (e != hipSuccess) return hip_status(e, "score launch");
   lk::SelectArgs se{page_lse, share_out, sel, cnt, c->seq_lens, batch, c->max_pages_per_seq,
                     sh.hkv, sh.G, sh.B, sh.k, len_add, c->block_table, sel_phys, c->num_phys_pages};
@@ -182,8 +190,13 @@ extern "C" {
 
 size_t lk_summary_record_bytes(const lk_config* cfg) {
   if (!cfg || cfg->head_dim <= 0 || cfg->page_size <= 0 || cfg->rank <= 0) return 0;
-  const size_t e = cfg->kv_dtype == LK_BF16 ? 2 : (cfg->kv_dtype == LK_F32 ? 4 : 0);
   const size_t d = cfg->head_dim, B = cfg->page_size, r = cfg->rank;
+  if (cfg->summary_format == LK_SUMMARY_I4) {
+    if (d % 2) return 0;
+    return (d + r * d / 2 + B * r + 2 * (B + r + 1) + 15) / 16 * 16;
+  }
+  if (cfg->summary_format != LK_SUMMARY_KV) return 0;
+  const size_t e = cfg->kv_dtype == LK_BF16 ? 2 : (cfg->kv_dtype == LK_F32 ? 4 : 0);
   return (d + r * d + B * r) * e;
 }
 
@@ -220,7 +233,7 @@ lk_status lk_build_page_summary(const lk_config* cfg, const lk_cache* cache, con
   if (n_pages > 0 && !phys_page_ids) return fail(LK_ERR_INVALID_ARG, "phys_page_ids is null");
   if (n_pages == 0) return ok();
   lk::BuildArgs ba{cache->k_pool, cache->summary_pool, phys_page_ids, eigvals_out, n_pages,
-                   cache->num_phys_pages, sh.hkv, nullptr, nullptr, 0, {}};
+                   cache->num_phys_pages, sh.hkv, nullptr, nullptr, 0, {}, sh.q4 ? 1 : 0};
   return hip_status(lk::launch_build(sh.dt, sh.r, ba, static_cast<hipStream_t>(stream)), "build launch");
 }
 
@@ -248,7 +261,7 @@ lk_status lk_score_select(const lk_config* cfg, const lk_cache* cache, int32_t b
     lk::ScoreArgs sa{q, cache->summary_pool, cache->block_table, cache->seq_lens, page_lse_out, batch,
                      cache->max_pages_per_seq, cache->num_phys_pages, sh.hkv, sh.hq, cfg->scale, 0,
                      lk::AppendDuty{}};
-    return hip_status(lk::launch_score(sh.dt, sh.r, sh.G, sa, s), "score launch");
+    return hip_status(lk::launch_score(sh.dt, sh.r, sh.G, sh.q4, sa, s), "score launch");
   }
   float* lse = page_lse_out ? page_lse_out : at<float>(ws, L.page_lse);
   return enqueue_score_select(sh, cfg, cache, batch, q, lse, share_out, sel_pages, sel_count, nullptr, 0,
@@ -309,7 +322,7 @@ lk_status lk_decode_step(const lk_config* cfg, const lk_cache* cache, int32_t ba
   lk::AppendDuty app{cache->k_pool, cache->v_pool, k_new, v_new, build_list};
   lk::ScoreArgs sa{q, cache->summary_pool, cache->block_table, cache->seq_lens, page_lse, batch,
                    cache->max_pages_per_seq, cache->num_phys_pages, sh.hkv, sh.hq, cfg->scale, 1, app};
-  st = hip_status(lk::launch_score(sh.dt, sh.r, sh.G, sa, s), "score launch");
+  st = hip_status(lk::launch_score(sh.dt, sh.r, sh.G, sh.q4, sa, s), "score launch");
   if (st != LK_OK) return st;
   // 2-3) selection and the attention splits: one fused launch when the table
   //      fits one workgroup's selection, else a selection then an attention launch
@@ -344,7 +357,8 @@ lk_status lk_decode_step(const lk_config* cfg, const lk_cache* cache, int32_t ba
   lk::BuildArgs ba{cache->k_pool, cache->summary_pool, build_list, nullptr, batch,
                    cache->num_phys_pages, sh.hkv, cache->seq_lens, cache->block_table,
                    cache->max_pages_per_seq,
-                   {at<float>(ws, L.part_o), at<float>(ws, L.part_ml), out, lse_out, n_merge, sh.G, sh.hq}};
+                   {at<float>(ws, L.part_o), at<float>(ws, L.part_ml), out, lse_out, n_merge, sh.G, sh.hq},
+                   sh.q4 ? 1 : 0};
   return hip_status(lk::launch_build(sh.dt, sh.r, ba, s), "build launch");
 }
 

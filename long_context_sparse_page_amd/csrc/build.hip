@@ -105,6 +105,69 @@ __device__ __forceinline__ int sturm_count(const float* sd, const float* se2, fl
   return c;
 }
 
+// Quantized record (Q4Layout): symmetric absmax quantization per row, the
+// scale rounded to fp16 and the codes taken against that stored scale,
+// rounding half to even: s = fp16(max |x| / L), code = clamp(rint(x / s), -L, L)
+// with L = 7 for the basis (one scale per basis vector) and L = 127 for the
+// centroid and for each token's coefficients; an all-zero row has s = 0.
+__device__ __forceinline__ float q4_scale(float amax, float levels) {
+  return (float)(_Float16)(amax / levels);
+}
+__device__ __forceinline__ int q4_code(float x, float s, float levels) {
+  if (!(s > 0.f)) return 0;
+  return (int)fminf(fmaxf(rintf(x / s), -levels), levels);
+}
+
+// The final record values: centroid sMu[c]; basis row k < KEPT is
+// sV[k][c] * sSign[k]; coefficient (i, k) is sZ[i][k] * sigma_k * sign_k on
+// nonzero modes.  Runs on the builder's kBuildThreads threads.
+template <int R, int KEPT>
+__device__ __forceinline__ void write_q4_record(const BuildArgs& a, int phys, int kvh, const float* sMu,
+                                                const float* sV, const float* sSign, const float* sZ,
+                                                const float* sSigma, const int* sNz) {
+  constexpr int D = kHeadDim;
+  constexpr int B = 64;
+  constexpr Q4Layout L{R};
+  __shared__ float sBs[R], sCs[B], sMs;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  auto basis_at = [&](int k, int c) { return k < KEPT ? sV[k * D + c] * sSign[k] : 0.f; };
+  auto coef_at = [&](int i, int k) { return (k < KEPT && sNz[k]) ? sZ[i * KEPT + k] * sSigma[k] * sSign[k] : 0.f; };
+  // scales: basis rows by waves (two dims per lane), the centroid by wave 0,
+  // each token's coefficients by one thread
+  for (int k = wave; k < R; k += kBuildWaves) {
+    const float m = group_max<kWave>(fmaxf(fabsf(basis_at(k, lane)), fabsf(basis_at(k, lane + kWave))));
+    if (lane == 0) sBs[k] = q4_scale(m, 7.f);
+  }
+  if (wave == 0) {
+    const float m = group_max<kWave>(fmaxf(fabsf(sMu[lane]), fabsf(sMu[lane + kWave])));
+    if (lane == 0) sMs = q4_scale(m, 127.f);
+  }
+  if (tid < B) {
+    float m = 0.f;
+#pragma unroll
+    for (int k = 0; k < R; ++k) m = fmaxf(m, fabsf(coef_at(tid, k)));
+    sCs[tid] = q4_scale(m, 127.f);
+  }
+  __syncthreads();
+  uint8_t* rec = reinterpret_cast<uint8_t*>(a.summary) + ((size_t)phys * a.hkv + kvh) * L.bytes();
+  for (int x = tid; x < D; x += kBuildThreads) rec[x] = (uint8_t)(int8_t)q4_code(sMu[x], sMs, 127.f);
+  for (int x = tid; x < R * D / 2; x += kBuildThreads) {
+    const int k = x / (D / 2), c = 2 * (x % (D / 2));
+    const int lo = q4_code(basis_at(k, c), sBs[k], 7.f), hi = q4_code(basis_at(k, c + 1), sBs[k], 7.f);
+    rec[L.basis() + x] = (uint8_t)((lo & 0xF) | ((hi & 0xF) << 4));
+  }
+  for (int x = tid; x < B * R; x += kBuildThreads)
+    rec[L.coef() + x] = (uint8_t)(int8_t)q4_code(coef_at(x / R, x % R), sCs[x / R], 127.f);
+  uint16_t* cs = reinterpret_cast<uint16_t*>(rec + L.cscale());
+  uint16_t* bs = reinterpret_cast<uint16_t*>(rec + L.bscale());
+  if (tid < B) cs[tid] = __builtin_bit_cast(uint16_t, (_Float16)sCs[tid]);
+  if (tid < R) bs[tid] = __builtin_bit_cast(uint16_t, (_Float16)sBs[tid]);
+  if (tid == 0) *reinterpret_cast<uint16_t*>(rec + L.mscale()) = __builtin_bit_cast(uint16_t, (_Float16)sMs);
+  for (int x = L.mscale() + 2 + tid; x < L.bytes(); x += kBuildThreads) rec[x] = 0;
+}
+
 template <typename T, int R>
 __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
   constexpr int B = 64;
@@ -505,6 +568,10 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
   __syncthreads();
 
   // 9) write the record: centroid | basis rows | coefficients
+  if (a.q4) {
+    write_q4_record<R, KEPT>(a, phys, kvh, sMu, sV, sSign, &sZ[0][0], sSigma, sNz);
+    return;
+  }
   constexpr int REC = D + R * D + B * R;
   T* rec = reinterpret_cast<T*>(a.summary) + ((size_t)phys * a.hkv + kvh) * REC;
   for (int x = tid; x < REC; x += kBuildThreads) {

@@ -8,6 +8,22 @@ namespace lk {
 
 enum DType : int { kF32 = 0, kBF16 = 1 };
 
+// Byte layout of a quantized (int4 basis / int8 coefficients and centroid)
+// summary record at d = 128, B = 64 and rank r: centroid int8[d] | basis
+// int4[r][d/2] (byte c of row m: dims 2c in the low nibble, 2c+1 in the high
+// one) | coefficients int8[B][r] | coefficient scales fp16[B] | basis scales
+// fp16[r] | centroid scale fp16, padded to 16 bytes.
+struct Q4Layout {
+  static constexpr int kD = 128, kB = 64;
+  int r;
+  __host__ __device__ constexpr int basis() const { return kD; }
+  __host__ __device__ constexpr int coef() const { return kD + r * kD / 2; }
+  __host__ __device__ constexpr int cscale() const { return coef() + kB * r; }
+  __host__ __device__ constexpr int bscale() const { return cscale() + 2 * kB; }
+  __host__ __device__ constexpr int mscale() const { return bscale() + 2 * r; }
+  __host__ __device__ constexpr int bytes() const { return (mscale() + 2 + 15) / 16 * 16; }
+};
+
 // The cache append of a decode step, carried out by the scorer's first
 // workgroup of every (sequence, KV head): the new key and value go to slot
 // T mod B of logical page T / B (T = seq_lens[seq] before the step), and
@@ -90,9 +106,11 @@ struct BuildArgs {
     float* lse_out;
     int32_t n_splits, group, hq;
   } merge;
+  int32_t q4;                  // records in the quantized layout (Q4Layout)
 };
 
-hipError_t launch_score(DType dt, int rank, int group, const ScoreArgs& a, hipStream_t s);
+// q4: the summary records use Q4Layout (bf16 queries only)
+hipError_t launch_score(DType dt, int rank, int group, bool q4, const ScoreArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 // merge = false leaves the split partials for the decode step's build launch
 hipError_t launch_attn(DType dt, int group, const AttnArgs& a, bool merge, hipStream_t s);

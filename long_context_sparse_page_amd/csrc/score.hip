@@ -273,6 +273,90 @@ __device__ __forceinline__ void load_group(GroupLoads<R>& L, const bf16_t* summ,
   }
 }
 
+// Reconstruction and per-head LSE of a group of NR records whose projections
+// P[slot * G + g] (slot = record * (R + 1) + row; row 0 = centroid) are in
+// LDS, RC records at a time: every record's logits (lane = token) in one
+// pass, z_i = P[0] + s_i * sum_m c_i[m] P[m + 1] (s_i = 1 unless SCALED), one
+// transpose through LDS, then the records' LSEs side by side (independent
+// chains), and one store per head group.  coef(r, c, s) gives this lane's
+// token coefficients of record r and their scale.
+template <int R, int G, int NR, bool SCALED, typename Coef>
+__device__ __forceinline__ void group_lse(const float* P, float* Z, Coef coef, const bool (&valid)[NR], float* out,
+                                          int max_pages, int g0, int j_end, int lane, float zscale) {
+  constexpr int B = 64;
+  constexpr int ROWS = R + 1;
+  constexpr int LPH = kWave / G;
+  constexpr int TPL = B / LPH;
+  constexpr int RC = (16 / G) < NR ? (16 / G) : NR;  // records per LDS transpose (RC * G <= 16)
+#pragma unroll
+  for (int c0 = 0; c0 < NR; c0 += RC) {
+    float z[RC][G];
+#pragma unroll
+    for (int rr = 0; rr < RC; ++rr) {
+      const int r = c0 + rr;
+      float c[R], cs;
+      coef(r, c, cs);
+      const float* Pr = P + r * ROWS * G;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float acc;
+        if constexpr (SCALED) {
+          acc = 0.f;
+#pragma unroll
+          for (int m = 0; m < R; ++m) acc = fmaf(c[m], Pr[(m + 1) * G + g], acc);
+          acc = fmaf(cs, acc, Pr[g]);
+        } else {
+          acc = Pr[g];
+#pragma unroll
+          for (int m = 0; m < R; ++m) acc = fmaf(c[m], Pr[(m + 1) * G + g], acc);
+        }
+        z[rr][g] = acc * zscale;
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < RC; ++rr)
+#pragma unroll
+      for (int g = 0; g < G; ++g) Z[(rr * G + g) * B + lane] = z[rr][g];
+    wave_lds_fence();
+    const int hg = lane / LPH;
+    const int t0 = (lane % LPH) * TPL;
+    float res[RC];
+#pragma unroll
+    for (int rr = 0; rr < RC; ++rr) {
+      float v[TPL];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < TPL; ++t) {
+        v[t] = Z[(rr * G + hg) * B + t0 + t];
+        mx = fmaxf(mx, v[t]);
+      }
+      mx = group_max<LPH>(mx);
+      float sum = 0.f;
+#pragma unroll
+      for (int t = 0; t < TPL; ++t) sum += fast_exp2(v[t] - mx);
+      sum = group_sum<LPH>(sum);
+      res[rr] = valid[c0 + rr] ? (mx + fast_log2(sum)) * kLn2 : -INFINITY;
+    }
+    // lane hg * LPH + rr of head group hg writes record c0 + rr
+    const int rsel = lane % LPH;
+    if constexpr (RC <= LPH) {
+      float val = res[0];
+#pragma unroll
+      for (int rr = 1; rr < RC; ++rr)
+        if (rsel == rr) val = res[rr];
+      const int j = g0 + c0 + rsel;
+      if (rsel < RC && j < j_end) out[(size_t)hg * max_pages + j] = val;
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < RC; ++rr) {
+        const int j = g0 + c0 + rr;
+        if (rr % LPH == rsel && j < j_end) out[(size_t)hg * max_pages + j] = res[rr];
+      }
+    }
+    if (c0 + RC < NR) wave_lds_fence();  // Z is rewritten by the next records
+  }
+}
+
 template <int R, int G>
 __global__ __launch_bounds__(kScoreWaves * kWave) void score_mfma_kernel(ScoreArgs a) {
   constexpr int B = 64;
@@ -360,69 +444,14 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_mfma_kernel(ScoreAr
       }
     }
     wave_lds_fence();
-    // Reconstruction and per-head LSE, RC records at a time: every record's
-    // logits (lane = token) in one pass, one transpose through LDS, then the
-    // records' LSEs side by side (independent chains), one store per head.
+    group_lse<R, G, NR, false>(
+        P, Z,
+        [&](int r, float (&c)[R], float& cs) {
 #pragma unroll
-    for (int c0 = 0; c0 < NR; c0 += RC) {
-      float z[RC][G];
-#pragma unroll
-      for (int rr = 0; rr < RC; ++rr) {
-        const int r = c0 + rr;
-        float c[R];
-#pragma unroll
-        for (int m = 0; m < R; ++m) c[m] = (m & 1) ? bf16_hi(cur.cw[r][m >> 1]) : bf16_lo(cur.cw[r][m >> 1]);
-        const float* Pr = P + r * ROWS * G;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float acc = Pr[g];
-#pragma unroll
-          for (int m = 0; m < R; ++m) acc = fmaf(c[m], Pr[(m + 1) * G + g], acc);
-          z[rr][g] = acc * zscale;
-        }
-      }
-#pragma unroll
-      for (int rr = 0; rr < RC; ++rr)
-#pragma unroll
-        for (int g = 0; g < G; ++g) Z[(rr * G + g) * B + lane] = z[rr][g];
-      wave_lds_fence();
-      const int hg = lane / LPH;
-      const int t0 = (lane % LPH) * TPL;
-      float res[RC];
-#pragma unroll
-      for (int rr = 0; rr < RC; ++rr) {
-        float v[TPL];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < TPL; ++t) {
-          v[t] = Z[(rr * G + hg) * B + t0 + t];
-          mx = fmaxf(mx, v[t]);
-        }
-        mx = group_max<LPH>(mx);
-        float sum = 0.f;
-#pragma unroll
-        for (int t = 0; t < TPL; ++t) sum += fast_exp2(v[t] - mx);
-        sum = group_sum<LPH>(sum);
-        res[rr] = cur.valid[c0 + rr] ? (mx + fast_log2(sum)) * kLn2 : -INFINITY;
-      }
-      // lane hg * LPH + rr of head group hg writes record c0 + rr
-      const int rsel = lane % LPH;
-      if constexpr (RC <= LPH) {
-        float val = res[0];
-#pragma unroll
-        for (int rr = 1; rr < RC; ++rr)
-          if (rsel == rr) val = res[rr];
-        const int j = g0 + c0 + rsel;
-        if (rsel < RC && j < j_end) out[(size_t)hg * a.max_pages + j] = val;
-      } else {
-#pragma unroll
-        for (int rr = 0; rr < RC; ++rr) {
-          const int j = g0 + c0 + rr;
-          if (rr % LPH == rsel && j < j_end) out[(size_t)hg * a.max_pages + j] = res[rr];
-        }
-      }
-      if (c0 + RC < NR) wave_lds_fence();  // Z is rewritten by the next records
-    }
+          for (int m = 0; m < R; ++m) c[m] = (m & 1) ? bf16_hi(cur.cw[r][m >> 1]) : bf16_lo(cur.cw[r][m >> 1]);
+          cs = 1.f;
+        },
+        cur.valid, out, a.max_pages, g0, j_end, lane, zscale);
   }
 }
 
@@ -436,6 +465,232 @@ static hipError_t launch_score_mfma(int group, const ScoreArgs& a, hipStream_t s
     case 2: hipLaunchKernelGGL((score_mfma_kernel<R, 2>), grid, block, 0, s, a); break;
     case 4: hipLaunchKernelGGL((score_mfma_kernel<R, 4>), grid, block, 0, s, a); break;
     case 8: hipLaunchKernelGGL((score_mfma_kernel<R, 8>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Quantized records (Q4Layout) with bf16 queries: the projection on the matrix
+// cores with the integer codes as bf16 operands (small integers are exact in
+// bf16), scales applied to the fp32 products.
+//
+// K mapping: lane (col, kg) of K-step t covers dims 32 kg + 8 t .. +7, so a
+// lane reads 32 consecutive dims of its row over the four K-steps: one
+// 16-byte load of an int4 basis row, two of the int8 centroid (the queries use
+// the same mapping).  Codes are converted biased (int4 + 8, int8 + 128: plain
+// byte-to-float conversions) and the bias is removed from the products,
+// sum_c q_c code_c = sum_c q_c (code_c + bias) - bias * S_g with S_g = sum_c q_c.
+// Tiles: NR * R / 16 tiles of basis rows (column = record * R + row), then
+// one tile of the NR centroids.  The reconstruction and LSE are those of the
+// bf16 records, with the per-token coefficient scale.
+template <int R> struct Q4Group {
+  static constexpr int NR = R >= 16 ? 2 : (R >= 8 ? 4 : 8);  // records per wave
+  static constexpr int BT = NR * R / 16;                       // basis tiles
+  static constexpr int SLOTS = NR * (R + 1);
+};
+
+__device__ __forceinline__ uint32_t bf16x2_of(float lo, float hi) {  // both exact in bf16
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+__device__ __forceinline__ float ubyte_f(uint32_t x, int b) { return (float)((x >> (8 * b)) & 0xffu); }
+
+// K-step operand of 8 int4 codes (one 32-bit word, element j in nibble j) as
+// bf16 values of code + 8.
+__device__ __forceinline__ bf16x8_t q4_operand(uint32_t w) {
+  w ^= 0x88888888u;
+  const uint32_t even = w & 0x0f0f0f0fu, odd = (w >> 4) & 0x0f0f0f0fu;
+  uint4 o;
+  o.x = bf16x2_of(ubyte_f(even, 0), ubyte_f(odd, 0));
+  o.y = bf16x2_of(ubyte_f(even, 1), ubyte_f(odd, 1));
+  o.z = bf16x2_of(ubyte_f(even, 2), ubyte_f(odd, 2));
+  o.w = bf16x2_of(ubyte_f(even, 3), ubyte_f(odd, 3));
+  return __builtin_bit_cast(bf16x8_t, o);
+}
+// K-step operand of 8 int8 codes (two 32-bit words) as bf16 values of code + 128.
+__device__ __forceinline__ bf16x8_t q8_operand(uint32_t w0, uint32_t w1) {
+  w0 ^= 0x80808080u;
+  w1 ^= 0x80808080u;
+  uint4 o;
+  o.x = bf16x2_of(ubyte_f(w0, 0), ubyte_f(w0, 1));
+  o.y = bf16x2_of(ubyte_f(w0, 2), ubyte_f(w0, 3));
+  o.z = bf16x2_of(ubyte_f(w1, 0), ubyte_f(w1, 1));
+  o.w = bf16x2_of(ubyte_f(w1, 2), ubyte_f(w1, 3));
+  return __builtin_bit_cast(bf16x8_t, o);
+}
+__device__ __forceinline__ float half_bits_f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
+
+template <int R, int G>
+__global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs a) {
+  constexpr int B = 64;
+  constexpr int D = kHeadDim;
+  constexpr int ROWS = R + 1;
+  constexpr int NR = Q4Group<R>::NR;
+  constexpr int BT = Q4Group<R>::BT;
+  constexpr int SLOTS = Q4Group<R>::SLOTS;
+  constexpr Q4Layout L{R};
+  constexpr int REC = L.bytes();
+  static_assert(G <= 8 && NR <= 16 && BT * 16 == NR * R, "tile shapes");
+
+  __shared__ float sP[kScoreWaves][SLOTS * G];
+  constexpr int RC = (16 / G) < NR ? (16 / G) : NR;
+  __shared__ float sZ[kScoreWaves][RC * G * B];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int seq = blockIdx.z;
+  const int kvh = blockIdx.y;
+  append_duty<bf16_t>(a, seq, kvh);
+  const int j0 = (blockIdx.x * kScoreWaves + wave) * NR;
+  if (j0 >= a.max_pages) return;
+  const int col = lane & 15;
+  const int kg = lane >> 4;
+  const uint8_t* summ = reinterpret_cast<const uint8_t*>(a.summary);
+  const int32_t* bt = a.block_table + (size_t)seq * a.max_pages;
+
+  // Loads that do not depend on the sequence length go out first (as for
+  // bf16 records): block-table slice, queries, then every record byte.
+  int phys_all[NR];
+#pragma unroll
+  for (int x = 0; x < NR; ++x) phys_all[x] = bt[min(j0 + x, a.max_pages - 1)];
+  const int len_raw = a.seq_lens[seq] + a.len_add;
+  uint4 qw[4];  // query min(col, G - 1), dims 32 kg .. 32 kg + 31
+  {
+    const bf16_t* q = reinterpret_cast<const bf16_t*>(a.q) + ((size_t)seq * a.hq + (size_t)kvh * G) * D;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      qw[t] = *reinterpret_cast<const uint4*>(q + (size_t)min(col, G - 1) * D + 32 * kg + 8 * t);
+  }
+  bool valid[NR];
+  const uint8_t* recp[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    valid[r] = phys_all[r] >= 0 && phys_all[r] < a.num_phys;
+    recp[r] = summ + ((size_t)(valid[r] ? phys_all[r] : 0) * a.hkv + kvh) * REC;
+  }
+  uint4 wb[BT];     // basis row (record, row) = column of tile tau: 32 codes
+  uint32_t bsc[BT]; // its scale (fp16 bits)
+#pragma unroll
+  for (int tau = 0; tau < BT; ++tau) {
+    const int slot = 16 * tau + col;
+    const int r = slot / R, m = slot % R;
+    const uint8_t* rp = recp[0];
+#pragma unroll
+    for (int x = 1; x < NR; ++x) if (x == r) rp = recp[x];
+    wb[tau] = *reinterpret_cast<const uint4*>(rp + L.basis() + m * (D / 2) + 16 * kg);
+    bsc[tau] = *reinterpret_cast<const uint16_t*>(rp + L.bscale() + 2 * m);
+  }
+  uint4 wm[2];      // centroid of record min(col, NR - 1): 32 codes
+  uint32_t msc;
+  {
+    const int r = min(col, NR - 1);
+    const uint8_t* rp = recp[0];
+#pragma unroll
+    for (int x = 1; x < NR; ++x) if (x == r) rp = recp[x];
+    wm[0] = *reinterpret_cast<const uint4*>(rp + 32 * kg);
+    wm[1] = *reinterpret_cast<const uint4*>(rp + 32 * kg + 16);
+    msc = *reinterpret_cast<const uint16_t*>(rp + L.mscale());
+  }
+  uint32_t cw[NR][(R + 3) / 4];  // this lane's token: R int8 codes
+  uint32_t csc[NR];              // and their scale (fp16 bits)
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const uint8_t* cp = recp[r] + L.coef() + (size_t)lane * R;
+    if constexpr (R == 16) {
+      const uint4 v = *reinterpret_cast<const uint4*>(cp);
+      cw[r][0] = v.x; cw[r][1] = v.y; cw[r][2] = v.z; cw[r][3] = v.w;
+    } else if constexpr (R == 8) {
+      const uint2 v = *reinterpret_cast<const uint2*>(cp);
+      cw[r][0] = v.x; cw[r][1] = v.y;
+    } else {
+      cw[r][0] = *reinterpret_cast<const uint32_t*>(cp);
+    }
+    csc[r] = *reinterpret_cast<const uint16_t*>(recp[r] + L.cscale() + 2 * lane);
+  }
+  asm volatile("" ::: "memory");  // keep the loads above in one batch (as for bf16 records)
+
+  if (len_raw <= 0) return;
+  int n_scored = (len_raw - 1) / B;
+  if (n_scored > a.max_pages - 1) n_scored = a.max_pages - 1;
+  if (j0 >= n_scored) return;
+  const int j_end = min(j0 + NR, n_scored);
+
+  // S_g = sum of query g over all dims (lanes col, col + 16, col + 32, col + 48)
+  float qs = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t w[4] = {qw[t].x, qw[t].y, qw[t].z, qw[t].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qs += bf16_lo(w[i]) + bf16_hi(w[i]);
+  }
+  qs = xor32_sum(xor16_sum(qs));
+  float Sg[4];  // S of the 4 queries whose products this lane holds (rows 4 kg + i)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float s0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qs), min(i, G - 1)));
+    const float s1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qs), min(4 + i, G - 1)));
+    Sg[i] = kg ? s1 : s0;
+  }
+
+  const float zscale = a.scale * kLog2e;
+  float* out = a.page_lse + ((size_t)seq * a.hq + (size_t)kvh * G) * a.max_pages;
+  float* P = sP[wave];
+  float* Z = sZ[wave];
+  bf16x8_t qa[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) qa[t] = __builtin_bit_cast(bf16x8_t, qw[t]);
+
+  // basis tiles: P[record * ROWS + 1 + row][g] = scale * (acc - 8 S_g)
+#pragma unroll
+  for (int tau = 0; tau < BT; ++tau) {
+    const uint32_t w[4] = {wb[tau].x, wb[tau].y, wb[tau].z, wb[tau].w};
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], q4_operand(w[t]), acc, 0, 0, 0);
+    const int slot = 16 * tau + col;
+    const int r = slot / R, m = slot % R;
+    const float sc = half_bits_f(bsc[tau]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int g = 4 * kg + i;
+      if (g < G) P[(r * ROWS + 1 + m) * G + g] = sc * (acc[i] - 8.f * Sg[i]);
+    }
+  }
+  // centroid tile: P[record * ROWS][g] = scale * (acc - 128 S_g)
+  {
+    const uint32_t w[8] = {wm[0].x, wm[0].y, wm[0].z, wm[0].w, wm[1].x, wm[1].y, wm[1].z, wm[1].w};
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], q8_operand(w[2 * t], w[2 * t + 1]), acc, 0, 0, 0);
+    const float sc = half_bits_f(msc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int g = 4 * kg + i;
+      if (g < G && col < NR) P[(col * ROWS) * G + g] = sc * (acc[i] - 128.f * Sg[i]);
+    }
+  }
+  wave_lds_fence();
+  group_lse<R, G, NR, true>(
+      P, Z,
+      [&](int r, float (&c)[R], float& cs) {
+#pragma unroll
+        for (int m = 0; m < R; ++m) c[m] = (float)(int8_t)((cw[r][m >> 2] >> (8 * (m & 3))) & 0xffu);
+        cs = half_bits_f(csc[r]);
+      },
+      valid, out, a.max_pages, j0, j_end, lane, zscale);
+}
+
+template <int R>
+static hipError_t launch_score_q4(int group, const ScoreArgs& a, hipStream_t s) {
+  constexpr int per_block = kScoreWaves * Q4Group<R>::NR;
+  dim3 grid((a.max_pages + per_block - 1) / per_block, a.hkv, a.batch);
+  dim3 block(kScoreWaves * kWave);
+  switch (group) {
+    case 1: hipLaunchKernelGGL((score_q4_kernel<R, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((score_q4_kernel<R, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((score_q4_kernel<R, 4>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((score_q4_kernel<R, 8>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -467,7 +722,16 @@ static hipError_t launch_score_t(int rank, int group, const ScoreArgs& a, hipStr
   }
 }
 
-hipError_t launch_score(DType dt, int rank, int group, const ScoreArgs& a, hipStream_t s) {
+hipError_t launch_score(DType dt, int rank, int group, bool q4, const ScoreArgs& a, hipStream_t s) {
+  if (q4) {
+    if (dt != kBF16) return hipErrorInvalidValue;
+    switch (rank) {
+      case 4: return launch_score_q4<4>(group, a, s);
+      case 8: return launch_score_q4<8>(group, a, s);
+      case 16: return launch_score_q4<16>(group, a, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   if (dt == kBF16) {
     switch (rank) {
       case 1: return launch_score_mfma<1>(group, a, s);

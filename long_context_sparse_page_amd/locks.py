@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(_HERE, "liblocks.so")
 
 LK_OK, LK_ERR_INVALID_ARG, LK_ERR_UNSUPPORTED, LK_ERR_WORKSPACE, LK_ERR_HIP = range(5)
 LK_F32, LK_BF16 = 0, 1
+LK_SUMMARY_KV, LK_SUMMARY_I4 = 0, 1
 
 EXPORTED = (
     "lk_summary_record_bytes",
@@ -53,6 +54,7 @@ class lk_config(ctypes.Structure):
         ("token_budget", ctypes.c_int32),
         ("kv_dtype", ctypes.c_int32),
         ("scale", ctypes.c_float),
+        ("summary_format", ctypes.c_int32),
     ]
 
 
@@ -123,10 +125,11 @@ def _check(status: int) -> None:
 
 
 def make_config(head_dim=128, page_size=64, rank=8, num_q_heads=4, num_kv_heads=1,
-                token_budget=512, kv_dtype=LK_F32, scale=None) -> lk_config:
+                token_budget=512, kv_dtype=LK_F32, scale=None, summary_format=LK_SUMMARY_KV) -> lk_config:
     if scale is None:
         scale = head_dim ** -0.5
-    return lk_config(head_dim, page_size, rank, num_q_heads, num_kv_heads, token_budget, kv_dtype, scale)
+    return lk_config(head_dim, page_size, rank, num_q_heads, num_kv_heads, token_budget, kv_dtype, scale,
+                     summary_format)
 
 
 def make_cache(k_pool, v_pool, summary_pool, block_table, seq_lens) -> lk_cache:

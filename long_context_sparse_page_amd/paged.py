@@ -33,7 +33,8 @@ class DeviceCache:
         self.w = w
         self.device = device
         self.cfg = L.make_config(w.head_dim, w.page_size, w.rank, w.num_q_heads, w.num_kv_heads,
-                                 w.token_budget, LK_DTYPE[w.dtype], w.scale)
+                                 w.token_budget, LK_DTYPE[w.dtype], w.scale,
+                                 L.LK_SUMMARY_I4 if w.summary == "i4" else L.LK_SUMMARY_KV)
         B, d, hkv = w.page_size, w.head_dim, w.num_kv_heads
         pages = capacity_pages or [w.pages_needed(s) for s in range(w.batch)]
         self.max_pages = max(pages)
@@ -51,9 +52,14 @@ class DeviceCache:
         fill = float("nan") if poison else 0.0
         self.k_pool = torch.full((total, hkv, B, d), fill, dtype=tdt, device=device)
         self.v_pool = torch.full((total, hkv, B, d), fill, dtype=tdt, device=device)
-        rec = L.lk_summary_record_bytes(self.cfg) // (2 if w.dtype == "bf16" else 4)
+        if w.summary == "i4":  # byte records; 0xff poison
+            rec = L.lk_summary_record_bytes(self.cfg)
+            self.summary_pool = torch.full((total, hkv, rec), 255 if poison else 0, dtype=torch.uint8,
+                                           device=device)
+        else:
+            rec = L.lk_summary_record_bytes(self.cfg) // (2 if w.dtype == "bf16" else 4)
+            self.summary_pool = torch.full((total, hkv, rec), fill, dtype=tdt, device=device)
         self.record_elems = rec
-        self.summary_pool = torch.full((total, hkv, rec), fill, dtype=tdt, device=device)
         self.block_table = torch.from_numpy(bt).to(device)
         self.seq_lens = torch.tensor(w.context, dtype=torch.int32, device=device)
         self.ws_bytes = L.lk_workspace_size(self.cfg, w.batch, self.max_pages)

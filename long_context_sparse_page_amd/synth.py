@@ -58,6 +58,7 @@ class Workload:
     steps: int                    # decode steps (each appends one token)
     carriers: tuple               # (lo, hi) carriers per query head, inclusive
     scale: float = field(default=0.0)
+    summary: str = "kv"           # page summaries in the KV dtype ("kv") or int4/int8 ("i4")
 
     def __post_init__(self):
         if not self.scale:
@@ -76,7 +77,7 @@ class Workload:
 
 
 def workload(wid: int, *, rank: int | None = None, budget: int | None = None,
-             batch: int | None = None, steps: int | None = None) -> Workload:
+             batch: int | None = None, steps: int | None = None, summary: str | None = None) -> Workload:
     """The five decode workloads of the Locks decode path.
 
     0: tiny fp32 case (1 sequence, 4 query heads on 1 KV head, 4064 tokens:
@@ -110,6 +111,8 @@ def workload(wid: int, *, rank: int | None = None, budget: int | None = None,
         w.context = (w.context * batch)[:batch]
     if steps is not None:
         w.steps = steps
+    if summary is not None:
+        w.summary = summary
     return w
 
 

@@ -45,8 +45,62 @@ def q_device(q64: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
     return (t.to(torch.bfloat16) if dtype == "bf16" else t.to(torch.float32)).to(device)
 
 
+def oracle_quant(w, K_pages, n_pages) -> lo.QuantSummary:
+    """The oracle's int4/int8 summaries (codes and scales) of the first n pages."""
+    return lo.quantize_summary(lo.build_page_summaries(K_pages[:n_pages], w.rank, "f64"))
+
+
 def oracle_summaries(w, K_pages, n_pages):
+    """The summaries the scorer reads: rounded to the KV dtype, or quantized
+    and dequantized for int4/int8 records."""
+    if w.summary == "i4":
+        return lo.dequantize_summary(oracle_quant(w, K_pages, n_pages))
     return lo.build_page_summaries(K_pages[:n_pages], w.rank, w.dtype)
+
+
+# ---- int4/int8 record bytes (the layout documented in include/locks.h) ----
+def q4_offsets(d: int, B: int, r: int) -> dict:
+    o = {"mu": 0, "basis": d, "coef": d + r * d // 2}
+    o["cscale"] = o["coef"] + B * r
+    o["bscale"] = o["cscale"] + 2 * B
+    o["mscale"] = o["bscale"] + 2 * r
+    o["bytes"] = (o["mscale"] + 2 + 15) // 16 * 16
+    return o
+
+
+def pack_q4_records(qs: lo.QuantSummary) -> np.ndarray:
+    """uint8 [n, record bytes] of quantized summaries."""
+    n, r, d = qs.basis_q.shape
+    B = qs.coeffs_q.shape[1]
+    o = q4_offsets(d, B, r)
+    out = np.zeros((n, o["bytes"]), dtype=np.uint8)
+    out[:, :d] = qs.centroid_q.astype(np.int8).view(np.uint8)
+    lo4 = qs.basis_q[:, :, 0::2] & 0xF
+    hi4 = qs.basis_q[:, :, 1::2] & 0xF
+    out[:, o["basis"]:o["coef"]] = (lo4 | (hi4 << 4)).astype(np.uint8).reshape(n, -1)
+    out[:, o["coef"]:o["cscale"]] = qs.coeffs_q.astype(np.int8).view(np.uint8).reshape(n, -1)
+    out[:, o["cscale"]:o["bscale"]] = qs.coeffs_s.astype(np.float16).view(np.uint8).reshape(n, -1)
+    out[:, o["bscale"]:o["mscale"]] = qs.basis_s.astype(np.float16).view(np.uint8).reshape(n, -1)
+    out[:, o["mscale"]:o["mscale"] + 2] = qs.centroid_s.astype(np.float16).view(np.uint8).reshape(n, -1)
+    return out
+
+
+def unpack_q4_records(buf: np.ndarray, d: int, B: int, r: int) -> lo.QuantSummary:
+    """Codes and scales of uint8 [n, record bytes] records."""
+    buf = np.ascontiguousarray(buf, dtype=np.uint8)
+    n = buf.shape[0]
+    o = q4_offsets(d, B, r)
+    mq = buf[:, :d].view(np.int8).astype(np.int64)
+    packed = buf[:, o["basis"]:o["coef"]].reshape(n, r, d // 2).astype(np.int64)
+    bq = np.zeros((n, r, d), dtype=np.int64)
+    bq[:, :, 0::2] = ((packed & 0xF) ^ 8) - 8
+    bq[:, :, 1::2] = ((packed >> 4) ^ 8) - 8
+    cq = buf[:, o["coef"]:o["cscale"]].view(np.int8).reshape(n, B, r).astype(np.int64)
+    f16 = lambda a, b: np.ascontiguousarray(buf[:, a:b]).view(np.float16).astype(np.float64)
+    return lo.QuantSummary(centroid_q=mq, centroid_s=f16(o["mscale"], o["mscale"] + 2)[:, 0],
+                           basis_q=bq, basis_s=f16(o["bscale"], o["mscale"]), coeffs_q=cq,
+                           coeffs_s=f16(o["cscale"], o["bscale"]), eigvals=np.zeros((n, B)),
+                           r_eff=np.full(n, r))
 
 
 def oracle_head(w, q_g, K_pages, V_pages, T, summary=None):

@@ -50,6 +50,13 @@ def test_record_bytes_and_budget():
     assert L.lk_summary_record_bytes(cfg(rank=4)) == 1792
     assert L.lk_summary_record_bytes(cfg(rank=16)) == 6400
     assert L.lk_summary_record_bytes(cfg(kv_dtype=L.LK_F32)) == 6656
+    # int4 basis + int8 coefficients and centroid + fp16 scales, padded to 16 bytes:
+    # 128 + 8*64 + 64*8 codes and 2*(64 + 8 + 1) scale bytes = 1298 -> 1312
+    i4 = dict(summary_format=L.LK_SUMMARY_I4)
+    assert L.lk_summary_record_bytes(cfg(**i4)) == 1312
+    assert L.lk_summary_record_bytes(cfg(rank=4, **i4)) == 784      # 128 + 256 + 256 + 138 = 778
+    assert L.lk_summary_record_bytes(cfg(rank=16, **i4)) == 2352    # 128 + 1024 + 1024 + 162 = 2338
+    assert L.lk_summary_record_bytes(cfg(summary_format=5)) == 0
     assert L.lk_page_budget(cfg()) == 32
     assert L.lk_page_budget(cfg(token_budget=2049)) == 33
     assert L.lk_page_budget(cfg(token_budget=256)) == 4
@@ -75,6 +82,9 @@ def test_workspace_size_scales():
     (dict(token_budget=64 * 2000), L.LK_ERR_UNSUPPORTED),
     (dict(kv_dtype=7), L.LK_ERR_INVALID_ARG),
     (dict(scale=float("nan")), L.LK_ERR_INVALID_ARG),
+    (dict(summary_format=2), L.LK_ERR_INVALID_ARG),
+    (dict(summary_format=1, kv_dtype=0), L.LK_ERR_UNSUPPORTED),  # int4/int8 records need bf16 queries
+    (dict(summary_format=1, rank=2), L.LK_ERR_UNSUPPORTED),
 ])
 def test_config_rejected(kw, status):
     with pytest.raises(L.LocksError) as e:

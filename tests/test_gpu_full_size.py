@@ -68,19 +68,20 @@ def _check_structure(w, sel, cnt, out, lse, lens):
             assert (g[c:] == -1).all()
 
 
-@pytest.mark.parametrize("wid,rank,budget", [
-    (1, None, None),          # 32K x 8
-    (2, None, None),          # 128K x 4 (the bench workload)
-    (3, None, None),          # one 1M-token sequence
-    (4, None, None),          # 64 sequences, 4K..256K, r = 8, b = 1024
-    (4, 4, 256),
-    (4, 16, 4096),
+@pytest.mark.parametrize("wid,rank,budget,summary", [
+    (1, None, None, "kv"),    # 32K x 8
+    (2, None, None, "kv"),    # 128K x 4 (the bench workload)
+    (3, None, None, "kv"),    # one 1M-token sequence
+    (4, None, None, "kv"),    # 64 sequences, 4K..256K, r = 8, b = 1024
+    (4, 4, 256, "kv"),
+    (4, 16, 4096, "kv"),
+    (2, None, None, "i4"),    # 128K x 4 with int4 / int8 summary records
 ])
-def test_full_size_decode(gpu, wid, rank, budget):
+def test_full_size_decode(gpu, wid, rank, budget, summary):
     steps = 2
-    w = synth.workload(wid, rank=rank, budget=budget, steps=steps)
+    w = synth.workload(wid, rank=rank, budget=budget, steps=steps, summary=summary)
     say("full size", w.name, "r", w.rank, "b", w.token_budget, "batch", w.batch,
-        "tokens", sum(w.context), "steps", steps)
+        "tokens", sum(w.context), "steps", steps, "summary", w.summary)
     dc = DeviceCache(w)
     dc.fill_from_synth(threads=16)
     dc.build_all()
@@ -134,7 +135,7 @@ def test_full_size_decode(gpu, wid, rank, budget):
         K, V = K.reshape(n_pages, B, d), V.reshape(n_pages, B, d)
         qg = q64[s, h * G:(h + 1) * G]
         hs, summ = ref.oracle_head(w, qg, K, V, lens[s])
-        oracle[(s, h)] = (hs, summ)
+        oracle[(s, h)] = (hs, summ if w.summary == "kv" else ref.oracle_quant(w, K, summ.centroid.shape[0]))
         n_mr = lo.most_recent_page(lens[s], w.page_size)
         gsel = sel[s, h, :cnt[s, h]]
         msg = ref.selection_mismatch(gsel, hs.selected, hs.m_bar, n_mr, k, rel=2e-2)
@@ -151,6 +152,11 @@ def test_full_size_decode(gpu, wid, rank, budget):
 
     # scorer isolation: the oracle's records for the sampled pairs
     for (s, h), (hs, summ) in oracle.items():
+        if w.summary == "i4":
+            n = summ.centroid_q.shape[0]
+            phys = torch.from_numpy(dc.block_table_host[s, :n].astype(np.int64)).cuda()
+            dc.summary_pool[phys, h] = torch.from_numpy(ref.pack_q4_records(summ)).cuda()
+            continue
         n = summ.centroid.shape[0]
         recs = np.concatenate([summ.centroid, summ.basis.reshape(n, -1), summ.coeffs.reshape(n, -1)], axis=1)
         phys = torch.from_numpy(dc.block_table_host[s, :n].astype(np.int64)).cuda()

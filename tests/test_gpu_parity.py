@@ -536,3 +536,190 @@ def test_selector_tiers(gpu, T, budget, capacity, group):
     w, dc, K, V, q64 = _selector_case(T, budget, capacity=capacity, group=group)
     sel, hs = _run_selector(w, dc, K, V, q64)
     assert len(sel) == len(hs.selected)
+
+
+# ----------------------------------------------------------------------------
+# int4 / int8 summary records (LK_SUMMARY_I4)
+# ----------------------------------------------------------------------------
+def small_q4(batch=2, ctx=(4096 + 32, 64 * 9 + 17), rank=8, budget=512, steps=0, hq=32, hkv=8):
+    w = small_bf16(batch=batch, ctx=ctx, rank=rank, budget=budget, steps=steps, hq=hq, hkv=hkv)
+    w.name = "small-q4"
+    w.summary = "i4"
+    return w
+
+
+def upload_q4_records(dc: DeviceCache, w, quants):
+    """Write oracle int4/int8 records (packed as include/locks.h documents)."""
+    for (s, h), qs in quants.items():
+        n = qs.centroid_q.shape[0]
+        phys = torch.from_numpy(dc.block_table_host[s, :n].astype(np.int64)).cuda()
+        dc.summary_pool[phys, h] = torch.from_numpy(ref.pack_q4_records(qs)).cuda()
+
+
+def _codes_match(gq, oq, gs, os_, x, tol):
+    """Scales within one fp16 ulp; codes equal except by one step, and where the
+    scales agree only where the oracle's x / s lies within tol of a rounding
+    boundary.  Returns the fraction of differing codes."""
+    np.testing.assert_allclose(gs, os_, rtol=2.0 ** -10, atol=0)
+    assert (np.abs(gq - oq) <= 1).all()
+    t = x / np.where(os_ > 0, os_, 1.0)[..., None]
+    off = np.abs(t - np.floor(t) - 0.5)
+    bad = (gq != oq) & (gs == os_)[..., None] & (off > tol)
+    assert not bad.any(), f"{bad.sum()} codes differ away from a rounding boundary"
+    return (gq != oq).mean()
+
+
+@pytest.mark.parametrize("rank", [4, 8, 16])
+def test_q4_build_matches_oracle(gpu, rank):
+    T = 64 * 24 + 5
+    w = small_q4(batch=1, ctx=(T,), rank=rank)
+    say("int4/int8 build: T", T, "r", rank, "KV heads", w.num_kv_heads)
+    dc = DeviceCache(w, poison=True)
+    dc.fill_from_synth()
+    dc.build_all()
+    torch.cuda.synchronize()
+    n, d, B = T // 64, w.head_dim, w.page_size
+    phys = torch.from_numpy(dc.block_table_host[0, :n].astype(np.int64)).cuda()
+    fr, compared = [], 0
+    for h in range(w.num_kv_heads):
+        K, _ = ref.host_pages(w, 0, h, T)
+        summ = lo.build_page_summaries(K[:n], rank, "f64")
+        qs = lo.quantize_summary(summ)
+        g = ref.unpack_q4_records(dc.summary_pool[phys, h].cpu().numpy(), d, B, rank)
+        fr.append(_codes_match(g.centroid_q, qs.centroid_q, g.centroid_s, qs.centroid_s, summ.centroid, 0.01))
+        # bases and coefficients where the spectrum separates every kept mode
+        lam = summ.eigvals
+        sep = np.min(np.abs(np.diff(lam[:, :rank + 1], axis=1)), axis=1) / lam[:, 0]
+        ok = sep >= 1e-2
+        compared += int(ok.sum())
+        if ok.any():
+            fr.append(_codes_match(g.basis_q[ok], qs.basis_q[ok], g.basis_s[ok], qs.basis_s[ok],
+                                   summ.basis[ok], 0.01))
+            fr.append(_codes_match(g.coeffs_q[ok], qs.coeffs_q[ok], g.coeffs_s[ok], qs.coeffs_s[ok],
+                                   summ.coeffs[ok], 0.05))
+        # every page: dequantized basis rows stay unit vectors within the quantization error
+        back = lo.dequantize_summary(g)
+        norms = np.linalg.norm(back.basis, axis=2)
+        live = g.basis_s > 0
+        assert (np.abs(norms[live] - 1) <= np.sqrt(d) * g.basis_s[live] / 2 + 1e-3).all()
+    say("pages with separated modes", compared, "of", n * w.num_kv_heads, "; differing codes", max(fr))
+    if rank <= 8:
+        assert compared >= n * w.num_kv_heads // 2
+
+
+@pytest.mark.parametrize("rank", [4, 8, 16])
+def test_q4_score_select_on_oracle_records(gpu, rank):
+    w = small_q4(rank=rank)
+    say("int4/int8 scorer isolation: r", rank, w.context)
+    dc = DeviceCache(w, poison=True)
+    dc.fill_from_synth()
+    T = w.context
+    q64 = ref.host_queries(w, 0, T)
+    quants, summaries = {}, {}
+    for s in range(w.batch):
+        for h in range(w.num_kv_heads):
+            K, _ = ref.host_pages(w, s, h, T[s])
+            n_mr = lo.most_recent_page(T[s], w.page_size)
+            quants[(s, h)] = ref.oracle_quant(w, K, n_mr)
+            summaries[(s, h)] = lo.dequantize_summary(quants[(s, h)])
+    res = run_oracle_all(w, T, q64, summaries)
+    upload_q4_records(dc, w, quants)
+    o = dc.outputs()
+    dc.score_select(ref.q_device(q64, w.dtype), o)
+    torch.cuda.synchronize()
+    worst = check_scores(w, dc, o, res, T, atol=1e-3)
+    say("max page LSE error", worst)
+    assert worst < 1e-4
+
+
+def test_q4_end_to_end(gpu):
+    """GPU-built int4/int8 records: the scorer agrees with the oracle scoring the
+    GPU's own records, the page LSE stays near the oracle's own quantization,
+    and attention over the GPU's selection matches the oracle's."""
+    w = small_q4()
+    say("int4/int8 end to end", w.context)
+    dc = DeviceCache(w, poison=True)
+    dc.fill_from_synth()
+    dc.build_all()
+    T = w.context
+    q64 = ref.host_queries(w, 0, T)
+    qd = ref.q_device(q64, w.dtype)
+    o = dc.outputs()
+    dc.score_select(qd, o)
+    dc.sparse_attn(qd, o["sel"], o["cnt"], o)
+    torch.cuda.synchronize()
+    page_lse = o["page_lse"].cpu().numpy()
+    sel, cnt = o["sel"].cpu().numpy(), o["cnt"].cpu().numpy()
+    out = o["out"].float().cpu().numpy().astype(np.float64)
+    G, d, B, r = w.group, w.head_dim, w.page_size, w.rank
+    own_err, ora_err, att_err = 0.0, [], 0.0
+    for s in range(w.batch):
+        n_mr = lo.most_recent_page(T[s], B)
+        phys = torch.from_numpy(dc.block_table_host[s, :n_mr].astype(np.int64)).cuda()
+        for h in range(w.num_kv_heads):
+            K, V = ref.host_pages(w, s, h, T[s])
+            qg = q64[s, h * G:(h + 1) * G]
+            own = lo.dequantize_summary(ref.unpack_q4_records(dc.summary_pool[phys, h].cpu().numpy(), d, B, r))
+            own_lse = lo.reconstructed_page_lse(qg, own, w.scale)
+            got = page_lse[s, h * G:(h + 1) * G, :n_mr]
+            own_err = max(own_err, np.abs(got - own_lse).max())
+            hs, _ = ref.oracle_head(w, qg, K, V, T[s])
+            ora_err.append(np.abs(got - hs.page_lse).ravel())
+            gsel = sel[s, h, :cnt[s, h]]
+            eo, _ = lo.attend(qg, lo.gather_tokens(K, gsel, T[s], B), lo.gather_tokens(V, gsel, T[s], B), w.scale)
+            att_err = max(att_err, ref.rel_l2(out[s, h * G:(h + 1) * G], eo).max())
+    ora_err = np.concatenate(ora_err)
+    say("scorer vs its own records", own_err, "; vs the oracle's quantization: max", ora_err.max(),
+        "p99", np.quantile(ora_err, 0.99), "; attention rel L2", att_err)
+    assert own_err < 1e-3
+    assert ora_err.max() < 5e-2
+    assert att_err <= 2e-2
+
+
+def test_q4_decode_steps(gpu):
+    """lk_decode_step with int4/int8 records over steps that complete pages
+    (built in-stream): every check step, the selection is well formed and the
+    page LSE of sampled heads matches the oracle scoring the GPU's records."""
+    w = small_q4(batch=3, ctx=(187, 508, 64 * 30 + 60), steps=70, budget=512)
+    say("int4/int8 decode steps", w.context, "steps", w.steps)
+    dc = DeviceCache(w, poison=True)
+    dc.fill_from_synth()
+    dc.build_all()
+    rng = np.random.default_rng(9)
+    lens = list(w.context)
+    G, d, B, r = w.group, w.head_dim, w.page_size, w.rank
+    kv = {(s, h): synth.keys_values(w, s, h) for s in range(w.batch) for h in (0, 5)}
+    worst = 0.0
+    for step in range(w.steps):
+        q = rng.standard_normal((w.batch, w.num_q_heads, d)).astype(np.float32)
+        kn = rng.standard_normal((w.batch, w.num_kv_heads, d)).astype(np.float32)
+        vn = rng.standard_normal((w.batch, w.num_kv_heads, d)).astype(np.float32)
+        for (s, h), (kk, vv) in kv.items():
+            kn[s, h], vn[s, h] = kk[lens[s]], vv[lens[s]]
+        q64 = ref.stored(q, w.dtype)
+        o = dc.outputs()
+        dc.decode_step(ref.q_device(q64, w.dtype), to_storage(kn, w.dtype).cuda(), to_storage(vn, w.dtype).cuda(), o)
+        lens = [t + 1 for t in lens]
+        if step % 10 != 9:
+            continue
+        torch.cuda.synchronize()
+        assert dc.seq_lens.cpu().tolist() == lens
+        o2 = dc.outputs()
+        dc.score_select(ref.q_device(q64, w.dtype), o2)
+        torch.cuda.synchronize()
+        page_lse = o2["page_lse"].cpu().numpy()
+        sel, cnt = o["sel"].cpu().numpy(), o["cnt"].cpu().numpy()
+        k = lo.page_budget(w.token_budget, B)
+        for (s, h) in kv:
+            n_mr = lo.most_recent_page(lens[s], B)
+            assert cnt[s, h] == min(k, n_mr + 1)
+            g = sel[s, h, :cnt[s, h]]
+            assert g[0] == 0 and g[-1] == n_mr and (np.diff(g) > 0).all()
+            if n_mr == 0:
+                continue
+            phys = torch.from_numpy(dc.block_table_host[s, :n_mr].astype(np.int64)).cuda()
+            own = lo.dequantize_summary(ref.unpack_q4_records(dc.summary_pool[phys, h].cpu().numpy(), d, B, r))
+            want = lo.reconstructed_page_lse(q64[s, h * G:(h + 1) * G], own, w.scale)
+            worst = max(worst, np.abs(page_lse[s, h * G:(h + 1) * G, :n_mr] - want).max())
+    say("decode steps: max page LSE error against the GPU's own records", worst)
+    assert worst < 1e-3
