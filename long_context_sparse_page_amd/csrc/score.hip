@@ -481,8 +481,9 @@ static hipError_t launch_score_mfma(int group, const ScoreArgs& a, hipStream_t s
 // the same mapping).  Codes are converted biased (int4 + 8, int8 + 128: plain
 // byte-to-float conversions) and the bias is removed from the products,
 // sum_c q_c code_c = sum_c q_c (code_c + bias) - bias * S_g with S_g = sum_c q_c.
-// Tiles: NR * R / 16 tiles of basis rows (column = record * R + row), then
-// one tile of the NR centroids.  The reconstruction and LSE are those of the
+// Tiles: one tile of the NR centroids, whose column NR is a column of ones
+// (its products are the S_g), then NR * R / 16 tiles of basis rows (column =
+// record * R + row).  The reconstruction and LSE are those of the
 // bf16 records, with the per-token coefficient scale.
 template <int R> struct Q4Group {
   static constexpr int NR = R >= 16 ? 2 : (R >= 8 ? 4 : 8);  // records per wave
@@ -490,8 +491,8 @@ template <int R> struct Q4Group {
   static constexpr int SLOTS = NR * (R + 1);
 };
 
-__device__ __forceinline__ uint32_t bf16x2_of(float lo, float hi) {  // both exact in bf16
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+__device__ __forceinline__ uint32_t bf16x2_of(float lo, float hi) {  // both exact in bf16: the high halves
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 __device__ __forceinline__ float ubyte_f(uint32_t x, int b) { return (float)((x >> (8 * b)) & 0xffu); }
 
@@ -499,7 +500,10 @@ __device__ __forceinline__ float ubyte_f(uint32_t x, int b) { return (float)((x 
 // bf16 values of code + 8.
 __device__ __forceinline__ bf16x8_t q4_operand(uint32_t w) {
   w ^= 0x88888888u;
-  const uint32_t even = w & 0x0f0f0f0fu, odd = (w >> 4) & 0x0f0f0f0fu;
+  uint32_t even = w & 0x0f0f0f0fu, odd = (w >> 4) & 0x0f0f0f0fu;
+  // opaque to the compiler, so each byte below converts with one v_cvt_f32_ubyteN
+  // instead of a bit-field extract followed by a conversion
+  asm("" : "+v"(even), "+v"(odd));
   uint4 o;
   o.x = bf16x2_of(ubyte_f(even, 0), ubyte_f(odd, 0));
   o.y = bf16x2_of(ubyte_f(even, 1), ubyte_f(odd, 1));
@@ -574,9 +578,10 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
   for (int tau = 0; tau < BT; ++tau) {
     const int slot = 16 * tau + col;
     const int r = slot / R, m = slot % R;
-    const uint8_t* rp = recp[0];
+    constexpr int RPT = 16 / R;  // records of one tile
+    const uint8_t* rp = recp[tau * RPT];
 #pragma unroll
-    for (int x = 1; x < NR; ++x) if (x == r) rp = recp[x];
+    for (int x = 1; x < RPT; ++x) if (r == tau * RPT + x) rp = recp[tau * RPT + x];
     wb[tau] = *reinterpret_cast<const uint4*>(rp + L.basis() + m * (D / 2) + 16 * kg);
     bsc[tau] = *reinterpret_cast<const uint16_t*>(rp + L.bscale() + 2 * m);
   }
@@ -615,23 +620,6 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
   if (j0 >= n_scored) return;
   const int j_end = min(j0 + NR, n_scored);
 
-  // S_g = sum of query g over all dims (lanes col, col + 16, col + 32, col + 48)
-  float qs = 0.f;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const uint32_t w[4] = {qw[t].x, qw[t].y, qw[t].z, qw[t].w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) qs += bf16_lo(w[i]) + bf16_hi(w[i]);
-  }
-  qs = xor32_sum(xor16_sum(qs));
-  float Sg[4];  // S of the 4 queries whose products this lane holds (rows 4 kg + i)
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float s0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qs), min(i, G - 1)));
-    const float s1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qs), min(4 + i, G - 1)));
-    Sg[i] = kg ? s1 : s0;
-  }
-
   const float zscale = a.scale * kLog2e;
   float* out = a.page_lse + ((size_t)seq * a.hq + (size_t)kvh * G) * a.max_pages;
   float* P = sP[wave];
@@ -640,6 +628,31 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
 #pragma unroll
   for (int t = 0; t < 4; ++t) qa[t] = __builtin_bit_cast(bf16x8_t, qw[t]);
 
+  // centroid tile first: columns 0 .. NR-1 are the centroids, column NR is a
+  // column of ones, whose products are S_g = sum of query g over all dims
+  float Sg[4];  // S of the queries whose products this lane holds (rows 4 kg + i)
+  {
+    const uint32_t w[8] = {wm[0].x, wm[0].y, wm[0].z, wm[0].w, wm[1].x, wm[1].y, wm[1].z, wm[1].w};
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      bf16x8_t op = q8_operand(w[2 * t], w[2 * t + 1]);
+      if (col == NR) op = __builtin_bit_cast(bf16x8_t, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], op, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float s0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc[i]), NR));       // rows i
+      const float s1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc[i]), 16 + NR));  // rows 4 + i
+      Sg[i] = kg ? s1 : s0;
+    }
+    const float sc = half_bits_f(msc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int g = 4 * kg + i;
+      if (g < G && col < NR) P[(col * ROWS) * G + g] = sc * (acc[i] - 128.f * Sg[i]);
+    }
+  }
   // basis tiles: P[record * ROWS + 1 + row][g] = scale * (acc - 8 S_g)
 #pragma unroll
   for (int tau = 0; tau < BT; ++tau) {
@@ -654,20 +667,6 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
     for (int i = 0; i < 4; ++i) {
       const int g = 4 * kg + i;
       if (g < G) P[(r * ROWS + 1 + m) * G + g] = sc * (acc[i] - 8.f * Sg[i]);
-    }
-  }
-  // centroid tile: P[record * ROWS][g] = scale * (acc - 128 S_g)
-  {
-    const uint32_t w[8] = {wm[0].x, wm[0].y, wm[0].z, wm[0].w, wm[1].x, wm[1].y, wm[1].z, wm[1].w};
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], q8_operand(w[2 * t], w[2 * t + 1]), acc, 0, 0, 0);
-    const float sc = half_bits_f(msc);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int g = 4 * kg + i;
-      if (g < G && col < NR) P[(col * ROWS) * G + g] = sc * (acc[i] - 128.f * Sg[i]);
     }
   }
   wave_lds_fence();
