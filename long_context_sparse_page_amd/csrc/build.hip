@@ -20,7 +20,8 @@
 //   4. back-transformation by the reflectors.
 // All B eigenvalues (for the optional eigenvalue output) are found by plain
 // bisection, one lane per eigenvalue.  The K tile is widened to fp32 and
-// centred in LDS, stored transposed (D^T) for the Gram and the basis.
+// centred in LDS, stored transposed (D^T); the Gram D D^T runs on the matrix
+// cores with each fp32 entry split into three bf16 terms.
 //
 // Zero-mode rule: eigenvalue <= 1e-5 * lambda_1 or <= 1e-10 * sum_i ||k_i||^2.
 // Sign rule: each basis vector's largest-magnitude entry is made positive.
@@ -247,28 +248,64 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
   }
   __syncthreads();
 
-  // 3) Gram A = D D^T, a 4 x 4 tile per thread (both halves: exactly symmetric)
+  // 3) Gram A = D D^T on the matrix cores (v_mfma_f32_16x16x32_bf16): each
+  //    fp32 entry of D is the sum of three bf16 terms d1 + d2 + d3 (each the
+  //    bf16 rounding of what the previous ones leave), and the six products
+  //    d_a d_b^T with a + b <= 4 are accumulated in fp32 (the dropped ones lie
+  //    below fp32 rounding).  Wave w computes the 16 x 16 tiles (w, J); tiles
+  //    with w <= J are written with their mirror images (on diagonal tiles the
+  //    entries with row <= col), so the Gram is exactly symmetric.
   {
-    const int ti = tid >> 4, tj = tid & 15;
-    float acc[4][4];
+    const int col = lane & 15, kg = lane >> 4;
+    // operand of K-step t for row `row`: dims 32 t + 8 kg .. +7, three bf16 terms
+    auto split_operand = [&](int row, int t, bf16x8_t (&o)[3]) {
+      uint32_t w[3][4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+      for (int p = 0; p < 4; ++p) {
+        const int c = 32 * t + 8 * kg + 2 * p;
+        float x[2] = {sDT[c][row], sDT[c + 1][row]};
+        uint32_t h[3][2];
 #pragma unroll
-      for (int y = 0; y < 4; ++y) acc[x][y] = 0.f;
-    for (int c = 0; c < D; ++c) {
-      const float4 xi = *reinterpret_cast<const float4*>(&sDT[c][4 * ti]);
-      const float4 yj = *reinterpret_cast<const float4*>(&sDT[c][4 * tj]);
-      const float xa[4] = {xi.x, xi.y, xi.z, xi.w};
-      const float ya[4] = {yj.x, yj.y, yj.z, yj.w};
+        for (int e = 0; e < 2; ++e) {
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
+          for (int q = 0; q < 3; ++q) {
+            const __bf16 v = (__bf16)x[e];
+            h[q][e] = __builtin_bit_cast(uint16_t, v);
+            x[e] -= (float)v;  // exact: the remainder of a bf16 rounding
+          }
+        }
 #pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(xa[x], ya[y], acc[x][y]);
+        for (int q = 0; q < 3; ++q) w[q][p] = h[q][0] | (h[q][1] << 16);
+      }
+#pragma unroll
+      for (int q = 0; q < 3; ++q) o[q] = __builtin_bit_cast(bf16x8_t, make_uint4(w[q][0], w[q][1], w[q][2], w[q][3]));
+    };
+    bf16x8_t ar[4][3];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) split_operand(16 * wave + col, t, ar[t]);
+    for (int J = 0; J < 4; ++J) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        bf16x8_t br[3];
+        split_operand(16 * J + col, t, br);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[t][0], br[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[t][0], br[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[t][1], br[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[t][1], br[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[t][0], br[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[t][2], br[0], acc, 0, 0, 0);
+      }
+      // lane holds rows 16 w + 4 kg + i, column 16 J + col
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * wave + 4 * kg + i, c = 16 * J + col;
+        if (wave < J || (wave == J && r <= c)) {
+          sA[r][c] = acc[i];
+          sA[c][r] = acc[i];
+        }
+      }
     }
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int y = 0; y < 4; ++y) sA[4 * ti + x][4 * tj + y] = acc[x][y];
   }
   __syncthreads();
 
