@@ -66,6 +66,12 @@ __all__ = [
     "dequantize_summary",
     "QUANT_BASIS_LEVELS",
     "QUANT_ROW_LEVELS",
+    "envelope_page_score",
+    "moment_core_score",
+    "centroid_score",
+    "combine_shares",
+    "select_by_rule",
+    "head_coverage",
 ]
 
 # Eigenvalue thresholds of the zero-mode rule ([Locks] §4 "Build" states the
@@ -365,6 +371,80 @@ def decode_head(q, keys_pages, values_pages, seq_len: int, summary: PageSummary,
     Vv = gather_tokens(values_pages, sel, seq_len, B)
     out, lse = attend(q, K, Vv, scale)
     return HeadStep(s_hat, m_bar, sel, out, lse)
+
+
+# ----------------------------------------------------------------------------
+# rival page scores and GQA combine rules (diagnostics: [Locks] §3 Lemma 2,
+# App. A.5 Prop. 3 / Eq. (A.2), Table B.1, Table D.17)
+# ----------------------------------------------------------------------------
+def envelope_page_score(q, keys, scale: float) -> np.ndarray:
+    """Envelope score of [Locks] Lemma 2: e_j(q) = sum_c max(q_c u_jc, q_c l_jc)
+    with u, l the page's per-dimension key maxima and minima, times the logit
+    scale (an upper bound of every within-page logit).  keys [n, B, d] -> [G, n]."""
+    q = np.asarray(q, dtype=np.float64)
+    keys = np.asarray(keys, dtype=np.float64)
+    u, lo = keys.max(axis=1), keys.min(axis=1)                       # [n, d]
+    e = np.maximum(q[:, None, :] * u[None], q[:, None, :] * lo[None])  # [G, n, d]
+    return scale * e.sum(axis=-1)
+
+
+def moment_core_score(q, summary: PageSummary, scale: float) -> np.ndarray:
+    """Rank-r moment core of [Locks] Eq. (A.2), the second-cumulant truncation
+    of the page log-mass: scale q.mu + (scale^2 / 2B) sum_{k<=r} sigma_k^2 (v_k.q)^2,
+    plus log B so it estimates s_j like Eq. (1) (log B is page-independent).
+    sigma_k^2 are the kept Gram eigenvalues (zero modes have zero basis rows)."""
+    q = np.asarray(q, dtype=np.float64)
+    n, r, d = summary.basis.shape
+    B = summary.coeffs.shape[1]
+    a = scale * (q @ summary.centroid.T)                              # [G, n]
+    proj = np.einsum("nrd,gd->gnr", summary.basis, q)                 # [G, n, r]
+    lam = summary.eigvals[:, :r]                                      # [n, r]
+    quad = (scale ** 2 / (2 * B)) * np.einsum("nr,gnr->gn", lam, proj ** 2)
+    return a + quad + np.log(B)
+
+
+def centroid_score(q, summary: PageSummary, scale: float) -> np.ndarray:
+    """Centroid-only score: Eq. (1) at r = 0, scale q.mu + log B."""
+    q = np.asarray(q, dtype=np.float64)
+    B = summary.coeffs.shape[1]
+    return scale * (q @ summary.centroid.T) + np.log(B)
+
+
+def combine_shares(page_scores, rule: str) -> np.ndarray:
+    """One ranking value per page from per-head log-mass estimates [G, n]:
+    "share_average" (the shipped rule, [Locks] §4): mean over heads of the
+    normalized shares; "group_max": their maximum; "group_mass": the summed
+    unnormalized mass sum_g e^{s_g} (as its log).  The pages name group-max
+    and group-mass without formulas; these are the plain readings."""
+    s = np.asarray(page_scores, dtype=np.float64)
+    if rule == "group_mass":
+        return _logsumexp(s, axis=0)
+    shares = np.exp(s - _logsumexp(s, axis=-1)[:, None])
+    if rule == "share_average":
+        return shares.mean(axis=0)
+    if rule == "group_max":
+        return shares.max(axis=0)
+    raise ValueError(f"unknown combine rule {rule!r}")
+
+
+def select_by_rule(page_scores, n_mr: int, k: int, rule: str) -> list:
+    """Selections of one GQA group: one shared set for "share_average",
+    "group_max" and "group_mass", one set per head for "per_head" (each head's
+    own top-(k-2) by its share).  Returns a list of G page-index arrays."""
+    s = np.asarray(page_scores, dtype=np.float64)
+    G = s.shape[0]
+    if rule == "per_head":
+        return [select_pages(np.exp(s[g] - _logsumexp(s[g])), n_mr, k) for g in range(G)]
+    return [select_pages(combine_shares(s, rule), n_mr, k)] * G
+
+
+def head_coverage(exact_page_lse, selections) -> np.ndarray:
+    """Per-head coverage gamma_S(q_g) = sum_{j in S_g} m_g(j) of the exact
+    page-mass shares over the scored pages ([Locks] Lemma 1); [G]."""
+    s = np.asarray(exact_page_lse, dtype=np.float64)
+    m = np.exp(s - _logsumexp(s, axis=-1)[:, None])
+    n = s.shape[1]
+    return np.array([m[g, [j for j in sel if j < n]].sum() for g, sel in enumerate(selections)])
 
 
 # ----------------------------------------------------------------------------

@@ -414,3 +414,81 @@ def test_quantized_build_zero_modes_and_score_perturbation():
     dz = np.abs(logits(back) - logits(summ)).max(axis=-1)
     ds = np.abs(lo.reconstructed_page_lse(q, back, scale) - lo.reconstructed_page_lse(q, summ, scale))
     assert (ds <= dz + 1e-12).all() and dz.max() > 0
+
+
+# ----------------------------------------------------------------------------
+# rival scores and GQA combine rules (diagnostics)
+# ----------------------------------------------------------------------------
+def test_envelope_bounds_every_logit_and_is_content_blind():
+    """[Locks] Lemma 2: the envelope score upper-bounds every within-page logit
+    (so s_j <= e_j + log B), and depends on a page only through its
+    per-dimension extremes: a page whose columns are permuted independently
+    (same extremes, other keys) gets the same envelope score but another mass."""
+    rng = np.random.default_rng(31)
+    d, B = 128, 64
+    keys = rng.standard_normal((6, B, d))
+    q = rng.standard_normal((4, d)) * 2.0
+    scale = 1 / np.sqrt(d)
+    env = lo.envelope_page_score(q, keys, scale)
+    logits = scale * np.einsum("gd,nbd->gnb", q, keys)
+    assert (logits.max(axis=-1) <= env + 1e-12).all()
+    assert (lo.exact_page_lse(q, keys, scale) <= env + np.log(B) + 1e-12).all()
+    shuffled = np.stack([rng.permutation(keys[0][:, c]) for c in range(d)], axis=1)[None]
+    np.testing.assert_allclose(lo.envelope_page_score(q, shuffled, scale), env[:, :1], rtol=0, atol=1e-12)
+    assert np.abs(lo.exact_page_lse(q, shuffled, scale) - lo.exact_page_lse(q, keys[:1], scale)).max() > 1e-3
+
+
+def test_moment_core_is_the_second_order_truncation():
+    """[Locks] Eq. (A.2): with keys mu + eps * delta, the exact page log-mass
+    minus the moment core shrinks like eps^3 (the truncation drops the third
+    and higher cumulants; a wrong second-order coefficient would leave eps^2);
+    at r >= rank the rank-r form equals (1/(2Bd)) q^T D^T D q directly."""
+    rng = np.random.default_rng(32)
+    d, B, rho = 128, 64, 6
+    dev = rng.standard_normal((3, B, rho)) @ rng.standard_normal((3, rho, d))
+    dev -= dev.mean(axis=1, keepdims=True)
+    mu = rng.standard_normal((3, 1, d))
+    q = rng.standard_normal((2, d)) * 3.0
+    scale = 1 / np.sqrt(d)
+    errs = []
+    for eps in (0.02, 0.01):
+        keys = mu + eps * dev
+        summ = lo.build_page_summaries(keys, 8, "f64")
+        errs.append(np.abs(lo.exact_page_lse(q, keys, scale) - lo.moment_core_score(q, summ, scale)).max())
+        D = keys - keys.mean(axis=1, keepdims=True)
+        direct = scale * (q @ keys.mean(axis=1).T) + np.log(B) + np.einsum(
+            "gd,nbd,nbe,ge->gn", q, D, D, q) / (2 * B * d)
+        np.testing.assert_allclose(lo.moment_core_score(q, summ, scale), direct, rtol=0, atol=1e-10)
+    assert errs[0] / errs[1] > 6.0, errs
+
+
+def test_centroid_score_is_rank_zero():
+    rng = np.random.default_rng(33)
+    keys = rng.standard_normal((4, 64, 128))
+    summ = lo.build_page_summaries(keys, 8, "f64")
+    q = rng.standard_normal((3, 128))
+    zeroed = lo.PageSummary(centroid=summ.centroid, basis=summ.basis, coeffs=np.zeros_like(summ.coeffs),
+                            eigvals=summ.eigvals, r_eff=summ.r_eff)
+    np.testing.assert_allclose(lo.centroid_score(q, summ, 0.088), lo.reconstructed_page_lse(q, zeroed, 0.088),
+                               rtol=0, atol=1e-12)
+
+
+def test_combine_rules_coverage_orderings():
+    """On exact shares: share-average has the largest group-mean coverage of
+    every shared rule ([Locks] Cor. 3), each head's own selection covers that
+    head at least as well as any shared one, and with G = 1 every rule is the
+    same selection."""
+    rng = np.random.default_rng(34)
+    for trial in range(40):
+        G, n = 4, int(rng.integers(20, 80))
+        s = rng.standard_normal((G, n)) * rng.uniform(0.5, 4.0)
+        n_mr, k = n, int(rng.integers(3, 12))
+        cov = {r: lo.head_coverage(s, lo.select_by_rule(s, n_mr, k, r))
+               for r in ("share_average", "group_max", "group_mass", "per_head")}
+        assert cov["share_average"].mean() >= cov["group_max"].mean() - 1e-12
+        assert cov["share_average"].mean() >= cov["group_mass"].mean() - 1e-12
+        for r in ("share_average", "group_max", "group_mass"):
+            assert (cov["per_head"] >= cov[r] - 1e-12).all()
+        one = s[:1]
+        sels = [lo.select_by_rule(one, n_mr, k, r)[0].tolist() for r in ("share_average", "group_max", "group_mass", "per_head")]
+        assert all(x == sels[0] for x in sels)
