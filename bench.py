@@ -186,6 +186,31 @@ def main():
     torch.cuda.synchronize()
     build_ms = ev0.elapsed_time(ev1) / reps
 
+    # the same keys re-paged into 16-token pages, summarized in the int4 basis /
+    # int8 row format (r = 8) of the pages' deployment: one bulk call
+    n_full = [w.context[s] // B for s in range(w.batch)]
+    src = torch.cat([bulk.k_pool[torch.from_numpy(bulk.block_table_host[s, :n_full[s]].astype(np.int64)).to(dev)]
+                     for s in range(w.batch)])
+    k16 = src.view(-1, hkv, B // 16, 16, d).permute(0, 2, 1, 3, 4).reshape(-1, hkv, 16, d).contiguous()
+    del src
+    cfg16 = L.make_config(d, 16, 8, hq, hkv, w.token_budget, L.LK_BF16, w.scale, L.LK_SUMMARY_I4)
+    s16 = torch.zeros((k16.shape[0], hkv, L.lk_summary_record_bytes(cfg16)), dtype=torch.uint8, device=dev)
+    cache16 = L.make_cache(k16, None, s16, bulk.block_table, bulk.seq_lens)
+    ids16 = torch.arange(k16.shape[0], dtype=torch.int32, device=dev)
+
+    def build16():
+        L.lk_build_page_summary(cfg16, cache16, ids16, k16.shape[0], None, None, 0, sp)
+    build16()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(reps):
+        build16()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    build16_ms = ev0.elapsed_time(ev1) / reps
+    pages16 = int(k16.shape[0])
+    del k16, s16
+
     result = {
         "metric": "decode-attn steps/s and achieved HBM GB/s at 128K ctx, budget 2048 tok",
         "value": 1e3 / ms_per_step,
@@ -227,6 +252,8 @@ def main():
                            "speedup_of_locks_step": dense_ms / ms_per_step},
         "bulk_build": {"pages": len(ids), "page_heads": len(ids) * hkv, "ms": build_ms,
                        "page_heads_per_s": len(ids) * hkv / (build_ms * 1e-3)},
+        "bulk_build_page16_r8i4": {"pages": pages16, "page_heads": pages16 * hkv, "ms": build16_ms,
+                                   "page_heads_per_s": pages16 * hkv / (build16_ms * 1e-3)},
     }
 
     if args.copy_bytes:

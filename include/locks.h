@@ -99,7 +99,9 @@ typedef enum { LK_SUMMARY_KV = 0, LK_SUMMARY_I4 = 1 } lk_summary_format;
  * GQA grouping, per-head token budget b, storage dtype and logit scale. */
 typedef struct {
   int32_t head_dim;      /* d; 128 is supported                              */
-  int32_t page_size;     /* B; 64 is supported                               */
+  int32_t page_size;     /* B; 64 is supported, and 16 for
+                          * lk_build_page_summary only (LK_ERR_UNSUPPORTED
+                          * from every other entry point)                 */
   int32_t rank;          /* r in {1, 2, 4, 8, 16}; modes beyond the page's
                           * nonzero modes are stored as zeros              */
   int32_t num_q_heads;   /* Hq                                               */
@@ -149,7 +151,10 @@ lk_status lk_workspace_size(const lk_config* cfg, int32_t batch,
  * record is written in kv_dtype (round to nearest even).
  *   phys_page_ids  int32 [n_pages] device; entries < 0 are skipped.
  *   eigvals_out    optional fp32 [n_pages][Hkv][B], sorted descending, >= 0.
- * Pages must be full (all B token slots written). */
+ * Pages must be full (all B token slots written).  At B = 16 the
+ * eigendecomposition is a cyclic Jacobi iteration on the 16 x 16 Gram (the
+ * page-size study of the Locks appendix, Table D.10); the record layout and
+ * every rule above are the same, with B = 16. */
 lk_status lk_build_page_summary(const lk_config* cfg, const lk_cache* cache,
                                 const int32_t* phys_page_ids, int32_t n_pages,
                                 float* eigvals_out, void* ws, size_t ws_bytes,

@@ -16,7 +16,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "liblocks.so")
-SOURCES = ["api.hip", "score.hip", "select.hip", "attn.hip", "build.hip"]
+SOURCES = ["api.hip", "score.hip", "select.hip", "attn.hip", "build.hip", "build16.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

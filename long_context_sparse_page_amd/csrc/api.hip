@@ -51,7 +51,9 @@ struct Shape {
   bool q4;  // LK_SUMMARY_I4 records
 };
 
-lk_status check_config(const lk_config* cfg, Shape* sh) {
+// build_only: the caller only builds summaries, which is also built for pages
+// of 16 tokens
+lk_status check_config(const lk_config* cfg, Shape* sh, bool build_only = false) {
   if (!cfg) return fail(LK_ERR_INVALID_ARG, "config is null");
   if (cfg->head_dim <= 0 || cfg->page_size <= 0 || cfg->rank <= 0 || cfg->num_q_heads <= 0 ||
       cfg->num_kv_heads <= 0 || cfg->token_budget <= 0)
@@ -68,7 +70,10 @@ lk_status check_config(const lk_config* cfg, Shape* sh) {
   if (k < 2)
     return fail(LK_ERR_INVALID_ARG, "page budget ceil(b/B) = %d < 2 (the sink and the most recent page need two slots)", k);
   if (cfg->head_dim != 128) return fail(LK_ERR_UNSUPPORTED, "head_dim %d: only 128 is built", cfg->head_dim);
-  if (cfg->page_size != 64) return fail(LK_ERR_UNSUPPORTED, "page_size %d: only 64 is built", cfg->page_size);
+  if (cfg->page_size == 16 && !build_only)
+    return fail(LK_ERR_UNSUPPORTED, "page_size 16 is built for lk_build_page_summary only");
+  if (cfg->page_size != 64 && cfg->page_size != 16)
+    return fail(LK_ERR_UNSUPPORTED, "page_size %d: built page sizes are 64 and 16", cfg->page_size);
   const int r = cfg->rank;
   if (r != 1 && r != 2 && r != 4 && r != 8 && r != 16)
     return fail(LK_ERR_UNSUPPORTED, "rank %d: built ranks are 1, 2, 4, 8, 16", r);
@@ -224,7 +229,7 @@ lk_status lk_build_page_summary(const lk_config* cfg, const lk_cache* cache, con
   (void)ws;
   (void)ws_bytes;
   Shape sh;
-  lk_status st = check_config(cfg, &sh);
+  lk_status st = check_config(cfg, &sh, true);
   if (st != LK_OK) return st;
   if (!cache) return fail(LK_ERR_INVALID_ARG, "cache is null");
   if (!cache->k_pool || !cache->summary_pool) return fail(LK_ERR_INVALID_ARG, "k_pool / summary_pool is null");
@@ -234,7 +239,9 @@ lk_status lk_build_page_summary(const lk_config* cfg, const lk_cache* cache, con
   if (n_pages == 0) return ok();
   lk::BuildArgs ba{cache->k_pool, cache->summary_pool, phys_page_ids, eigvals_out, n_pages,
                    cache->num_phys_pages, sh.hkv, nullptr, nullptr, 0, {}, sh.q4 ? 1 : 0};
-  return hip_status(lk::launch_build(sh.dt, sh.r, ba, static_cast<hipStream_t>(stream)), "build launch");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (sh.B == 16) return hip_status(lk::launch_build16(sh.dt, sh.r, ba, s), "build launch");
+  return hip_status(lk::launch_build(sh.dt, sh.r, ba, s), "build launch");
 }
 
 lk_status lk_score_select(const lk_config* cfg, const lk_cache* cache, int32_t batch, const void* q,

@@ -9,17 +9,19 @@ namespace lk {
 enum DType : int { kF32 = 0, kBF16 = 1 };
 
 // Byte layout of a quantized (int4 basis / int8 coefficients and centroid)
-// summary record at d = 128, B = 64 and rank r: centroid int8[d] | basis
-// int4[r][d/2] (byte c of row m: dims 2c in the low nibble, 2c+1 in the high
-// one) | coefficients int8[B][r] | coefficient scales fp16[B] | basis scales
-// fp16[r] | centroid scale fp16, padded to 16 bytes.
+// summary record at d = 128, page size b (64 unless given) and rank r:
+// centroid int8[d] | basis int4[r][d/2] (byte c of row m: dims 2c in the low
+// nibble, 2c+1 in the high one) | coefficients int8[b][r] | coefficient
+// scales fp16[b] | basis scales fp16[r] | centroid scale fp16, padded to 16
+// bytes.
 struct Q4Layout {
-  static constexpr int kD = 128, kB = 64;
+  static constexpr int kD = 128;
   int r;
+  int b = 64;
   __host__ __device__ constexpr int basis() const { return kD; }
   __host__ __device__ constexpr int coef() const { return kD + r * kD / 2; }
-  __host__ __device__ constexpr int cscale() const { return coef() + kB * r; }
-  __host__ __device__ constexpr int bscale() const { return cscale() + 2 * kB; }
+  __host__ __device__ constexpr int cscale() const { return coef() + b * r; }
+  __host__ __device__ constexpr int bscale() const { return cscale() + 2 * b; }
   __host__ __device__ constexpr int mscale() const { return bscale() + 2 * r; }
   __host__ __device__ constexpr int bytes() const { return (mscale() + 2 + 15) / 16 * 16; }
 };
@@ -115,6 +117,8 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 // merge = false leaves the split partials for the decode step's build launch
 hipError_t launch_attn(DType dt, int group, const AttnArgs& a, bool merge, hipStream_t s);
 hipError_t launch_build(DType dt, int rank, const BuildArgs& a, hipStream_t s);
+// Pages of 16 tokens (bulk builds only: no merge or length commit)
+hipError_t launch_build16(DType dt, int rank, const BuildArgs& a, hipStream_t s);
 // Decode step: selection (se) and attention splits (a) in one launch, for
 // tables of up to 3072 pages per sequence (select_attn_fusable).
 bool select_attn_fusable(const SelectArgs& se);

@@ -30,6 +30,7 @@ _P_KEYS = 3
 _P_VALUES = 4
 _P_QUERY = 5
 _P_LENGTHS = 6
+_P_ISOTROPIC = 7
 
 LOCAL_RANK = 8
 GLOBAL_RANK = 4
@@ -210,3 +211,11 @@ def queries(w: Workload, step: int, seq: int, kv_head: int, seq_len: int,
             q[g] += QUERY_SCALE * bases[p].sum(axis=0)
         q[g] += QUERY_NOISE * rq.standard_normal(d)
     return q.astype(np.float32), chosen
+
+
+def isotropic_pages(n: int, page_size: int = 16, head_dim: int = 128, stream: int = 0) -> np.ndarray:
+    """``n`` pages of i.i.d. N(0, 1) keys, fp32 [n, page_size, head_dim]: the
+    flat-spectrum (isotropic) null of the Locks appendix ("Spectral tails").
+    ``stream`` selects an independent draw."""
+    rng = _rng(_P_ISOTROPIC, page_size, head_dim, stream)
+    return rng.standard_normal((n, page_size, head_dim), dtype=np.float32)

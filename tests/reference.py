@@ -140,3 +140,16 @@ def selection_mismatch(gpu_sel, ora_sel, m_bar, n_mr, k, rel=1e-4):
 def rel_l2(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     """Per-row ||a - b|| / ||b||."""
     return np.linalg.norm(a - b, axis=-1) / np.maximum(np.linalg.norm(b, axis=-1), 1e-30)
+
+
+def codes_match(gq, oq, gs, os_, x, tol):
+    """Scales within one fp16 ulp; codes equal except by one step, and where the
+    scales agree only where the oracle's x / s lies within tol of a rounding
+    boundary.  Returns the fraction of differing codes."""
+    np.testing.assert_allclose(gs, os_, rtol=2.0 ** -10, atol=0)
+    assert (np.abs(gq - oq) <= 1).all()
+    t = x / np.where(os_ > 0, os_, 1.0)[..., None]
+    off = np.abs(t - np.floor(t) - 0.5)
+    bad = (gq != oq) & (gs == os_)[..., None] & (off > tol)
+    assert not bad.any(), f"{bad.sum()} codes differ away from a rounding boundary"
+    return (gq != oq).mean()

@@ -7,6 +7,7 @@ from host validation and never launches a kernel (the fake device addresses
 are never dereferenced)."""
 
 import ctypes
+import json
 import os
 import re
 import subprocess
@@ -60,6 +61,35 @@ def test_record_bytes_and_budget():
     assert L.lk_page_budget(cfg()) == 32
     assert L.lk_page_budget(cfg(token_budget=2049)) == 33
     assert L.lk_page_budget(cfg(token_budget=256)) == 4
+
+
+def test_page16_record_bytes_match_table_d10(golden_dir):
+    """Quantized records at B = 16 hold Table D.10's logical payload (Locks App.
+    D, "State accounting") plus the fp16 scales (B + r + 1 of them), padded to
+    16 bytes; the shipped r8i4 record is about a tenth of the page's bf16 KV."""
+    g = json.load(open(os.path.join(golden_dir, "table_d10_bytes.json")))
+    for row in g["rows"]:
+        if row["basis_bits"] != 4 or row["rank"] == 2:
+            continue
+        r = row["rank"]
+        got = L.lk_summary_record_bytes(cfg(page_size=16, rank=r, summary_format=L.LK_SUMMARY_I4))
+        assert got == (row["bytes"] + 2 * (16 + r + 1) + 15) // 16 * 16
+    r8 = L.lk_summary_record_bytes(cfg(page_size=16, rank=8, summary_format=L.LK_SUMMARY_I4))
+    assert r8 == 832 and abs((768 + 2 * 25) / g["kv_bytes"] - 0.10) < 0.001
+    assert L.lk_summary_record_bytes(cfg(page_size=16)) == (128 + 8 * 128 + 16 * 8) * 2
+
+
+def test_page16_is_a_build_only_config():
+    c16 = cfg(page_size=16)
+    # accepted by the builder (argument errors come first), refused elsewhere
+    expect(L.LK_ERR_INVALID_ARG, L.lk_build_page_summary, c16, fake_cache(), None, 3, None, None, 0, 0)
+    L.lk_build_page_summary(c16, fake_cache(), None, 0, None, None, 0, 0)
+    expect(L.LK_ERR_UNSUPPORTED, L.lk_score_select, c16, fake_cache(), 2, FAKE, None, None, FAKE, FAKE,
+           0x100000, 1 << 30, 0)
+    expect(L.LK_ERR_UNSUPPORTED, L.lk_decode_step, c16, fake_cache(), 2, FAKE, FAKE, FAKE, FAKE, None, None,
+           None, 0x100000, 1 << 30, 0)
+    expect(L.LK_ERR_UNSUPPORTED, L.lk_build_page_summary, cfg(page_size=32), fake_cache(), FAKE, 3, None, None,
+           0, 0)
 
 
 def test_workspace_size_scales():

@@ -556,17 +556,7 @@ def upload_q4_records(dc: DeviceCache, w, quants):
         dc.summary_pool[phys, h] = torch.from_numpy(ref.pack_q4_records(qs)).cuda()
 
 
-def _codes_match(gq, oq, gs, os_, x, tol):
-    """Scales within one fp16 ulp; codes equal except by one step, and where the
-    scales agree only where the oracle's x / s lies within tol of a rounding
-    boundary.  Returns the fraction of differing codes."""
-    np.testing.assert_allclose(gs, os_, rtol=2.0 ** -10, atol=0)
-    assert (np.abs(gq - oq) <= 1).all()
-    t = x / np.where(os_ > 0, os_, 1.0)[..., None]
-    off = np.abs(t - np.floor(t) - 0.5)
-    bad = (gq != oq) & (gs == os_)[..., None] & (off > tol)
-    assert not bad.any(), f"{bad.sum()} codes differ away from a rounding boundary"
-    return (gq != oq).mean()
+_codes_match = ref.codes_match
 
 
 @pytest.mark.parametrize("rank", [4, 8, 16])
