@@ -105,6 +105,19 @@ __device__ __forceinline__ int sturm_count(const float* sd, const float* se2, fl
   }
   return c;
 }
+// The same count with T in registers (every lane holds all of d and e^2).
+__device__ __forceinline__ int sturm_count_reg(const float (&d)[64], const float (&e2)[64], float sigma, float pivmin) {
+  float q = d[0] - sigma;
+  if (fabsf(q) < pivmin) q = -pivmin;
+  int c = q < 0.f ? 1 : 0;
+#pragma unroll
+  for (int i = 1; i < 64; ++i) {
+    q = (d[i] - sigma) - e2[i - 1] * __builtin_amdgcn_rcpf(q);
+    if (fabsf(q) < pivmin) q = -pivmin;
+    c += q < 0.f ? 1 : 0;
+  }
+  return c;
+}
 
 // Quantized record (Q4Layout): symmetric absmax quantization per row, the
 // scale rounded to fp16 and the codes taken against that stored scale,
@@ -183,12 +196,12 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
   __shared__ float sA[B + 1][LA];          // Gram (+ a zero pad row); reflectors below the diagonal; later the basis
   __shared__ float sMu[D];
   __shared__ float sd[B], se[B], se2[B];   // tridiagonal T (e[i] couples i, i + 1)
-  __shared__ float su[2][B], sp[B];        // reflectors (double-buffered) and p = 2 A22 u
+  __shared__ float sp4[2][kBuildWaves][B]; // partial sums of A u, one row per wave (by step parity)
+  __shared__ float scol[2][B];             // the column after next, published by its owner
   __shared__ float sRed[2][kBuildWaves];
   __shared__ float sLam[KEPT];             // top eigenvalues, descending
   __shared__ float sZ[B][KEPT];            // eigenvectors (of T, then of A)
-  __shared__ float sRP[B][KEPT], sDU[B][KEPT], sDU2[B][KEPT], sML[B][KEPT], sZZ[B][KEPT];  // inverse-iteration factors
-  __shared__ int sSW[B][KEPT];
+  __shared__ float4 sF[B][KEPT];           // inverse-iteration factors, one float4 per row
   __shared__ float sSigma[KEPT], sSign[KEPT];
   __shared__ int sNz[KEPT];
   __shared__ float sBound[2];
@@ -309,91 +322,94 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
   }
   __syncthreads();
 
-  // 4) Householder tridiagonalization.  Step k zeroes column k below the
-  //    subdiagonal with H = I - 2 u u^T (||u|| = 1), u stored in A[k+1.., k];
-  //    with p = 2 A22 u and w = p - (u.p) u, A22 <- A22 - u w^T - w u^T.
-  //    Two barriers per step: wave 0 updates column 0 of A22 itself and
-  //    derives the next reflector from it before the step's closing barrier.
-  auto reflector = [&](int k, float x, int buf) {  // wave 0; x = A[k+1+lane][k] (0 past the end)
-    const int m = B - 1 - k;
-    const float nrm2 = group_sum<kWave>(x * x);
-    const float x0 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
-    float u = 0.f, alpha = 0.f;
-    if (nrm2 > 0.f) {
-      const float nrm = sqrtf(nrm2);
-      alpha = x0 >= 0.f ? -nrm : nrm;
-      const float inv = __builtin_amdgcn_rsqf(2.f * (nrm2 + nrm * fabsf(x0)));  // 1 / ||x - alpha e_1||
-      u = (lane == 0 ? x - alpha : x) * inv;
-    }
-    su[buf][lane] = lane < m ? u : 0.f;  // zero tail: row blocks may run past column m
-    if (lane < m) sA[k + 1 + lane][k] = u;
-    if (lane == 0) se[k] = alpha;
-  };
-  if (tid < LA) sA[B][tid] = 0.f;  // pad row and pad column, read by the blocks of the last rows
-  if (tid < B) sA[tid][B] = 0.f;
-  if (wave == 0) {
-    if (lane == 0) sd[0] = sA[0][0];
-    reflector(0, lane < B - 1 ? sA[1 + lane][0] : 0.f, 0);
-  }
-  __syncthreads();
-  const int mrow = tid >> 2, mq = tid & 3;   // matvec / update: row and column quarter
-  for (int k = 0; k < B - 2; ++k) {
-    const int m = B - 1 - k;
-    const int buf = k & 1;
-    const float* uu = su[buf];
-    // p = 2 A22 u: row mrow, columns mq + 4 s (clamped loads, masked terms);
-    // the four quarters are summed over lanes
-    // (columns 16 mq .. 16 mq + 15; entries past m meet zero reflector entries
-    // and stay inside sA thanks to the pad row)
+  // 4) Householder tridiagonalization with A in registers: wave q keeps
+  //    columns 16 q .. 16 q + 15 of every row (lane = row).  Step k zeroes
+  //    column k below the subdiagonal with H = I - 2 u u^T (||u|| = 1, u_r = 0
+  //    for r <= k; u is also stored below the diagonal of column k of sA for
+  //    the back-transformation).  With p = 2 A u (the sum of the four waves'
+  //    partial sums), K = u.p and w = p - K u (rows > k), every wave applies
+  //    A <- A - u w^T - w u^T to its own columns.  One barrier per step: at
+  //    it the waves exchange their partial sums of p and the owner of column
+  //    k + 2 publishes that column; every wave then brings its copy of the
+  //    next column up to date itself and forms the next reflector from it
+  //    (the same arithmetic in every wave), so the next products start
+  //    without a second barrier.  LDS buffers alternate by step parity.
+  const int q0 = 16 * wave;  // first column of this wave
+  typedef float f32x16_t __attribute__((ext_vector_type(16)));
+  f32x16_t Ar;  // a vector, so that the uniform column index below stays in registers
+#pragma unroll
+  for (int t = 0; t < 16; ++t) Ar[t] = sA[lane][q0 + t];
+  float colnext = sA[lane][1];  // column k + 1 as of the start of step k
+  float ur;                     // u_k of this row
+  {
+    const float x = sA[lane][0];
+    __syncthreads();  // every wave has read the Gram columns that the reflectors overwrite
+    // reflector of column k from x = A[lane][k] (zero for lane <= k), formed
+    // by every wave; wave 0 stores it
+    auto reflector = [&](int k, float xk) {
+      const float nrm2 = group_sum<kWave>(xk * xk);
+      const float x0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xk), k + 1));
+      float u = 0.f, alpha = 0.f;
+      if (nrm2 > 0.f) {
+        const float nrm = sqrtf(nrm2);
+        alpha = x0 >= 0.f ? -nrm : nrm;
+        const float inv = __builtin_amdgcn_rsqf(2.f * (nrm2 + nrm * fabsf(x0)));  // 1 / ||x - alpha e_{k+1}||
+        u = (lane == k + 1 ? xk - alpha : xk) * inv;
+      }
+      if (wave == 0) {
+        if (lane > k) sA[lane][k] = u;
+        if (lane == 0) se[k] = alpha;
+      }
+      return u;
+    };
+    if (wave == 0 && lane == 0) sd[0] = x;
+    ur = reflector(0, lane > 0 ? x : 0.f);
+    float uj[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) uj[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ur), q0 + t));
     float pp = 0.f;
-    if (mrow < m) {
-      const float* Ar = &sA[k + 1 + mrow][k + 1 + 16 * mq];
-      const float* ub = uu + 16 * mq;
 #pragma unroll
-      for (int t = 0; t < 16; ++t) pp = fmaf(Ar[t], ub[t], pp);
-    }
-    pp += dpp<kDppXor1>(pp);
-    pp += dpp<kDppXor2>(pp);
-    pp *= 2.f;
-    float up = (mq == 0 && mrow < m) ? pp * uu[mrow] : 0.f;
-    up = group_sum<kWave>(up);
-    if (mq == 0 && mrow < m) sp[mrow] = pp;
-    if (lane == 0) sRed[1][wave] = up;
+    for (int t = 0; t < 16; ++t) pp = fmaf(Ar[t], uj[t], pp);
+    sp4[0][wave][lane] = pp;
     __syncthreads();
-    float Kup = 0.f;
+    for (int k = 0; k < B - 2; ++k) {
+      const int buf = k & 1;
+      const bool live = q0 + 15 > k;  // this wave holds columns > k
+      const float p = 2.f * ((sp4[buf][0][lane] + sp4[buf][1][lane]) + (sp4[buf][2][lane] + sp4[buf][3][lane]));
+      const float Kup = group_sum<kWave>(ur * p);
+      const float wr = lane > k ? p - Kup * ur : 0.f;
+      if (live) {
 #pragma unroll
-    for (int w = 0; w < kBuildWaves; ++w) Kup += sRed[1][w];
-    if (mrow < m) {  // columns 1 .. m-1 of A22
-      const float ui = uu[mrow], wi = sp[mrow] - Kup * ui;
-      float* Ar = &sA[k + 1 + mrow][k + 1 + 16 * mq];
-      const float* ub = uu + 16 * mq;
-      const float* pb = sp + 16 * mq;
+        for (int t = 0; t < 16; ++t) {
+          const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wr), q0 + t));
+          Ar[t] = Ar[t] - (ur * wj + wr * uj[t]);
+        }
+      }
+      const int c = k + 1;
+      if (c >= B - 2) break;  // the last reflector was u_{B-3}
+      // column c, brought up to date with this step, gives u_c
+      if (k > 0) colnext = scol[buf][lane];
+      const float uc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ur), c));
+      const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wr), c));
+      colnext = colnext - (ur * wc + wr * uc);
+      if (wave == 0 && lane == c) sd[c] = colnext;
+      ur = reflector(c, lane > c ? colnext : 0.f);
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const int j = 16 * mq + t;
-        const float uj = ub[t], wj = pb[t] - Kup * uj;
-        const float nv = Ar[t] - (ui * wj + wi * uj);
-        if (j >= 1 && j < m) Ar[t] = nv;
+      for (int t = 0; t < 16; ++t) uj[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ur), q0 + t));
+      pp = 0.f;
+      if (q0 + 15 > c) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) pp = fmaf(Ar[t], uj[t], pp);
       }
+      sp4[buf ^ 1][wave][lane] = pp;
+      if (c + 1 < B - 2 && wave == (c + 1) / 16) scol[buf ^ 1][lane] = Ar[c + 1 - q0];  // column c + 1, for the next step
+      __syncthreads();
     }
-    if (wave == 0) {  // column 0 of A22 (= column k + 1 of A), then the next reflector
-      const float u0 = uu[0], w0 = sp[0] - Kup * u0;
-      float a0 = 0.f;
-      if (lane < m) {
-        const float ul = uu[lane], wl = sp[lane] - Kup * ul;
-        a0 = sA[k + 1 + lane][k + 1] - (ul * w0 + wl * u0);
-        sA[k + 1 + lane][k + 1] = a0;
-      }
-      if (lane == 0) sd[k + 1] = a0;
-      wave_lds_fence();
-      if (k + 1 < B - 2) reflector(k + 1, lane < m - 1 ? sA[k + 2 + lane][k + 1] : 0.f, buf ^ 1);
-    }
-    __syncthreads();
   }
-  if (tid == 0) {
-    sd[B - 1] = sA[B - 1][B - 1];
-    se[B - 2] = sA[B - 1][B - 2];
-    se[B - 1] = 0.f;
+  if (wave == kBuildWaves - 1) {  // the last 2 x 2 block (columns 62, 63)
+    const float a62 = Ar[14], a63 = Ar[15];
+    if (lane == B - 2) sd[B - 2] = a62;
+    if (lane == B - 1) { sd[B - 1] = a63; se[B - 2] = a62; se[B - 1] = 0.f; }
   }
   __syncthreads();
   if (tid < B) se2[tid] = se[tid] * se[tid];
@@ -412,36 +428,49 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
   const float pivmin = fmaxf(tnorm * 1e-30f, 1e-30f);
   const float tol = 2.f * 1.19209290e-7f * tnorm;
 
-  // 5) the KEPT largest eigenvalues: wave w takes the w-th, (w+4)-th, ...;
-  //    each pass counts below 64 shifts spread over the current interval
+  // 5) the KEPT largest eigenvalues: wave w takes the w-th, (w+4)-th, ...
+  //    (KW of them) at once, each on its own segment of SL = 64 / KW lanes;
+  //    a pass counts the eigenvalues below SL shifts spread over the
+  //    segment's interval, which shrinks (SL + 1)-fold.  T is read into
+  //    registers once.
+  {
+    float dreg[B], e2reg[B];
 #pragma unroll
-  for (int s = 0; s < KW; ++s) {
-    const int kk = wave + kBuildWaves * s;
-    if (kk >= KEPT) break;
+    for (int i = 0; i < B; ++i) { dreg[i] = sd[i]; e2reg[i] = se2[i]; }
+    constexpr int SL = kWave / KW;
+    const int seg = lane / SL, sl = lane % SL;
+    const int kk = wave + kBuildWaves * seg;
     const int target = B - 1 - kk;          // ascending index of the kk-th largest
+    const uint64_t segmask = SL == kWave ? ~0ull : (((1ull << SL) - 1ull) << (seg * SL));
     float lo = glo, hi = ghi;
-    for (int it = 0; it < 12 && hi - lo > tol; ++it) {
+    bool more = kk < KEPT;
+    for (int it = 0; it < 16; ++it) {
+      more = more && hi - lo > tol;
+      if (!__ballot(more)) break;
       const float width = hi - lo;
-      const float sig = lo + width * (float)(lane + 1) * (1.f / 65.f);
-      const int cnt = sturm_count(sd, se2, sig, pivmin);
-      const uint64_t below = __ballot(cnt <= target);   // shifts at or below the eigenvalue
-      const int nl = below ? 64 - __clzll(below) : 0;   // highest such lane + 1
-      const float nlo = nl > 0 ? lo + width * (float)nl * (1.f / 65.f) : lo;
-      const float nhi = nl < 64 ? lo + width * (float)(nl + 1) * (1.f / 65.f) : hi;
-      if (nlo == lo && nhi == hi) break;  // below the resolution of fp32
-      lo = nlo;
-      hi = nhi;
+      const float sig = lo + width * (float)(sl + 1) * (1.f / (float)(SL + 1));
+      const int cnt = sturm_count_reg(dreg, e2reg, sig, pivmin);
+      const uint64_t below = __ballot(cnt <= target) & segmask;      // shifts at or below the eigenvalue
+      const int nl = below ? 64 - __clzll(below) - seg * SL : 0;      // highest such lane of the segment + 1
+      const float nlo = nl > 0 ? lo + width * (float)nl * (1.f / (float)(SL + 1)) : lo;
+      const float nhi = nl < SL ? lo + width * (float)(nl + 1) * (1.f / (float)(SL + 1)) : hi;
+      if (nlo == lo && nhi == hi) more = false;  // below the resolution of fp32
+      if (more) { lo = nlo; hi = nhi; }
     }
-    if (lane == 0) sLam[kk] = 0.5f * (lo + hi);
+    if (kk < KEPT && sl == 0) sLam[kk] = 0.5f * (lo + hi);
   }
   __syncthreads();
 
   // 6) inverse iteration on T: lane kk of wave 0 factors T - lambda_kk I once
   //    with partial pivoting (row i swaps with row i + 1 when |e_i| > |pivot|),
-  //    then solves kInvIters times from a fixed varied start
+  //    then solves kInvIters times from a fixed varied start.  Without
+  //    branches: the right-hand side and the swap flags stay in registers,
+  //    and row i of the factors is one float4 in LDS (reciprocal pivot, the
+  //    two entries right of the pivot, multiplier).
   if (wave == 0 && lane < KEPT) {
     const int kk = lane;
     const float lam = sLam[kk];
+    uint64_t swm = 0ull;  // bit i: rows i and i + 1 swapped
     {
       float ddc = sd[0] - lam, duc = se[0];
 #pragma unroll
@@ -449,49 +478,48 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
         const float dl = se[i];
         const float ddn = sd[i + 1] - lam;
         const float dun = i + 1 < B - 1 ? se[i + 1] : 0.f;
-        if (fabsf(ddc) >= fabsf(dl)) {
-          const float rp = __builtin_amdgcn_rcpf(fabsf(ddc) < pivmin ? pivmin : ddc);
-          const float mlt = dl * rp;
-          sRP[i][kk] = rp; sDU[i][kk] = duc; sDU2[i][kk] = 0.f; sML[i][kk] = mlt; sSW[i][kk] = 0;
-          ddc = ddn - mlt * duc;
-          duc = dun;
-        } else {
-          const float mlt = ddc * __builtin_amdgcn_rcpf(dl);
-          sRP[i][kk] = __builtin_amdgcn_rcpf(dl); sDU[i][kk] = ddn; sDU2[i][kk] = dun; sML[i][kk] = mlt;
-          sSW[i][kk] = 1;
-          ddc = duc - mlt * ddn;
-          duc = -mlt * dun;
-        }
+        const bool keep = fabsf(ddc) >= fabsf(dl);
+        const float rp = __builtin_amdgcn_rcpf(keep ? (fabsf(ddc) < pivmin ? pivmin : ddc) : dl);
+        const float mlt = (keep ? dl : ddc) * rp;
+        sF[i][kk] = make_float4(rp, keep ? duc : ddn, keep ? 0.f : dun, mlt);
+        if (!keep) swm |= 1ull << i;
+        const float nddc = keep ? ddn - mlt * duc : duc - mlt * ddn;
+        duc = keep ? dun : -mlt * dun;
+        ddc = nddc;
       }
-      sRP[B - 1][kk] = __builtin_amdgcn_rcpf(fabsf(ddc) < pivmin ? pivmin : ddc);
+      sF[B - 1][kk] = make_float4(__builtin_amdgcn_rcpf(fabsf(ddc) < pivmin ? pivmin : ddc), 0.f, 0.f, 0.f);
     }
+    float z[B];
     float nrm2 = 0.f;
 #pragma unroll
     for (int i = 0; i < B; ++i) {
       const uint32_t hsh = (uint32_t)(i * 2654435761u) ^ (uint32_t)((kk + 1) * 40503u);
-      const float b = 0.5f + (float)((hsh >> 9) & 1023) * (1.f / 1024.f);
-      sZZ[i][kk] = b;
-      nrm2 = fmaf(b, b, nrm2);
+      z[i] = 0.5f + (float)((hsh >> 9) & 1023) * (1.f / 1024.f);
+      nrm2 = fmaf(z[i], z[i], nrm2);
     }
     float scale = __builtin_amdgcn_rsqf(nrm2);
     for (int itr = 0; itr < kInvIters; ++itr) {
-      // forward: apply the row swaps and multipliers to the right-hand side
-      float zc = sZZ[0][kk] * scale;
+      // forward: the row swaps and multipliers applied to the right-hand side
+      float zc = z[0] * scale;
 #pragma unroll
       for (int i = 0; i < B - 1; ++i) {
-        const float zn = sZZ[i + 1][kk] * scale;
-        const float mlt = sML[i][kk];
-        if (sSW[i][kk]) { sZ[i][kk] = zn; zc = zc - mlt * zn; }
-        else { sZ[i][kk] = zc; zc = zn - mlt * zc; }
+        if (i % 8 == 0) asm volatile("" ::: "memory");  // loads run at most 8 rows ahead
+        const float zn = z[i + 1] * scale;
+        const float mlt = sF[i][kk].w;
+        const bool sw = (swm >> i) & 1ull;
+        z[i] = sw ? zn : zc;
+        zc = sw ? zc - mlt * zn : zn - mlt * zc;
       }
-      // back substitution, the solution written over the right-hand side
-      float x1 = zc * sRP[B - 1][kk], x2 = 0.f;
-      sZZ[B - 1][kk] = x1;
+      // back substitution, in place
+      float x1 = zc * sF[B - 1][kk].x, x2 = 0.f;
+      z[B - 1] = x1;
       nrm2 = x1 * x1;
 #pragma unroll
       for (int i = B - 2; i >= 0; --i) {
-        const float x = (sZ[i][kk] - sDU[i][kk] * x1 - sDU2[i][kk] * x2) * sRP[i][kk];
-        sZZ[i][kk] = x;
+        if (i % 8 == 6) asm volatile("" ::: "memory");
+        const float4 f = sF[i][kk];
+        const float x = (z[i] - f.y * x1 - f.z * x2) * f.x;
+        z[i] = x;
         nrm2 = fmaf(x, x, nrm2);
         x2 = x1;
         x1 = x;
@@ -499,7 +527,7 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
       scale = __builtin_amdgcn_rsqf(nrm2);
     }
 #pragma unroll
-    for (int i = 0; i < B; ++i) sZ[i][kk] = sZZ[i][kk] * scale;
+    for (int i = 0; i < B; ++i) sZ[i][kk] = z[i] * scale;
   }
   __syncthreads();
   // re-orthogonalize within clusters of close eigenvalues (wave 0, lane = row)
