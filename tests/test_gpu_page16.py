@@ -208,3 +208,56 @@ def test_page16_isotropic_null(gpu, golden_dir):
     assert (np.abs(ev - summ.eigvals) <= 1e-5 * lam1).all()
     fo = summ.eigvals[:, :g["rank"]].sum(1) / summ.eigvals.sum(1)
     assert np.abs(fr - fo).max() <= 1e-5
+
+
+def test_page16_full_size_bulk(gpu):
+    """The bulk build the bench times: the 128K x 4 keys (32 q / 8 KV heads,
+    bf16) re-paged into 32,768 pages of 16 tokens, int4/int8 records at r = 8,
+    one lk_build_page_summary call over all 262,144 page-heads; sampled
+    page-heads against the oracle (codes and scales), every eigenvalue output
+    checked for order and sign."""
+    from long_context_sparse_page_amd.paged import DeviceCache
+
+    w = synth.workload(2, steps=0)
+    say("16-token bulk build at full size:", w.name, "pages of 16:", sum(w.context) // B, "KV heads", w.num_kv_heads)
+    dc = DeviceCache(w)
+    dc.fill_from_synth(threads=16)
+    torch.cuda.synchronize()
+    hkv = w.num_kv_heads
+    src = torch.cat([dc.k_pool[torch.from_numpy(dc.block_table_host[s, :w.context[s] // 64].astype(np.int64)).cuda()]
+                     for s in range(w.batch)])
+    k16 = src.view(-1, hkv, 64 // B, B, D).permute(0, 2, 1, 3, 4).reshape(-1, hkv, B, D).contiguous()
+    del src
+    n = int(k16.shape[0])
+    cfg = L.make_config(D, B, 8, w.num_q_heads, hkv, w.token_budget, L.LK_BF16, w.scale, L.LK_SUMMARY_I4)
+    rb = L.lk_summary_record_bytes(cfg)
+    spool = torch.full((n, hkv, rb), 0xAB, dtype=torch.uint8, device="cuda")
+    ev = torch.full((n, hkv, B), -1.0, dtype=torch.float32, device="cuda")
+    cache = L.make_cache(k16, None, spool, dc.block_table, dc.seq_lens)
+    ids = torch.arange(n, dtype=torch.int32, device="cuda")
+    L.lk_build_page_summary(cfg, cache, ids, n, ev, None, 0, None)
+    torch.cuda.synchronize()
+    evh = ev.cpu().numpy()
+    assert (evh >= 0).all() and (np.diff(evh, axis=2) <= 0).all(), "eigenvalues not sorted descending / negative"
+    rng = np.random.default_rng(16)
+    pick = rng.choice(n * hkv, size=256, replace=False)
+    pg, hd = pick // hkv, pick % hkv
+    keys = k16[torch.from_numpy(pg).cuda(), torch.from_numpy(hd).cuda()].double().cpu().numpy()
+    recs = spool[torch.from_numpy(pg).cuda(), torch.from_numpy(hd).cuda()].cpu().numpy()
+    say("sampled page-heads", len(pick))
+    summ = lo.build_page_summaries(keys, 8, "f64")
+    lam1 = summ.eigvals[:, :1]
+    assert (np.abs(evh[pg, hd] - summ.eigvals) <= 1e-5 * lam1).all()
+    qs = lo.quantize_summary(summ)
+    g = ref.unpack_q4_records(recs, D, B, 8)
+    ref.codes_match(g.centroid_q, qs.centroid_q, g.centroid_s, qs.centroid_s, summ.centroid, 0.01)
+    k = np.minimum(summ.r_eff, 8)
+    lam = summ.eigvals
+    sep = np.array([np.min(np.abs(np.diff(lam[i, :k[i] + 1])), initial=np.inf) / max(lam[i, 0], 1e-30)
+                    for i in range(len(pick))])
+    ok = (sep >= 1e-2) & (k == 8)
+    say("page-heads with separated modes", int(ok.sum()), "of", len(pick))
+    assert ok.sum() >= len(pick) // 4
+    fb = ref.codes_match(g.basis_q[ok], qs.basis_q[ok], g.basis_s[ok], qs.basis_s[ok], summ.basis[ok], 0.01)
+    fc = ref.codes_match(g.coeffs_q[ok], qs.coeffs_q[ok], g.coeffs_s[ok], qs.coeffs_s[ok], summ.coeffs[ok], 0.05)
+    say("differing codes: basis", fb, "coefficients", fc)
