@@ -35,6 +35,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--summary", choices=("kv", "i4"), default="kv",
                    help="page summaries in the KV dtype (bf16, the default) or int4 basis / int8 rows")
+    p.add_argument("--workload", type=int, choices=(2, 3, 4), default=2,
+                   help="2: 128K x 4 (the headline); 3: one 1M-token sequence; "
+                        "4: 64 sequences of 4K..256K tokens (in-stream builds in most steps)")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="also run a plain device copy of this size (counter calibration)")
     return p.parse_args()
@@ -56,7 +59,8 @@ def main():
     dev = "cuda"
     total_steps = args.warmup + args.steps
     per_layer = -(-total_steps // args.layers)
-    w = synth.workload(2, steps=per_layer + 1, summary=args.summary)
+    extra = 64  # further steps timed one by one (in-stream build split, below)
+    w = synth.workload(args.workload, steps=per_layer + 1 + -(-extra // args.layers), summary=args.summary)
     B, d, G, hkv, hq = w.page_size, w.head_dim, w.group, w.num_kv_heads, w.num_q_heads
     e = 2  # bf16
     t0 = time.time()
@@ -187,7 +191,106 @@ def main():
     build_ms = ev0.elapsed_time(ev1) / reps
 
     # the same keys re-paged into 16-token pages, summarized in the int4 basis /
-    # int8 row format (r = 8) of the pages' deployment: one bulk call
+    # int8 row format (r = 8) of the pages' deployment: one bulk call (128K x 4 only)
+    page16 = bulk_build_page16(L, w, bulk, reps, stream, ev0, ev1) if args.workload == 2 else None
+
+    # per-step durations over further steps (events between consecutive steps),
+    # split by whether the step's append completes a page of some sequence (the
+    # step's last launch then also builds that page's summary)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(extra + 1)]
+    lens_at = [[int(x) for x in c.seq_lens.cpu().tolist()] for c in layers]
+    builds = []
+    evs[0].record(stream)
+    for j in range(extra):
+        i = total_steps + j
+        li = i % len(layers)
+        builds.append(any(T % B == B - 1 for T in lens_at[li]))
+        lens_at[li] = [T + 1 for T in lens_at[li]]
+        step(i)
+        evs[j + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([evs[j].elapsed_time(evs[j + 1]) * 1e3 for j in range(extra)])
+    with_b = np.array(builds)
+    in_stream = {"steps": extra, "steps_with_build": int(with_b.sum()),
+                 "us_median_without_build": float(np.median(per[~with_b])) if (~with_b).any() else None,
+                 "us_median_with_build": float(np.median(per[with_b])) if with_b.any() else None}
+
+    wl = {2: "128K-context decode, batch 4",
+          3: "1M-token decode, batch 1",
+          4: f"mixed-length decode, batch {w.batch}, lengths log-uniform in [4K, 256K] (seeded, mean "
+             f"{int(np.mean(w.context))} tokens)"}[args.workload]
+    result = {
+        "metric": "decode-attn steps/s and achieved HBM GB/s at 128K ctx, budget 2048 tok" if args.workload == 2
+                  else "decode-attn steps/s and achieved HBM GB/s",
+        "value": 1e3 / ms_per_step,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl + ", Llama-3.1-8B attention shape (32 q / 8 KV heads, d=128), "
+                        f"bf16 KV, page 64, rank {w.rank}, budget {w.token_budget} tokens; one step = lk_decode_step "
+                        "on one layer"
+                        + ("; int4 basis / int8 coefficient and centroid summaries" if args.summary == "i4" else ""),
+            "summary_records": "bf16" if args.summary == "kv" else "int4 basis, int8 coefficients and centroid",
+            "record_bytes": rec,
+            "global_batch": w.batch, "seq_len": w.context[0] if len(set(w.context)) == 1 else "mixed",
+            "page_size": B, "rank": w.rank,
+            "token_budget": w.token_budget, "num_q_heads": hq, "num_kv_heads": hkv, "layers_rotated": args.layers,
+            "parallelism": "single GPU",
+        },
+        "achieved_GBps": bytes_step / (ms_per_step * 1e-3) / 1e9,
+        "algorithmic_bytes_per_step": bytes_step,
+        "hbm_frac": bytes_step / (ms_per_step * 1e-3) / 8e12,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": ("score_mfma_kernel" if args.summary == "kv" else "score_q4_kernel") + " (reconstructed page LSE)",
+            "achieved": score_gbs,
+            "peak": 8000.0,
+            "unit": "GB/s",
+            "frac": score_gbs / 8000.0,
+            "traffic": recorded_traffic(TRAFFIC_PROFILE[args.summary]),
+            "launch_us": score_ms * 1e3,
+            "bytes_per_launch": score_bytes,
+        },
+        "dense_baseline": {"ms": dense_ms, "GBps": dense_bytes / (dense_ms * 1e-3) / 1e9,
+                           "speedup_of_locks_step": dense_ms / ms_per_step},
+        "bulk_build": {"pages": len(ids), "page_heads": len(ids) * hkv, "ms": build_ms,
+                       "page_heads_per_s": len(ids) * hkv / (build_ms * 1e-3)},
+        "in_stream_build": in_stream,
+    }
+    if page16 is not None:
+        result["bulk_build_page16_r8i4"] = page16
+
+    if args.copy_bytes:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters scale
+        # the scorer's counters to bytes
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = args.copy_bytes
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, lens_now, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def bulk_build_page16(L, w, bulk, reps, stream, ev0, ev1):
+    """The keys of every complete 64-token page re-paged into 16-token pages
+    and summarized in the int4 basis / int8 row format at r = 8, one
+    lk_build_page_summary call, timed over ``reps`` calls."""
+    import torch
+
+    dev, sp = "cuda", stream.cuda_stream
+    B, d, hkv, hq = w.page_size, w.head_dim, w.num_kv_heads, w.num_q_heads
     n_full = [w.context[s] // B for s in range(w.batch)]
     src = torch.cat([bulk.k_pool[torch.from_numpy(bulk.block_table_host[s, :n_full[s]].astype(np.int64)).to(dev)]
                      for s in range(w.batch)])
@@ -210,65 +313,8 @@ def main():
     build16_ms = ev0.elapsed_time(ev1) / reps
     pages16 = int(k16.shape[0])
     del k16, s16
-
-    result = {
-        "metric": "decode-attn steps/s and achieved HBM GB/s at 128K ctx, budget 2048 tok",
-        "value": 1e3 / ms_per_step,
-        "unit": "steps/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {
-            "workload": "128K-context decode, batch 4, Llama-3.1-8B attention shape (32 q / 8 KV heads, d=128), "
-                        "bf16 KV, page 64, rank 8, budget 2048 tokens; one step = lk_decode_step on one layer"
-                        + ("; int4 basis / int8 coefficient and centroid summaries" if args.summary == "i4" else ""),
-            "summary_records": "bf16" if args.summary == "kv" else "int4 basis, int8 coefficients and centroid",
-            "record_bytes": rec,
-            "global_batch": w.batch, "seq_len": w.context[0], "page_size": B, "rank": w.rank,
-            "token_budget": w.token_budget, "num_q_heads": hq, "num_kv_heads": hkv, "layers_rotated": args.layers,
-            "parallelism": "single GPU",
-        },
-        "achieved_GBps": bytes_step / (ms_per_step * 1e-3) / 1e9,
-        "algorithmic_bytes_per_step": bytes_step,
-        "hbm_frac": bytes_step / (ms_per_step * 1e-3) / 8e12,
-        "roofline": {
-            "bound": "hbm",
-            "kernel": ("score_mfma_kernel" if args.summary == "kv" else "score_q4_kernel") + " (reconstructed page LSE)",
-            "achieved": score_gbs,
-            "peak": 8000.0,
-            "unit": "GB/s",
-            "frac": score_gbs / 8000.0,
-            "traffic": recorded_traffic(TRAFFIC_PROFILE[args.summary]),
-            "launch_us": score_ms * 1e3,
-            "bytes_per_launch": score_bytes,
-        },
-        "dense_baseline": {"ms": dense_ms, "GBps": dense_bytes / (dense_ms * 1e-3) / 1e9,
-                           "speedup_of_locks_step": dense_ms / ms_per_step},
-        "bulk_build": {"pages": len(ids), "page_heads": len(ids) * hkv, "ms": build_ms,
-                       "page_heads_per_s": len(ids) * hkv / (build_ms * 1e-3)},
-        "bulk_build_page16_r8i4": {"pages": pages16, "page_heads": pages16 * hkv, "ms": build16_ms,
-                                   "page_heads_per_s": pages16 * hkv / (build16_ms * 1e-3)},
-    }
-
-    if args.copy_bytes:
-        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters scale
-        # the scorer's counters to bytes
-        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        result["copy_calibration_bytes"] = args.copy_bytes
-
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, lens_now, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+    return {"pages": pages16, "page_heads": pages16 * hkv, "ms": build16_ms,
+            "page_heads_per_s": pages16 * hkv / (build16_ms * 1e-3)}
 
 
 TRAFFIC_PROFILE = {"kv": "profiles/score_mfma_128K_b4_hbm_traffic.txt",
@@ -310,11 +356,16 @@ def cpu_baseline(w, lens_now, seconds):
     import reference as ref
 
     T = lens_now[0]
+    k = lo.page_budget(w.token_budget, w.page_size)
+    # per-pair oracle cost grows with the scored and attended pages: other
+    # lengths are scaled from the sampled pair by (n_mr + k)
+    n0 = lo.most_recent_page(T, w.page_size) + k
+    scale = sum(w.num_kv_heads * (lo.most_recent_page(t, w.page_size) + k) / n0 for t in lens_now)
     with threadpool_limits(limits=1):
         K, V = ref.host_pages(w, 0, 0, T)
         n_mr = lo.most_recent_page(T, w.page_size)
         summ = ref.oracle_summaries(w, K, n_mr)
-        q64 = ref.host_queries(w, 0, [T] * w.batch)[0, :w.group]
+        q64 = ref.stored(synth.queries(w, 0, 0, 0, T)[0], w.dtype)
         n, t0 = 0, time.perf_counter()
         while True:
             lo.decode_head(q64, K, V, T, summ, w.token_budget, w.scale)
@@ -324,9 +375,11 @@ def cpu_baseline(w, lens_now, seconds):
                 break
     per_pair = el / n
     pairs = w.batch * w.num_kv_heads
-    return {"value": 1.0 / (per_pair * pairs), "unit": "steps/s", "cores": 1, "kind": "oracle",
+    how = (f"scaled x{pairs} to one step" if len(set(lens_now)) == 1 else
+           f"scaled x{scale:.1f} to one step's {pairs} pairs by scored + attended pages")
+    return {"value": 1.0 / (per_pair * scale), "unit": "steps/s", "cores": 1, "kind": "oracle",
             "sample": f"1 of {pairs} (sequence, KV head) pairs at {T} tokens, {n} steps of score+share+select+"
-                      f"attend in fp64 ({el:.1f}s), scaled x{pairs} to one step; host has {os.cpu_count()} cores"}
+                      f"attend in fp64 ({el:.1f}s), {how}; host has {os.cpu_count()} cores"}
 
 
 if __name__ == "__main__":

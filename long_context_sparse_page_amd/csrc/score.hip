@@ -386,10 +386,12 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_mfma_kernel(ScoreAr
   const bf16_t* summ = reinterpret_cast<const bf16_t*>(a.summary);
   const int32_t* bt = a.block_table + (size_t)seq * a.max_pages;
 
-  // Loads that do not depend on the sequence length go out first: the
-  // wave's block-table slice (clamped in bounds), the group's queries, and
-  // then every record of the wave (pages past the sequence end are masked
-  // when results are written).
+  // The wave's block-table slice (clamped in bounds), the sequence length and
+  // the group's queries are requested first; a wave wholly past the scored
+  // pages (ragged batches: the grid covers max_pages for every sequence)
+  // leaves once the length is in, before any record load; the others then
+  // request every record of the wave at once (pages past the sequence end are
+  // masked when results are written).
   int phys_all[PAGES_PER_WAVE];
 #pragma unroll
   for (int x = 0; x < PAGES_PER_WAVE; ++x) phys_all[x] = bt[min(j0 + x, a.max_pages - 1)];
@@ -403,20 +405,18 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_mfma_kernel(ScoreAr
       qa[t] = __builtin_bit_cast(bf16x8_t,
                                  *reinterpret_cast<const uint4*>(q + (size_t)min(col, G - 1) * D + 32 * t + 8 * kg));
   }
+  int n_scored = len_raw <= 0 ? 0 : (len_raw - 1) / B;
+  if (n_scored > a.max_pages - 1) n_scored = a.max_pages - 1;
+  if (j0 >= n_scored) return;
   constexpr int GPW = ScoreGroup<R>::GROUPS_PER_WAVE;
   GroupLoads<R> grp[GPW];
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi)
     load_group<R>(grp[gi], summ, phys_all + gi * NR, a.num_phys, a.hkv, kvh, col, kg, lane);
   // The loads above have no side effects, so without this fence the compiler
-  // would move them below the length checks and between the products (each
-  // move adds a wait for earlier loads before later ones are issued).
+  // would move them between the products (each move adds a wait for earlier
+  // loads before later ones are issued).
   asm volatile("" ::: "memory");
-
-  if (len_raw <= 0) return;
-  int n_scored = (len_raw - 1) / B;
-  if (n_scored > a.max_pages - 1) n_scored = a.max_pages - 1;
-  if (j0 >= n_scored) return;
   const int j_end = min(j0 + PAGES_PER_WAVE, n_scored);
 
   const float zscale = a.scale * kLog2e;
@@ -552,8 +552,9 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
   const uint8_t* summ = reinterpret_cast<const uint8_t*>(a.summary);
   const int32_t* bt = a.block_table + (size_t)seq * a.max_pages;
 
-  // Loads that do not depend on the sequence length go out first (as for
-  // bf16 records): block-table slice, queries, then every record byte.
+  // Block-table slice, sequence length and queries first; waves wholly past
+  // the scored pages leave before any record load; then every record byte at
+  // once (as for bf16 records).
   int phys_all[NR];
 #pragma unroll
   for (int x = 0; x < NR; ++x) phys_all[x] = bt[min(j0 + x, a.max_pages - 1)];
@@ -565,6 +566,9 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
     for (int t = 0; t < 4; ++t)
       qw[t] = *reinterpret_cast<const uint4*>(q + (size_t)min(col, G - 1) * D + 32 * kg + 8 * t);
   }
+  int n_scored = len_raw <= 0 ? 0 : (len_raw - 1) / B;
+  if (n_scored > a.max_pages - 1) n_scored = a.max_pages - 1;
+  if (j0 >= n_scored) return;
   bool valid[NR];
   const uint8_t* recp[NR];
 #pragma unroll
@@ -613,11 +617,6 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
     csc[r] = *reinterpret_cast<const uint16_t*>(recp[r] + L.cscale() + 2 * lane);
   }
   asm volatile("" ::: "memory");  // keep the loads above in one batch (as for bf16 records)
-
-  if (len_raw <= 0) return;
-  int n_scored = (len_raw - 1) / B;
-  if (n_scored > a.max_pages - 1) n_scored = a.max_pages - 1;
-  if (j0 >= n_scored) return;
   const int j_end = min(j0 + NR, n_scored);
 
   const float zscale = a.scale * kLog2e;
