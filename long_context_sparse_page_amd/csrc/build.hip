@@ -351,7 +351,7 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
       const float x0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xk), k + 1));
       float u = 0.f, alpha = 0.f;
       if (nrm2 > 0.f) {
-        const float nrm = sqrtf(nrm2);
+        const float nrm = __builtin_amdgcn_sqrtf(nrm2);
         alpha = x0 >= 0.f ? -nrm : nrm;
         const float inv = __builtin_amdgcn_rsqf(2.f * (nrm2 + nrm * fabsf(x0)));  // 1 / ||x - alpha e_{k+1}||
         u = (lane == k + 1 ? xk - alpha : xk) * inv;
@@ -378,30 +378,36 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
       const float p = 2.f * ((sp4[buf][0][lane] + sp4[buf][1][lane]) + (sp4[buf][2][lane] + sp4[buf][3][lane]));
       const float Kup = group_sum<kWave>(ur * p);
       const float wr = lane > k ? p - Kup * ur : 0.f;
+      const int c = k + 1;
+      const bool more = c < B - 2;  // u_c exists (the last reflector is u_{B-3})
+      // the next reflector first: column c, brought up to date with this step,
+      // gives u_c (independent of this wave's own column updates below)
+      float un = 0.f;
+      if (more) {
+        if (k > 0) colnext = scol[buf][lane];
+        const float uc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ur), c));
+        const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wr), c));
+        colnext = colnext - (ur * wc + wr * uc);
+        if (wave == 0 && lane == c) sd[c] = colnext;
+        un = reflector(c, lane > c ? colnext : 0.f);
+      }
       if (live) {
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
           const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wr), q0 + t));
-          Ar[t] = Ar[t] - (ur * wj + wr * uj[t]);
+          Ar[t] = fmaf(-wr, uj[t], fmaf(-ur, wj, Ar[t]));
         }
       }
-      const int c = k + 1;
-      if (c >= B - 2) break;  // the last reflector was u_{B-3}
-      // column c, brought up to date with this step, gives u_c
-      if (k > 0) colnext = scol[buf][lane];
-      const float uc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ur), c));
-      const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wr), c));
-      colnext = colnext - (ur * wc + wr * uc);
-      if (wave == 0 && lane == c) sd[c] = colnext;
-      ur = reflector(c, lane > c ? colnext : 0.f);
+      if (!more) break;
+      ur = un;
 #pragma unroll
       for (int t = 0; t < 16; ++t) uj[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ur), q0 + t));
-      pp = 0.f;
+      float pq[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
       if (q0 + 15 > c) {
 #pragma unroll
-        for (int t = 0; t < 16; ++t) pp = fmaf(Ar[t], uj[t], pp);
+        for (int t = 0; t < 16; ++t) pq[t & 3] = fmaf(Ar[t], uj[t], pq[t & 3]);
       }
-      sp4[buf ^ 1][wave][lane] = pp;
+      sp4[buf ^ 1][wave][lane] = (pq[0] + pq[1]) + (pq[2] + pq[3]);
       if (c + 1 < B - 2 && wave == (c + 1) / 16) scol[buf ^ 1][lane] = Ar[c + 1 - q0];  // column c + 1, for the next step
       __syncthreads();
     }
