@@ -11,10 +11,11 @@
 // eigenproblem is solved the way one computes a few eigenpairs of a dense
 // symmetric matrix (Golub & Van Loan, Matrix Computations, ch. 8):
 //   1. Householder reduction to tridiagonal form T = Q^T A Q (62 reflections;
-//      the reflector vectors are kept in the strict lower part of A);
-//   2. the r largest eigenvalues of T by Sturm-sequence multisection (each of
-//      a wave's 64 lanes counts the eigenvalues below its own shift, so an
-//      interval shrinks 65-fold per pass);
+//      reflector k is kept as row k of the LDS copy of A);
+//   2. the r largest eigenvalues of T by Sturm-sequence multisection (a
+//      wave's eigenvalues at once on lane segments: each lane counts the
+//      eigenvalues below its own shift, so an interval shrinks (SL + 1)-fold
+//      per pass with SL lanes per eigenvalue);
 //   3. their eigenvectors of T by inverse iteration with partial pivoting,
 //      re-orthogonalized within clusters of close eigenvalues;
 //   4. back-transformation by the reflectors.
@@ -36,7 +37,7 @@ constexpr int kMergeThreads = 512;      // decode-step launch: one merged output
 constexpr int kBuildWaves = kBuildThreads / kWave;
 constexpr float kZeroModeRtol = 1e-5f;
 constexpr float kZeroModeFloor = 1e-10f;
-constexpr int kInvIters = 3;         // inverse-iteration passes per eigenvector
+constexpr int kInvIters = 2;         // inverse-iteration passes per eigenvector
 constexpr float kClusterTol = 1e-3f; // eigenvalues this close (relative to lambda_1) are re-orthogonalized
 
 // Decode step: combine the attention split partials of (seq, kvh) for its G
@@ -189,11 +190,11 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
   constexpr int KEPT = R < B ? R : B;
   constexpr int KW = (KEPT + kBuildWaves - 1) / kBuildWaves;  // eigenvectors per wave
   constexpr int LDT = 68;                  // D^T row stride (16-byte aligned rows)
-  constexpr int LA = B + 1;
+  constexpr int LA = B + 4;                // 16-byte aligned rows
   static_assert(KEPT <= 16, "rank above 16");
 
   __shared__ float sDT[D][LDT];            // D^T: sDT[c][i] = delta_i[c]
-  __shared__ float sA[B + 1][LA];          // Gram (+ a zero pad row); reflectors below the diagonal; later the basis
+  __shared__ __attribute__((aligned(16))) float sA[B + 1][LA];  // Gram; then reflector k in row k (zero in columns <= k); later the basis
   __shared__ float sMu[D];
   __shared__ float sd[B], se[B], se2[B];   // tridiagonal T (e[i] couples i, i + 1)
   __shared__ float sp4[2][kBuildWaves][B]; // partial sums of A u, one row per wave (by step parity)
@@ -325,8 +326,7 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
   // 4) Householder tridiagonalization with A in registers: wave q keeps
   //    columns 16 q .. 16 q + 15 of every row (lane = row).  Step k zeroes
   //    column k below the subdiagonal with H = I - 2 u u^T (||u|| = 1, u_r = 0
-  //    for r <= k; u is also stored below the diagonal of column k of sA for
-  //    the back-transformation).  With p = 2 A u (the sum of the four waves'
+  //    for r <= k; u is also stored as row k of sA for the back-transformation).  With p = 2 A u (the sum of the four waves'
   //    partial sums), K = u.p and w = p - K u (rows > k), every wave applies
   //    A <- A - u w^T - w u^T to its own columns.  One barrier per step: at
   //    it the waves exchange their partial sums of p and the owner of column
@@ -357,7 +357,7 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
         u = (lane == k + 1 ? xk - alpha : xk) * inv;
       }
       if (wave == 0) {
-        if (lane > k) sA[lane][k] = u;
+        sA[k][lane] = u;  // row k: u, zero in columns <= k
         if (lane == 0) se[k] = alpha;
       }
       return u;
@@ -556,28 +556,38 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
   }
   __syncthreads();
 
-  // 7) back-transformation y = H_0 H_1 ... H_{B-3} z (lane = row; wave w
-  //    takes eigenvectors w, w + 4, ...)
+  // 7) back-transformation y = H_0 H_1 ... H_{B-3} z: eight eigenvectors per
+  //    wave, lane 8 v + b holding rows 8 b .. 8 b + 7 of eigenvector 8 w + v,
+  //    so each reflector costs a partial dot product of 8 rows and a sum over
+  //    8 lanes; reflector k is row k of sA (16-byte reads)
   {
-    float y[KW];
+    constexpr int VW = 8;
+    const int v = lane >> 3, b = lane & 7;
+    const int kk = VW * wave + v;
+    const bool act = VW * wave < KEPT;  // uniform
+    float y[8];
+    if (act) {
 #pragma unroll
-    for (int s = 0; s < KW; ++s) {
-      const int kk = wave + kBuildWaves * s;
-      y[s] = kk < KEPT ? sZ[lane][kk] : 0.f;
-    }
-    for (int k = B - 3; k >= 0; --k) {
-      const float u = lane > k ? sA[lane][k] : 0.f;
+      for (int i = 0; i < 8; ++i) y[i] = kk < KEPT ? sZ[8 * b + i][kk] : 0.f;
+      for (int k = B - 3; k >= 0; --k) {
+        const float4 ua = *reinterpret_cast<const float4*>(&sA[k][8 * b]);
+        const float4 ub = *reinterpret_cast<const float4*>(&sA[k][8 * b + 4]);
+        const float u[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
+        float d0 = 0.f, d1 = 0.f;
 #pragma unroll
-      for (int s = 0; s < KW; ++s) {
-        const float dot = group_sum<kWave>(u * y[s]);
-        y[s] = fmaf(-2.f * dot, u, y[s]);
+        for (int i = 0; i < 8; i += 2) {
+          d0 = fmaf(u[i], y[i], d0);
+          d1 = fmaf(u[i + 1], y[i + 1], d1);
+        }
+        const float f = -2.f * group_sum<VW>(d0 + d1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = fmaf(f, u[i], y[i]);
       }
     }
-    __syncthreads();  // every wave is done with the reflectors and sZ
+    __syncthreads();  // every wave is done with sZ
+    if (act && kk < KEPT) {
 #pragma unroll
-    for (int s = 0; s < KW; ++s) {
-      const int kk = wave + kBuildWaves * s;
-      if (kk < KEPT) sZ[lane][kk] = y[s];
+      for (int i = 0; i < 8; ++i) sZ[8 * b + i][kk] = y[i];
     }
   }
 
