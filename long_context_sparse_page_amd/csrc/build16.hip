@@ -17,6 +17,15 @@
 // rotated diagonal pair set to a_pp - t a_pq, a_qq + t a_pq and a_pq to 0.
 // Sweeps stop once the off-diagonal energy is below 1e-13 of the total, or
 // after 12.
+//
+// The rounds are bound by LDS latency, so the wave keeps little else in LDS
+// (about 6 KB: the 16 x 16 matrices, the centroid, a round's rotations) and
+// many waves share a CU.  The key tile is read twice, both times straight
+// into registers: in the matrix-core operand layout for the Gram (the
+// centroid of a lane's dimensions is a sum over the 16 lanes of its DPP row,
+// which hold those dimensions of the 16 tokens) and, from L2, with two
+// dimensions per lane for the basis, which is formed, signed and written from
+// registers.
 
 #include "common.cuh"
 #include "kernels.h"
@@ -25,13 +34,23 @@ namespace lk {
 
 constexpr int kB16 = 16;
 constexpr int kB16Waves = 4;
-constexpr int kB16Ld = 17;   // padded row of the 16 x 16 matrices
-constexpr int kB16DLd = 132; // padded row of D (16 x 128)
+constexpr int kB16Ld = 17;  // padded row of the 16 x 16 matrices
 
 __device__ __forceinline__ float b16_q_scale(float amax, float levels) { return (float)(_Float16)(amax / levels); }
 __device__ __forceinline__ int b16_q_code(float x, float s, float levels) {
   if (!(s > 0.f)) return 0;
   return (int)fminf(fmaxf(rintf(x / s), -levels), levels);
+}
+// two consecutive elements
+__device__ __forceinline__ void load2(const bf16_t* p, float& a, float& b) {
+  const uint32_t v = *reinterpret_cast<const uint32_t*>(p);
+  a = bf16_lo(v);
+  b = bf16_hi(v);
+}
+__device__ __forceinline__ void load2(const float* p, float& a, float& b) {
+  const float2 v = *reinterpret_cast<const float2*>(p);
+  a = v.x;
+  b = v.y;
 }
 
 template <typename T, int R>
@@ -39,69 +58,69 @@ __global__ __launch_bounds__(kB16Waves * kWave) void build16_kernel(BuildArgs a)
   constexpr int B = kB16;
   constexpr int D = kHeadDim;
   constexpr int KEPT = R < B ? R : B;
-  __shared__ float sD[kB16Waves][B][kB16DLd];       // centred keys, row i = delta_i
-  __shared__ float sA[kB16Waves][2][B][kB16Ld];     // Gram / rotated matrix (ping-pong)
-  __shared__ float sU[kB16Waves][2][B][kB16Ld];     // accumulated rotations
+  __shared__ float sA[kB16Waves][2][B][kB16Ld];   // Gram / rotated matrix (ping-pong)
+  __shared__ float sU[kB16Waves][2][B][kB16Ld];   // accumulated rotations
   __shared__ float sMu[kB16Waves][D];
-  __shared__ float sRot[kB16Waves][B][2];           // per index: J[i][i], J[partner][i]
+  __shared__ float sRot[kB16Waves][B][2];         // per index: J[i][i], J[partner][i]
   __shared__ int sPart[kB16Waves][B];
-  __shared__ float sV[kB16Waves][KEPT][D];          // basis rows (before the sign)
+  __shared__ int sOrder[kB16Waves][B];
+  __shared__ float sLam[kB16Waves][B];
   __shared__ float sSign[kB16Waves][KEPT];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int item = blockIdx.x * kB16Waves + wave;   // (page, KV head) pair
+  const int item = blockIdx.x * kB16Waves + wave;  // (page, KV head) pair
   if (item >= a.n * a.hkv) return;
   const int idx = item / a.hkv, kvh = item % a.hkv;
   const int phys = a.phys_ids[idx];
   if (phys < 0 || phys >= a.num_phys) return;
-
-  // 1) K tile (16 x 128), energy sum ||k_i||^2, centroid, centring
   const T* K = reinterpret_cast<const T*>(a.k_pool) + (((size_t)phys * a.hkv + kvh) * B) * D;
+
+  // 1) Gram operand layout: lane (row col, kg) holds dims 32 t + 8 kg .. +7 of
+  //    row col for the K-steps t; the basis layout: dims 2 lane, 2 lane + 1 of
+  //    every row (requested now, used after the eigensolver)
+  const int col = lane & 15, kg = lane >> 4;
+  float x[4][8];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) load8(K + (size_t)col * D + 32 * t + 8 * kg, x[t]);
+  float db[B][2];
+#pragma unroll
+  for (int i = 0; i < B; ++i) load2(K + (size_t)i * D + 2 * lane, db[i][0], db[i][1]);
+
+  // energy sum_i ||k_i||^2; centroid (a sum over the 16 lanes of a DPP row);
+  // centring
   float en = 0.f;
 #pragma unroll
-  for (int x = 0; x < B * D / kWave / 8; ++x) {  // 4 chunks of 8 elements per lane
-    const int e = (lane + kWave * x) * 8;
-    const int row = e / D, c0 = e % D;
-    float v[8];
-    load8(K + (size_t)row * D + c0, v);
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) { sD[wave][row][c0 + t] = v[t]; en = fmaf(v[t], v[t], en); }
-  }
+    for (int e = 0; e < 8; ++e) en = fmaf(x[t][e], x[t][e], en);
   const float energy = group_sum<kWave>(en);
-  wave_lds_fence();
 #pragma unroll
-  for (int x = 0; x < D / kWave; ++x) {
-    const int c = lane + kWave * x;
-    float s = 0.f;
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int i = 0; i < B; ++i) s += sD[wave][i][c];
-    const float mu = s * (1.0f / B);
-    sMu[wave][c] = mu;
-#pragma unroll
-    for (int i = 0; i < B; ++i) sD[wave][i][c] -= mu;
-  }
-  wave_lds_fence();
+    for (int e = 0; e < 8; ++e) {
+      const float mu = group_sum<16>(x[t][e]) * (1.0f / B);
+      if (col == 0) sMu[wave][32 * t + 8 * kg + e] = mu;
+      x[t][e] -= mu;
+    }
 
-  // 2) Gram on the matrix cores: A = B = rows of D (lane (col, kg), K-step t:
-  //    dims 32 t + 8 kg .. +7), three bf16 terms per entry
+  // 2) Gram D D^T on the matrix cores: three bf16 terms per entry
   {
-    const int col = lane & 15, kg = lane >> 4;
     bf16x8_t op[4][3];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       uint32_t w[3][4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        float x[2] = {sD[wave][col][32 * t + 8 * kg + 2 * p], sD[wave][col][32 * t + 8 * kg + 2 * p + 1]};
+        float v2[2] = {x[t][2 * p], x[t][2 * p + 1]};
         uint32_t h[3][2];
 #pragma unroll
         for (int e = 0; e < 2; ++e)
 #pragma unroll
           for (int q = 0; q < 3; ++q) {
-            const __bf16 v = (__bf16)x[e];
+            const __bf16 v = (__bf16)v2[e];
             h[q][e] = __builtin_bit_cast(uint16_t, v);
-            x[e] -= (float)v;  // exact: the remainder of a bf16 rounding
+            v2[e] -= (float)v;  // exact: the remainder of a bf16 rounding
           }
 #pragma unroll
         for (int q = 0; q < 3; ++q) w[q][p] = h[q][0] | (h[q][1] << 16);
@@ -129,8 +148,8 @@ __global__ __launch_bounds__(kB16Waves * kWave) void build16_kernel(BuildArgs a)
     }
     // U = I
 #pragma unroll
-    for (int x = 0; x < B * B / kWave; ++x) {
-      const int e = lane + kWave * x;
+    for (int y = 0; y < B * B / kWave; ++y) {
+      const int e = lane + kWave * y;
       sU[wave][0][e / B][e % B] = (e / B == e % B) ? 1.f : 0.f;
     }
   }
@@ -142,8 +161,8 @@ __global__ __launch_bounds__(kB16Waves * kWave) void build16_kernel(BuildArgs a)
   for (int sweep = 0; sweep < 12; ++sweep) {
     float off = 0.f, tot = 0.f;
 #pragma unroll
-    for (int x = 0; x < B * B / kWave; ++x) {
-      const int e = lane + kWave * x;
+    for (int y = 0; y < B * B / kWave; ++y) {
+      const int e = lane + kWave * y;
       const float v = sA[wave][cur][e / B][e % B];
       tot = fmaf(v, v, tot);
       if (e / B != e % B) off = fmaf(v, v, off);
@@ -176,8 +195,8 @@ __global__ __launch_bounds__(kB16Waves * kWave) void build16_kernel(BuildArgs a)
       // A' = J^T A J (entry (a, b) with a <= b, mirrored), U' = U J
       const int nxt = cur ^ 1;
 #pragma unroll
-      for (int x = 0; x < B * B / kWave; ++x) {
-        const int e = lane + kWave * x;
+      for (int y = 0; y < B * B / kWave; ++y) {
+        const int e = lane + kWave * y;
         const int i = e / B, j = e % B;
         const int ia = min(i, j), jb = max(i, j);
         const int pa = sPart[wave][ia], pb = sPart[wave][jb];
@@ -202,9 +221,7 @@ __global__ __launch_bounds__(kB16Waves * kWave) void build16_kernel(BuildArgs a)
   }
 
   // 4) eigenvalues (diagonal), descending order by rank counting (ties to the
-  //    lower index); the kept modes' indices
-  __shared__ int sOrder[kB16Waves][B];
-  __shared__ float sLam[kB16Waves][B];
+  //    lower index)
   if (lane < B) {
     const float li = sA[wave][cur][lane][lane];
     int rank = 0;
@@ -221,32 +238,31 @@ __global__ __launch_bounds__(kB16Waves * kWave) void build16_kernel(BuildArgs a)
   const float thresh = fmaxf(1e-5f * lam1, 1e-10f * energy);
   if (a.eigvals_out && lane < B) a.eigvals_out[((size_t)idx * a.hkv + kvh) * B + lane] = fmaxf(sLam[wave][lane], 0.f);
 
-  // 5) basis V[k][c] = sum_i D[i][c] U[i][idx_k] / sigma_k, then signs
+  // 5) basis rows V[k][c] = sum_i D[i][c] U[i][idx_k] / sigma_k for this lane's
+  //    dims c = 2 lane, 2 lane + 1, then the signs (largest |entry| positive,
+  //    ties to the lower dim)
+  const float mu0 = sMu[wave][2 * lane], mu1 = sMu[wave][2 * lane + 1];
+#pragma unroll
+  for (int i = 0; i < B; ++i) { db[i][0] -= mu0; db[i][1] -= mu1; }
+  float vb[KEPT][2];
 #pragma unroll
   for (int k = 0; k < KEPT; ++k) {
     const int ik = sOrder[wave][k];
     const bool nz = lam1 > 0.f && sLam[wave][k] > thresh;
     const float inv = nz ? 1.f / sqrtf(sLam[wave][k]) : 0.f;
+    float v0 = 0.f, v1 = 0.f;
 #pragma unroll
-    for (int x = 0; x < D / kWave; ++x) {
-      const int c = lane + kWave * x;
-      float v = 0.f;
-#pragma unroll
-      for (int i = 0; i < B; ++i) v = fmaf(sD[wave][i][c], sU[wave][cur][i][ik], v);
-      sV[wave][k][c] = v * inv;
+    for (int i = 0; i < B; ++i) {
+      const float uik = sU[wave][cur][i][ik];
+      v0 = fmaf(db[i][0], uik, v0);
+      v1 = fmaf(db[i][1], uik, v1);
     }
-  }
-  wave_lds_fence();
-#pragma unroll
-  for (int k = 0; k < KEPT; ++k) {
-    float best = -1.f, val = 0.f;
-    int bidx = D;
-#pragma unroll
-    for (int x = 0; x < D / kWave; ++x) {
-      const int c = lane + kWave * x;
-      const float v = sV[wave][k][c];
-      if (fabsf(v) > best || (fabsf(v) == best && c < bidx)) { best = fabsf(v); val = v; bidx = c; }
-    }
+    v0 *= inv;
+    v1 *= inv;
+    // this lane's candidate: the larger |entry| of its two dims (ties: the lower)
+    float best = fabsf(v0), val = v0;
+    int bidx = 2 * lane;
+    if (fabsf(v1) > best) { best = fabsf(v1); val = v1; bidx = 2 * lane + 1; }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
       const float b2 = __shfl_xor(best, o);
@@ -254,10 +270,12 @@ __global__ __launch_bounds__(kB16Waves * kWave) void build16_kernel(BuildArgs a)
       const int i2 = __shfl_xor(bidx, o);
       if (b2 > best || (b2 == best && i2 < bidx)) { best = b2; val = v2; bidx = i2; }
     }
-    if (lane == 0) sSign[wave][k] = val < 0.f ? -1.f : 1.f;
+    const float sg = val < 0.f ? -1.f : 1.f;
+    vb[k][0] = v0 * sg;
+    vb[k][1] = v1 * sg;
+    if (lane == 0) sSign[wave][k] = sg;
   }
   wave_lds_fence();
-  auto basis_at = [&](int k, int c) { return k < KEPT ? sV[wave][k][c] * sSign[wave][k] : 0.f; };
   auto coef_at = [&](int i, int k) -> float {
     if (k >= KEPT) return 0.f;
     const bool nz = lam1 > 0.f && sLam[wave][k] > thresh;
@@ -268,51 +286,43 @@ __global__ __launch_bounds__(kB16Waves * kWave) void build16_kernel(BuildArgs a)
   if (!a.q4) {
     constexpr int REC = D + R * D + B * R;
     T* rec = reinterpret_cast<T*>(a.summary) + ((size_t)phys * a.hkv + kvh) * REC;
-    for (int x = lane; x < REC; x += kWave) {
-      float v;
-      if (x < D) v = sMu[wave][x];
-      else if (x < D + R * D) v = basis_at((x - D) / D, (x - D) % D);
-      else v = coef_at((x - D - R * D) / R, (x - D - R * D) % R);
-      Elem<T>::store(rec + x, v);
+    Elem<T>::store(rec + 2 * lane, mu0);
+    Elem<T>::store(rec + 2 * lane + 1, mu1);
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      Elem<T>::store(rec + D + k * D + 2 * lane, k < KEPT ? vb[k][0] : 0.f);
+      Elem<T>::store(rec + D + k * D + 2 * lane + 1, k < KEPT ? vb[k][1] : 0.f);
     }
+    for (int y = lane; y < B * R; y += kWave) Elem<T>::store(rec + D + R * D + y, coef_at(y / R, y % R));
     return;
   }
-  // int4 basis / int8 coefficients and centroid (same rule as the 64-token builder)
+  // int4 basis / int8 coefficients and centroid (the 64-token builder's rule)
   constexpr Q4Layout L{R, B};
   uint8_t* rec = reinterpret_cast<uint8_t*>(a.summary) + ((size_t)phys * a.hkv + kvh) * L.bytes();
-  float bsc[R];
+  const float msc = b16_q_scale(group_max<kWave>(fmaxf(fabsf(mu0), fabsf(mu1))), 127.f);
+  rec[2 * lane] = (uint8_t)(int8_t)b16_q_code(mu0, msc, 127.f);
+  rec[2 * lane + 1] = (uint8_t)(int8_t)b16_q_code(mu1, msc, 127.f);
+  float bsc_lane = 0.f;  // lane k < R: basis row k's scale
 #pragma unroll
-  for (int k = 0; k < R; ++k)
-    bsc[k] = b16_q_scale(group_max<kWave>(fmaxf(fabsf(basis_at(k, lane)), fabsf(basis_at(k, lane + kWave)))), 7.f);
-  const float msc = b16_q_scale(group_max<kWave>(fmaxf(fabsf(sMu[wave][lane]), fabsf(sMu[wave][lane + kWave]))), 127.f);
-  float csc = 0.f;  // lane i < B: token i's coefficient scale
+  for (int k = 0; k < R; ++k) {
+    const float v0 = k < KEPT ? vb[k][0] : 0.f, v1 = k < KEPT ? vb[k][1] : 0.f;
+    const float bs = b16_q_scale(group_max<kWave>(fmaxf(fabsf(v0), fabsf(v1))), 7.f);
+    const int lo = b16_q_code(v0, bs, 7.f), hi = b16_q_code(v1, bs, 7.f);
+    rec[L.basis() + k * (D / 2) + lane] = (uint8_t)((lo & 0xF) | ((hi & 0xF) << 4));
+    if (lane == k) bsc_lane = bs;
+  }
   if (lane < B) {
     float m = 0.f;
 #pragma unroll
     for (int k = 0; k < R; ++k) m = fmaxf(m, fabsf(coef_at(lane, k)));
-    csc = b16_q_scale(m, 127.f);
-  }
-  for (int x = lane; x < D; x += kWave) rec[x] = (uint8_t)(int8_t)b16_q_code(sMu[wave][x], msc, 127.f);
-#pragma unroll
-  for (int k = 0; k < R; ++k) {
-    const int c = 2 * lane;  // D / 2 = 64 bytes per row: one per lane
-    const int lo = b16_q_code(basis_at(k, c), bsc[k], 7.f), hi = b16_q_code(basis_at(k, c + 1), bsc[k], 7.f);
-    rec[L.basis() + k * (D / 2) + lane] = (uint8_t)((lo & 0xF) | ((hi & 0xF) << 4));
-  }
-  if (lane < B) {
+    const float csc = b16_q_scale(m, 127.f);
 #pragma unroll
     for (int k = 0; k < R; ++k) rec[L.coef() + lane * R + k] = (uint8_t)(int8_t)b16_q_code(coef_at(lane, k), csc, 127.f);
     reinterpret_cast<uint16_t*>(rec + L.cscale())[lane] = __builtin_bit_cast(uint16_t, (_Float16)csc);
   }
-  if (lane < R) {
-    float s = bsc[0];
-#pragma unroll
-    for (int k = 1; k < R; ++k)
-      if (lane == k) s = bsc[k];
-    reinterpret_cast<uint16_t*>(rec + L.bscale())[lane] = __builtin_bit_cast(uint16_t, (_Float16)s);
-  }
+  if (lane < R) reinterpret_cast<uint16_t*>(rec + L.bscale())[lane] = __builtin_bit_cast(uint16_t, (_Float16)bsc_lane);
   if (lane == 0) *reinterpret_cast<uint16_t*>(rec + L.mscale()) = __builtin_bit_cast(uint16_t, (_Float16)msc);
-  for (int x = L.mscale() + 2 + lane; x < L.bytes(); x += kWave) rec[x] = 0;
+  for (int y = L.mscale() + 2 + lane; y < L.bytes(); y += kWave) rec[y] = 0;
 }
 
 template <typename T>
