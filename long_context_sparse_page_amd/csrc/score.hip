@@ -45,12 +45,13 @@ __device__ __forceinline__ void load_coeffs(const T* p, float (&c)[R]) {
   }
 }
 
-// Decode-step cache append (AppendDuty), done by workgroup x = 0 of every
-// (sequence, KV head) before anything else: 16-byte copies of the new key and
-// value rows into slot T mod B of page T / B, and the build-list entry.
+// Decode-step cache append (AppendDuty), done by the workgroup of page chunk
+// 0 of every (sequence, KV head) before anything else: 16-byte copies of the
+// new key and value rows into slot T mod B of page T / B, and the build-list
+// entry.
 template <typename T>
-__device__ __forceinline__ void append_duty(const ScoreArgs& a, int seq, int kvh) {
-  if (a.app.k_new == nullptr || blockIdx.x != 0) return;
+__device__ __forceinline__ void append_duty(const ScoreArgs& a, int seq, int kvh, int chunk) {
+  if (a.app.k_new == nullptr || chunk != 0) return;
   constexpr int B = 64;
   constexpr int D = kHeadDim;
   constexpr int VEC = 16 / sizeof(T);
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_kernel(ScoreArgs a)
   const int wave = threadIdx.x / kWave;
   const int seq = blockIdx.z;
   const int kvh = blockIdx.y;
-  append_duty<T>(a, seq, kvh);
+  append_duty<T>(a, seq, kvh, blockIdx.x);
   const int len = a.seq_lens[seq] + a.len_add;
   if (len <= 0) return;
   int n_scored = (len - 1) / B;
@@ -376,10 +377,12 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_mfma_kernel(ScoreAr
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar table loads
+  // grid (KV head, page chunk, sequence): the KV heads of a page, whose
+  // records sit side by side, are dispatched together
   const int seq = blockIdx.z;
-  const int kvh = blockIdx.y;
-  append_duty<bf16_t>(a, seq, kvh);
-  const int j0 = (blockIdx.x * kScoreWaves + wave) * PAGES_PER_WAVE;
+  const int kvh = blockIdx.x;
+  append_duty<bf16_t>(a, seq, kvh, blockIdx.y);
+  const int j0 = (blockIdx.y * kScoreWaves + wave) * PAGES_PER_WAVE;
   if (j0 >= a.max_pages) return;
   const int col = lane & 15;       // B column / A row of this lane
   const int kg = lane >> 4;        // K group (8 dims) within a K-step
@@ -458,7 +461,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_mfma_kernel(ScoreAr
 template <int R>
 static hipError_t launch_score_mfma(int group, const ScoreArgs& a, hipStream_t s) {
   constexpr int per_block = kScoreWaves * ScoreGroup<R>::GROUPS_PER_WAVE * ScoreGroup<R>::NR;
-  dim3 grid((a.max_pages + per_block - 1) / per_block, a.hkv, a.batch);
+  dim3 grid(a.hkv, (a.max_pages + per_block - 1) / per_block, a.batch);
   dim3 block(kScoreWaves * kWave);
   switch (group) {
     case 1: hipLaunchKernelGGL((score_mfma_kernel<R, 1>), grid, block, 0, s, a); break;
@@ -543,9 +546,9 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int seq = blockIdx.z;
-  const int kvh = blockIdx.y;
-  append_duty<bf16_t>(a, seq, kvh);
-  const int j0 = (blockIdx.x * kScoreWaves + wave) * NR;
+  const int kvh = blockIdx.x;  // grid (KV head, page chunk, sequence), as for bf16 records
+  append_duty<bf16_t>(a, seq, kvh, blockIdx.y);
+  const int j0 = (blockIdx.y * kScoreWaves + wave) * NR;
   if (j0 >= a.max_pages) return;
   const int col = lane & 15;
   const int kg = lane >> 4;
@@ -682,7 +685,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
 template <int R>
 static hipError_t launch_score_q4(int group, const ScoreArgs& a, hipStream_t s) {
   constexpr int per_block = kScoreWaves * Q4Group<R>::NR;
-  dim3 grid((a.max_pages + per_block - 1) / per_block, a.hkv, a.batch);
+  dim3 grid(a.hkv, (a.max_pages + per_block - 1) / per_block, a.batch);
   dim3 block(kScoreWaves * kWave);
   switch (group) {
     case 1: hipLaunchKernelGGL((score_q4_kernel<R, 1>), grid, block, 0, s, a); break;
