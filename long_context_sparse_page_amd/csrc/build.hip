@@ -199,7 +199,7 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
   __shared__ float sd[B], se[B], se2[B];   // tridiagonal T (e[i] couples i, i + 1)
   __shared__ float sp4[2][kBuildWaves][B]; // partial sums of A u, one row per wave (by step parity)
   __shared__ float scol[2][B];             // the column after next, published by its owner
-  __shared__ float sRed[2][kBuildWaves];
+  __shared__ float sRed[kBuildWaves];
   __shared__ float sLam[KEPT];             // top eigenvalues, descending
   __shared__ float sZ[B][KEPT];            // eigenvectors (of T, then of A)
   __shared__ float4 sF[B][KEPT];           // inverse-iteration factors, one float4 per row
@@ -240,11 +240,11 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
     for (int t = 0; t < 8; ++t) { sDT[c0 + t][row] = v[t]; en = fmaf(v[t], v[t], en); }
   }
   en = group_sum<kWave>(en);
-  if (lane == 0) sRed[0][wave] = en;
+  if (lane == 0) sRed[wave] = en;
   __syncthreads();
   float energy = 0.f;
 #pragma unroll
-  for (int w = 0; w < kBuildWaves; ++w) energy += sRed[0][w];
+  for (int w = 0; w < kBuildWaves; ++w) energy += sRed[w];
 
   // 2) centroid and centring
   if (tid < D) {
