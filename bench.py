@@ -59,7 +59,9 @@ def main():
     dev = "cuda"
     total_steps = args.warmup + args.steps
     per_layer = -(-total_steps // args.layers)
-    extra = 64  # further steps timed one by one (in-stream build split, below)
+    # further steps timed one by one (in-stream build split, below): a page per
+    # layer copy, so each copy's sequences complete exactly one page in them
+    extra = synth.workload(args.workload).page_size * args.layers
     w = synth.workload(args.workload, steps=per_layer + 1 + -(-extra // args.layers), summary=args.summary)
     B, d, G, hkv, hq = w.page_size, w.head_dim, w.group, w.num_kv_heads, w.num_q_heads
     e = 2  # bf16

@@ -20,9 +20,10 @@
 //      re-orthogonalized within clusters of close eigenvalues;
 //   4. back-transformation by the reflectors.
 // All B eigenvalues (for the optional eigenvalue output) are found by plain
-// bisection, one lane per eigenvalue.  The K tile is widened to fp32 and
-// centred in LDS, stored transposed (D^T); the Gram D D^T runs on the matrix
-// cores with each fp32 entry split into three bf16 terms.
+// bisection, one lane per eigenvalue.  The K tile takes no LDS: it is read
+// from global memory (then L2) where it is needed, for the centroid, as the
+// Gram's operands and for the basis, and centred in registers; the Gram D D^T
+// runs on the matrix cores with each fp32 entry split into three bf16 terms.
 //
 // Zero-mode rule: eigenvalue <= 1e-5 * lambda_1 or <= 1e-10 * sum_i ||k_i||^2.
 // Sign rule: each basis vector's largest-magnitude entry is made positive.
@@ -189,11 +190,10 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
   constexpr int D = kHeadDim;
   constexpr int KEPT = R < B ? R : B;
   constexpr int KW = (KEPT + kBuildWaves - 1) / kBuildWaves;  // eigenvectors per wave
-  constexpr int LDT = 68;                  // D^T row stride (16-byte aligned rows)
   constexpr int LA = B + 4;                // 16-byte aligned rows
   static_assert(KEPT <= 16, "rank above 16");
 
-  __shared__ float sDT[D][LDT];            // D^T: sDT[c][i] = delta_i[c]
+  __shared__ float sHalf[2][D];            // column sums of K over rows 0..31 and 32..63
   __shared__ __attribute__((aligned(16))) float sA[B + 1][LA];  // Gram; then reflector k in row k (zero in columns <= k); later the basis
   __shared__ float sMu[D];
   __shared__ float sd[B], se[B], se2[B];   // tridiagonal T (e[i] couples i, i + 1)
@@ -226,58 +226,48 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
   if (tid >= kBuildThreads) return;
   if (phys < 0 || phys >= a.num_phys) return;
 
-  // 1) load K (32 elements per thread), energy sum ||k_i||^2, transpose into LDS
+  // 1) centroid and energy sum ||k_i||^2 straight from the K tile: thread
+  //    (column c, half h) sums rows 32 h .. 32 h + 31 of column c (the tile is
+  //    read again from L2 where D is needed, so it takes no LDS)
   const T* K = reinterpret_cast<const T*>(a.k_pool) + (((size_t)phys * a.hkv + kvh) * B) * D;
-  float en = 0.f;
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int x = tid + kBuildThreads * it;
-    const int row = x >> 4;
-    const int c0 = (x & 15) * 8;
-    float v[8];
-    load8(K + (size_t)row * D + c0, v);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) { sDT[c0 + t][row] = v[t]; en = fmaf(v[t], v[t], en); }
+  {
+    const int c = tid & (D - 1), h = tid >> 7;
+    float sum = 0.f, en = 0.f;
+#pragma unroll 8
+    for (int i = 0; i < B / 2; ++i) {
+      const float v = Elem<T>::load(K + (size_t)(32 * h + i) * D + c);
+      sum += v;
+      en = fmaf(v, v, en);
+    }
+    sHalf[h][c] = sum;
+    en = group_sum<kWave>(en);
+    if (lane == 0) sRed[wave] = en;
   }
-  en = group_sum<kWave>(en);
-  if (lane == 0) sRed[wave] = en;
   __syncthreads();
   float energy = 0.f;
 #pragma unroll
   for (int w = 0; w < kBuildWaves; ++w) energy += sRed[w];
-
-  // 2) centroid and centring
-  if (tid < D) {
-    float s = 0.f;
-    for (int i = 0; i < B; ++i) s += sDT[tid][i];
-    sMu[tid] = s * (1.0f / B);
-  }
-  __syncthreads();
-  {
-    const int c = tid >> 1;
-    const int i0 = (tid & 1) * (B / 2);
-    const float mu = sMu[c];
-#pragma unroll
-    for (int i = 0; i < B / 2; ++i) sDT[c][i0 + i] -= mu;
-  }
+  if (tid < D) sMu[tid] = (sHalf[0][tid] + sHalf[1][tid]) * (1.0f / B);
   __syncthreads();
 
-  // 3) Gram A = D D^T on the matrix cores (v_mfma_f32_16x16x32_bf16): each
+  // 2) Gram A = D D^T on the matrix cores (v_mfma_f32_16x16x32_bf16): each
   //    fp32 entry of D is the sum of three bf16 terms d1 + d2 + d3 (each the
   //    bf16 rounding of what the previous ones leave), and the six products
   //    d_a d_b^T with a + b <= 4 are accumulated in fp32 (the dropped ones lie
-  //    below fp32 rounding).  Wave w computes the 16 x 16 tiles (w, J); tiles
-  //    with w <= J are written with their mirror images (on diagonal tiles the
-  //    entries with row <= col), so the Gram is exactly symmetric.
+  //    below fp32 rounding).  Wave w computes the 16 x 16 tiles (w, J) for
+  //    J >= w and writes them with their mirror images (on diagonal tiles the
+  //    entries with row <= col), so the Gram is exactly symmetric.  The rows
+  //    come straight from the K tile (L2), centred with the centroid.
   {
     const int col = lane & 15, kg = lane >> 4;
-    // operand of K-step t for row `row`: dims 32 t + 8 kg .. +7, three bf16 terms
-    auto split_operand = [&](int row, int t, bf16x8_t (&o)[3]) {
+    // operand of K-step t from K's dims 32 t + 8 kg .. +7 of one row: the
+    // centred values as three bf16 terms
+    auto split_operand = [&](const float (&k8)[8], int t, bf16x8_t (&o)[3]) {
       uint32_t w[3][4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const int c = 32 * t + 8 * kg + 2 * p;
-        float x[2] = {sDT[c][row], sDT[c + 1][row]};
+        float x[2] = {k8[2 * p] - sMu[c], k8[2 * p + 1] - sMu[c + 1]};
         uint32_t h[3][2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
@@ -295,14 +285,22 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
       for (int q = 0; q < 3; ++q) o[q] = __builtin_bit_cast(bf16x8_t, make_uint4(w[q][0], w[q][1], w[q][2], w[q][3]));
     };
     bf16x8_t ar[4][3];
+    {
+      float k8[4][8];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) split_operand(16 * wave + col, t, ar[t]);
-    for (int J = 0; J < 4; ++J) {
+      for (int t = 0; t < 4; ++t) load8(K + (size_t)(16 * wave + col) * D + 32 * t + 8 * kg, k8[t]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) split_operand(k8[t], t, ar[t]);
+    }
+    for (int J = wave; J < 4; ++J) {
+      float k8[4][8];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) load8(K + (size_t)(16 * J + col) * D + 32 * t + 8 * kg, k8[t]);
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         bf16x8_t br[3];
-        split_operand(16 * J + col, t, br);
+        split_operand(k8[t], t, br);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[t][0], br[0], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[t][0], br[1], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[t][1], br[0], acc, 0, 0, 0);
@@ -314,7 +312,7 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * wave + 4 * kg + i, c = 16 * J + col;
-        if (wave < J || (wave == J && r <= c)) {
+        if (wave < J || r <= c) {
           sA[r][c] = acc[i];
           sA[c][r] = acc[i];
         }
@@ -323,7 +321,7 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
   }
   __syncthreads();
 
-  // 4) Householder tridiagonalization with A in registers: wave q keeps
+  // 3) Householder tridiagonalization with A in registers: wave q keeps
   //    columns 16 q .. 16 q + 15 of every row (lane = row).  Step k zeroes
   //    column k below the subdiagonal with H = I - 2 u u^T (||u|| = 1, u_r = 0
   //    for r <= k; u is also stored as row k of sA for the back-transformation).  With p = 2 A u (the sum of the four waves'
@@ -434,7 +432,7 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
   const float pivmin = fmaxf(tnorm * 1e-30f, 1e-30f);
   const float tol = 2.f * 1.19209290e-7f * tnorm;
 
-  // 5) the KEPT largest eigenvalues: wave w takes the w-th, (w+4)-th, ...
+  // 4) the KEPT largest eigenvalues: wave w takes the w-th, (w+4)-th, ...
   //    (KW of them) at once, each on its own segment of SL = 64 / KW lanes;
   //    a pass counts the eigenvalues below SL shifts spread over the
   //    segment's interval, which shrinks (SL + 1)-fold.  T is read into
@@ -467,7 +465,7 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
   }
   __syncthreads();
 
-  // 6) inverse iteration on T: lane kk of wave 0 factors T - lambda_kk I once
+  // 5) inverse iteration on T: lane kk of wave 0 factors T - lambda_kk I once
   //    with partial pivoting (row i swaps with row i + 1 when |e_i| > |pivot|),
   //    then solves kInvIters times from a fixed varied start.  Without
   //    branches: the right-hand side and the swap flags stay in registers,
@@ -556,7 +554,7 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
   }
   __syncthreads();
 
-  // 7) back-transformation y = H_0 H_1 ... H_{B-3} z: eight eigenvectors per
+  // 6) back-transformation y = H_0 H_1 ... H_{B-3} z: eight eigenvectors per
   //    wave, lane 8 v + b holding rows 8 b .. 8 b + 7 of eigenvector 8 w + v,
   //    so each reflector costs a partial dot product of 8 rows and a sum over
   //    8 lanes; reflector k is row k of sA (16-byte reads)
@@ -615,16 +613,25 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
   }
   __syncthreads();
 
-  // 8) basis V[k][c] = sum_i D[i][c] Y[i][k] / sigma_k  (stored in sA)
+  // 7) basis V[k][c] = sum_i D[i][c] Y[i][k] / sigma_k (stored in sA): thread
+  //    (column c, half h) reads column c of the K tile again (L2), centres it
+  //    and forms rows k = h, h + 2, ...
   float* sV = &sA[0][0];
-  for (int w = tid; w < KEPT * D; w += kBuildThreads) {
-    const int k = w / D, c = w % D;
-    float v = 0.f;
-    if (sNz[k]) {
-      for (int i = 0; i < B; ++i) v = fmaf(sDT[c][i], sZ[i][k], v);
-      v /= sSigma[k];
+  {
+    const int c = tid & (D - 1), h = tid >> 7;
+    const float mu = sMu[c];
+    float dc[B];
+#pragma unroll
+    for (int i = 0; i < B; ++i) dc[i] = Elem<T>::load(K + (size_t)i * D + c) - mu;
+    for (int k = h; k < KEPT; k += 2) {
+      float v = 0.f;
+      if (sNz[k]) {
+#pragma unroll
+        for (int i = 0; i < B; ++i) v = fmaf(dc[i], sZ[i][k], v);
+        v /= sSigma[k];
+      }
+      sV[k * D + c] = v;
     }
-    sV[k * D + c] = v;
   }
   __syncthreads();
   // sign: largest |entry| positive (ties to the lower dim)
@@ -648,7 +655,7 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
   }
   __syncthreads();
 
-  // 9) write the record: centroid | basis rows | coefficients
+  // 8) write the record: centroid | basis rows | coefficients
   if (a.q4) {
     write_q4_record<R, KEPT>(a, phys, kvh, sMu, sV, sSign, &sZ[0][0], sSigma, sNz);
     return;
