@@ -333,6 +333,9 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
   //    (the same arithmetic in every wave), so the next products start
   //    without a second barrier.  LDS buffers alternate by step parity.
   const int q0 = 16 * wave;  // first column of this wave
+  // wave 0, as a per-lane predicate: its stores below are exec-masked rather
+  // than branched around, so the step body stays one basic block
+  const bool wave0 = tid < kWave;
   typedef float f32x16_t __attribute__((ext_vector_type(16)));
   f32x16_t Ar;  // a vector, so that the uniform column index below stays in registers
 #pragma unroll
@@ -343,25 +346,31 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
     const float x = sA[lane][0];
     __syncthreads();  // every wave has read the Gram columns that the reflectors overwrite
     // reflector of column k from x = A[lane][k] (zero for lane <= k), formed
-    // by every wave; wave 0 stores it
-    auto reflector = [&](int k, float xk) {
+    // by every wave with selects only (a zero column gives u = 0, alpha = 0)
+    auto reflector = [&](int k, float xk, float& alpha) {
       const float nrm2 = group_sum<kWave>(xk * xk);
       const float x0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xk), k + 1));
-      float u = 0.f, alpha = 0.f;
-      if (nrm2 > 0.f) {
-        const float nrm = __builtin_amdgcn_sqrtf(nrm2);
-        alpha = x0 >= 0.f ? -nrm : nrm;
-        const float inv = __builtin_amdgcn_rsqf(2.f * (nrm2 + nrm * fabsf(x0)));  // 1 / ||x - alpha e_{k+1}||
-        u = (lane == k + 1 ? xk - alpha : xk) * inv;
-      }
-      if (wave == 0) {
-        sA[k][lane] = u;  // row k: u, zero in columns <= k
+      const float nrm = __builtin_amdgcn_sqrtf(nrm2);
+      const bool nz = nrm2 > 0.f;
+      alpha = nz ? (x0 >= 0.f ? -nrm : nrm) : 0.f;
+      const float inv = __builtin_amdgcn_rsqf(2.f * (nrm2 + nrm * fabsf(x0)));  // 1 / ||x - alpha e_{k+1}||
+      return nz ? (lane == k + 1 ? xk - alpha : xk) * inv : 0.f;
+    };
+    // wave 0 keeps reflector k as row k of sA (zero in columns <= k) and the
+    // subdiagonal entry alpha
+    auto keep = [&](int k, float u, float alpha) {
+      if (wave0) {
+        sA[k][lane] = u;
         if (lane == 0) se[k] = alpha;
       }
-      return u;
     };
-    if (wave == 0 && lane == 0) sd[0] = x;
-    ur = reflector(0, lane > 0 ? x : 0.f);
+    if (wave0 && lane == 0) sd[0] = x;
+    if (wave0) scol[0][lane] = colnext;  // column 1, read by every wave at step 0
+    {
+      float alpha;
+      ur = reflector(0, lane > 0 ? x : 0.f, alpha);
+      keep(0, ur, alpha);
+    }
     float uj[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) uj[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ur), q0 + t));
@@ -370,45 +379,53 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
     for (int t = 0; t < 16; ++t) pp = fmaf(Ar[t], uj[t], pp);
     sp4[0][wave][lane] = pp;
     __syncthreads();
-    for (int k = 0; k < B - 2; ++k) {
+    // p = 2 A u_k, K = u_k.p and w = p - K u_k (zero in rows <= k)
+    auto step_w = [&](int k) {
       const int buf = k & 1;
-      const bool live = q0 + 15 > k;  // this wave holds columns > k
       const float p = 2.f * ((sp4[buf][0][lane] + sp4[buf][1][lane]) + (sp4[buf][2][lane] + sp4[buf][3][lane]));
       const float Kup = group_sum<kWave>(ur * p);
-      const float wr = lane > k ? p - Kup * ur : 0.f;
-      const int c = k + 1;
-      const bool more = c < B - 2;  // u_c exists (the last reflector is u_{B-3})
-      // the next reflector first: column c, brought up to date with this step,
-      // gives u_c (independent of this wave's own column updates below)
-      float un = 0.f;
-      if (more) {
-        if (k > 0) colnext = scol[buf][lane];
-        const float uc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ur), c));
-        const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wr), c));
-        colnext = colnext - (ur * wc + wr * uc);
-        if (wave == 0 && lane == c) sd[c] = colnext;
-        un = reflector(c, lane > c ? colnext : 0.f);
-      }
-      if (live) {
+      return lane > k ? p - Kup * ur : 0.f;
+    };
+    // A <- A - u w^T - w u^T on this wave's columns.  Columns at or left of k
+    // take exact zero updates (u_k and w vanish in rows <= k), so every wave
+    // runs it unguarded.
+    auto update = [&](float wr) {
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wr), q0 + t));
-          Ar[t] = fmaf(-wr, uj[t], fmaf(-ur, wj, Ar[t]));
-        }
+      for (int t = 0; t < 16; ++t) {
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wr), q0 + t));
+        Ar[t] = fmaf(-wr, uj[t], fmaf(-ur, wj, Ar[t]));
       }
-      if (!more) break;
+    };
+    // Steps 0 .. B - 4 also form the next reflector; the body has no branch
+    // before the barrier's stores, so the column updates can be scheduled
+    // into the latency of the reflector's reduction.
+    for (int k = 0; k < B - 3; ++k) {
+      const int buf = k & 1;
+      const float wr = step_w(k);
+      const int c = k + 1;
+      // the next reflector first: column c, brought up to date with this
+      // step, gives u_c (independent of this wave's own column updates)
+      colnext = scol[buf][lane];
+      const float uc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ur), c));
+      const float wc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wr), c));
+      colnext = colnext - (ur * wc + wr * uc);
+      if (wave0 && lane == c) sd[c] = colnext;
+      float alpha;
+      const float un = reflector(c, lane > c ? colnext : 0.f, alpha);
+      update(wr);
       ur = un;
 #pragma unroll
       for (int t = 0; t < 16; ++t) uj[t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ur), q0 + t));
+      // columns <= c meet u_c's zeros: their terms are exact zeros
       float pq[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
-      if (q0 + 15 > c) {
 #pragma unroll
-        for (int t = 0; t < 16; ++t) pq[t & 3] = fmaf(Ar[t], uj[t], pq[t & 3]);
-      }
+      for (int t = 0; t < 16; ++t) pq[t & 3] = fmaf(Ar[t], uj[t], pq[t & 3]);
       sp4[buf ^ 1][wave][lane] = (pq[0] + pq[1]) + (pq[2] + pq[3]);
+      keep(c, ur, alpha);
       if (c + 1 < B - 2 && wave == (c + 1) / 16) scol[buf ^ 1][lane] = Ar[c + 1 - q0];  // column c + 1, for the next step
       __syncthreads();
     }
+    update(step_w(B - 3));  // the last reflector u_{B-3}: update only
   }
   if (wave == kBuildWaves - 1) {  // the last 2 x 2 block (columns 62, 63)
     const float a62 = Ar[14], a63 = Ar[15];
@@ -476,20 +493,32 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
     const float lam = sLam[kk];
     uint64_t swm = 0ull;  // bit i: rows i and i + 1 swapped
     {
-      float ddc = sd[0] - lam, duc = se[0];
+      // T in registers first, so the factorization's dependent chain waits
+      // on no LDS read (its factor stores would otherwise hold each read up)
+      float dT[B], eT[B];
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        dT[i] = sd[i];
+        eT[i] = se[i];
+      }
+      float ddc = dT[0] - lam, duc = eT[0];
 #pragma unroll
       for (int i = 0; i < B - 1; ++i) {
-        const float dl = se[i];
-        const float ddn = sd[i + 1] - lam;
-        const float dun = i + 1 < B - 1 ? se[i + 1] : 0.f;
+        const float dl = eT[i];
+        const float ddn = dT[i + 1] - lam;
+        const float dun = i + 1 < B - 1 ? eT[i + 1] : 0.f;
+        // both pivot choices are carried through and the row with the larger
+        // pivot is selected at the end (a discarded choice may be inf/NaN):
+        // the dependent chain per row is clamp, reciprocal, product, select
         const bool keep = fabsf(ddc) >= fabsf(dl);
-        const float rp = __builtin_amdgcn_rcpf(keep ? (fabsf(ddc) < pivmin ? pivmin : ddc) : dl);
-        const float mlt = (keep ? dl : ddc) * rp;
-        sF[i][kk] = make_float4(rp, keep ? duc : ddn, keep ? 0.f : dun, mlt);
+        const float rk = __builtin_amdgcn_rcpf(fabsf(ddc) < pivmin ? pivmin : ddc);
+        const float rs = __builtin_amdgcn_rcpf(dl);
+        const float mk = dl * rk, ms = ddc * rs;
+        const float nk = ddn - mk * duc, ns = duc - ms * ddn;
+        sF[i][kk] = make_float4(keep ? rk : rs, keep ? duc : ddn, keep ? 0.f : dun, keep ? mk : ms);
         if (!keep) swm |= 1ull << i;
-        const float nddc = keep ? ddn - mlt * duc : duc - mlt * ddn;
-        duc = keep ? dun : -mlt * dun;
-        ddc = nddc;
+        duc = keep ? dun : -ms * dun;
+        ddc = keep ? nk : ns;
       }
       sF[B - 1][kk] = make_float4(__builtin_amdgcn_rcpf(fabsf(ddc) < pivmin ? pivmin : ddc), 0.f, 0.f, 0.f);
     }
@@ -504,12 +533,15 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
     float scale = __builtin_amdgcn_rsqf(nrm2);
     for (int itr = 0; itr < kInvIters; ++itr) {
       // forward: the row swaps and multipliers applied to the right-hand side
+      // (the multipliers are read first, so no LDS read waits inside the chain)
+      float mw[B - 1];
+#pragma unroll
+      for (int i = 0; i < B - 1; ++i) mw[i] = sF[i][kk].w;
       float zc = z[0] * scale;
 #pragma unroll
       for (int i = 0; i < B - 1; ++i) {
-        if (i % 8 == 0) asm volatile("" ::: "memory");  // loads run at most 8 rows ahead
         const float zn = z[i + 1] * scale;
-        const float mlt = sF[i][kk].w;
+        const float mlt = mw[i];
         const bool sw = (swm >> i) & 1ull;
         z[i] = sw ? zn : zc;
         zc = sw ? zc - mlt * zn : zn - mlt * zc;
@@ -520,7 +552,7 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
       nrm2 = x1 * x1;
 #pragma unroll
       for (int i = B - 2; i >= 0; --i) {
-        if (i % 8 == 6) asm volatile("" ::: "memory");
+        if (i % 16 == 14) asm volatile("" ::: "memory");  // factor reads run at most 16 rows ahead
         const float4 f = sF[i][kk];
         const float x = (z[i] - f.y * x1 - f.z * x2) * f.x;
         z[i] = x;
