@@ -120,7 +120,9 @@ def main():
     ms_total = ev0.elapsed_time(ev1)
     ms_per_step = ms_total / args.steps
 
-    # algorithmic bytes of one step at the lengths reached
+    # algorithmic bytes of one step at the lengths reached: per (sequence, KV
+    # head) every scored record plus its G page-LSE floats, the selected pages'
+    # K and V; per sequence the queries, outputs and the appended k/v
     rec = L.lk_summary_record_bytes(base.cfg)
     k_pages = L.lk_page_budget(base.cfg)
     lens_now = [int(x) for x in layers[0].seq_lens.cpu().tolist()]

@@ -17,7 +17,7 @@ notation; beside them sit the plain definitions the method is checked against
 Library primitives used as steps: ``numpy.linalg.eigh`` (the small symmetric
 eigendecomposition of the build), matrix products, sorting.
 
-Readings taken where the pages leave a step open (each is listed in the design doc):
+Readings taken where the pages leave a step open:
   * the most-recent page is the page holding the newest token (possibly
     partial); pages before it are complete, summarized and scored; page 0
     (the sink) is scored but never a candidate;
