@@ -36,8 +36,6 @@ namespace lk {
 constexpr int kBuildThreads = 256;
 constexpr int kMergeThreads = 512;      // decode-step launch: one merged output per thread for G <= 4
 constexpr int kBuildWaves = kBuildThreads / kWave;
-constexpr float kZeroModeRtol = 1e-5f;
-constexpr float kZeroModeFloor = 1e-10f;
 constexpr int kInvIters = 2;         // inverse-iteration passes per eigenvector
 constexpr float kClusterTol = 1e-3f; // eigenvalues this close (relative to lambda_1) are re-orthogonalized
 

@@ -235,7 +235,7 @@ __global__ __launch_bounds__(kB16Waves * kWave) void build16_kernel(BuildArgs a)
   }
   wave_lds_fence();
   const float lam1 = sLam[wave][0];
-  const float thresh = fmaxf(1e-5f * lam1, 1e-10f * energy);
+  const float thresh = fmaxf(kZeroModeRtol * lam1, kZeroModeFloor * energy);
   if (a.eigvals_out && lane < B) a.eigvals_out[((size_t)idx * a.hkv + kvh) * B + lane] = fmaxf(sLam[wave][lane], 0.f);
 
   // 5) basis rows V[k][c] = sum_i D[i][c] U[i][idx_k] / sigma_k for this lane's

@@ -8,6 +8,12 @@ namespace lk {
 
 enum DType : int { kF32 = 0, kBF16 = 1 };
 
+// Zero-mode rule of both summary builders: a Gram eigenvalue at or below
+// kZeroModeRtol * lambda_1 or kZeroModeFloor * sum_i ||k_i||^2 is a zero mode
+// (zero basis row and coefficients).
+constexpr float kZeroModeRtol = 1e-5f;
+constexpr float kZeroModeFloor = 1e-10f;
+
 // Byte layout of a quantized (int4 basis / int8 coefficients and centroid)
 // summary record at d = 128, page size b (64 unless given) and rank r:
 // centroid int8[d] | basis int4[r][d/2] (byte c of row m: dims 2c in the low
