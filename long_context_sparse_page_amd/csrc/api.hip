@@ -119,7 +119,8 @@ lk_status check_table(const lk_cache* c, const Shape& sh) {
 
 // Workspace regions.
 struct Layout {
-  size_t page_lse, sel_pages, sel_count, sel_phys, part_o, part_ml, build_list, total;
+  size_t page_lse, sel_pages, sel_count, sel_phys, part_o, part_ml, build_list, cand_key, cand_page, cand_phys,
+      cand_cnt, chunk_ms, total;
   int n_splits;
 };
 
@@ -138,6 +139,15 @@ Layout layout(const Shape& sh, int batch, int max_pages) {
   L.part_o = off; off = align_up(off + sizeof(float) * (size_t)batch * sh.hkv * L.n_splits * sh.G * sh.d);
   L.part_ml = off; off = align_up(off + sizeof(float) * (size_t)batch * sh.hkv * L.n_splits * sh.G * 2);
   L.build_list = off; off = align_up(off + sizeof(int32_t) * (size_t)batch);
+  // candidate lists of the chunked selection, reserved whenever the table and
+  // budget admit it (whether a call uses it also depends on its pair count)
+  const size_t n_lists = (size_t)batch * sh.hkv * lk::select_chunk_capacity(max_pages, sh.k);
+  const size_t n_entries = n_lists * (sh.k > 2 ? sh.k - 2 : 0);
+  L.cand_key = off; off = align_up(off + sizeof(uint32_t) * n_entries);
+  L.cand_page = off; off = align_up(off + sizeof(int32_t) * n_entries);
+  L.cand_phys = off; off = align_up(off + sizeof(int32_t) * n_entries);
+  L.cand_cnt = off; off = align_up(off + sizeof(int32_t) * n_lists);
+  L.chunk_ms = off; off = align_up(off + sizeof(float) * n_lists * sh.G * 2);
   L.total = off;
   return L;
 }
@@ -159,17 +169,30 @@ lk_status hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// The chunked selection's lists, when the call's shape uses it.
+void attach_chunk_lists(lk::SelectArgs& se, void* ws, const Layout& L) {
+  se.n_chunks = lk::select_chunks(se.batch, se.hkv, se.max_pages, se.k);
+  if (se.n_chunks > 0) {
+    se.cand_key = at<uint32_t>(ws, L.cand_key);
+    se.cand_page = at<int32_t>(ws, L.cand_page);
+    se.cand_phys = at<int32_t>(ws, L.cand_phys);
+    se.cand_cnt = at<int32_t>(ws, L.cand_cnt);
+    se.chunk_ms = at<float>(ws, L.chunk_ms);
+  }
+}
+
 // Score (+ the decode step's append when app.k_new is set) and select.
 lk_status enqueue_score_select(const Shape& sh, const lk_config* cfg, const lk_cache* c, int batch,
                                const void* q, float* page_lse, float* share_out, int32_t* sel,
                                int32_t* cnt, int32_t* sel_phys, int len_add, const lk::AppendDuty& app,
-                               hipStream_t s) {
+                               void* ws, const Layout& L, hipStream_t s) {
   lk::ScoreArgs sa{q, c->summary_pool, c->block_table, c->seq_lens, page_lse,
                    batch, c->max_pages_per_seq, c->num_phys_pages, sh.hkv, sh.hq, cfg->scale, len_add, app};
   hipError_t e = lk::launch_score(sh.dt, sh.r, sh.G, sh.q4, sa, s);
   if (e != hipSuccess) return hip_status(e, "score launch");
   lk::SelectArgs se{page_lse, share_out, sel, cnt, c->seq_lens, batch, c->max_pages_per_seq,
                     sh.hkv, sh.G, sh.B, sh.k, len_add, c->block_table, sel_phys, c->num_phys_pages};
+  attach_chunk_lists(se, ws, L);
   return hip_status(lk::launch_select(se, s), "select launch");
 }
 
@@ -272,7 +295,7 @@ lk_status lk_score_select(const lk_config* cfg, const lk_cache* cache, int32_t b
   }
   float* lse = page_lse_out ? page_lse_out : at<float>(ws, L.page_lse);
   return enqueue_score_select(sh, cfg, cache, batch, q, lse, share_out, sel_pages, sel_count, nullptr, 0,
-                              lk::AppendDuty{}, s);
+                              lk::AppendDuty{}, ws, L, s);
 }
 
 lk_status lk_sparse_decode_attn(const lk_config* cfg, const lk_cache* cache, int32_t batch, const void* q,
@@ -352,6 +375,7 @@ lk_status lk_decode_step(const lk_config* cfg, const lk_cache* cache, int32_t ba
     se.sel_pages = sel;
     se.sel_count = cnt;
     se.sel_phys = sel_phys;
+    attach_chunk_lists(se, ws, L);
     st = hip_status(lk::launch_select(se, s), "select launch");
     if (st != LK_OK) return st;
     int ns = 0;

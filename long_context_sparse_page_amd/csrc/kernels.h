@@ -72,7 +72,25 @@ struct SelectArgs {
   const int32_t* block_table;  // with sel_phys: physical page of every selected page
   int32_t* sel_phys;           // optional [batch][Hkv][k]
   int32_t num_phys;
+  // Chunked selection (select_chunks() > 0): per chunk of kSelChunkPages pages
+  // its top-(k-2) candidates, in page order, and their count.
+  uint32_t* cand_key = nullptr;   // [batch][Hkv][n_chunks][k - 2]
+  int32_t* cand_page = nullptr;   // [batch][Hkv][n_chunks][k - 2]
+  int32_t* cand_phys = nullptr;   // [batch][Hkv][n_chunks][k - 2], their physical pages
+  int32_t* cand_cnt = nullptr;    // [batch][Hkv][n_chunks]
+  float* chunk_ms = nullptr;      // [batch][Hkv][n_chunks][G][2]: per-head max and sum of 2^(s2 - max)
+  int32_t n_chunks = 0;
 };
+
+// Chunked selection of long tables: pages per chunk workgroup, and the chunk
+// count a table of max_pages pages with page budget k uses (0: the table is
+// selected by one workgroup per (sequence, KV head)).  select_chunk_capacity
+// ignores how many pairs there are (it sizes the workspace); select_chunks
+// also requires few pairs, where one workgroup per pair would leave most of
+// the chip idle.
+constexpr int kSelChunkPages = 2048;
+int select_chunk_capacity(int max_pages, int k);
+int select_chunks(int batch, int hkv, int max_pages, int k);
 
 struct AttnArgs {
   const void* q;

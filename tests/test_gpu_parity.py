@@ -374,25 +374,29 @@ def test_decode_step_table_full(gpu):
     assert torch.isfinite(o["out"][0].float()).all()
 
 
-def _selector_case(T, budget, capacity=None, group=4, layout=None, hold_last=False):
-    """fp32 single-sequence cache holding T tokens whose keys may be rearranged
+def _selector_case(T, budget, capacity=None, group=4, layout=None, hold_last=False, pad=0):
+    """fp32 cache whose sequence 0 holds T tokens whose keys may be rearranged
     by ``layout(keys)`` (page copies make exact ties); returns the workload,
     cache, host K/V pages and fp64 queries.  hold_last: the cache holds the
-    first T - 1 tokens only (T % 64 != 0), for a decode step to append the last."""
+    first T - 1 tokens only (T % 64 != 0), for a decode step to append the last.
+    pad: that many more sequences of one token each (one page of capacity), so
+    that a wide table is selected with many (sequence, KV head) pairs."""
     w = synth.workload(0, budget=budget)
-    w.context = [T]
+    w.batch = 1 + pad
+    w.context = [T] + [1] * pad
     w.num_q_heads = group
-    dc = DeviceCache(w, poison=True, capacity_pages=[capacity] if capacity else None)
+    caps = [capacity or w.pages_needed(0)] + [1] * pad
+    dc = DeviceCache(w, poison=True, capacity_pages=caps if (capacity or pad) else None)
     kk, vv = synth.keys_values(w, 0, 0)
     kk, vv = kk[:T].copy(), vv[:T].copy()
-    q = np.random.default_rng(T).standard_normal((1, group, w.head_dim)).astype(np.float32)
+    q = np.random.default_rng(T).standard_normal((1 + pad, group, w.head_dim)).astype(np.float32)
     if layout is not None:
         q = layout(kk, q)
     n_write = T - 1 if hold_last else T
     assert not hold_last or T % w.page_size != 0
     dc.write_tokens(0, 0, 0, to_storage(kk[:n_write], w.dtype), to_storage(vv[:n_write], w.dtype))
     if hold_last:
-        dc.seq_lens.fill_(T - 1)
+        dc.seq_lens[0] = T - 1
         dc.held = (kk[T - 1:T], vv[T - 1:T])
     dc.build_all()
     B, d = w.page_size, w.head_dim
@@ -404,15 +408,15 @@ def _selector_case(T, budget, capacity=None, group=4, layout=None, hold_last=Fal
     return w, dc, K.reshape(n_pages, B, d), V.reshape(n_pages, B, d), ref.stored(q, w.dtype)
 
 
-def _run_selector(w, dc, K, V, q64):
+def _run_selector(w, dc, K, V, q64, outputs=False):
     T = w.context
     hs, _ = ref.oracle_head(w, q64[0], K, V, T[0])
     o = dc.outputs()
     dc.score_select(ref.q_device(q64, w.dtype), o)
     torch.cuda.synchronize()
     check_scores(w, dc, o, {(0, 0): (hs, None, K, V)}, T, atol=1e-3)
-    sel = o["sel"].cpu().numpy()[0, 0, :o["cnt"].cpu().numpy()[0, 0]]
-    return [int(x) for x in sel], hs
+    sel = [int(x) for x in o["sel"].cpu().numpy()[0, 0, :o["cnt"].cpu().numpy()[0, 0]]]
+    return (sel, hs, o) if outputs else (sel, hs)
 
 
 def test_selector_ties_overflow_list(gpu):
@@ -507,6 +511,7 @@ def _hot_copies(kk, q):
     (64 * 101 + 3, 4096, None, 4, None, None),                   # budget 64 pages
     (64 * 700 + 40, 1024, 2500, 2, None, None),                  # 5 pages per thread, G = 2
     (64 * 2000 + 7, 2048, 3000, 1, None, None),                  # 6 pages per thread, G = 1
+    (64 * 700 + 40, 1024, 5000, 2, None, None),                  # chunked selection, then attention
     (64 * 20 + 9, 128, None, 4, None, None),                     # k = 2: sink and most recent
     (64 * 20 + 9, 2048, None, 4, None, None),                    # every page selected
     (64 * 1 + 1, 2048, None, 4, None, None),                     # two pages
@@ -525,17 +530,64 @@ def test_decode_step_selection(gpu, T, budget, capacity, group, layout, expect):
     assert len(sel) == len(hs.selected)
 
 
-@pytest.mark.parametrize("T,budget,capacity,group", [
-    (64 * 101 + 3, 4096, None, 4),     # fewer threads hold candidates than the budget needs
-    (64 * 300 + 7, 2048, 3300, 4),     # 1024-thread tier, scores loaded twice
-    (64 * 700 + 40, 1024, 13000, 4),   # largest-table tier at G = 4
-    (64 * 500 + 1, 2048, 9000, 8),     # 1024-thread tier at G = 8
+# Tables wider than 3072 pages: with fewer than 128 (sequence, KV head) pairs
+# the chunked selection (chunk workgroups, then a merge per pair), with 128
+# pairs (pad 127) one 1024-thread workgroup per pair.
+@pytest.mark.parametrize("T,budget,capacity,group,pad", [
+    (64 * 101 + 3, 4096, None, 4, 0),      # fewer threads hold candidates than the budget needs
+    (64 * 300 + 7, 2048, 3300, 4, 0),      # chunked, 2 chunks
+    (64 * 300 + 7, 2048, 3300, 4, 127),    # 1024-thread tier, scores loaded twice
+    (64 * 700 + 40, 1024, 13000, 4, 0),    # chunked, 7 chunks
+    (64 * 700 + 40, 1024, 13000, 4, 127),  # 17 pages per thread
+    (64 * 500 + 1, 2048, 9000, 8, 0),      # chunked at G = 8
+    (64 * 500 + 1, 2048, 9000, 8, 127),    # 1024-thread tier at G = 8
+    (64 * 3000 + 5, 4096, 20000, 4, 0),    # chunked, 10 chunks of 62 candidates (largest merge list)
+    (64 * 3000 + 5, 4096, 20000, 4, 127),  # 24 pages per thread
+    (64 * 20 + 9, 2048, 5000, 4, 0),       # chunked table, every page selected (shares still written)
 ])
-def test_selector_tiers(gpu, T, budget, capacity, group):
-    say("selector tier: T", T, "budget", budget, "capacity", capacity, "G", group)
-    w, dc, K, V, q64 = _selector_case(T, budget, capacity=capacity, group=group)
-    sel, hs = _run_selector(w, dc, K, V, q64)
+def test_selector_tiers(gpu, T, budget, capacity, group, pad):
+    say("selector tier: T", T, "budget", budget, "capacity", capacity, "G", group, "pad", pad)
+    w, dc, K, V, q64 = _selector_case(T, budget, capacity=capacity, group=group, pad=pad)
+    sel, hs, o = _run_selector(w, dc, K, V, q64, outputs=True)
     assert len(sel) == len(hs.selected)
+    if pad:  # the one-token sequences: nothing scored, the sink page alone
+        cnt = o["cnt"].cpu().numpy()[1:, 0]
+        sp = o["sel"].cpu().numpy()[1:, 0]
+        assert (cnt == 1).all() and (sp[:, 0] == 0).all() and (sp[:, 1:] == -1).all()
+
+
+def _spread_hot_copies(kk, q):
+    """41 tied dominant pages spread over several 2048-page chunks."""
+    n = kk.shape[0] // 64
+    hot = sorted(np.random.default_rng(21).choice(np.arange(2, n - 1), size=40, replace=False).tolist())
+    u = np.random.default_rng(22).standard_normal(kk.shape[1])
+    u /= np.linalg.norm(u)
+    base = kk[64:128] + 2.0 * u
+    for p in [1] + hot:
+        kk[p * 64:(p + 1) * 64] = base
+    return (q * 0.1 + 3.0 * np.sqrt(kk.shape[1]) * u).astype(np.float32)
+
+
+@pytest.mark.parametrize("layout,expect", [(_copies_of_page1, "lowest"), (_spread_hot_copies, "hot")])
+def test_chunked_selector_ties(gpu, layout, expect):
+    """Ties across chunks: every chunk keeps its lowest-index tied pages and the
+    merge takes the lowest overall (all candidates tie: the chunks' block-wide
+    fallback; 41 tied dominant pages over several chunks: the short lists)."""
+    T = 64 * 5000 + 10
+    say("chunked selector ties:", layout.__name__, "T", T)
+    w, dc, K, V, q64 = _selector_case(T, 2048, capacity=6000, layout=layout)
+    sel, hs = _run_selector(w, dc, K, V, q64)
+    n_mr = lo.most_recent_page(T, w.page_size)
+    if expect == "lowest":
+        want = [0] + list(range(1, 31)) + [n_mr]
+    else:
+        hot = sorted(np.random.default_rng(21).choice(np.arange(2, T // 64 - 1), size=40,
+                                                      replace=False).tolist())
+        tied = sorted([1] + hot)
+        assert min(hs.m_bar[j] for j in tied) > max(hs.m_bar[j] for j in range(1, n_mr) if j not in tied)
+        want = sorted([0, n_mr] + tied[:30])
+    assert list(hs.selected) == want
+    assert sel == want
 
 
 # ----------------------------------------------------------------------------
