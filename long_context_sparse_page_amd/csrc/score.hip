@@ -362,12 +362,9 @@ template <int R, int G>
 __global__ __launch_bounds__(kScoreWaves * kWave) void score_mfma_kernel(ScoreArgs a) {
   constexpr int B = 64;
   constexpr int D = kHeadDim;
-  constexpr int ROWS = R + 1;
   constexpr int NR = ScoreGroup<R>::NR;
   constexpr int SLOTS = ScoreGroup<R>::SLOTS;
   constexpr int TILES = ScoreGroup<R>::TILES;
-  constexpr int LPH = kWave / G;
-  constexpr int TPL = B / LPH;
   constexpr int PAGES_PER_WAVE = ScoreGroup<R>::GROUPS_PER_WAVE * NR;
   static_assert(G <= 8, "at most 8 query heads per KV head");
 

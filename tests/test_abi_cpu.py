@@ -101,6 +101,22 @@ def test_workspace_size_scales():
     assert a >= 4 * 32 * 2049 * 4 + 4 * 8 * 32 * 4
 
 
+@pytest.mark.parametrize("kw,pages", [
+    (dict(), 2049), (dict(), 16400), (dict(token_budget=4096), 20000),
+    (dict(num_q_heads=8, num_kv_heads=8), 9000), (dict(num_q_heads=64, num_kv_heads=8), 12000),
+    (dict(summary_format=1), 16400), (dict(token_budget=128), 16400),
+])
+def test_workspace_for_a_batch_serves_every_smaller_batch(kw, pages):
+    """A workspace sized for `batch` sequences serves calls with fewer: the
+    size never shrinks as the batch grows, whichever selection path a batch
+    size takes (wide tables with few (sequence, KV head) pairs are selected in
+    chunks, which need candidate lists in the workspace)."""
+    c = cfg(**kw)
+    sizes = [L.lk_workspace_size(c, b, pages) for b in range(1, 40)]
+    assert all(x <= y for x, y in zip(sizes, sizes[1:])), sizes
+    assert all(x % 256 == 0 for x in sizes)
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=64), L.LK_ERR_UNSUPPORTED),
     (dict(page_size=16), L.LK_ERR_UNSUPPORTED),
