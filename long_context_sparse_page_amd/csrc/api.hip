@@ -361,7 +361,7 @@ lk_status lk_decode_step(const lk_config* cfg, const lk_cache* cache, int32_t ba
   lk::SelectArgs se{page_lse, nullptr, sel_pages, sel_count, cache->seq_lens, batch, cache->max_pages_per_seq,
                     sh.hkv, sh.G, sh.B, sh.k, 1, cache->block_table, nullptr, cache->num_phys_pages};
   const bool fused = lk::select_attn_fusable(se);
-  const int n_merge = fused ? lk::select_attn_splits(sh.k) : n_splits;
+  const int n_merge = fused ? lk::select_attn_splits(sh.k) : n_splits;  // = list_attn_splits(k) when chunked
   if (fused) {
     lk::AttnArgs aa{q, cache->k_pool, cache->v_pool, cache->block_table, cache->seq_lens, nullptr, nullptr, nullptr,
                     at<float>(ws, L.part_o), at<float>(ws, L.part_ml), out, lse_out,
@@ -376,11 +376,26 @@ lk_status lk_decode_step(const lk_config* cfg, const lk_cache* cache, int32_t ba
     se.sel_count = cnt;
     se.sel_phys = sel_phys;
     attach_chunk_lists(se, ws, L);
-    st = hip_status(lk::launch_select(se, s), "select launch");
-    if (st != LK_OK) return st;
-    int ns = 0;
-    st = enqueue_attn(sh, cfg, cache, batch, q, sel, cnt, sel_phys, out, lse_out, ws, L, 1, false, s, &ns);
-    if (st != LK_OK) return st;
+    if (se.n_chunks > 0) {
+      // chunked selection: the chunk lists, then attention whose waves merge
+      // them (the selection is written only when the caller asked for it)
+      se.sel_pages = sel_pages;
+      se.sel_count = sel_count;
+      st = hip_status(lk::launch_select_lists(se, s), "select launch");
+      if (st != LK_OK) return st;
+      lk::AttnArgs aa{q, cache->k_pool, cache->v_pool, cache->block_table, cache->seq_lens, nullptr, nullptr, nullptr,
+                      at<float>(ws, L.part_o), at<float>(ws, L.part_ml), out, lse_out,
+                      batch, cache->max_pages_per_seq, cache->num_phys_pages, sh.hkv, sh.hq, sh.k,
+                      n_merge, 1, cfg->scale, 1};
+      st = hip_status(lk::launch_list_attn(sh.dt, se, aa, s), "attention launch");
+      if (st != LK_OK) return st;
+    } else {
+      st = hip_status(lk::launch_select(se, s), "select launch");
+      if (st != LK_OK) return st;
+      int ns = 0;
+      st = enqueue_attn(sh, cfg, cache, batch, q, sel, cnt, sel_phys, out, lse_out, ws, L, 1, false, s, &ns);
+      if (st != LK_OK) return st;
+    }
   }
   // 4) one launch of (sequence, KV head) workgroups: merge the attention
   //    partials, advance the stored lengths, and summarize pages the append

@@ -813,4 +813,141 @@ hipError_t launch_select_attn(DType dt, const SelectArgs& se, const AttnArgs& a,
   return dt == kBF16 ? launch_select_attn_t<bf16_t>(se, a, s) : launch_select_attn_t<float>(se, a, s);
 }
 
+
+// ---------------------------------------------------------------------------
+// Decode step, chunked selection (long tables, few (sequence, KV head) pairs):
+// attention whose waves merge the pair's chunk lists themselves.  Workgroup =
+// 4 waves per (split, KV head, sequence); wave w of split s attends unit
+// 4 s + w (half (4 s + w) & 1 of selection entry (4 s + w) >> 1).  Every wave
+// reads the list slots and counts of its pair (one round trip, with its
+// queries), takes the top-(k-2) entries as the selection merge does (ties to
+// the earlier entry = the lower page) and picks its own entry from the lane
+// that holds it: no barrier before the K/V loads.  Wave 0 of split 0 writes
+// the selection when it is asked for.
+template <typename T, int G, int CR>
+__global__ __launch_bounds__(kAttnWaves * kWave) void list_attn_kernel(SelectArgs se, AttnArgs a) {
+  constexpr int B = 64;
+  const int split = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const size_t pair = (size_t)seq * se.hkv + kvh;
+  const int k = se.k, ktop = k - 2, C = se.n_chunks;
+  const int32_t* bt = se.block_table + (size_t)seq * se.max_pages;
+  uint32_t ck[CR];
+  int cp[CR], cq[CR];
+#pragma unroll
+  for (int r = 0; r < CR; ++r) {
+    const int x = lane + kWave * r;
+    const int c = x / ktop, i = x - c * ktop;
+    const bool in = c < C;
+    const size_t at = pair * C * ktop + (in ? x : 0);
+    const int n = se.cand_cnt[pair * C + (in ? c : 0)];
+    const uint32_t kv = se.cand_key[at];
+    ck[r] = (in && i < n) ? kv : 0u;
+    cp[r] = se.cand_page[at];
+    cq[r] = se.cand_phys[at];
+  }
+  const int sg = lane >> 3;
+  const int e = lane & 7;
+  QLane<T, G> q;
+  q.load(a, seq, kvh, e);
+  const int len = se.seq_lens[seq] + se.len_add;
+  int n_mr = len > 0 ? (len - 1) / B : 0;
+  if (n_mr > se.max_pages - 1) n_mr = se.max_pages - 1;
+  const int ph0 = bt[0], phr = bt[n_mr];
+  const int n_cand = n_mr > 0 ? n_mr - 1 : 0;
+  const int u = split * kAttnWaves + wave;
+  const int x = u >> 1;  // this wave's selection entry
+  int32_t* so = (split == 0 && wave == 0 && se.sel_pages) ? se.sel_pages + pair * k : nullptr;
+  int pg = -1, phys = -1, cnt = 0;
+  if (len <= 0) {
+    if (so) {
+      for (int s = lane; s < k; s += kWave) so[s] = -1;
+      if (lane == 0) se.sel_count[pair] = 0;
+    }
+  } else if (min(ktop, n_cand) == n_cand) {  // every page 0 .. n_mr
+    cnt = n_mr + 1;
+    if (x <= n_mr) { pg = x; phys = bt[x]; }
+    if (so) {
+      for (int s = lane; s < k; s += kWave) so[s] = s <= n_mr ? s : -1;
+      if (lane == 0) se.sel_count[pair] = cnt;
+    }
+  } else {
+    int nz = 0;  // k - 2, fewer only if non-finite scores left keys at zero
+#pragma unroll
+    for (int r = 0; r < CR; ++r) nz += __popcll(__ballot(ck[r] != 0u));
+    const int n_top = min(ktop, nz);
+    cnt = n_top + 2;
+    if (x == 0) { pg = 0; phys = ph0; }
+    else if (x == n_top + 1) { pg = n_mr; phys = phr; }
+    if (n_top > 0) {
+      int mp = -1, mq = -1;
+      bool have = false;
+      wave_take_in_order<CR>(ck, n_top, [&](int slot, int r) {
+        if (slot == x - 1) { mp = cp[r]; mq = cq[r]; have = true; }
+        if (so) so[1 + slot] = cp[r];
+      });
+      const uint64_t hb = __ballot(have);
+      if (hb) {
+        const int src = __ffsll((unsigned long long)hb) - 1;
+        pg = __builtin_amdgcn_readlane(mp, src);
+        phys = __builtin_amdgcn_readlane(mq, src);
+      }
+    }
+    if (so) {
+      if (lane == 0) { so[0] = 0; so[n_top + 1] = n_mr; se.sel_count[pair] = cnt; }
+      for (int s = n_top + 2 + lane; s < k; s += kWave) so[s] = -1;
+    }
+  }
+
+  float m[G], l[G], o[G][16];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[g][i] = 0.f;
+  }
+  if (x < cnt && pg >= 0 && pg <= n_mr && phys >= 0 && phys < a.num_phys) {
+    const int half = u & 1;
+    KV16<T> kr[kAttnTPG], vr[kAttnTPG];
+    issue_unit<T>(a, kvh, phys, half, sg, e, kr, vr);
+    const int n_tok = ((pg == n_mr) ? len - n_mr * B : B) - half * kAttnHalf;
+    if (n_tok > 0) attend_unit<T, G>(q, kr, vr, n_tok, sg, a.scale * kLog2e, m, l, o);
+  }
+  combine_write<G, kAttnWaves>(a, pair * a.n_splits + split, wave, lane, m, l, o);
+}
+
+int list_attn_splits(int k) { return (2 * k + kAttnWaves - 1) / kAttnWaves; }
+
+template <typename T, int G>
+static hipError_t launch_list_attn_g(const SelectArgs& se, const AttnArgs& a, hipStream_t s) {
+  const dim3 grid(a.n_splits, a.hkv, a.batch), block(kAttnWaves * kWave);
+  const int entries = se.n_chunks * (se.k - 2);
+  if (entries <= 4 * kWave) hipLaunchKernelGGL((list_attn_kernel<T, G, 4>), grid, block, 0, s, se, a);
+  else if (entries <= 8 * kWave) hipLaunchKernelGGL((list_attn_kernel<T, G, 8>), grid, block, 0, s, se, a);
+  else if (entries <= 12 * kWave) hipLaunchKernelGGL((list_attn_kernel<T, G, 12>), grid, block, 0, s, se, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_list_attn_t(const SelectArgs& se, const AttnArgs& a, hipStream_t s) {
+  switch (se.group) {
+    case 1: return launch_list_attn_g<T, 1>(se, a, s);
+    case 2: return launch_list_attn_g<T, 2>(se, a, s);
+    case 4: return launch_list_attn_g<T, 4>(se, a, s);
+    case 8: return launch_list_attn_g<T, 8>(se, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_list_attn(DType dt, const SelectArgs& se, const AttnArgs& a, hipStream_t s) {
+  if (se.n_chunks <= 0 || !se.cand_key || !se.cand_page || !se.cand_phys || !se.cand_cnt || se.k < 3 ||
+      se.page_size != 64 || se.seq_lens != a.seq_lens || a.n_splits != list_attn_splits(se.k) ||
+      se.hkv != a.hkv || se.batch != a.batch)
+    return hipErrorInvalidValue;
+  return dt == kBF16 ? launch_list_attn_t<bf16_t>(se, a, s) : launch_list_attn_t<float>(se, a, s);
+}
+
 }  // namespace lk

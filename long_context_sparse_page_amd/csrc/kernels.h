@@ -138,6 +138,9 @@ struct BuildArgs {
 // q4: the summary records use Q4Layout (bf16 queries only)
 hipError_t launch_score(DType dt, int rank, int group, bool q4, const ScoreArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+// Chunked selection without its merge (a.n_chunks > 0): the per-chunk lists
+// only, for launch_list_attn.
+hipError_t launch_select_lists(const SelectArgs& a, hipStream_t s);
 // merge = false leaves the split partials for the decode step's build launch
 hipError_t launch_attn(DType dt, int group, const AttnArgs& a, bool merge, hipStream_t s);
 hipError_t launch_build(DType dt, int rank, const BuildArgs& a, hipStream_t s);
@@ -148,5 +151,11 @@ hipError_t launch_build16(DType dt, int rank, const BuildArgs& a, hipStream_t s)
 bool select_attn_fusable(const SelectArgs& se);
 int select_attn_splits(int k);  // attention splits of the fused launch
 hipError_t launch_select_attn(DType dt, const SelectArgs& se, const AttnArgs& a, hipStream_t s);
+// Decode step with the chunked selection: attention over the selection merged
+// from the chunk lists (launch_select_lists) by every attention wave; split 0
+// writes the selection when se.sel_pages is set.  One unit per wave,
+// a.n_splits = list_attn_splits(k).
+int list_attn_splits(int k);
+hipError_t launch_list_attn(DType dt, const SelectArgs& se, const AttnArgs& a, hipStream_t s);
 
 }  // namespace lk

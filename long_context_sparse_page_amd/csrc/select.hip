@@ -37,31 +37,6 @@ constexpr int kChunkMaxChunks = 12;
 constexpr int kChunkPairsBelow = 128;                     // fewer pairs than this
 static_assert(kChunkNPT * kChunkThreads == kSelChunkPages, "chunk tiling");
 
-// One wave: the n largest of the list keys ck (CR per lane, entry lane + 64 r,
-// 0 = no entry; at least n nonzero), ties to the earlier entries; emit(slot, r)
-// for each taken entry of this lane, slot = its rank in list order.  Returns
-// how many entries of row 0 (entries 0 .. 63) were taken.
-template <int CR, typename Emit>
-__device__ __forceinline__ int wave_take_in_order(const uint32_t (&ck)[CR], int n, Emit emit) {
-  const uint32_t t = wave_nth_largest<CR>(ck, n);
-  int n_gt = 0;
-#pragma unroll
-  for (int r = 0; r < CR; ++r) n_gt += __popcll(__ballot(ck[r] > t));
-  const int take_eq = n - n_gt;
-  int eq_before = 0, out_before = 0, row0 = 0;
-#pragma unroll
-  for (int r = 0; r < CR; ++r) {
-    const bool eq = ck[r] == t;
-    const uint64_t be = __ballot(eq);
-    const bool take = ck[r] > t || (eq && eq_before + lanes_below(be) < take_eq);
-    eq_before += __popcll(be);
-    const uint64_t bs = __ballot(take);
-    if (take) emit(out_before + lanes_below(bs), r);
-    out_before += __popcll(bs);
-    if (r == 0) row0 = out_before;
-  }
-  return row0;
-}
 }  // namespace
 
 int select_chunk_capacity(int max_pages, int k) {
@@ -384,8 +359,7 @@ __global__ __launch_bounds__(kWave) void select_merge_kernel(SelectArgs a) {
     return;
   }
   const int n_cand = n_mr > 0 ? n_mr - 1 : 0;
-  const int n_top = min(ktop, n_cand);
-  if (n_top == n_cand) {  // every page 0 .. n_mr
+  if (min(ktop, n_cand) == n_cand) {  // every page 0 .. n_mr
     for (int s = lane; s < k; s += kWave) {
       sel[s] = s <= n_mr ? s : -1;
       if (selp) selp[s] = s <= n_mr ? valid_phys(bt[s]) : -1;
@@ -393,6 +367,11 @@ __global__ __launch_bounds__(kWave) void select_merge_kernel(SelectArgs a) {
     if (lane == 0) a.sel_count[pair] = n_mr + 1;
     return;
   }
+  // k - 2 entries, fewer only if non-finite scores left keys at zero
+  int nz = 0;
+#pragma unroll
+  for (int r = 0; r < CR; ++r) nz += __popcll(__ballot(ck[r] != 0u));
+  const int n_top = min(ktop, nz);
   if (lane == 0) {
     sel[0] = 0;
     sel[n_top + 1] = n_mr;
@@ -403,17 +382,18 @@ __global__ __launch_bounds__(kWave) void select_merge_kernel(SelectArgs a) {
     sel[s] = -1;
     if (selp) selp[s] = -1;
   }
-  wave_take_in_order<CR>(ck, n_top, [&](int slot, int r) {
+  if (n_top > 0) wave_take_in_order<CR>(ck, n_top, [&](int slot, int r) {
     sel[1 + slot] = cp[r];
     if (selp) selp[1 + slot] = valid_phys(cq[r]);
   });
 }
 
 template <int G>
-static hipError_t launch_chunked_g(const SelectArgs& a, hipStream_t s) {
+static hipError_t launch_chunked_g(const SelectArgs& a, hipStream_t s, bool merge) {
   const dim3 cg(a.n_chunks, a.hkv, a.batch);
   hipLaunchKernelGGL((select_part_kernel<G>), cg, dim3(kPartThreads), 0, s, a);
   hipLaunchKernelGGL((select_chunk_kernel<G>), cg, dim3(kChunkThreads), 0, s, a);
+  if (!merge) return hipGetLastError();
   const int entries = a.n_chunks * (a.k - 2);  // list slots, all read by the merge
   const dim3 mg(a.hkv, a.batch);
   if (entries <= kWave) hipLaunchKernelGGL((select_merge_kernel<1>), mg, dim3(kWave), 0, s, a);
@@ -425,15 +405,15 @@ static hipError_t launch_chunked_g(const SelectArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-static hipError_t launch_chunked(const SelectArgs& a, hipStream_t s) {
+static hipError_t launch_chunked(const SelectArgs& a, hipStream_t s, bool merge) {
   if (a.n_chunks != select_chunks(a.batch, a.hkv, a.max_pages, a.k) || a.n_chunks <= 0 || !a.cand_key ||
       !a.cand_page || !a.cand_phys || !a.cand_cnt || !a.chunk_ms)
     return hipErrorInvalidValue;
   switch (a.group) {
-    case 1: return launch_chunked_g<1>(a, s);
-    case 2: return launch_chunked_g<2>(a, s);
-    case 4: return launch_chunked_g<4>(a, s);
-    case 8: return launch_chunked_g<8>(a, s);
+    case 1: return launch_chunked_g<1>(a, s, merge);
+    case 2: return launch_chunked_g<2>(a, s, merge);
+    case 4: return launch_chunked_g<4>(a, s, merge);
+    case 8: return launch_chunked_g<8>(a, s, merge);
     default: return hipErrorInvalidValue;
   }
 }
@@ -464,9 +444,14 @@ static hipError_t launch_sel_g(int G, dim3 grid, const SelectArgs& a, hipStream_
   return hipGetLastError();
 }
 
+hipError_t launch_select_lists(const SelectArgs& a, hipStream_t s) {
+  if (a.k > kMaxSelect || a.group > kMaxGroup || a.n_chunks <= 0) return hipErrorInvalidValue;
+  return launch_chunked(a, s, false);
+}
+
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   if (a.k > kMaxSelect || a.group > kMaxGroup) return hipErrorInvalidValue;
-  if (a.n_chunks > 0) return launch_chunked(a, s);
+  if (a.n_chunks > 0) return launch_chunked(a, s, true);
   const int n = a.max_pages;  // bound on scored pages per sequence
   const int G = a.group;
   dim3 grid(a.hkv, a.batch);

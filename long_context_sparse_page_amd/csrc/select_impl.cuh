@@ -120,6 +120,32 @@ __device__ __forceinline__ uint32_t wave_nth_largest(const uint32_t (&x)[R], int
   return t;
 }
 
+// One wave: the n largest of the list keys ck (CR per lane, entry lane + 64 r,
+// 0 = no entry; at least n nonzero), ties to the earlier entries; emit(slot, r)
+// for each taken entry of this lane, slot = its rank in list order.  Returns
+// how many entries of row 0 (entries 0 .. 63) were taken.
+template <int CR, typename Emit>
+__device__ __forceinline__ int wave_take_in_order(const uint32_t (&ck)[CR], int n, Emit emit) {
+  const uint32_t t = wave_nth_largest<CR>(ck, n);
+  int n_gt = 0;
+#pragma unroll
+  for (int r = 0; r < CR; ++r) n_gt += __popcll(__ballot(ck[r] > t));
+  const int take_eq = n - n_gt;
+  int eq_before = 0, out_before = 0, row0 = 0;
+#pragma unroll
+  for (int r = 0; r < CR; ++r) {
+    const bool eq = ck[r] == t;
+    const uint64_t be = __ballot(eq);
+    const bool take = ck[r] > t || (eq && eq_before + lanes_below(be) < take_eq);
+    eq_before += __popcll(be);
+    const uint64_t bs = __ballot(take);
+    if (take) emit(out_before + lanes_below(bs), r);
+    out_before += __popcll(bs);
+    if (r == 0) row0 = out_before;
+  }
+  return row0;
+}
+
 // Page-order positions of the entries flagged by pred(i), thread t holding
 // pages t + BS*i (i < NPT <= 64): one ballot per slot, the [NPT][NW] wave
 // counts through LDS (one barrier); lane l of each wave then sums column l

@@ -556,6 +556,33 @@ def test_selector_tiers(gpu, T, budget, capacity, group, pad):
         assert (cnt == 1).all() and (sp[:, 0] == 0).all() and (sp[:, 1:] == -1).all()
 
 
+@pytest.mark.parametrize("group", [2, 8])
+def test_chunked_decode_step_without_selection_outputs(gpu, group):
+    """The decode step through the chunked selection, once with the selection
+    written out and once without: bit-identical attention outputs and LSEs,
+    and lengths advanced alike (the attention waves merge the chunk lists
+    themselves either way)."""
+    T = 64 * 700 + 40
+    say("chunked decode step with and without selection outputs: G", group)
+    outs = []
+    for with_sel in (True, False):
+        w, dc, K, V, q64 = _selector_case(T, 1024, capacity=5000, group=group, hold_last=True)
+        o = dc.outputs()
+        kn, vn = dc.held
+        dc.decode_step(ref.q_device(q64, w.dtype), to_storage(kn, w.dtype).cuda()[None],
+                       to_storage(vn, w.dtype).cuda()[None], o, with_sel=with_sel)
+        torch.cuda.synchronize()
+        assert dc.seq_lens.cpu().tolist() == [T]
+        outs.append((o["out"].cpu().numpy(), o["lse"].cpu().numpy()))
+        if with_sel:
+            hs, _ = ref.oracle_head(w, q64[0], K, V, T)
+            sel = [int(x) for x in o["sel"].cpu().numpy()[0, 0, :o["cnt"].cpu().numpy()[0, 0]]]
+            msg = ref.selection_mismatch(sel, hs.selected, hs.m_bar, lo.most_recent_page(T, w.page_size),
+                                         lo.page_budget(w.token_budget, w.page_size))
+            assert msg is None, msg
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
 def _spread_hot_copies(kk, q):
     """41 tied dominant pages spread over several 2048-page chunks."""
     n = kk.shape[0] // 64
