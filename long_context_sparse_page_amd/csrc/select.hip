@@ -17,7 +17,8 @@
 //     candidates when fewer);
 //   select_merge_kernel, one wave per pair: the top-(k-2) of the concatenated
 //     chunk lists, ties to the earlier entry = the lower page, written as
-//     select_block writes the selection.
+//     select_block writes the selection (lk_score_select; the decode step
+//     instead merges the lists in its attention launch, list_attn_kernel).
 // A page of a top-(k-2) under that order is within the top-(k-2) of any
 // subset holding it (its chunk), so the lists hold every page the pair's
 // selection needs.
