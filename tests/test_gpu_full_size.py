@@ -76,6 +76,7 @@ def _check_structure(w, sel, cnt, out, lse, lens):
     (4, 4, 256, "kv"),
     (4, 16, 4096, "kv"),
     (2, None, None, "i4"),    # 128K x 4 with int4 / int8 summary records
+    (3, None, None, "i4"),    # one 1M-token sequence with int4 / int8 records (chunked selection)
 ])
 def test_full_size_decode(gpu, wid, rank, budget, summary):
     steps = 2
