@@ -259,7 +259,7 @@ def main():
             "peak": 8000.0,
             "unit": "GB/s",
             "frac": score_gbs / 8000.0,
-            "traffic": recorded_traffic(TRAFFIC_PROFILE[args.summary]),
+            "traffic": recorded_traffic(TRAFFIC_PROFILE[args.summary]) if args.workload in TRAFFIC_WORKLOADS else None,
             "launch_us": score_ms * 1e3,
             "bytes_per_launch": score_bytes,
         },
@@ -321,8 +321,11 @@ def bulk_build_page16(L, w, bulk, reps, stream, ev0, ev1):
             "page_heads_per_s": pages16 * hkv / (build16_ms * 1e-3)}
 
 
+# scorer HBM traffic per launch, from rocprofv3 counters taken on the 128K x 4
+# workload: reported for that workload only (other workloads move other bytes)
 TRAFFIC_PROFILE = {"kv": "profiles/score_mfma_128K_b4_hbm_traffic.txt",
                    "i4": "profiles/score_q4_128K_b4_hbm_traffic.txt"}
+TRAFFIC_WORKLOADS = (2,)
 
 
 def recorded_traffic(profile):
