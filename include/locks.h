@@ -135,9 +135,11 @@ int32_t lk_page_budget(const lk_config* cfg);
 
 /* Workspace bytes that every entry point below needs for `batch` sequences of
  * up to `max_pages_per_seq` pages.  One workspace of this size serves all of
- * them; it holds intermediate scores, selections and attention partials, and
- * its contents need no initialization.  Calls that share a workspace must be
- * ordered on one stream (concurrent calls on one workspace race). */
+ * them, and every smaller batch; it holds intermediate scores, selections,
+ * the per-chunk candidate lists that long tables with few (sequence, KV head)
+ * pairs are selected through, and attention partials, and its contents need
+ * no initialization.  Calls that share a workspace must be ordered on one
+ * stream (concurrent calls on one workspace race). */
 lk_status lk_workspace_size(const lk_config* cfg, int32_t batch,
                             int32_t max_pages_per_seq, size_t* bytes);
 
