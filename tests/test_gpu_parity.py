@@ -544,6 +544,8 @@ def test_decode_step_selection(gpu, T, budget, capacity, group, layout, expect):
     (64 * 3000 + 5, 4096, 20000, 4, 0),    # chunked, 10 chunks of 62 candidates (largest merge list)
     (64 * 3000 + 5, 4096, 20000, 4, 127),  # 24 pages per thread
     (64 * 20 + 9, 2048, 5000, 4, 0),       # chunked table, every page selected (shares still written)
+    (64 * 2000 + 7, 2048, 5000, 1, 0),     # chunked at G = 1
+    (64 * 2000 + 7, 256, 5000, 4, 0),      # chunked, k = 4: two candidates per chunk list
 ])
 def test_selector_tiers(gpu, T, budget, capacity, group, pad):
     say("selector tier: T", T, "budget", budget, "capacity", capacity, "G", group, "pad", pad)
