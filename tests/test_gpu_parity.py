@@ -374,16 +374,16 @@ def test_decode_step_table_full(gpu):
     assert torch.isfinite(o["out"][0].float()).all()
 
 
-def _selector_case(T, budget, capacity=None, group=4, layout=None, hold_last=False, pad=0):
+def _selector_case(T, budget, capacity=None, group=4, layout=None, hold_last=False, pad=0, pad_len=1):
     """fp32 cache whose sequence 0 holds T tokens whose keys may be rearranged
     by ``layout(keys)`` (page copies make exact ties); returns the workload,
     cache, host K/V pages and fp64 queries.  hold_last: the cache holds the
     first T - 1 tokens only (T % 64 != 0), for a decode step to append the last.
-    pad: that many more sequences of one token each (one page of capacity), so
-    that a wide table is selected with many (sequence, KV head) pairs."""
+    pad: that many more sequences of pad_len tokens each (one page of capacity),
+    so that a wide table is selected with many (sequence, KV head) pairs."""
     w = synth.workload(0, budget=budget)
     w.batch = 1 + pad
-    w.context = [T] + [1] * pad
+    w.context = [T] + [pad_len] * pad
     w.num_q_heads = group
     caps = [capacity or w.pages_needed(0)] + [1] * pad
     dc = DeviceCache(w, poison=True, capacity_pages=caps if (capacity or pad) else None)
@@ -533,29 +533,34 @@ def test_decode_step_selection(gpu, T, budget, capacity, group, layout, expect):
 # Tables wider than 3072 pages: with fewer than 128 (sequence, KV head) pairs
 # the chunked selection (chunk workgroups, then a merge per pair), with 128
 # pairs (pad 127) one 1024-thread workgroup per pair.
-@pytest.mark.parametrize("T,budget,capacity,group,pad", [
-    (64 * 101 + 3, 4096, None, 4, 0),      # fewer threads hold candidates than the budget needs
-    (64 * 300 + 7, 2048, 3300, 4, 0),      # chunked, 2 chunks
-    (64 * 300 + 7, 2048, 3300, 4, 127),    # 1024-thread tier, scores loaded twice
-    (64 * 700 + 40, 1024, 13000, 4, 0),    # chunked, 7 chunks
-    (64 * 700 + 40, 1024, 13000, 4, 127),  # 17 pages per thread
-    (64 * 500 + 1, 2048, 9000, 8, 0),      # chunked at G = 8
-    (64 * 500 + 1, 2048, 9000, 8, 127),    # 1024-thread tier at G = 8
-    (64 * 3000 + 5, 4096, 20000, 4, 0),    # chunked, 10 chunks of 62 candidates (largest merge list)
-    (64 * 3000 + 5, 4096, 20000, 4, 127),  # 24 pages per thread
-    (64 * 20 + 9, 2048, 5000, 4, 0),       # chunked table, every page selected (shares still written)
-    (64 * 2000 + 7, 2048, 5000, 1, 0),     # chunked at G = 1
-    (64 * 2000 + 7, 256, 5000, 4, 0),      # chunked, k = 4: two candidates per chunk list
+@pytest.mark.parametrize("T,budget,capacity,group,pad,pad_len", [
+    (64 * 101 + 3, 4096, None, 4, 0, 1),      # fewer threads hold candidates than the budget needs
+    (64 * 300 + 7, 2048, 3300, 4, 0, 1),      # chunked, 2 chunks
+    (64 * 300 + 7, 2048, 3300, 4, 127, 1),    # 1024-thread tier, scores loaded twice
+    (64 * 700 + 40, 1024, 13000, 4, 0, 1),    # chunked, 7 chunks
+    (64 * 700 + 40, 1024, 13000, 4, 127, 1),  # 17 pages per thread
+    (64 * 500 + 1, 2048, 9000, 8, 0, 1),      # chunked at G = 8
+    (64 * 500 + 1, 2048, 9000, 8, 127, 1),    # 1024-thread tier at G = 8
+    (64 * 3000 + 5, 4096, 20000, 4, 0, 1),    # chunked, 10 chunks of 62 candidates (largest merge list)
+    (64 * 3000 + 5, 4096, 20000, 4, 127, 1),  # 24 pages per thread
+    (64 * 20 + 9, 2048, 5000, 4, 0, 1),       # chunked table, every page selected (shares still written)
+    (64 * 2000 + 7, 2048, 5000, 1, 0, 1),     # chunked at G = 1
+    (64 * 2000 + 7, 256, 5000, 4, 0, 1),      # chunked, k = 4: two candidates per chunk list
+    (64 * 700 + 40, 1024, 5000, 4, 3, 1),   # chunked, with three one-token sequences in the batch
+    (64 * 700 + 40, 1024, 5000, 4, 3, 0),   # chunked, with three empty sequences in the batch
 ])
-def test_selector_tiers(gpu, T, budget, capacity, group, pad):
-    say("selector tier: T", T, "budget", budget, "capacity", capacity, "G", group, "pad", pad)
-    w, dc, K, V, q64 = _selector_case(T, budget, capacity=capacity, group=group, pad=pad)
+def test_selector_tiers(gpu, T, budget, capacity, group, pad, pad_len):
+    say("selector tier: T", T, "budget", budget, "capacity", capacity, "G", group, "pad", pad, "x", pad_len)
+    w, dc, K, V, q64 = _selector_case(T, budget, capacity=capacity, group=group, pad=pad, pad_len=pad_len)
     sel, hs, o = _run_selector(w, dc, K, V, q64, outputs=True)
     assert len(sel) == len(hs.selected)
-    if pad:  # the one-token sequences: nothing scored, the sink page alone
+    if pad:  # the short sequences: one token -> the sink page alone; empty -> nothing
         cnt = o["cnt"].cpu().numpy()[1:, 0]
         sp = o["sel"].cpu().numpy()[1:, 0]
-        assert (cnt == 1).all() and (sp[:, 0] == 0).all() and (sp[:, 1:] == -1).all()
+        if pad_len:
+            assert (cnt == 1).all() and (sp[:, 0] == 0).all() and (sp[:, 1:] == -1).all()
+        else:
+            assert (cnt == 0).all() and (sp == -1).all()
 
 
 @pytest.mark.parametrize("group", [2, 8])
