@@ -230,8 +230,9 @@ def test_build_and_score_bf16(gpu):
 
 
 def test_decode_steps_bf16(gpu):
-    """lk_decode_step over many steps (pages complete and are built in-stream)."""
-    w = small_bf16(batch=3, ctx=(64 * 3 - 5, 64 * 7 + 60, 1), steps=70, budget=256)
+    """lk_decode_step over many steps (pages complete and are built in-stream);
+    the last sequence starts empty, so its first step appends token 0."""
+    w = small_bf16(batch=4, ctx=(64 * 3 - 5, 64 * 7 + 60, 1, 0), steps=70, budget=256)
     say("decode steps bf16", w.context, "steps", w.steps)
     dc = DeviceCache(w, poison=True)
     dc.fill_from_synth()
