@@ -295,13 +295,19 @@ def page_budget(token_budget: int, page_size: int) -> int:
 
 
 def most_recent_page(seq_len: int, page_size: int) -> int:
-    """Index of the page that holds the newest token."""
+    """Index of the page that holds the newest token; -1 for an empty sequence
+    (no token, hence no page)."""
+    if seq_len <= 0:
+        return -1
     return (seq_len - 1) // page_size
 
 
 def select_pages(m_bar, n_mr: int, k: int) -> np.ndarray:
     """Sink page 0, the most recent page n_mr, and the top-(k-2) candidates
-    1..n_mr-1 by m_bar (ties to the lower index); ascending page indices."""
+    1..n_mr-1 by m_bar (ties to the lower index); ascending page indices.
+    An empty sequence (n_mr < 0) has no page to select."""
+    if n_mr < 0:
+        return np.zeros(0, dtype=np.int64)
     if n_mr == 0:
         return np.array([0], dtype=np.int64)
     m_bar = np.asarray(m_bar, dtype=np.float64)
@@ -316,7 +322,10 @@ def select_pages(m_bar, n_mr: int, k: int) -> np.ndarray:
 # ----------------------------------------------------------------------------
 def gather_tokens(pages_kv, pages, seq_len: int, page_size: int) -> np.ndarray:
     """Tokens of the listed logical pages, in page order; the page holding the
-    newest token contributes only its filled slots.  ``pages_kv`` [n, B, d]."""
+    newest token contributes only its filled slots.  ``pages_kv`` [n, B, d].
+    No page gives an empty [0, d] array."""
+    if len(pages) == 0:
+        return np.zeros((0, pages_kv.shape[-1]))
     out = []
     for j in pages:
         filled = min(page_size, seq_len - j * page_size)
@@ -326,8 +335,12 @@ def gather_tokens(pages_kv, pages, seq_len: int, page_size: int) -> np.ndarray:
 
 def attend(q, keys, values, scale: float):
     """o = sum_i alpha_i v_i with alpha = softmax(q^T k * scale); also the
-    log-sum-exp of the logits.  ``q`` [G, d], ``keys``/``values`` [T, d]."""
+    log-sum-exp of the logits.  ``q`` [G, d], ``keys``/``values`` [T, d].
+    With no token (an empty sequence) the sum is empty: o = 0 and the
+    log-sum-exp is log 0 = -inf."""
     q = np.asarray(q, dtype=np.float64)
+    if np.asarray(keys).shape[0] == 0:
+        return np.zeros((q.shape[0], np.asarray(values).shape[-1])), np.full(q.shape[0], -np.inf)
     z = scale * (q @ np.asarray(keys, dtype=np.float64).T)   # [G, T]
     m = z.max(axis=1, keepdims=True)
     w = np.exp(z - m)

@@ -321,6 +321,30 @@ def test_gather_tokens_partial_tail_and_decode_head_dense_limit():
     assert list(hs.selected) == [0]
 
 
+def test_empty_sequence_selects_nothing_and_attends_to_nothing():
+    """A sequence with no token holds no page: the selection is empty (its size
+    min(k, n_mr + 1) is 0), and attention is an empty sum, whose log-sum-exp is
+    log 0 = -inf (as torch.logsumexp gives over an empty axis) and whose output
+    is the zero vector."""
+    rng = np.random.default_rng(17)
+    B, d, G, k = 8, 16, 2, 4
+    keys = rng.standard_normal((3, B, d))
+    vals = rng.standard_normal((3, B, d))
+    q = rng.standard_normal((G, d))
+    for T in range(0, 3 * B + 1):
+        n_mr = lo.most_recent_page(T, B)
+        assert n_mr == (-1 if T == 0 else (T - 1) // B)
+        s = lo.build_page_summaries(keys[:max(n_mr, 0)], 4)
+        hs = lo.decode_head(q, keys, vals, T, s, token_budget=k * B, scale=0.25)
+        assert len(hs.selected) == min(k, n_mr + 1)
+        assert hs.page_lse.shape == (G, max(n_mr, 0))
+    hs = lo.decode_head(q, keys, vals, 0, lo.build_page_summaries(keys[:0], 4), token_budget=k * B, scale=0.25)
+    assert hs.selected.size == 0 and hs.m_bar.size == 0
+    empty_lse = torch.logsumexp(torch.empty((G, 0), dtype=torch.float64), dim=1).numpy()
+    np.testing.assert_array_equal(hs.lse, empty_lse)
+    np.testing.assert_array_equal(hs.out, np.zeros((G, d)))
+
+
 # ---------------------------------------------------------------- byte model
 def test_table_d10_byte_accounting(golden_dir):
     g = json.load(open(os.path.join(golden_dir, "table_d10_bytes.json")))
