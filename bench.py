@@ -32,12 +32,13 @@ def parse():
     p.add_argument("--layers", type=int, default=4, help="layer copies rotated across steps")
     p.add_argument("--kernel-reps", type=int, default=200, help="timed launches of the scorer alone")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--cpu-steps", type=int, default=3, help="whole oracle steps timed for the CPU baseline")
     p.add_argument("--summary", choices=("kv", "i4"), default="kv",
                    help="page summaries in the KV dtype (bf16, the default) or int4 basis / int8 rows")
     p.add_argument("--workload", type=int, choices=(2, 3, 4), default=2,
                    help="2: 128K x 4 (the headline); 3: one 1M-token sequence; "
                         "4: 64 sequences of 4K..256K tokens (in-stream builds in most steps)")
+    p.add_argument("--no-q4", action="store_true", help="skip the int4 / int8 record run of the default line")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="also run a plain device copy of this size (counter calibration)")
     return p.parse_args()
@@ -62,7 +63,11 @@ def main():
     # further steps timed one by one (in-stream build split, below): a page per
     # layer copy, so each copy's sequences complete exactly one page in them
     extra = synth.workload(args.workload).page_size * args.layers
-    w = synth.workload(args.workload, steps=per_layer + 1 + -(-extra // args.layers), summary=args.summary)
+    # the default line also times the same step with int4 / int8 summary
+    # records on the same cache (a second summary pool per layer copy)
+    with_q4 = args.summary == "kv" and args.workload == 2 and not args.no_q4
+    runs = 2 if with_q4 else 1
+    w = synth.workload(args.workload, steps=runs * per_layer + 1 + -(-extra // args.layers), summary=args.summary)
     B, d, G, hkv, hq = w.page_size, w.head_dim, w.group, w.num_kv_heads, w.num_q_heads
     e = 2  # bf16
     t0 = time.time()
@@ -215,6 +220,9 @@ def main():
     torch.cuda.synchronize()
     per = np.array([evs[j].elapsed_time(evs[j + 1]) * 1e3 for j in range(extra)])
     with_b = np.array(builds)
+    step_us = {"median": float(np.median(per)), "p10": float(np.percentile(per, 10)),
+               "p90": float(np.percentile(per, 90)), "mean": float(per.mean()), "steps": int(extra),
+               "note": "one event pair per step (adds a little per step over the window mean)"}
     in_stream = {"steps": extra, "steps_with_build": int(with_b.sum()),
                  "us_median_without_build": float(np.median(per[~with_b])) if (~with_b).any() else None,
                  "us_median_with_build": float(np.median(per[with_b])) if with_b.any() else None}
@@ -267,8 +275,14 @@ def main():
                            "speedup_of_locks_step": dense_ms / ms_per_step},
         "bulk_build": {"pages": len(ids), "page_heads": len(ids) * hkv, "ms": build_ms,
                        "page_heads_per_s": len(ids) * hkv / (build_ms * 1e-3)},
+        "step_us": step_us,
         "in_stream_build": in_stream,
     }
+    ceil = hbm_ceilings(torch, stream)
+    result["hbm_ceilings"] = ceil
+    result["step_frac_of_read_ceiling"] = result["achieved_GBps"] / ceil["read_GBps"]
+    if with_q4:
+        result["int4_records"] = q4_variant(L, w, layers, qs, kns, vns, out, lse, stream, args, ws, ws_bytes)
     if page16 is not None:
         result["bulk_build_page16_r8i4"] = page16
 
@@ -283,8 +297,110 @@ def main():
         result["copy_calibration_bytes"] = args.copy_bytes
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, lens_now, args.cpu_seconds)
+        result["cpu_baseline"] = run_cpu_baseline(w, lens_now, args.cpu_steps)
     print(json.dumps(result), flush=True)
+
+
+def hbm_ceilings(torch, stream):
+    """Same-run reference rates: a 2 GiB fp32 sum (reads only) and a 1 GiB
+    device copy (read + write), each timed over 10 calls."""
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    x = torch.ones(1 << 29, dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        x.sum()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(10):
+        x.sum()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    read = x.numel() * 4 / (ev0.elapsed_time(ev1) / 10 * 1e-3) / 1e9
+    del x
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    copy = 2 * src.numel() / (ev0.elapsed_time(ev1) / 10 * 1e-3) / 1e9
+    return {"read_GBps": read, "read_kind": "torch.sum over 2 GiB fp32",
+            "copy_GBps": copy, "copy_kind": "1 GiB device copy, read + write bytes"}
+
+
+def q4_variant(L, w, layers, qs, kns, vns, out, lse, stream, args, ws, ws_bytes):
+    """The default step with int4 basis / int8 coefficient and centroid
+    records: every page complete at the current lengths of each layer copy is
+    summarized into a second (uint8) summary pool, then the step and the
+    scorer alone are timed as for the bf16 records."""
+    import torch
+
+    B, d, G, hkv, hq = w.page_size, w.head_dim, w.group, w.num_kv_heads, w.num_q_heads
+    sp = stream.cuda_stream
+    cfg = L.make_config(d, B, w.rank, hq, hkv, w.token_budget, L.LK_BF16, w.scale, L.LK_SUMMARY_I4)
+    rec = L.lk_summary_record_bytes(cfg)
+    need = L.lk_workspace_size(cfg, w.batch, layers[0].max_pages)
+    if need > ws_bytes:
+        ws, ws_bytes = torch.empty(need, dtype=torch.uint8, device="cuda"), need
+    caches = []
+    for c in layers:
+        pool = torch.empty((c.num_phys, hkv, rec), dtype=torch.uint8, device="cuda")
+        lens = [int(x) for x in c.seq_lens.cpu().tolist()]
+        ids = torch.tensor([int(p) for s in range(w.batch) for p in c.block_table_host[s, :lens[s] // B]],
+                           dtype=torch.int32, device="cuda")
+        cache = L.make_cache(c.k_pool, c.v_pool, pool, c.block_table, c.seq_lens)
+        L.lk_build_page_summary(cfg, cache, ids, ids.numel(), None, ws, ws_bytes, sp)
+        caches.append((cache, pool))
+    torch.cuda.synchronize()
+    n = len(caches)
+    nv = len(qs)
+
+    def step(i):
+        L.lk_decode_step(cfg, caches[i % n][0], w.batch, qs[i % nv], kns[i % nv], vns[i % nv], out, lse,
+                         None, None, ws, ws_bytes, sp)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.warmup, args.warmup + args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    lens_now = [int(x) for x in layers[0].seq_lens.cpu().tolist()]
+    k_pages = L.lk_page_budget(cfg)
+    e = 2
+    step_bytes = w.batch * (2 * hq * d * e + 2 * hkv * d * e * 2)
+    for T in lens_now:
+        n_mr = (T - 1) // B
+        step_bytes += hkv * (n_mr * (rec + 4 * G) + ((min(k_pages, n_mr + 1) - 1) * B + T - n_mr * B) * 2 * d * e)
+    page_lse = torch.empty((w.batch, hq, layers[0].max_pages), dtype=torch.float32, device="cuda")
+
+    def score(i):
+        L.lk_score_select(cfg, caches[i % n][0], w.batch, qs[i % nv], page_lse, None, None, None, ws, ws_bytes, sp)
+    for i in range(8):
+        score(i)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.kernel_reps):
+        score(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    score_ms = ev0.elapsed_time(ev1) / args.kernel_reps
+    score_bytes = sum(hkv * ((T - 1) // B) for T in lens_now) * (rec + 4 * G)
+    return {"records": "int4 basis (per-vector fp16 scales), int8 coefficients (per-token scales) and centroid",
+            "record_bytes": rec, "ms_per_step": ms, "steps_per_s": 1e3 / ms,
+            "algorithmic_bytes_per_step": step_bytes, "achieved_GBps": step_bytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": step_bytes / (ms * 1e-3) / 8e12,
+            "scorer": {"kernel": "score_q4_kernel", "launch_us": score_ms * 1e3, "bytes_per_launch": score_bytes,
+                       "achieved_GBps": score_bytes / (score_ms * 1e-3) / 1e9,
+                       "frac": score_bytes / (score_ms * 1e-3) / 8e12,
+                       "traffic": recorded_traffic(TRAFFIC_PROFILE["i4"])}}
 
 
 def bulk_build_page16(L, w, bulk, reps, stream, ev0, ev1):
@@ -349,45 +465,174 @@ def recorded_traffic(profile):
         return None
 
 
-def cpu_baseline(w, lens_now, seconds):
-    """The fp64 oracle, single-threaded, on a bounded sample: one (sequence, KV
-    head) pair of the same workload at the same length, its score + share +
-    select + attend timed over repeated steps and scaled to a whole step
-    (batch x KV heads pairs).  Its summary build is not timed."""
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_worker(conn, wargs, pairs, lens):
+    """One process of the CPU baseline: holds its (sequence, KV head) pairs'
+    stored K / V, the oracle's own summaries of their complete pages and a
+    query, then runs the oracle's decode step on them whenever asked."""
     from threadpoolctl import threadpool_limits
 
     from long_context_sparse_page_amd import synth
     from oracle import locks_oracle as lo
 
-    sys.path.insert(0, os.path.join(os.path.dirname(os.path.abspath(__file__)), "tests"))
-    import reference as ref
-
-    T = lens_now[0]
-    k = lo.page_budget(w.token_budget, w.page_size)
-    # per-pair oracle cost grows with the scored and attended pages: other
-    # lengths are scaled from the sampled pair by (n_mr + k)
-    n0 = lo.most_recent_page(T, w.page_size) + k
-    scale = sum(w.num_kv_heads * (lo.most_recent_page(t, w.page_size) + k) / n0 for t in lens_now)
+    w = synth.workload(wargs["wid"], rank=wargs["rank"], budget=wargs["budget"], steps=wargs["steps"],
+                       summary=wargs["summary"])
+    w.batch, w.context = wargs["batch"], list(wargs["context"])
     with threadpool_limits(limits=1):
-        K, V = ref.host_pages(w, 0, 0, T)
-        n_mr = lo.most_recent_page(T, w.page_size)
-        summ = ref.oracle_summaries(w, K, n_mr)
-        q64 = ref.stored(synth.queries(w, 0, 0, 0, T)[0], w.dtype)
-        n, t0 = 0, time.perf_counter()
-        while True:
-            lo.decode_head(q64, K, V, T, summ, w.token_budget, w.scale)
-            n += 1
-            el = time.perf_counter() - t0
-            if el >= seconds:
-                break
-    per_pair = el / n
-    pairs = w.batch * w.num_kv_heads
-    how = (f"scaled x{pairs} to one step" if len(set(lens_now)) == 1 else
-           f"scaled x{scale:.1f} to one step's {pairs} pairs by scored + attended pages")
-    return {"value": 1.0 / (per_pair * scale), "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"1 of {pairs} (sequence, KV head) pairs at {T} tokens, {n} steps of score+share+select+"
-                      f"attend in fp64 ({el:.1f}s), {how}; host has {os.cpu_count()} cores"}
+        t0 = time.perf_counter()
+        data = []
+        B, d = w.page_size, w.head_dim
+        for (s, h) in pairs:
+            T = lens[s]
+            k, v = synth.keys_values(w, s, h)
+            n_pages = -(-T // B)
+            K = np.zeros((n_pages * B, d))
+            V = np.zeros((n_pages * B, d))
+            K[:T] = lo.storage_round(k[:T], w.dtype)
+            V[:T] = lo.storage_round(v[:T], w.dtype)
+            K, V = K.reshape(n_pages, B, d), V.reshape(n_pages, B, d)
+            n_mr = lo.most_recent_page(T, B)
+            if w.summary == "i4":
+                summ = lo.dequantize_summary(lo.quantize_summary(lo.build_page_summaries(K[:n_mr], w.rank, "f64")))
+            else:
+                summ = lo.build_page_summaries(K[:n_mr], w.rank, w.dtype)
+            q = lo.storage_round(synth.queries(w, 0, s, h, T)[0], w.dtype)
+            data.append((q, K, V, T, summ))
+        conn.send(time.perf_counter() - t0)
+        while conn.recv() == "step":
+            t0 = time.perf_counter()
+            for q, K, V, T, summ in data:
+                lo.decode_head(q, K, V, T, summ, w.token_budget, w.scale)
+            conn.send(time.perf_counter() - t0)
+
+
+def cpu_baseline(w, lens_now, steps=3, workers=None, max_pairs=64):
+    """The fp64 oracle's decode step (score + share + select + attend from its
+    own resident summaries, at the lengths the GPU reached) on the host: every
+    (sequence, KV head) pair of the batch (a seeded sample of max_pairs pairs
+    when there are more, scaled by scored + attended pages), spread over
+    ``workers`` processes of one thread each.  Each of ``steps`` whole steps
+    is timed twice: with every worker at once (all cores) and with the
+    workers one after another (one core).  Medians; the summary build is the
+    untimed setup."""
+    import multiprocessing as mp
+
+    P = workers or min(16, len(os.sched_getaffinity(0)))
+    all_pairs = [(s, h) for s in range(w.batch) for h in range(w.num_kv_heads)]
+    B = w.page_size
+    k = -(-w.token_budget // B)
+
+    def cost(p):  # scored pages + attended pages of a pair
+        return (lens_now[p[0]] - 1) // B + k
+
+    pairs = all_pairs
+    if len(all_pairs) > max_pairs:
+        idx = np.random.default_rng(20261202).choice(len(all_pairs), size=max_pairs, replace=False)
+        pairs = [all_pairs[i] for i in sorted(idx)]
+    scale = sum(cost(p) for p in all_pairs) / sum(cost(p) for p in pairs)
+    P = min(P, len(pairs))
+    wargs = {"wid": w.wid, "rank": w.rank, "budget": w.token_budget, "steps": w.steps, "summary": w.summary,
+             "batch": w.batch, "context": list(w.context)}
+
+    def recv(i):  # a worker's reply, or an error if it has died
+        while not conns[i].poll(1.0):
+            if not procs[i].is_alive():
+                raise RuntimeError(f"CPU baseline worker {i} ended (exit code {procs[i].exitcode})")
+        return conns[i].recv()
+
+    ctx = mp.get_context("fork")
+    conns, procs = [], []
+    for i in range(P):
+        a, b = ctx.Pipe()
+        pr = ctx.Process(target=_oracle_worker, args=(b, wargs, pairs[i::P], list(lens_now)), daemon=True)
+        pr.start()
+        conns.append(a)
+        procs.append(pr)
+    try:
+        setup = max(recv(i) for i in range(P))
+        t_all, t_one = [], []
+        for _ in range(steps):
+            t0 = time.perf_counter()
+            for c in conns:
+                c.send("step")
+            for i in range(P):
+                recv(i)
+            t_all.append(time.perf_counter() - t0)
+            one = 0.0
+            for i, c in enumerate(conns):  # one worker at a time: one core busy
+                c.send("step")
+                one += recv(i)
+            t_one.append(one)
+    finally:
+        for i, c in enumerate(conns):
+            if procs[i].is_alive():
+                c.send("quit")
+        for pr in procs:
+            pr.join(timeout=30)
+            if pr.is_alive():
+                pr.kill()
+    med_all = float(np.median(t_all)) * scale
+    med_one = float(np.median(t_one)) * scale
+    how = (f"all {len(all_pairs)} (sequence, KV head) pairs" if pairs is all_pairs else
+           f"a seeded sample of {len(pairs)} of {len(all_pairs)} pairs, scaled x{scale:.2f} by scored + "
+           f"attended pages")
+    return {"value": 1.0 / med_all, "unit": "steps/s", "cores": P, "kind": "oracle",
+            "sample": f"{how} at the lengths the GPU reached, score + share + select + attend in fp64 from "
+                      f"the oracle's own summaries; median of {steps} whole steps on {P} worker processes of "
+                      f"one thread; summary build untimed ({setup:.1f}s)",
+            "step_s_all_cores": med_all,
+            "one_core": {"value": 1.0 / med_one, "unit": "steps/s", "cores": 1, "step_s": med_one},
+            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count()}
+
+
+def cpu_baseline_child(argv):
+    """Entry of the CPU-baseline child process (no GPU work in it): prints one
+    JSON line."""
+    p = argparse.ArgumentParser()
+    p.add_argument("--workload", type=int)
+    p.add_argument("--rank", type=int)
+    p.add_argument("--budget", type=int)
+    p.add_argument("--steps-done", type=int)
+    p.add_argument("--summary")
+    p.add_argument("--lens")
+    p.add_argument("--context", default=None, help="initial lengths (default: the workload's)")
+    p.add_argument("--cpu-steps", type=int, default=3)
+    a = p.parse_args(argv)
+    from long_context_sparse_page_amd import synth
+
+    w = synth.workload(a.workload, rank=a.rank, budget=a.budget, steps=a.steps_done, summary=a.summary)
+    if a.context:
+        w.context = json.loads(a.context)
+        w.batch = len(w.context)
+    print(json.dumps(cpu_baseline(w, json.loads(a.lens), steps=a.cpu_steps)), flush=True)
+
+
+def run_cpu_baseline(w, lens_now, cpu_steps):
+    """The CPU baseline in a fresh child process (it holds no GPU state)."""
+    import subprocess
+
+    cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-child", "--workload", str(w.wid),
+           "--rank", str(w.rank), "--budget", str(w.token_budget), "--steps-done", str(w.steps),
+           "--summary", w.summary, "--lens", json.dumps([int(t) for t in lens_now]),
+           "--context", json.dumps([int(t) for t in w.context]),
+           "--cpu-steps", str(cpu_steps)]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=900)
+    if r.returncode != 0:
+        raise RuntimeError(f"CPU baseline failed:\n{r.stderr[-2000:]}")
+    return json.loads(r.stdout.strip().splitlines()[-1])
 
 
 if __name__ == "__main__":
-    main()
+    if len(sys.argv) > 1 and sys.argv[1] == "--cpu-baseline-child":
+        cpu_baseline_child(sys.argv[2:])
+    else:
+        main()

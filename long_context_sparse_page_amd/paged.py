@@ -29,7 +29,7 @@ def to_storage(x: np.ndarray, dtype: str) -> torch.Tensor:
 
 class DeviceCache:
     def __init__(self, w: synth.Workload, device: str = "cuda", perm_seed: int | None = 1,
-                 poison: bool = False, capacity_pages: list | None = None):
+                 poison: bool = False, capacity_pages: list | None = None, ws_fill: int | None = None):
         self.w = w
         self.device = device
         self.cfg = L.make_config(w.head_dim, w.page_size, w.rank, w.num_q_heads, w.num_kv_heads,
@@ -63,9 +63,28 @@ class DeviceCache:
         self.block_table = torch.from_numpy(bt).to(device)
         self.seq_lens = torch.tensor(w.context, dtype=torch.int32, device=device)
         self.ws_bytes = L.lk_workspace_size(self.cfg, w.batch, self.max_pages)
-        self.ws = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=device)  # zero once (arrival counters)
+        # the workspace needs no initialization; ws_fill writes a byte pattern
+        # into it (0xFF: NaN floats, -1 integers; the default with poison) for
+        # tests that check that
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        if ws_fill is None and poison:
+            ws_fill = 0xFF
+        if ws_fill is not None:
+            self.ws.fill_(ws_fill)
         self.cache = L.make_cache(self.k_pool, self.v_pool, self.summary_pool, self.block_table,
                                   self.seq_lens)
+
+    def set_budget(self, token_budget: int, ws_fill: int | None = 0xFF) -> None:
+        """Use another token budget on the same cache; the workspace is
+        reallocated (and filled with ws_fill) when the budget needs more."""
+        self.w.token_budget = token_budget
+        self.cfg.token_budget = token_budget
+        need = L.lk_workspace_size(self.cfg, self.w.batch, self.max_pages)
+        if need > self.ws_bytes:
+            self.ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+            if ws_fill is not None:
+                self.ws.fill_(ws_fill)
+        self.ws_bytes = max(need, self.ws_bytes)
 
     # ------------------------------------------------------------- filling
     def fill_from_synth(self, threads: int = 8) -> None:

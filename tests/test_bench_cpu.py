@@ -40,26 +40,37 @@ def test_recorded_traffic_follows_the_source_hash(tmp_path, monkeypatch):
     assert bench.recorded_traffic("missing.txt") is None
 
 
-def test_cpu_baseline_on_a_small_sample():
+def test_cpu_baseline_times_whole_steps():
+    """Every pair of the batch, whole steps on worker processes (all at once
+    and one at a time), medians, the CPU model recorded."""
     from long_context_sparse_page_amd import synth
 
-    w = synth.workload(0)
-    r = bench.cpu_baseline(w, list(w.context), 0.3)
-    assert r["kind"] == "oracle" and r["cores"] == 1 and r["unit"] == "steps/s"
-    assert r["value"] > 0
-    assert "1 of 1" in r["sample"]
+    w = synth.workload(0, batch=2)
+    w.context = [4064, 2 * 4064]
+    r = bench.cpu_baseline(w, list(w.context), steps=3, workers=2)
+    assert r["kind"] == "oracle" and r["cores"] == 2 and r["unit"] == "steps/s"
+    assert r["value"] > 0 and r["one_core"]["cores"] == 1 and r["one_core"]["value"] > 0
+    assert "all 2 (sequence, KV head) pairs" in r["sample"] and "median of 3 whole steps" in r["sample"]
+    assert r["cpu_model"]
 
 
-@pytest.mark.parametrize("lens,expect", [([4064, 4064], 2.0), ([4064, 2 * 4064], None)])
-def test_cpu_baseline_scales_by_pages(lens, expect):
-    """Equal lengths scale by the pair count; other lengths by scored + attended pages."""
+def test_cpu_baseline_sample_is_scaled_by_pages():
+    """More pairs than the sample holds: a seeded sample, scaled by scored +
+    attended pages, and said so."""
     from long_context_sparse_page_amd import synth
 
-    w = synth.workload(0)
-    w.batch = 2
+    w = synth.workload(0, batch=2)
     w.context = [4064, 4064]
-    r = bench.cpu_baseline(w, lens, 0.2)
-    if expect is not None:
-        assert "scaled x2 to one step" in r["sample"]
-    else:
-        assert "by scored + attended pages" in r["sample"]
+    r = bench.cpu_baseline(w, list(w.context), steps=3, workers=1, max_pairs=1)
+    assert "a seeded sample of 1 of 2 pairs, scaled x2.00" in r["sample"]
+    assert r["cores"] == 1
+
+
+def test_cpu_baseline_child_prints_one_json_line():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--cpu-baseline-child", "--workload", "0",
+                        "--rank", "8", "--budget", "512", "--steps-done", "0", "--summary", "kv",
+                        "--lens", "[4064]", "--cpu-steps", "3"], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    import json
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    assert d["kind"] == "oracle" and d["value"] > 0

@@ -212,21 +212,112 @@ def test_build_and_score_bf16(gpu):
     torch.cuda.synchronize()
     worst_iso = check_scores(w, dc, o, res, T, atol=1e-3)
     say("scorer isolation: max page LSE error", worst_iso)
-    # end to end: GPU-built records
+    # end to end: GPU-built records, every matching rule
     dc.build_all()
     o = dc.outputs()
     dc.score_select(qd, o)
     dc.sparse_attn(qd, o["sel"], o["cnt"], o)
     torch.cuda.synchronize()
-    page_lse = o["page_lse"].cpu().numpy()
-    errs = []
-    for (s, h), (hs, _, _, _) in res.items():
-        n_mr = lo.most_recent_page(T[s], w.page_size)
-        errs.append(np.abs(page_lse[s, h * w.group:(h + 1) * w.group, :n_mr] - hs.page_lse).ravel())
-    errs = np.concatenate(errs)
-    say("end-to-end bf16 page LSE error: max", errs.max(), "p99.9", np.quantile(errs, 0.999),
-        "frac>1e-3", (errs > 1e-3).mean())
-    assert errs.max() < 1e-2
+    tot = check_all_pairs(w, dc, o, q64, T)
+    say("end to end:", tot)
+
+
+def check_all_pairs(w, dc, o, q64, lens, pairs=None, page_lse=None, e2e_lse_gate=True):
+    """ref.check_pair on every (or the listed) (sequence, KV head) of the
+    outputs o, with the GPU's own records read back from the pool."""
+    page_lse = o["page_lse"].cpu().numpy() if page_lse is None else page_lse
+    sel, cnt = o["sel"].cpu().numpy(), o["cnt"].cpu().numpy()
+    out = o["out"].float().cpu().numpy().astype(np.float64)
+    lse = o["lse"].cpu().numpy()
+    G = w.group
+    tot = ref.PairCheck()
+    if pairs is None:
+        pairs = [(s, h) for s in range(w.batch) for h in range(w.num_kv_heads)]
+    for (s, h) in pairs:
+        K, V = ref.host_pages(w, s, h, lens[s])
+        n_mr = lo.most_recent_page(lens[s], w.page_size)
+        own = ref.gpu_summaries(dc, w, s, h, max(n_mr, 0))
+        hs = slice(h * G, (h + 1) * G)
+        tot.merge(ref.check_pair(w, q64[s, hs], K, V, lens[s], sel[s, h, :cnt[s, h]], own=own,
+                                 gpu_page_lse=page_lse[s, hs], gpu_out=out[s, hs], gpu_lse=lse[s, hs],
+                                 tag=f"seq {s} head {h} T {lens[s]}", e2e_lse_gate=e2e_lse_gate))
+        assert (sel[s, h, cnt[s, h]:] == -1).all()
+    return tot
+
+
+# Accuracy bar of the fp32 builder against the fp64 oracle on separated modes
+# (test_build_matches_oracle_fp32): basis entries within 2e-4, coefficients
+# within 2e-4 of the page's largest coefficient.
+FP32_BASIS_ATOL = 2e-4
+FP32_COEFF_RTOL = 2e-4
+
+
+@pytest.mark.parametrize("rank", [4, 8, 16])
+def test_bf16_records_match_oracle(gpu, rank):
+    """GPU-built bf16 records against the oracle's build rounded the same way
+    (round to nearest even from fp64): eigenvalues within 1e-5 lambda_1, and
+    captured energy sum_{k<=r} lambda_k and tail tau within 1e-5 relative on
+    every page; the centroid on every page and, where every kept mode is
+    separated (relative eigenvalue gaps >= 1e-2 up to mode r + 1), the basis
+    rows and coefficients (signs by the largest-entry convention).
+
+    Each stored element is the bf16 rounding of the builder's fp32 value, so
+    it can differ from the oracle's rounding by one ulp, and by more only
+    where the fp32 value itself is off by more than an ulp, i.e. on elements
+    far smaller than their vector.  Gates: the centroid within one ulp;
+    basis and coefficients within one ulp plus the fp32 builder's accuracy
+    bar, and at least 99.5% of their elements within one ulp."""
+    T = 64 * 40 + 5
+    w = small_bf16(batch=1, ctx=(T,), rank=rank)
+    say("bf16 records vs the oracle: T", T, "r", rank, "KV heads", w.num_kv_heads)
+    dc = DeviceCache(w, poison=True)
+    dc.fill_from_synth()
+    ids, ev = dc.build_all(eigvals=True)
+    torch.cuda.synchronize()
+    n = T // w.page_size
+    assert ids == dc.block_table_host[0, :n].tolist()
+    ev = ev.cpu().numpy().astype(np.float64)
+    ulps = {"centroid": [], "basis": [], "coeffs": []}
+    excess = {"basis": 0.0, "coeffs": 0.0}  # largest |gpu - oracle| - ulp, over the fp32 bar
+    compared = 0
+    for h in range(w.num_kv_heads):
+        K, _ = ref.host_pages(w, 0, h, T)
+        ora = lo.build_page_summaries(K[:n], rank, "bf16")
+        own = ref.gpu_summaries(dc, w, 0, h, n)
+        lam = ora.eigvals
+        lam1 = lam[:, :1]
+        assert (np.abs(ev[:, h] - lam) <= 1e-5 * lam1).all(), f"head {h}: eigenvalues"
+        cap_g, cap_o = ev[:, h, :rank].sum(1), lam[:, :rank].sum(1)
+        tail_g, tail_o = ev[:, h, rank:].sum(1), lam[:, rank:].sum(1)
+        assert (np.abs(cap_g - cap_o) <= 1e-5 * cap_o).all(), f"head {h}: captured energy"
+        assert (np.abs(tail_g - tail_o) <= 1e-5 * np.maximum(tail_o, lam[:, 0])).all(), f"head {h}: tail"
+        ulps["centroid"].append(ref.bf16_ulps(own.centroid, ora.centroid).ravel())
+        gaps = (lam[:, :rank] - lam[:, 1:rank + 1]) / lam1
+        ok = gaps.min(axis=1) >= 1e-2
+        compared += int(ok.sum())
+        if not ok.any():
+            continue
+        for key, g, o, bar in (
+                ("basis", own.basis[ok], ora.basis[ok], np.full((int(ok.sum()), 1, 1), FP32_BASIS_ATOL)),
+                ("coeffs", own.coeffs[ok], ora.coeffs[ok],
+                 FP32_COEFF_RTOL * np.abs(ora.coeffs[ok]).max(axis=(1, 2), keepdims=True))):
+            u = ref.bf16_ulps(g, o)
+            ulps[key].append(u.ravel())
+            one = np.abs(ref.bf16_step_above(o) - np.abs(o))  # one ulp at each element
+            over = np.abs(g - o) - one
+            excess[key] = max(excess[key], float((over / bar).max()))
+    stats = {k: (int(np.concatenate(v).max()), float((np.concatenate(v) > 1).mean()),
+                 float((np.concatenate(v) > 0).mean())) if v else None for k, v in ulps.items()}
+    say("pages with separated modes", compared, "of", n * w.num_kv_heads,
+        "; (max ulps, fraction beyond one ulp, fraction differing):", stats,
+        "; largest excess over one ulp, in units of the fp32 bar:", excess)
+    assert stats["centroid"][0] <= 1
+    for key in ("basis", "coeffs"):
+        if stats[key] is not None:
+            assert excess[key] <= 1.0, f"{key}: beyond one ulp plus the fp32 bar ({excess[key]:.3g})"
+            assert stats[key][1] <= 0.005, f"{key}: {stats[key][1]:.3%} of elements beyond one ulp"
+    if rank <= 8:
+        assert compared >= n * w.num_kv_heads // 2
 
 
 def test_decode_steps_bf16(gpu):
@@ -253,22 +344,11 @@ def test_decode_steps_bf16(gpu):
         if step % 7 != 0 and step != w.steps - 1:
             continue
         say("check step", step, lens)
-        res = run_oracle_all(w, lens, q64)
-        out = o["out"].float().cpu().numpy().astype(np.float64)
-        sel = o["sel"].cpu().numpy()
-        cnt = o["cnt"].cpu().numpy()
-        k = lo.page_budget(w.token_budget, w.page_size)
-        for (s, h), (hs, _, K, V) in res.items():
-            n_mr = lo.most_recent_page(lens[s], w.page_size)
-            gsel = sel[s, h, :cnt[s, h]]
-            msg = ref.selection_mismatch(gsel, hs.selected, hs.m_bar, n_mr, k, rel=2e-2)
-            assert msg is None, f"step {step} seq {s} head {h}: {msg}"
-            pages = hs.selected if sorted(gsel) == sorted(hs.selected) else gsel
-            qg = q64[s, h * w.group:(h + 1) * w.group]
-            eo, _ = lo.attend(qg, lo.gather_tokens(K, pages, lens[s], w.page_size),
-                              lo.gather_tokens(V, pages, lens[s], w.page_size), w.scale)
-            e = ref.rel_l2(out[s, h * w.group:(h + 1) * w.group], eo).max()
-            assert e <= 2e-2, f"step {step} seq {s} head {h}: rel L2 {e}"
+        o2 = dc.outputs()  # the page scores of the same step (the decode step keeps them internal)
+        dc.score_select(ref.q_device(q64, w.dtype), o2)
+        torch.cuda.synchronize()
+        tot = check_all_pairs(w, dc, o, q64, lens, page_lse=o2["page_lse"].cpu().numpy())
+        say("  ", tot)
 
 
 def test_determinism_bf16(gpu):
@@ -555,13 +635,22 @@ def test_selector_tiers(gpu, T, budget, capacity, group, pad, pad_len):
     w, dc, K, V, q64 = _selector_case(T, budget, capacity=capacity, group=group, pad=pad, pad_len=pad_len)
     sel, hs, o = _run_selector(w, dc, K, V, q64, outputs=True)
     assert len(sel) == len(hs.selected)
-    if pad:  # the short sequences: one token -> the sink page alone; empty -> nothing
+    if pad:  # the short sequences against the oracle: one token -> the sink page alone; empty -> nothing
         cnt = o["cnt"].cpu().numpy()[1:, 0]
         sp = o["sel"].cpu().numpy()[1:, 0]
-        if pad_len:
-            assert (cnt == 1).all() and (sp[:, 0] == 0).all() and (sp[:, 1:] == -1).all()
-        else:
-            assert (cnt == 0).all() and (sp == -1).all()
+        dc.sparse_attn(ref.q_device(q64, w.dtype), o["sel"], o["cnt"], o)
+        torch.cuda.synchronize()
+        out = o["out"].cpu().numpy().astype(np.float64)
+        lse = o["lse"].cpu().numpy()
+        Kp = np.zeros((1, w.page_size, w.head_dim))
+        for i in range(pad):
+            hp = lo.decode_head(q64[1 + i], Kp, Kp, pad_len, lo.build_page_summaries(Kp[:0], w.rank),
+                                w.token_budget, w.scale)
+            assert cnt[i] == len(hp.selected) and list(sp[i, :cnt[i]]) == list(hp.selected)
+            assert (sp[i, cnt[i]:] == -1).all()
+            if pad_len == 0:  # an empty sum: output 0, log-sum-exp -inf
+                np.testing.assert_array_equal(out[1 + i], hp.out)
+                np.testing.assert_array_equal(lse[1 + i], hp.lse)
 
 
 @pytest.mark.parametrize("group", [2, 8])
@@ -710,9 +799,12 @@ def test_q4_score_select_on_oracle_records(gpu, rank):
 
 
 def test_q4_end_to_end(gpu):
-    """GPU-built int4/int8 records: the scorer agrees with the oracle scoring the
-    GPU's own records, the page LSE stays near the oracle's own quantization,
-    and attention over the GPU's selection matches the oracle's."""
+    """GPU-built int4/int8 records: the GPU's scores, selection and attention
+    against the oracle run on the GPU's own records (page LSE 1e-3, selection
+    band 1e-4, attention over the GPU's selection), and the oracle's
+    selections from the GPU's and from its own quantized records within the
+    band their score difference allows (the codes themselves are compared in
+    test_q4_build_matches_oracle)."""
     w = small_q4()
     say("int4/int8 end to end", w.context)
     dc = DeviceCache(w, poison=True)
@@ -725,38 +817,14 @@ def test_q4_end_to_end(gpu):
     dc.score_select(qd, o)
     dc.sparse_attn(qd, o["sel"], o["cnt"], o)
     torch.cuda.synchronize()
-    page_lse = o["page_lse"].cpu().numpy()
-    sel, cnt = o["sel"].cpu().numpy(), o["cnt"].cpu().numpy()
-    out = o["out"].float().cpu().numpy().astype(np.float64)
-    G, d, B, r = w.group, w.head_dim, w.page_size, w.rank
-    own_err, ora_err, att_err = 0.0, [], 0.0
-    for s in range(w.batch):
-        n_mr = lo.most_recent_page(T[s], B)
-        phys = torch.from_numpy(dc.block_table_host[s, :n_mr].astype(np.int64)).cuda()
-        for h in range(w.num_kv_heads):
-            K, V = ref.host_pages(w, s, h, T[s])
-            qg = q64[s, h * G:(h + 1) * G]
-            own = lo.dequantize_summary(ref.unpack_q4_records(dc.summary_pool[phys, h].cpu().numpy(), d, B, r))
-            own_lse = lo.reconstructed_page_lse(qg, own, w.scale)
-            got = page_lse[s, h * G:(h + 1) * G, :n_mr]
-            own_err = max(own_err, np.abs(got - own_lse).max())
-            hs, _ = ref.oracle_head(w, qg, K, V, T[s])
-            ora_err.append(np.abs(got - hs.page_lse).ravel())
-            gsel = sel[s, h, :cnt[s, h]]
-            eo, _ = lo.attend(qg, lo.gather_tokens(K, gsel, T[s], B), lo.gather_tokens(V, gsel, T[s], B), w.scale)
-            att_err = max(att_err, ref.rel_l2(out[s, h * G:(h + 1) * G], eo).max())
-    ora_err = np.concatenate(ora_err)
-    say("scorer vs its own records", own_err, "; vs the oracle's quantization: max", ora_err.max(),
-        "p99", np.quantile(ora_err, 0.99), "; attention rel L2", att_err)
-    assert own_err < 1e-3
-    assert ora_err.max() < 5e-2
-    assert att_err <= 2e-2
+    tot = check_all_pairs(w, dc, o, q64, T, e2e_lse_gate=False)
+    say("int4/int8 end to end:", tot)
 
 
 def test_q4_decode_steps(gpu):
     """lk_decode_step with int4/int8 records over steps that complete pages
-    (built in-stream): every check step, the selection is well formed and the
-    page LSE of sampled heads matches the oracle scoring the GPU's records."""
+    (built in-stream): every check step, the sampled heads' page LSE,
+    selection and attention against the oracle run on the GPU's own records."""
     w = small_q4(batch=3, ctx=(187, 508, 64 * 30 + 60), steps=70, budget=512)
     say("int4/int8 decode steps", w.context, "steps", w.steps)
     dc = DeviceCache(w, poison=True)
@@ -764,9 +832,9 @@ def test_q4_decode_steps(gpu):
     dc.build_all()
     rng = np.random.default_rng(9)
     lens = list(w.context)
-    G, d, B, r = w.group, w.head_dim, w.page_size, w.rank
+    d = w.head_dim
     kv = {(s, h): synth.keys_values(w, s, h) for s in range(w.batch) for h in (0, 5)}
-    worst = 0.0
+    tot = ref.PairCheck()
     for step in range(w.steps):
         q = rng.standard_normal((w.batch, w.num_q_heads, d)).astype(np.float32)
         kn = rng.standard_normal((w.batch, w.num_kv_heads, d)).astype(np.float32)
@@ -784,19 +852,6 @@ def test_q4_decode_steps(gpu):
         o2 = dc.outputs()
         dc.score_select(ref.q_device(q64, w.dtype), o2)
         torch.cuda.synchronize()
-        page_lse = o2["page_lse"].cpu().numpy()
-        sel, cnt = o["sel"].cpu().numpy(), o["cnt"].cpu().numpy()
-        k = lo.page_budget(w.token_budget, B)
-        for (s, h) in kv:
-            n_mr = lo.most_recent_page(lens[s], B)
-            assert cnt[s, h] == min(k, n_mr + 1)
-            g = sel[s, h, :cnt[s, h]]
-            assert g[0] == 0 and g[-1] == n_mr and (np.diff(g) > 0).all()
-            if n_mr == 0:
-                continue
-            phys = torch.from_numpy(dc.block_table_host[s, :n_mr].astype(np.int64)).cuda()
-            own = lo.dequantize_summary(ref.unpack_q4_records(dc.summary_pool[phys, h].cpu().numpy(), d, B, r))
-            want = lo.reconstructed_page_lse(q64[s, h * G:(h + 1) * G], own, w.scale)
-            worst = max(worst, np.abs(page_lse[s, h * G:(h + 1) * G, :n_mr] - want).max())
-    say("decode steps: max page LSE error against the GPU's own records", worst)
-    assert worst < 1e-3
+        tot.merge(check_all_pairs(w, dc, o, q64, lens, pairs=list(kv), page_lse=o2["page_lse"].cpu().numpy(),
+                                  e2e_lse_gate=False))
+    say("int4/int8 decode steps:", tot)
