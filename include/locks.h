@@ -221,6 +221,22 @@ lk_status lk_decode_step(const lk_config* cfg, const lk_cache* cache,
                          int32_t* sel_pages, int32_t* sel_count, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* lk_decode_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops or harnesses that forbid hipMalloc): the
+ * same step, with the same results, whose workspace is a library-owned static
+ * buffer of 128 MiB per GPU instead of a caller's workspace.  It allocates
+ * nothing.  The buffer lives while the library is loaded; every call on one
+ * GPU uses that GPU's buffer, so calls that overlap on one GPU (on different
+ * streams, or from different threads) race, and must be ordered by the
+ * caller.  A step whose workspace (the decode-step part of
+ * lk_workspace_size) exceeds 128 MiB returns LK_ERR_WORKSPACE with nothing
+ * enqueued.  Every other argument is as for lk_decode_step. */
+lk_status lk_decode_step_noalloc(const lk_config* cfg, const lk_cache* cache,
+                                 int32_t batch, const void* q,
+                                 const void* k_new, const void* v_new,
+                                 void* out, float* lse_out, int32_t* sel_pages,
+                                 int32_t* sel_count, void* stream);
+
 /* Static text for a status code. */
 const char* lk_status_string(lk_status status);
 

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/locks.h"
@@ -124,13 +125,15 @@ struct Layout {
   int n_splits;
 };
 
-Layout layout(const Shape& sh, int batch, int max_pages) {
+// decode_only: the regions lk_decode_step uses (its attention has the sparse
+// split count only); a workspace of the full size serves it too.
+Layout layout(const Shape& sh, int batch, int max_pages, bool decode_only = false) {
   Layout L{};
   const int per_sparse = kAttnWavesPerSplit * kUnitsPerWaveSparse;
   const int per_dense = kAttnWavesPerSplit * kUnitsPerWaveDense;
   const int ns_sparse = (2 * sh.k + per_sparse - 1) / per_sparse;
   const int ns_dense = (2 * max_pages + per_dense - 1) / per_dense;
-  L.n_splits = ns_sparse > ns_dense ? ns_sparse : ns_dense;
+  L.n_splits = (decode_only || ns_sparse > ns_dense) ? ns_sparse : ns_dense;
   size_t off = 0;
   L.page_lse = off; off = align_up(off + sizeof(float) * (size_t)batch * sh.hq * max_pages);
   L.sel_pages = off; off = align_up(off + sizeof(int32_t) * (size_t)batch * sh.hkv * sh.k);
@@ -210,6 +213,117 @@ lk_status enqueue_attn(const Shape& sh, const lk_config* cfg, const lk_cache* c,
                   n_splits, ups, cfg->scale, len_add};
   if (n_splits_out) *n_splits_out = n_splits;
   return hip_status(lk::launch_attn(sh.dt, sh.G, aa, merge, s), "attention launch");
+}
+
+lk_status check_decode_step(const lk_config* cfg, const lk_cache* cache, int batch, const void* q,
+                            const void* k_new, const void* v_new, const void* out, const int32_t* sel_pages,
+                            const int32_t* sel_count, Shape* sh) {
+  lk_status st = check_config(cfg, sh);
+  if (st != LK_OK) return st;
+  if ((st = check_cache(cache, true, true)) != LK_OK) return st;
+  if ((st = check_table(cache, *sh)) != LK_OK) return st;
+  if (batch <= 0) return fail(LK_ERR_INVALID_ARG, "batch %d <= 0", batch);
+  if (!q || !k_new || !v_new || !out) return fail(LK_ERR_INVALID_ARG, "q / k_new / v_new / out is null");
+  if ((sel_pages == nullptr) != (sel_count == nullptr))
+    return fail(LK_ERR_INVALID_ARG, "sel_pages and sel_count must both be given or both be null");
+  return LK_OK;
+}
+
+// The decode step's launches on stream s with workspace ws carved by L.
+lk_status enqueue_decode_step(const Shape& sh, const lk_config* cfg, const lk_cache* cache, int batch,
+                              const void* q, const void* k_new, const void* v_new, void* out, float* lse_out,
+                              int32_t* sel_pages, int32_t* sel_count, void* ws, const Layout& L, hipStream_t s) {
+  lk_status st;
+  int32_t* build_list = at<int32_t>(ws, L.build_list);
+  int32_t* sel_phys = at<int32_t>(ws, L.sel_phys);
+  float* page_lse = at<float>(ws, L.page_lse);
+
+  // 1) append (done by the scorer's prologue) + score, with T + 1
+  lk::AppendDuty app{cache->k_pool, cache->v_pool, k_new, v_new, build_list};
+  lk::ScoreArgs sa{q, cache->summary_pool, cache->block_table, cache->seq_lens, page_lse, batch,
+                   cache->max_pages_per_seq, cache->num_phys_pages, sh.hkv, sh.hq, cfg->scale, 1, app};
+  st = hip_status(lk::launch_score(sh.dt, sh.r, sh.G, sh.q4, sa, s), "score launch");
+  if (st != LK_OK) return st;
+  // 2-3) selection and the attention splits: one fused launch when the table
+  //      fits one workgroup's selection, else a selection then an attention launch
+  const int per = kAttnWavesPerSplit * kUnitsPerWaveSparse;
+  const int n_splits = (2 * sh.k + per - 1) / per;
+  lk::SelectArgs se{page_lse, nullptr, sel_pages, sel_count, cache->seq_lens, batch, cache->max_pages_per_seq,
+                    sh.hkv, sh.G, sh.B, sh.k, 1, cache->block_table, nullptr, cache->num_phys_pages};
+  const bool fused = lk::select_attn_fusable(se);
+  const int n_merge = fused ? lk::select_attn_splits(sh.k) : n_splits;  // = list_attn_splits(k) when chunked
+  if (fused) {
+    lk::AttnArgs aa{q, cache->k_pool, cache->v_pool, cache->block_table, cache->seq_lens, nullptr, nullptr, nullptr,
+                    at<float>(ws, L.part_o), at<float>(ws, L.part_ml), out, lse_out,
+                    batch, cache->max_pages_per_seq, cache->num_phys_pages, sh.hkv, sh.hq, sh.k,
+                    n_merge, 1, cfg->scale, 1};
+    st = hip_status(lk::launch_select_attn(sh.dt, se, aa, s), "selection + attention launch");
+    if (st != LK_OK) return st;
+  } else {
+    int32_t* sel = sel_pages ? sel_pages : at<int32_t>(ws, L.sel_pages);
+    int32_t* cnt = sel_count ? sel_count : at<int32_t>(ws, L.sel_count);
+    se.sel_pages = sel;
+    se.sel_count = cnt;
+    se.sel_phys = sel_phys;
+    attach_chunk_lists(se, ws, L);
+    if (se.n_chunks > 0) {
+      // chunked selection: the chunk lists, then attention whose waves merge
+      // them (the selection is written only when the caller asked for it)
+      se.sel_pages = sel_pages;
+      se.sel_count = sel_count;
+      st = hip_status(lk::launch_select_lists(se, s), "select launch");
+      if (st != LK_OK) return st;
+      lk::AttnArgs aa{q, cache->k_pool, cache->v_pool, cache->block_table, cache->seq_lens, nullptr, nullptr, nullptr,
+                      at<float>(ws, L.part_o), at<float>(ws, L.part_ml), out, lse_out,
+                      batch, cache->max_pages_per_seq, cache->num_phys_pages, sh.hkv, sh.hq, sh.k,
+                      n_merge, 1, cfg->scale, 1};
+      st = hip_status(lk::launch_list_attn(sh.dt, se, aa, s), "attention launch");
+      if (st != LK_OK) return st;
+    } else {
+      st = hip_status(lk::launch_select(se, s), "select launch");
+      if (st != LK_OK) return st;
+      int ns = 0;
+      st = enqueue_attn(sh, cfg, cache, batch, q, sel, cnt, sel_phys, out, lse_out, ws, L, 1, false, s, &ns);
+      if (st != LK_OK) return st;
+    }
+  }
+  // 4) one launch of (sequence, KV head) workgroups: merge the attention
+  //    partials, advance the stored lengths, and summarize pages the append
+  //    completed
+  lk::BuildArgs ba{cache->k_pool, cache->summary_pool, build_list, nullptr, batch,
+                   cache->num_phys_pages, sh.hkv, cache->seq_lens, cache->block_table,
+                   cache->max_pages_per_seq,
+                   {at<float>(ws, L.part_o), at<float>(ws, L.part_ml), out, lse_out, n_merge, sh.G, sh.hq},
+                   sh.q4 ? 1 : 0};
+  return hip_status(lk::launch_build(sh.dt, sh.r, ba, s), "build launch");
+}
+
+// Workspace of lk_decode_step_noalloc: one static buffer per GPU (each device
+// holds its own copy of this array while the library is loaded).  Host code
+// uses the device address from hipGetSymbolAddress, taken once per device
+// with that device current; the array's name itself is not a device address
+// in host code.
+constexpr size_t kStaticScratchBytes = size_t(128) << 20;
+__device__ __align__(256) static unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+lk_status static_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(LK_ERR_UNSUPPORTED, "device %d beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(LK_ERR_HIP, "hipGetSymbolAddress(scratch) gave no address");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return LK_OK;
 }
 
 }  // namespace
@@ -333,79 +447,28 @@ lk_status lk_decode_step(const lk_config* cfg, const lk_cache* cache, int32_t ba
                          const void* k_new, const void* v_new, void* out, float* lse_out,
                          int32_t* sel_pages, int32_t* sel_count, void* ws, size_t ws_bytes, void* stream) {
   Shape sh;
-  lk_status st = check_config(cfg, &sh);
+  lk_status st = check_decode_step(cfg, cache, batch, q, k_new, v_new, out, sel_pages, sel_count, &sh);
   if (st != LK_OK) return st;
-  if ((st = check_cache(cache, true, true)) != LK_OK) return st;
-  if ((st = check_table(cache, sh)) != LK_OK) return st;
-  if (batch <= 0) return fail(LK_ERR_INVALID_ARG, "batch %d <= 0", batch);
-  if (!q || !k_new || !v_new || !out) return fail(LK_ERR_INVALID_ARG, "q / k_new / v_new / out is null");
-  if ((sel_pages == nullptr) != (sel_count == nullptr))
-    return fail(LK_ERR_INVALID_ARG, "sel_pages and sel_count must both be given or both be null");
-  const Layout L = layout(sh, batch, cache->max_pages_per_seq);
+  const Layout L = layout(sh, batch, cache->max_pages_per_seq, true);
   if ((st = check_ws(L, ws, ws_bytes)) != LK_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  int32_t* build_list = at<int32_t>(ws, L.build_list);
-  int32_t* sel_phys = at<int32_t>(ws, L.sel_phys);
-  float* page_lse = at<float>(ws, L.page_lse);
+  return enqueue_decode_step(sh, cfg, cache, batch, q, k_new, v_new, out, lse_out, sel_pages, sel_count, ws, L,
+                             static_cast<hipStream_t>(stream));
+}
 
-  // 1) append (done by the scorer's prologue) + score, with T + 1
-  lk::AppendDuty app{cache->k_pool, cache->v_pool, k_new, v_new, build_list};
-  lk::ScoreArgs sa{q, cache->summary_pool, cache->block_table, cache->seq_lens, page_lse, batch,
-                   cache->max_pages_per_seq, cache->num_phys_pages, sh.hkv, sh.hq, cfg->scale, 1, app};
-  st = hip_status(lk::launch_score(sh.dt, sh.r, sh.G, sh.q4, sa, s), "score launch");
+lk_status lk_decode_step_noalloc(const lk_config* cfg, const lk_cache* cache, int32_t batch, const void* q,
+                                 const void* k_new, const void* v_new, void* out, float* lse_out,
+                                 int32_t* sel_pages, int32_t* sel_count, void* stream) {
+  Shape sh;
+  lk_status st = check_decode_step(cfg, cache, batch, q, k_new, v_new, out, sel_pages, sel_count, &sh);
   if (st != LK_OK) return st;
-  // 2-3) selection and the attention splits: one fused launch when the table
-  //      fits one workgroup's selection, else a selection then an attention launch
-  const int per = kAttnWavesPerSplit * kUnitsPerWaveSparse;
-  const int n_splits = (2 * sh.k + per - 1) / per;
-  lk::SelectArgs se{page_lse, nullptr, sel_pages, sel_count, cache->seq_lens, batch, cache->max_pages_per_seq,
-                    sh.hkv, sh.G, sh.B, sh.k, 1, cache->block_table, nullptr, cache->num_phys_pages};
-  const bool fused = lk::select_attn_fusable(se);
-  const int n_merge = fused ? lk::select_attn_splits(sh.k) : n_splits;  // = list_attn_splits(k) when chunked
-  if (fused) {
-    lk::AttnArgs aa{q, cache->k_pool, cache->v_pool, cache->block_table, cache->seq_lens, nullptr, nullptr, nullptr,
-                    at<float>(ws, L.part_o), at<float>(ws, L.part_ml), out, lse_out,
-                    batch, cache->max_pages_per_seq, cache->num_phys_pages, sh.hkv, sh.hq, sh.k,
-                    n_merge, 1, cfg->scale, 1};
-    st = hip_status(lk::launch_select_attn(sh.dt, se, aa, s), "selection + attention launch");
-    if (st != LK_OK) return st;
-  } else {
-    int32_t* sel = sel_pages ? sel_pages : at<int32_t>(ws, L.sel_pages);
-    int32_t* cnt = sel_count ? sel_count : at<int32_t>(ws, L.sel_count);
-    se.sel_pages = sel;
-    se.sel_count = cnt;
-    se.sel_phys = sel_phys;
-    attach_chunk_lists(se, ws, L);
-    if (se.n_chunks > 0) {
-      // chunked selection: the chunk lists, then attention whose waves merge
-      // them (the selection is written only when the caller asked for it)
-      se.sel_pages = sel_pages;
-      se.sel_count = sel_count;
-      st = hip_status(lk::launch_select_lists(se, s), "select launch");
-      if (st != LK_OK) return st;
-      lk::AttnArgs aa{q, cache->k_pool, cache->v_pool, cache->block_table, cache->seq_lens, nullptr, nullptr, nullptr,
-                      at<float>(ws, L.part_o), at<float>(ws, L.part_ml), out, lse_out,
-                      batch, cache->max_pages_per_seq, cache->num_phys_pages, sh.hkv, sh.hq, sh.k,
-                      n_merge, 1, cfg->scale, 1};
-      st = hip_status(lk::launch_list_attn(sh.dt, se, aa, s), "attention launch");
-      if (st != LK_OK) return st;
-    } else {
-      st = hip_status(lk::launch_select(se, s), "select launch");
-      if (st != LK_OK) return st;
-      int ns = 0;
-      st = enqueue_attn(sh, cfg, cache, batch, q, sel, cnt, sel_phys, out, lse_out, ws, L, 1, false, s, &ns);
-      if (st != LK_OK) return st;
-    }
-  }
-  // 4) one launch of (sequence, KV head) workgroups: merge the attention
-  //    partials, advance the stored lengths, and summarize pages the append
-  //    completed
-  lk::BuildArgs ba{cache->k_pool, cache->summary_pool, build_list, nullptr, batch,
-                   cache->num_phys_pages, sh.hkv, cache->seq_lens, cache->block_table,
-                   cache->max_pages_per_seq,
-                   {at<float>(ws, L.part_o), at<float>(ws, L.part_ml), out, lse_out, n_merge, sh.G, sh.hq},
-                   sh.q4 ? 1 : 0};
-  return hip_status(lk::launch_build(sh.dt, sh.r, ba, s), "build launch");
+  const Layout L = layout(sh, batch, cache->max_pages_per_seq, true);
+  if (L.total > kStaticScratchBytes)
+    return fail(LK_ERR_WORKSPACE, "the step needs %zu bytes of workspace, more than the %zu of the static buffer",
+                L.total, kStaticScratchBytes);
+  void* ws = nullptr;
+  if ((st = static_scratch(&ws)) != LK_OK) return st;
+  return enqueue_decode_step(sh, cfg, cache, batch, q, k_new, v_new, out, lse_out, sel_pages, sel_count, ws, L,
+                             static_cast<hipStream_t>(stream));
 }
 
 const char* lk_status_string(lk_status status) {

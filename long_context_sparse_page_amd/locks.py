@@ -33,6 +33,7 @@ EXPORTED = (
     "lk_sparse_decode_attn",
     "lk_dense_decode_attn",
     "lk_decode_step",
+    "lk_decode_step_noalloc",
     "lk_status_string",
     "lk_last_error",
 )
@@ -86,6 +87,7 @@ def _load() -> ctypes.CDLL:
         "lk_sparse_decode_attn": (I32, [cfg, cache, I32, P, P, P, P, P, P, SZ, P]),
         "lk_dense_decode_attn": (I32, [cfg, cache, I32, P, P, P, P, SZ, P]),
         "lk_decode_step": (I32, [cfg, cache, I32, P, P, P, P, P, P, P, P, SZ, P]),
+        "lk_decode_step_noalloc": (I32, [cfg, cache, I32, P, P, P, P, P, P, P, P]),
         "lk_status_string": (ctypes.c_char_p, [I32]),
         "lk_last_error": (ctypes.c_char_p, []),
     }
@@ -184,6 +186,13 @@ def lk_decode_step(cfg, cache, batch, q, k_new, v_new, out, lse_out, sel_pages, 
     _check(_lib.lk_decode_step(ctypes.byref(cfg), ctypes.byref(cache), batch, _ptr(q), _ptr(k_new),
                                _ptr(v_new), _ptr(out), _ptr(lse_out), _ptr(sel_pages), _ptr(sel_count),
                                _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def lk_decode_step_noalloc(cfg, cache, batch, q, k_new, v_new, out, lse_out, sel_pages, sel_count,
+                           stream=None) -> None:
+    _check(_lib.lk_decode_step_noalloc(ctypes.byref(cfg), ctypes.byref(cache), batch, _ptr(q), _ptr(k_new),
+                                       _ptr(v_new), _ptr(out), _ptr(lse_out), _ptr(sel_pages), _ptr(sel_count),
+                                       _stream(stream)))
 
 
 def lk_status_string(status: int) -> str:

@@ -191,6 +191,14 @@ def test_entry_points_reject_bad_arguments():
     expect(L.LK_ERR_WORKSPACE, L.lk_dense_decode_attn, c, fake_cache(), 2, FAKE, FAKE, None, ws + 4, ws_need, 0)
     expect(L.LK_ERR_WORKSPACE, L.lk_decode_step, c, fake_cache(), 2, FAKE, FAKE, FAKE, FAKE, None, None, None,
            ws, 16, 0)
+    # the decode step without a workspace argument: same validation, and a step
+    # whose workspace would exceed the static buffer is refused before any launch
+    expect(L.LK_ERR_INVALID_ARG, L.lk_decode_step_noalloc, c, fake_cache(), 2, FAKE, None, FAKE, FAKE, None, None,
+           None, 0)
+    expect(L.LK_ERR_INVALID_ARG, L.lk_decode_step_noalloc, c, fake_cache(), 0, FAKE, FAKE, FAKE, FAKE, None, None,
+           None, 0)
+    expect(L.LK_ERR_WORKSPACE, L.lk_decode_step_noalloc, c, fake_cache(max_pages_per_seq=20000), 256, FAKE, FAKE,
+           FAKE, FAKE, None, None, None, 0)
     # unsupported config through a compute entry point
     expect(L.LK_ERR_UNSUPPORTED, L.lk_score_select, cfg(head_dim=96), fake_cache(), 2, FAKE, None, None, FAKE,
            FAKE, ws, ws_need, 0)
