@@ -99,9 +99,7 @@ typedef enum { LK_SUMMARY_KV = 0, LK_SUMMARY_I4 = 1 } lk_summary_format;
  * GQA grouping, per-head token budget b, storage dtype and logit scale. */
 typedef struct {
   int32_t head_dim;      /* d; 128 is supported                              */
-  int32_t page_size;     /* B; 64 is supported, and 16 for
-                          * lk_build_page_summary only (LK_ERR_UNSUPPORTED
-                          * from every other entry point)                 */
+  int32_t page_size;     /* B; 64 or 16 (the pages' deployed size)         */
   int32_t rank;          /* r in {1, 2, 4, 8, 16}; modes beyond the page's
                           * nonzero modes are stored as zeros              */
   int32_t num_q_heads;   /* Hq                                               */

@@ -16,7 +16,7 @@ namespace {
 thread_local std::string g_last_error;
 
 // attention: a split is a workgroup of 4 waves; each wave takes this many
-// half pages (32-token units)
+// 32-token units (half a 64-token page, or two 16-token pages)
 constexpr int kAttnWavesPerSplit = 4;
 constexpr int kUnitsPerWaveSparse = 1;
 constexpr int kUnitsPerWaveDense = 32;
@@ -52,9 +52,7 @@ struct Shape {
   bool q4;  // LK_SUMMARY_I4 records
 };
 
-// build_only: the caller only builds summaries, which is also built for pages
-// of 16 tokens
-lk_status check_config(const lk_config* cfg, Shape* sh, bool build_only = false) {
+lk_status check_config(const lk_config* cfg, Shape* sh) {
   if (!cfg) return fail(LK_ERR_INVALID_ARG, "config is null");
   if (cfg->head_dim <= 0 || cfg->page_size <= 0 || cfg->rank <= 0 || cfg->num_q_heads <= 0 ||
       cfg->num_kv_heads <= 0 || cfg->token_budget <= 0)
@@ -71,8 +69,6 @@ lk_status check_config(const lk_config* cfg, Shape* sh, bool build_only = false)
   if (k < 2)
     return fail(LK_ERR_INVALID_ARG, "page budget ceil(b/B) = %d < 2 (the sink and the most recent page need two slots)", k);
   if (cfg->head_dim != 128) return fail(LK_ERR_UNSUPPORTED, "head_dim %d: only 128 is built", cfg->head_dim);
-  if (cfg->page_size == 16 && !build_only)
-    return fail(LK_ERR_UNSUPPORTED, "page_size 16 is built for lk_build_page_summary only");
   if (cfg->page_size != 64 && cfg->page_size != 16)
     return fail(LK_ERR_UNSUPPORTED, "page_size %d: built page sizes are 64 and 16", cfg->page_size);
   const int r = cfg->rank;
@@ -118,6 +114,9 @@ lk_status check_table(const lk_cache* c, const Shape& sh) {
   return LK_OK;
 }
 
+// 32-token attention units over n list entries (pages).
+int attn_units(const Shape& sh, int n) { return sh.B == 64 ? 2 * n : (n + 1) / 2; }
+
 // Workspace regions.
 struct Layout {
   size_t page_lse, sel_pages, sel_count, sel_phys, part_o, part_ml, build_list, cand_key, cand_page, cand_phys,
@@ -131,8 +130,8 @@ Layout layout(const Shape& sh, int batch, int max_pages, bool decode_only = fals
   Layout L{};
   const int per_sparse = kAttnWavesPerSplit * kUnitsPerWaveSparse;
   const int per_dense = kAttnWavesPerSplit * kUnitsPerWaveDense;
-  const int ns_sparse = (2 * sh.k + per_sparse - 1) / per_sparse;
-  const int ns_dense = (2 * max_pages + per_dense - 1) / per_dense;
+  const int ns_sparse = (attn_units(sh, sh.k) + per_sparse - 1) / per_sparse;
+  const int ns_dense = (attn_units(sh, max_pages) + per_dense - 1) / per_dense;
   L.n_splits = (decode_only || ns_sparse > ns_dense) ? ns_sparse : ns_dense;
   size_t off = 0;
   L.page_lse = off; off = align_up(off + sizeof(float) * (size_t)batch * sh.hq * max_pages);
@@ -191,7 +190,7 @@ lk_status enqueue_score_select(const Shape& sh, const lk_config* cfg, const lk_c
                                void* ws, const Layout& L, hipStream_t s) {
   lk::ScoreArgs sa{q, c->summary_pool, c->block_table, c->seq_lens, page_lse,
                    batch, c->max_pages_per_seq, c->num_phys_pages, sh.hkv, sh.hq, cfg->scale, len_add, app};
-  hipError_t e = lk::launch_score(sh.dt, sh.r, sh.G, sh.q4, sa, s);
+  hipError_t e = lk::launch_score(sh.dt, sh.B, sh.r, sh.G, sh.q4, sa, s);
   if (e != hipSuccess) return hip_status(e, "score launch");
   lk::SelectArgs se{page_lse, share_out, sel, cnt, c->seq_lens, batch, c->max_pages_per_seq,
                     sh.hkv, sh.G, sh.B, sh.k, len_add, c->block_table, sel_phys, c->num_phys_pages};
@@ -206,11 +205,11 @@ lk_status enqueue_attn(const Shape& sh, const lk_config* cfg, const lk_cache* c,
   const bool dense = sel == nullptr;
   const int ups = dense ? kUnitsPerWaveDense : kUnitsPerWaveSparse;
   const int per = kAttnWavesPerSplit * ups;
-  const int n_splits = dense ? (2 * c->max_pages_per_seq + per - 1) / per : (2 * sh.k + per - 1) / per;
+  const int n_splits = (attn_units(sh, dense ? c->max_pages_per_seq : sh.k) + per - 1) / per;
   lk::AttnArgs aa{q, c->k_pool, c->v_pool, c->block_table, c->seq_lens, sel, cnt, sel_phys,
                   at<float>(ws, L.part_o), at<float>(ws, L.part_ml), out, lse_out,
                   batch, c->max_pages_per_seq, c->num_phys_pages, sh.hkv, sh.hq, sh.k,
-                  n_splits, ups, cfg->scale, len_add};
+                  n_splits, ups, cfg->scale, len_add, sh.B};
   if (n_splits_out) *n_splits_out = n_splits;
   return hip_status(lk::launch_attn(sh.dt, sh.G, aa, merge, s), "attention launch");
 }
@@ -242,16 +241,15 @@ lk_status enqueue_decode_step(const Shape& sh, const lk_config* cfg, const lk_ca
   lk::AppendDuty app{cache->k_pool, cache->v_pool, k_new, v_new, build_list};
   lk::ScoreArgs sa{q, cache->summary_pool, cache->block_table, cache->seq_lens, page_lse, batch,
                    cache->max_pages_per_seq, cache->num_phys_pages, sh.hkv, sh.hq, cfg->scale, 1, app};
-  st = hip_status(lk::launch_score(sh.dt, sh.r, sh.G, sh.q4, sa, s), "score launch");
+  st = hip_status(lk::launch_score(sh.dt, sh.B, sh.r, sh.G, sh.q4, sa, s), "score launch");
   if (st != LK_OK) return st;
   // 2-3) selection and the attention splits: one fused launch when the table
-  //      fits one workgroup's selection, else a selection then an attention launch
-  const int per = kAttnWavesPerSplit * kUnitsPerWaveSparse;
-  const int n_splits = (2 * sh.k + per - 1) / per;
+  //      fits one workgroup's selection (64-token pages), else a selection then
+  //      an attention launch
   lk::SelectArgs se{page_lse, nullptr, sel_pages, sel_count, cache->seq_lens, batch, cache->max_pages_per_seq,
                     sh.hkv, sh.G, sh.B, sh.k, 1, cache->block_table, nullptr, cache->num_phys_pages};
   const bool fused = lk::select_attn_fusable(se);
-  const int n_merge = fused ? lk::select_attn_splits(sh.k) : n_splits;  // = list_attn_splits(k) when chunked
+  int n_merge = fused ? lk::select_attn_splits(sh.k) : lk::list_attn_splits(sh.k);  // the attention's splits
   if (fused) {
     lk::AttnArgs aa{q, cache->k_pool, cache->v_pool, cache->block_table, cache->seq_lens, nullptr, nullptr, nullptr,
                     at<float>(ws, L.part_o), at<float>(ws, L.part_ml), out, lse_out,
@@ -266,7 +264,7 @@ lk_status enqueue_decode_step(const Shape& sh, const lk_config* cfg, const lk_ca
     se.sel_count = cnt;
     se.sel_phys = sel_phys;
     attach_chunk_lists(se, ws, L);
-    if (se.n_chunks > 0) {
+    if (se.n_chunks > 0 && sh.B == 64) {
       // chunked selection: the chunk lists, then attention whose waves merge
       // them (the selection is written only when the caller asked for it)
       se.sel_pages = sel_pages;
@@ -282,8 +280,7 @@ lk_status enqueue_decode_step(const Shape& sh, const lk_config* cfg, const lk_ca
     } else {
       st = hip_status(lk::launch_select(se, s), "select launch");
       if (st != LK_OK) return st;
-      int ns = 0;
-      st = enqueue_attn(sh, cfg, cache, batch, q, sel, cnt, sel_phys, out, lse_out, ws, L, 1, false, s, &ns);
+      st = enqueue_attn(sh, cfg, cache, batch, q, sel, cnt, sel_phys, out, lse_out, ws, L, 1, false, s, &n_merge);
       if (st != LK_OK) return st;
     }
   }
@@ -295,6 +292,7 @@ lk_status enqueue_decode_step(const Shape& sh, const lk_config* cfg, const lk_ca
                    cache->max_pages_per_seq,
                    {at<float>(ws, L.part_o), at<float>(ws, L.part_ml), out, lse_out, n_merge, sh.G, sh.hq},
                    sh.q4 ? 1 : 0};
+  if (sh.B == 16) return hip_status(lk::launch_build16(sh.dt, sh.r, ba, s), "build launch");
   return hip_status(lk::launch_build(sh.dt, sh.r, ba, s), "build launch");
 }
 
@@ -366,7 +364,7 @@ lk_status lk_build_page_summary(const lk_config* cfg, const lk_cache* cache, con
   (void)ws;
   (void)ws_bytes;
   Shape sh;
-  lk_status st = check_config(cfg, &sh, true);
+  lk_status st = check_config(cfg, &sh);
   if (st != LK_OK) return st;
   if (!cache) return fail(LK_ERR_INVALID_ARG, "cache is null");
   if (!cache->k_pool || !cache->summary_pool) return fail(LK_ERR_INVALID_ARG, "k_pool / summary_pool is null");
@@ -405,7 +403,7 @@ lk_status lk_score_select(const lk_config* cfg, const lk_cache* cache, int32_t b
     lk::ScoreArgs sa{q, cache->summary_pool, cache->block_table, cache->seq_lens, page_lse_out, batch,
                      cache->max_pages_per_seq, cache->num_phys_pages, sh.hkv, sh.hq, cfg->scale, 0,
                      lk::AppendDuty{}};
-    return hip_status(lk::launch_score(sh.dt, sh.r, sh.G, sh.q4, sa, s), "score launch");
+    return hip_status(lk::launch_score(sh.dt, sh.B, sh.r, sh.G, sh.q4, sa, s), "score launch");
   }
   float* lse = page_lse_out ? page_lse_out : at<float>(ws, L.page_lse);
   return enqueue_score_select(sh, cfg, cache, batch, q, lse, share_out, sel_pages, sel_count, nullptr, 0,

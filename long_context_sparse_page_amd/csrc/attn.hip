@@ -7,7 +7,8 @@
 // All G query heads of a KV head read each K/V page once.
 //
 // Split kernel: a workgroup of 4 waves per (sequence, KV head, split); each
-// wave takes a run of consecutive half pages of the page list (32 tokens each).  Lane
+// wave takes a run of consecutive units of the page list, 32 tokens each: half
+// a page of 64 tokens, or two consecutive list entries of 16-token pages.  Lane
 // (sg = lane / 8, e = lane % 8) owns dims 16e..16e+15 of tokens sg, sg+8, ...,
 // so K and V are read with coalesced 16-byte loads (eight tokens x 256 bytes
 // per instruction), all issued before any arithmetic; the first half page's
@@ -125,6 +126,25 @@ __device__ __forceinline__ void issue_unit(const AttnArgs& a, int kvh, int ph, i
   for (int x = 0; x < kAttnTPG; ++x) {
     kr[x].load(Kp + (size_t)(sg + kAttnTG * x) * D);
     vr[x].load(Vp + (size_t)(sg + kAttnTG * x) * D);
+  }
+}
+
+// The same for a unit of two 16-token pages ph0, ph1 (list entries 2u, 2u + 1):
+// unit token 8 x + sg is token sg + 8 (x & 1) of page x >> 1, so the unit's 32
+// tokens are page ph0's 16 then page ph1's 16, in the order attend_unit masks.
+template <typename T>
+__device__ __forceinline__ void issue_unit16(const AttnArgs& a, int kvh, int ph0, int ph1, int sg, int e,
+                                             KV16<T> (&kr)[kAttnTPG], KV16<T> (&vr)[kAttnTPG]) {
+  constexpr int B = 16;
+  constexpr int D = kHeadDim;
+  const T* Kp = reinterpret_cast<const T*>(a.k_pool);
+  const T* Vp = reinterpret_cast<const T*>(a.v_pool);
+#pragma unroll
+  for (int x = 0; x < kAttnTPG; ++x) {
+    const int ph = x < 2 ? ph0 : ph1;
+    const size_t off = (((size_t)ph * a.hkv + kvh) * B + sg + kAttnTG * (x & 1)) * D + e * 16;
+    kr[x].load(Kp + off);
+    vr[x].load(Vp + off);
   }
 }
 
@@ -309,10 +329,82 @@ __device__ __forceinline__ void combine_write(const AttnArgs& a, size_t pidx, in
 // physical pages (nullptr: looked up) and `cnt_p` the list length; the lists
 // may live in global memory or LDS.  seq_len is a.seq_lens[seq], loaded by
 // the caller.
+// attn_split_block for pages of 16 tokens: unit u is list entries 2u and
+// 2u + 1 (issue_unit16); the first unit's loads go out before the lengths are
+// used, as at 64 tokens.
 template <typename T, int G>
+__device__ __forceinline__ void attn_split_block16(const AttnArgs& a, int split, int kvh, int seq, int seq_len,
+                                                   const int32_t* list, const int32_t* plist, const int32_t* cnt_p) {
+  constexpr int B = 16;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int sg = lane >> 3;
+  const int e = lane & 7;
+  const int32_t* bt = a.block_table + (size_t)seq * a.max_pages;
+  const int ups = a.pages_per_split;
+  const int u0 = (split * kAttnWaves + wave) * ups;
+  const int n_entries = list ? a.k : a.max_pages;  // list entries that exist in memory
+  // logical and physical page of list entry x (-1 past the entries in memory)
+  auto entry = [&](int x, int& pg, int& ph) {
+    pg = -1;
+    ph = -1;
+    if (x >= n_entries) return;
+    pg = list ? list[x] : x;
+    ph = plist ? plist[x] : ((pg >= 0 && pg < a.max_pages) ? bt[pg] : -1);
+  };
+  auto valid_phys = [&](int ph) { return ph >= 0 && ph < a.num_phys; };
+  int pg0, ph0, pg1, ph1;
+  entry(2 * u0, pg0, ph0);
+  entry(2 * u0 + 1, pg1, ph1);
+  const int len = seq_len + a.len_add;
+  const int cnt = list ? *cnt_p : 0;
+
+  QLane<T, G> q;
+  q.load(a, seq, kvh, e);
+  float m[G], l[G], o[G][16];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[g][i] = 0.f;
+  }
+  const float zscale = a.scale * kLog2e;
+  KV16<T> kr[kAttnTPG], vr[kAttnTPG];
+  bool loaded = false;
+  if (len > 0 && valid_phys(ph0)) {
+    issue_unit16<T>(a, kvh, ph0, valid_phys(ph1) ? ph1 : ph0, sg, e, kr, vr);
+    loaded = true;
+  }
+  int n_mr = len > 0 ? (len - 1) / B : -1;
+  if (n_mr > a.max_pages - 1) n_mr = a.max_pages - 1;
+  const int n_list = len <= 0 ? 0 : (list ? min(cnt, a.k) : n_mr + 1);
+  const int u1 = min(u0 + ups, (n_list + 1) / 2);
+  for (int u = u0; u < u1; ++u) {
+    if (u != u0) {
+      entry(2 * u, pg0, ph0);
+      entry(2 * u + 1, pg1, ph1);
+      loaded = valid_phys(ph0);
+      if (loaded) issue_unit16<T>(a, kvh, ph0, valid_phys(ph1) ? ph1 : ph0, sg, e, kr, vr);
+    }
+    if (!loaded || pg0 < 0 || pg0 > n_mr) continue;
+    // tokens from the unit's start on: page 0 whole (or its filled part when
+    // it is the most recent page, the last entry), then page 1 when present
+    int n_tok = pg0 == n_mr ? len - n_mr * B : B;
+    if (pg0 != n_mr && 2 * u + 1 < n_list && pg1 >= 0 && pg1 <= n_mr && valid_phys(ph1))
+      n_tok += pg1 == n_mr ? len - n_mr * B : B;
+    attend_unit<T, G>(q, kr, vr, n_tok, sg, zscale, m, l, o);
+  }
+  combine_write<G, kAttnWaves>(a, ((size_t)seq * a.hkv + kvh) * a.n_splits + split, wave, lane, m, l, o);
+}
+
+template <typename T, int G, int B>
 __device__ __forceinline__ void attn_split_block(const AttnArgs& a, int split, int kvh, int seq, int seq_len,
                                                  const int32_t* list, const int32_t* plist, const int32_t* cnt_p) {
-  constexpr int B = 64;
+  if constexpr (B == 16) {
+    attn_split_block16<T, G>(a, split, kvh, seq, seq_len, list, plist, cnt_p);
+    return;
+  }
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar page-list loads
   const int sg = lane >> 3;
@@ -376,13 +468,13 @@ __device__ __forceinline__ void attn_split_block(const AttnArgs& a, int split, i
   combine_write<G, kAttnWaves>(a, ((size_t)seq * a.hkv + kvh) * a.n_splits + split, wave, lane, m, l, o);
 }
 
-template <typename T, int G>
+template <typename T, int G, int B>
 __global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs a) {
   const int split = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
   const size_t pair = (size_t)seq * a.hkv + kvh;
   const int32_t* list = a.sel_pages ? a.sel_pages + pair * a.k : nullptr;
   const int32_t* plist = (list && a.sel_phys) ? a.sel_phys + pair * a.k : nullptr;
-  attn_split_block<T, G>(a, split, kvh, seq, a.seq_lens[seq], list, plist, list ? a.sel_count + pair : nullptr);
+  attn_split_block<T, G, B>(a, split, kvh, seq, a.seq_lens[seq], list, plist, list ? a.sel_count + pair : nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -754,23 +846,30 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_merge_kernel(AttnArgs
   }
 }
 
-template <typename T>
-static hipError_t launch_attn_t(int group, const AttnArgs& a, bool merge, hipStream_t s) {
+template <typename T, int B>
+static hipError_t launch_attn_tb(int group, const AttnArgs& a, bool merge, hipStream_t s) {
   dim3 grid(a.n_splits, a.hkv, a.batch);
   dim3 block(kAttnWaves * kWave);
   dim3 mgrid(a.hq, a.batch);
   switch (group) {
-    case 1: hipLaunchKernelGGL((attn_split_kernel<T, 1>), grid, block, 0, s, a);
+    case 1: hipLaunchKernelGGL((attn_split_kernel<T, 1, B>), grid, block, 0, s, a);
             if (merge) hipLaunchKernelGGL((attn_merge_kernel<T, 1>), mgrid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((attn_split_kernel<T, 2>), grid, block, 0, s, a);
+    case 2: hipLaunchKernelGGL((attn_split_kernel<T, 2, B>), grid, block, 0, s, a);
             if (merge) hipLaunchKernelGGL((attn_merge_kernel<T, 2>), mgrid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((attn_split_kernel<T, 4>), grid, block, 0, s, a);
+    case 4: hipLaunchKernelGGL((attn_split_kernel<T, 4, B>), grid, block, 0, s, a);
             if (merge) hipLaunchKernelGGL((attn_merge_kernel<T, 4>), mgrid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((attn_split_kernel<T, 8>), grid, block, 0, s, a);
+    case 8: hipLaunchKernelGGL((attn_split_kernel<T, 8, B>), grid, block, 0, s, a);
             if (merge) hipLaunchKernelGGL((attn_merge_kernel<T, 8>), mgrid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_attn_t(int group, const AttnArgs& a, bool merge, hipStream_t s) {
+  if (a.page_size == 64) return launch_attn_tb<T, 64>(group, a, merge, s);
+  if (a.page_size == 16) return launch_attn_tb<T, 16>(group, a, merge, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn(DType dt, int group, const AttnArgs& a, bool merge, hipStream_t s) {
@@ -809,7 +908,8 @@ int select_attn_splits(int k) { return (2 * k + kFusedWaves - 1) / kFusedWaves; 
 
 hipError_t launch_select_attn(DType dt, const SelectArgs& se, const AttnArgs& a, hipStream_t s) {
   if (!select_attn_fusable(se)) return hipErrorNotSupported;
-  if (se.seq_lens != a.seq_lens || a.n_splits != select_attn_splits(se.k)) return hipErrorInvalidValue;
+  if (se.seq_lens != a.seq_lens || a.n_splits != select_attn_splits(se.k) || a.page_size != 64)
+    return hipErrorInvalidValue;
   return dt == kBF16 ? launch_select_attn_t<bf16_t>(se, a, s) : launch_select_attn_t<float>(se, a, s);
 }
 
@@ -944,7 +1044,7 @@ static hipError_t launch_list_attn_t(const SelectArgs& se, const AttnArgs& a, hi
 
 hipError_t launch_list_attn(DType dt, const SelectArgs& se, const AttnArgs& a, hipStream_t s) {
   if (se.n_chunks <= 0 || !se.cand_key || !se.cand_page || !se.cand_phys || !se.cand_cnt || se.k < 3 ||
-      se.page_size != 64 || se.seq_lens != a.seq_lens || a.n_splits != list_attn_splits(se.k) ||
+      se.page_size != 64 || a.page_size != 64 || se.seq_lens != a.seq_lens || a.n_splits != list_attn_splits(se.k) ||
       se.hkv != a.hkv || se.batch != a.batch)
     return hipErrorInvalidValue;
   return dt == kBF16 ? launch_list_attn_t<bf16_t>(se, a, s) : launch_list_attn_t<float>(se, a, s);

@@ -29,6 +29,7 @@
 
 #include "common.cuh"
 #include "kernels.h"
+#include "merge_impl.cuh"
 
 namespace lk {
 
@@ -73,6 +74,12 @@ __global__ __launch_bounds__(kB16Waves * kWave) void build16_kernel(BuildArgs a)
   if (item >= a.n * a.hkv) return;
   const int idx = item / a.hkv, kvh = item % a.hkv;
   const int phys = a.phys_ids[idx];
+  // decode step (idx = sequence): merge the attention partials of (idx, kvh),
+  // then advance the sequence's length when its append was valid
+  const bool commit = a.commit_seq_lens && kvh == 0 && lane == 0;
+  const int len = commit ? a.commit_seq_lens[idx] : 0;
+  if (a.merge.part_o) merge_partials<T>(a, idx, kvh, lane, kWave);
+  if (commit && phys != -2) a.commit_seq_lens[idx] = len + 1;
   if (phys < 0 || phys >= a.num_phys) return;
   const T* K = reinterpret_cast<const T*>(a.k_pool) + (((size_t)phys * a.hkv + kvh) * B) * D;
 
@@ -343,7 +350,6 @@ static hipError_t launch_build16_t(int rank, const BuildArgs& a, hipStream_t s) 
 }
 
 hipError_t launch_build16(DType dt, int rank, const BuildArgs& a, hipStream_t s) {
-  if (a.merge.part_o || a.commit_seq_lens) return hipErrorInvalidValue;  // bulk builds only
   return dt == kBF16 ? launch_build16_t<bf16_t>(rank, a, s) : launch_build16_t<float>(rank, a, s);
 }
 

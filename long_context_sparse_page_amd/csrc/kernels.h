@@ -106,9 +106,10 @@ struct AttnArgs {
   void* out;                   // [batch][Hq][d]
   float* lse_out;              // optional [batch][Hq]
   int32_t batch, max_pages, num_phys, hkv, hq, k, n_splits;
-  int32_t pages_per_split;     // half-page units per wave (4 waves per split)
+  int32_t pages_per_split;     // 32-token units per wave (4 waves per split)
   float scale;
   int32_t len_add;
+  int32_t page_size = 64;      // 64: a unit is half a page; 16: two consecutive list entries
 };
 
 struct BuildArgs {
@@ -135,8 +136,8 @@ struct BuildArgs {
   int32_t q4;                  // records in the quantized layout (Q4Layout)
 };
 
-// q4: the summary records use Q4Layout (bf16 queries only)
-hipError_t launch_score(DType dt, int rank, int group, bool q4, const ScoreArgs& a, hipStream_t s);
+// q4: the summary records use Q4Layout (bf16 queries only); page_size 64 or 16
+hipError_t launch_score(DType dt, int page_size, int rank, int group, bool q4, const ScoreArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 // Chunked selection without its merge (a.n_chunks > 0): the per-chunk lists
 // only, for launch_list_attn.
@@ -144,7 +145,8 @@ hipError_t launch_select_lists(const SelectArgs& a, hipStream_t s);
 // merge = false leaves the split partials for the decode step's build launch
 hipError_t launch_attn(DType dt, int group, const AttnArgs& a, bool merge, hipStream_t s);
 hipError_t launch_build(DType dt, int rank, const BuildArgs& a, hipStream_t s);
-// Pages of 16 tokens (bulk builds only: no merge or length commit)
+// Pages of 16 tokens: one wave per (page, KV head); in the decode step (merge
+// and length commit set) wave (seq, kvh) first merges and commits as above
 hipError_t launch_build16(DType dt, int rank, const BuildArgs& a, hipStream_t s);
 // Decode step: selection (se) and attention splits (a) in one launch, for
 // tables of up to 3072 pages per sequence (select_attn_fusable).

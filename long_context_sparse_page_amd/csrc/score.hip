@@ -16,6 +16,10 @@
 //   LSE: z is transposed through LDS so that each query head's B logits sit
 //     on a group of 64/G lanes, reduced with DPP (max, then sum of exp2).
 // The page's bytes are read once, with 16-byte loads.
+//
+// Pages of B = 64 or B = 16 tokens.  With B = 16 a wave's lanes cover four
+// records' tokens at once (lane = 16 * record + token), so each page's
+// log-sum-exp is reduced within one 16-lane row, with no transpose.
 
 #include "common.cuh"
 #include "kernels.h"
@@ -23,9 +27,6 @@
 namespace lk {
 
 constexpr int kScoreWaves = 4;
-#ifndef LK_SCORE_GPW
-#define LK_SCORE_GPW 1
-#endif
 constexpr int kScorePagesPerWave = 8;
 constexpr int kScorePagesPerBlock = kScoreWaves * kScorePagesPerWave;
 
@@ -49,10 +50,9 @@ __device__ __forceinline__ void load_coeffs(const T* p, float (&c)[R]) {
 // 0 of every (sequence, KV head) before anything else: 16-byte copies of the
 // new key and value rows into slot T mod B of page T / B, and the build-list
 // entry.
-template <typename T>
+template <typename T, int B>
 __device__ __forceinline__ void append_duty(const ScoreArgs& a, int seq, int kvh, int chunk) {
   if (a.app.k_new == nullptr || chunk != 0) return;
-  constexpr int B = 64;
   constexpr int D = kHeadDim;
   constexpr int VEC = 16 / sizeof(T);
   constexpr int CH = D / VEC;  // 16-byte chunks per row
@@ -73,14 +73,13 @@ __device__ __forceinline__ void append_duty(const ScoreArgs& a, int seq, int kvh
   if (kvh == 0 && t == 0) a.app.build_list[seq] = !ok ? -2 : (slot == B - 1 ? phys : -1);
 }
 
-template <typename T, int R, int G>
+template <typename T, int R, int G, int B>
 __global__ __launch_bounds__(kScoreWaves * kWave) void score_kernel(ScoreArgs a) {
-  constexpr int B = 64;
   constexpr int D = kHeadDim;
   constexpr int ROWS = R + 1;                 // centroid + r basis rows
   constexpr int RG = (ROWS + 3) / 4;          // rows per lane group
   constexpr int LPH = kWave / G;              // lanes per query head in the LSE
-  constexpr int TPL = B / LPH;                // logits per lane in the LSE
+  constexpr int TPL = B >= LPH ? B / LPH : 1;  // logits per lane in the LSE (B = 64)
   constexpr size_t REC = (size_t)ROWS * D + (size_t)B * R;
 
   __shared__ float sP[kScoreWaves][ROWS * G];
@@ -90,7 +89,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_kernel(ScoreArgs a)
   const int wave = threadIdx.x / kWave;
   const int seq = blockIdx.z;
   const int kvh = blockIdx.y;
-  append_duty<T>(a, seq, kvh, blockIdx.x);
+  append_duty<T, B>(a, seq, kvh, blockIdx.x);
   const int len = a.seq_lens[seq] + a.len_add;
   if (len <= 0) return;
   int n_scored = (len - 1) / B;
@@ -157,35 +156,49 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_kernel(ScoreArgs a)
     }
     wave_lds_fence();
 
-    // reconstructed logits, lane = token
+    // reconstructed logits, lane = token (B = 16: lanes past the page repeat
+    // its tokens, and only the first row of 16 lanes is reduced)
     float c[R];
-    load_coeffs<T, R>(rec + (size_t)ROWS * D + (size_t)lane * R, c);
+    load_coeffs<T, R>(rec + (size_t)ROWS * D + (size_t)(lane % B) * R, c);
+    float zr[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float z = P[g];
 #pragma unroll
       for (int m = 0; m < R; ++m) z = fmaf(c[m], P[(m + 1) * G + g], z);
-      Z[g * B + lane] = z * zscale;
+      zr[g] = z * zscale;
     }
-    wave_lds_fence();
+    if constexpr (B == 16) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float mx = group_max<16>(zr[g]);
+        const float sum = group_sum<16>(fast_exp2(zr[g] - mx));
+        if (lane == g) out[(size_t)g * a.max_pages + j] = (mx + fast_log2(sum)) * kLn2;
+      }
+      wave_lds_fence();  // P is rewritten by the next page
+    } else {
+#pragma unroll
+      for (int g = 0; g < G; ++g) Z[g * B + lane] = zr[g];
+      wave_lds_fence();
 
-    // per-head log-sum-exp over the page's B logits
-    const int hg = lane / LPH;
-    const int t0 = (lane % LPH) * TPL;
-    float v[TPL];
-    float mx = -INFINITY;
+      // per-head log-sum-exp over the page's B logits
+      const int hg = lane / LPH;
+      const int t0 = (lane % LPH) * TPL;
+      float v[TPL];
+      float mx = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < TPL; ++t) {
-      v[t] = Z[hg * B + t0 + t];
-      mx = fmaxf(mx, v[t]);
+      for (int t = 0; t < TPL; ++t) {
+        v[t] = Z[hg * B + t0 + t];
+        mx = fmaxf(mx, v[t]);
+      }
+      mx = group_max<LPH>(mx);
+      float sum = 0.f;
+#pragma unroll
+      for (int t = 0; t < TPL; ++t) sum += fast_exp2(v[t] - mx);
+      sum = group_sum<LPH>(sum);
+      if (lane % LPH == 0) out[(size_t)hg * a.max_pages + j] = (mx + fast_log2(sum)) * kLn2;
+      wave_lds_fence();
     }
-    mx = group_max<LPH>(mx);
-    float sum = 0.f;
-#pragma unroll
-    for (int t = 0; t < TPL; ++t) sum += fast_exp2(v[t] - mx);
-    sum = group_sum<LPH>(sum);
-    if (lane % LPH == 0) out[(size_t)hg * a.max_pages + j] = (mx + fast_log2(sum)) * kLn2;
-    wave_lds_fence();
   }
 }
 
@@ -206,35 +219,48 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_kernel(ScoreArgs a)
 // this part a scattered read of many short-lived waves, each with one batch
 // of loads in flight, streams faster than fewer waves that loop over several
 // batches.
-template <int R> struct ScoreGroup {
+template <int R, int B = 64> struct ScoreGroup {
   static constexpr int NR = R >= 16 ? 2 : (R >= 8 ? 4 : (R >= 4 ? 8 : 16));  // records per group
   static constexpr int SLOTS = NR * (R + 1);
   static constexpr int TILES = (SLOTS + 15) / 16;
   static constexpr int CW = (R + 1) / 2;        // 32-bit words of one token's coefficients
-  static constexpr int GROUPS_PER_WAVE = LK_SCORE_GPW;
+  // coefficient sets a lane holds: its token of every record (B = 64), or
+  // token lane % 16 of record 4 p + lane / 16 for each pass p (B = 16)
+  static constexpr int CSETS = B == 64 ? NR : (NR + 3) / 4;
 };
 
 // One group's loads, held in registers until the group is computed.
-template <int R> struct GroupLoads {
-  uint4 wb[ScoreGroup<R>::TILES][4];             // B operand tiles
-  uint32_t cw[ScoreGroup<R>::NR][ScoreGroup<R>::CW];  // this lane's token coefficients (bf16 pairs)
-  bool valid[ScoreGroup<R>::NR];                 // record present in the pool (else the page scores -inf)
+template <int R, int B> struct GroupLoads {
+  uint4 wb[ScoreGroup<R, B>::TILES][4];                    // B operand tiles
+  uint32_t cw[ScoreGroup<R, B>::CSETS][ScoreGroup<R, B>::CW];  // token coefficients (bf16 pairs)
+  bool valid[ScoreGroup<R, B>::NR];                        // record present in the pool (else the page scores -inf)
 };
+
+// Pointer of record x of the group, x lane-dependent (a select over the
+// group's uniform record pointers).
+template <int NR, typename P>
+__device__ __forceinline__ P pick_record(P const (&recp)[NR], int x) {
+  P rp = recp[0];
+#pragma unroll
+  for (int y = 1; y < NR; ++y)
+    if (y == x) rp = recp[y];
+  return rp;
+}
 
 // Every load is unconditional, so the compiler keeps them in one batch with no
 // wait in between: a record that is not in the pool is read from physical
 // page 0 instead (always allocated) and its result discarded, and B columns
 // past the group's slots repeat its last slot (their products are unused).
-template <int R>
-__device__ __forceinline__ void load_group(GroupLoads<R>& L, const bf16_t* summ, const int* phys_g, int num_phys,
+template <int R, int B>
+__device__ __forceinline__ void load_group(GroupLoads<R, B>& L, const bf16_t* summ, const int* phys_g, int num_phys,
                                            int hkv, int kvh, int col, int kg, int lane) {
   constexpr int D = kHeadDim;
-  constexpr int B = 64;
   constexpr int ROWS = R + 1;
-  constexpr int NR = ScoreGroup<R>::NR;
-  constexpr int SLOTS = ScoreGroup<R>::SLOTS;
-  constexpr int TILES = ScoreGroup<R>::TILES;
-  constexpr int CW = ScoreGroup<R>::CW;
+  constexpr int NR = ScoreGroup<R, B>::NR;
+  constexpr int SLOTS = ScoreGroup<R, B>::SLOTS;
+  constexpr int TILES = ScoreGroup<R, B>::TILES;
+  constexpr int CW = ScoreGroup<R, B>::CW;
+  constexpr int CSETS = ScoreGroup<R, B>::CSETS;
   constexpr size_t REC = (size_t)ROWS * D + (size_t)B * R;
   const bf16_t* recp[NR];
 #pragma unroll
@@ -255,8 +281,10 @@ __device__ __forceinline__ void load_group(GroupLoads<R>& L, const bf16_t* summ,
       L.wb[tau][t] = *reinterpret_cast<const uint4*>(rp + (size_t)m * D + 32 * t + 8 * kg);
   }
 #pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const bf16_t* cp = recp[r] + (size_t)ROWS * D + (size_t)lane * R;
+  for (int r = 0; r < CSETS; ++r) {
+    const bf16_t* cp = B == 64 ? recp[r] + (size_t)ROWS * D + (size_t)lane * R
+                               : pick_record<NR>(recp, min(4 * r + (lane >> 4), NR - 1)) + (size_t)ROWS * D +
+                                     (size_t)(lane & 15) * R;
     if constexpr (R % 8 == 0) {
 #pragma unroll
       for (int x = 0; x < CW; x += 4) {
@@ -358,19 +386,66 @@ __device__ __forceinline__ void group_lse(const float* P, float* Z, Coef coef, c
   }
 }
 
-template <int R, int G>
+// The same at B = 16: lane 16 q + t holds token t of record 4 p + q in pass p,
+// so each record's logits sit on one row of 16 lanes and its per-head LSE is
+// a row reduction; lane 16 q + g then writes head g.  coef(p, c, s) gives the
+// lane's coefficients of pass p and their scale.
+template <int R, int G, int NR, bool SCALED, typename Coef>
+__device__ __forceinline__ void group_lse16(const float* P, Coef coef, const bool (&valid)[NR], float* out,
+                                            int max_pages, int g0, int j_end, int lane, float zscale) {
+  constexpr int ROWS = R + 1;
+  const int q = lane >> 4, t = lane & 15;
+#pragma unroll
+  for (int p = 0; p < (NR + 3) / 4; ++p) {
+    const int r = 4 * p + q;
+    const int rc = min(r, NR - 1);
+    float c[R], cs;
+    coef(p, c, cs);
+    const float* Pr = P + rc * ROWS * G;
+    float res[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float acc;
+      if constexpr (SCALED) {
+        acc = 0.f;
+#pragma unroll
+        for (int m = 0; m < R; ++m) acc = fmaf(c[m], Pr[(m + 1) * G + g], acc);
+        acc = fmaf(cs, acc, Pr[g]);
+      } else {
+        acc = Pr[g];
+#pragma unroll
+        for (int m = 0; m < R; ++m) acc = fmaf(c[m], Pr[(m + 1) * G + g], acc);
+      }
+      const float z = acc * zscale;
+      const float mx = group_max<16>(z);
+      const float sum = group_sum<16>(fast_exp2(z - mx));
+      res[g] = (mx + fast_log2(sum)) * kLn2;
+    }
+    float val = res[0];
+#pragma unroll
+    for (int g = 1; g < G; ++g)
+      if (t == g) val = res[g];
+    bool ok = valid[0];
+#pragma unroll
+    for (int x = 1; x < NR; ++x)
+      if (x == rc) ok = valid[x];
+    const int j = g0 + r;
+    if (t < G && r < NR && j < j_end) out[(size_t)t * max_pages + j] = ok ? val : -INFINITY;
+  }
+}
+
+template <int R, int G, int B>
 __global__ __launch_bounds__(kScoreWaves * kWave) void score_mfma_kernel(ScoreArgs a) {
-  constexpr int B = 64;
   constexpr int D = kHeadDim;
-  constexpr int NR = ScoreGroup<R>::NR;
-  constexpr int SLOTS = ScoreGroup<R>::SLOTS;
-  constexpr int TILES = ScoreGroup<R>::TILES;
-  constexpr int PAGES_PER_WAVE = ScoreGroup<R>::GROUPS_PER_WAVE * NR;
+  constexpr int NR = ScoreGroup<R, B>::NR;
+  constexpr int SLOTS = ScoreGroup<R, B>::SLOTS;
+  constexpr int TILES = ScoreGroup<R, B>::TILES;
+  constexpr int PAGES_PER_WAVE = NR;
   static_assert(G <= 8, "at most 8 query heads per KV head");
 
   __shared__ float sP[kScoreWaves][SLOTS * G];
   constexpr int RC = (16 / G) < NR ? (16 / G) : NR;  // records per LDS transpose (RC * G <= 16)
-  __shared__ float sZ[kScoreWaves][RC * G * B];
+  __shared__ float sZ[kScoreWaves][B == 64 ? RC * G * B : 1];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar table loads
@@ -378,7 +453,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_mfma_kernel(ScoreAr
   // records sit side by side, are dispatched together
   const int seq = blockIdx.z;
   const int kvh = blockIdx.x;
-  append_duty<bf16_t>(a, seq, kvh, blockIdx.y);
+  append_duty<bf16_t, B>(a, seq, kvh, blockIdx.y);
   const int j0 = (blockIdx.y * kScoreWaves + wave) * PAGES_PER_WAVE;
   if (j0 >= a.max_pages) return;
   const int col = lane & 15;       // B column / A row of this lane
@@ -408,11 +483,8 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_mfma_kernel(ScoreAr
   int n_scored = len_raw <= 0 ? 0 : (len_raw - 1) / B;
   if (n_scored > a.max_pages - 1) n_scored = a.max_pages - 1;
   if (j0 >= n_scored) return;
-  constexpr int GPW = ScoreGroup<R>::GROUPS_PER_WAVE;
-  GroupLoads<R> grp[GPW];
-#pragma unroll
-  for (int gi = 0; gi < GPW; ++gi)
-    load_group<R>(grp[gi], summ, phys_all + gi * NR, a.num_phys, a.hkv, kvh, col, kg, lane);
+  GroupLoads<R, B> cur;
+  load_group<R, B>(cur, summ, phys_all, a.num_phys, a.hkv, kvh, col, kg, lane);
   // The loads above have no side effects, so without this fence the compiler
   // would move them between the products (each move adds a wait for earlier
   // loads before later ones are issued).
@@ -424,11 +496,8 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_mfma_kernel(ScoreAr
   float* P = sP[wave];
   float* Z = sZ[wave];
 
-#pragma unroll
-  for (int gi = 0; gi < GPW; ++gi) {
-    const GroupLoads<R>& cur = grp[gi];
-    const int g0 = j0 + gi * NR;
-    if (g0 >= j_end) break;
+  {
+    const int g0 = j0;
     // projection on the matrix cores
 #pragma unroll
     for (int tau = 0; tau < TILES; ++tau) {
@@ -444,27 +513,26 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_mfma_kernel(ScoreAr
       }
     }
     wave_lds_fence();
-    group_lse<R, G, NR, false>(
-        P, Z,
-        [&](int r, float (&c)[R], float& cs) {
+    auto coef = [&](int r, float (&c)[R], float& cs) {
 #pragma unroll
-          for (int m = 0; m < R; ++m) c[m] = (m & 1) ? bf16_hi(cur.cw[r][m >> 1]) : bf16_lo(cur.cw[r][m >> 1]);
-          cs = 1.f;
-        },
-        cur.valid, out, a.max_pages, g0, j_end, lane, zscale);
+      for (int m = 0; m < R; ++m) c[m] = (m & 1) ? bf16_hi(cur.cw[r][m >> 1]) : bf16_lo(cur.cw[r][m >> 1]);
+      cs = 1.f;
+    };
+    if constexpr (B == 64) group_lse<R, G, NR, false>(P, Z, coef, cur.valid, out, a.max_pages, g0, j_end, lane, zscale);
+    else group_lse16<R, G, NR, false>(P, coef, cur.valid, out, a.max_pages, g0, j_end, lane, zscale);
   }
 }
 
-template <int R>
+template <int R, int B>
 static hipError_t launch_score_mfma(int group, const ScoreArgs& a, hipStream_t s) {
-  constexpr int per_block = kScoreWaves * ScoreGroup<R>::GROUPS_PER_WAVE * ScoreGroup<R>::NR;
+  constexpr int per_block = kScoreWaves * ScoreGroup<R, B>::NR;
   dim3 grid(a.hkv, (a.max_pages + per_block - 1) / per_block, a.batch);
   dim3 block(kScoreWaves * kWave);
   switch (group) {
-    case 1: hipLaunchKernelGGL((score_mfma_kernel<R, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((score_mfma_kernel<R, 2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((score_mfma_kernel<R, 4>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((score_mfma_kernel<R, 8>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((score_mfma_kernel<R, 1, B>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((score_mfma_kernel<R, 2, B>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((score_mfma_kernel<R, 4, B>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((score_mfma_kernel<R, 8, B>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -485,10 +553,11 @@ static hipError_t launch_score_mfma(int group, const ScoreArgs& a, hipStream_t s
 // (its products are the S_g), then NR * R / 16 tiles of basis rows (column =
 // record * R + row).  The reconstruction and LSE are those of the
 // bf16 records, with the per-token coefficient scale.
-template <int R> struct Q4Group {
+template <int R, int B = 64> struct Q4Group {
   static constexpr int NR = R >= 16 ? 2 : (R >= 8 ? 4 : 8);  // records per wave
   static constexpr int BT = NR * R / 16;                       // basis tiles
   static constexpr int SLOTS = NR * (R + 1);
+  static constexpr int CSETS = B == 64 ? NR : (NR + 3) / 4;    // coefficient sets per lane (as ScoreGroup)
 };
 
 __device__ __forceinline__ uint32_t bf16x2_of(float lo, float hi) {  // both exact in bf16: the high halves
@@ -524,27 +593,27 @@ __device__ __forceinline__ bf16x8_t q8_operand(uint32_t w0, uint32_t w1) {
 }
 __device__ __forceinline__ float half_bits_f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
 
-template <int R, int G>
+template <int R, int G, int B>
 __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs a) {
-  constexpr int B = 64;
   constexpr int D = kHeadDim;
   constexpr int ROWS = R + 1;
-  constexpr int NR = Q4Group<R>::NR;
-  constexpr int BT = Q4Group<R>::BT;
-  constexpr int SLOTS = Q4Group<R>::SLOTS;
-  constexpr Q4Layout L{R};
+  constexpr int NR = Q4Group<R, B>::NR;
+  constexpr int BT = Q4Group<R, B>::BT;
+  constexpr int SLOTS = Q4Group<R, B>::SLOTS;
+  constexpr int CSETS = Q4Group<R, B>::CSETS;
+  constexpr Q4Layout L{R, B};
   constexpr int REC = L.bytes();
   static_assert(G <= 8 && NR <= 16 && BT * 16 == NR * R, "tile shapes");
 
   __shared__ float sP[kScoreWaves][SLOTS * G];
   constexpr int RC = (16 / G) < NR ? (16 / G) : NR;
-  __shared__ float sZ[kScoreWaves][RC * G * B];
+  __shared__ float sZ[kScoreWaves][B == 64 ? RC * G * B : 1];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int seq = blockIdx.z;
   const int kvh = blockIdx.x;  // grid (KV head, page chunk, sequence), as for bf16 records
-  append_duty<bf16_t>(a, seq, kvh, blockIdx.y);
+  append_duty<bf16_t, B>(a, seq, kvh, blockIdx.y);
   const int j0 = (blockIdx.y * kScoreWaves + wave) * NR;
   if (j0 >= a.max_pages) return;
   const int col = lane & 15;
@@ -600,11 +669,13 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
     wm[1] = *reinterpret_cast<const uint4*>(rp + 32 * kg + 16);
     msc = *reinterpret_cast<const uint16_t*>(rp + L.mscale());
   }
-  uint32_t cw[NR][(R + 3) / 4];  // this lane's token: R int8 codes
-  uint32_t csc[NR];              // and their scale (fp16 bits)
+  uint32_t cw[CSETS][(R + 3) / 4];  // a token's R int8 codes (lane's token of record r, or of pass r at B = 16)
+  uint32_t csc[CSETS];              // and their scale (fp16 bits)
 #pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const uint8_t* cp = recp[r] + L.coef() + (size_t)lane * R;
+  for (int r = 0; r < CSETS; ++r) {
+    const uint8_t* rp = B == 64 ? recp[r] : pick_record<NR>(recp, min(4 * r + (lane >> 4), NR - 1));
+    const int tok = B == 64 ? lane : (lane & 15);
+    const uint8_t* cp = rp + L.coef() + (size_t)tok * R;
     if constexpr (R == 16) {
       const uint4 v = *reinterpret_cast<const uint4*>(cp);
       cw[r][0] = v.x; cw[r][1] = v.y; cw[r][2] = v.z; cw[r][3] = v.w;
@@ -614,7 +685,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
     } else {
       cw[r][0] = *reinterpret_cast<const uint32_t*>(cp);
     }
-    csc[r] = *reinterpret_cast<const uint16_t*>(recp[r] + L.cscale() + 2 * lane);
+    csc[r] = *reinterpret_cast<const uint16_t*>(rp + L.cscale() + 2 * tok);
   }
   asm volatile("" ::: "memory");  // keep the loads above in one batch (as for bf16 records)
   const int j_end = min(j0 + NR, n_scored);
@@ -669,78 +740,79 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
     }
   }
   wave_lds_fence();
-  group_lse<R, G, NR, true>(
-      P, Z,
-      [&](int r, float (&c)[R], float& cs) {
+  auto coef = [&](int r, float (&c)[R], float& cs) {
 #pragma unroll
-        for (int m = 0; m < R; ++m) c[m] = (float)(int8_t)((cw[r][m >> 2] >> (8 * (m & 3))) & 0xffu);
-        cs = half_bits_f(csc[r]);
-      },
-      valid, out, a.max_pages, j0, j_end, lane, zscale);
+    for (int m = 0; m < R; ++m) c[m] = (float)(int8_t)((cw[r][m >> 2] >> (8 * (m & 3))) & 0xffu);
+    cs = half_bits_f(csc[r]);
+  };
+  if constexpr (B == 64) group_lse<R, G, NR, true>(P, Z, coef, valid, out, a.max_pages, j0, j_end, lane, zscale);
+  else group_lse16<R, G, NR, true>(P, coef, valid, out, a.max_pages, j0, j_end, lane, zscale);
 }
 
-template <int R>
+template <int R, int B>
 static hipError_t launch_score_q4(int group, const ScoreArgs& a, hipStream_t s) {
-  constexpr int per_block = kScoreWaves * Q4Group<R>::NR;
+  constexpr int per_block = kScoreWaves * Q4Group<R, B>::NR;
   dim3 grid(a.hkv, (a.max_pages + per_block - 1) / per_block, a.batch);
   dim3 block(kScoreWaves * kWave);
   switch (group) {
-    case 1: hipLaunchKernelGGL((score_q4_kernel<R, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((score_q4_kernel<R, 2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((score_q4_kernel<R, 4>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((score_q4_kernel<R, 8>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((score_q4_kernel<R, 1, B>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((score_q4_kernel<R, 2, B>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((score_q4_kernel<R, 4, B>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((score_q4_kernel<R, 8, B>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <typename T, int R>
+template <typename T, int R, int B>
 static hipError_t launch_score_rg(int group, const ScoreArgs& a, hipStream_t s) {
   dim3 grid((a.max_pages + kScorePagesPerBlock - 1) / kScorePagesPerBlock, a.hkv, a.batch);
   dim3 block(kScoreWaves * kWave);
   switch (group) {
-    case 1: hipLaunchKernelGGL((score_kernel<T, R, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((score_kernel<T, R, 2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((score_kernel<T, R, 4>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((score_kernel<T, R, 8>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((score_kernel<T, R, 1, B>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((score_kernel<T, R, 2, B>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((score_kernel<T, R, 4, B>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((score_kernel<T, R, 8, B>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <typename T>
-static hipError_t launch_score_t(int rank, int group, const ScoreArgs& a, hipStream_t s) {
-  switch (rank) {
-    case 1: return launch_score_rg<T, 1>(group, a, s);
-    case 2: return launch_score_rg<T, 2>(group, a, s);
-    case 4: return launch_score_rg<T, 4>(group, a, s);
-    case 8: return launch_score_rg<T, 8>(group, a, s);
-    case 16: return launch_score_rg<T, 16>(group, a, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-hipError_t launch_score(DType dt, int rank, int group, bool q4, const ScoreArgs& a, hipStream_t s) {
+template <int B>
+static hipError_t launch_score_b(DType dt, int rank, int group, bool q4, const ScoreArgs& a, hipStream_t s) {
   if (q4) {
     if (dt != kBF16) return hipErrorInvalidValue;
     switch (rank) {
-      case 4: return launch_score_q4<4>(group, a, s);
-      case 8: return launch_score_q4<8>(group, a, s);
-      case 16: return launch_score_q4<16>(group, a, s);
+      case 4: return launch_score_q4<4, B>(group, a, s);
+      case 8: return launch_score_q4<8, B>(group, a, s);
+      case 16: return launch_score_q4<16, B>(group, a, s);
       default: return hipErrorInvalidValue;
     }
   }
   if (dt == kBF16) {
     switch (rank) {
-      case 1: return launch_score_mfma<1>(group, a, s);
-      case 2: return launch_score_mfma<2>(group, a, s);
-      case 4: return launch_score_mfma<4>(group, a, s);
-      case 8: return launch_score_mfma<8>(group, a, s);
-      case 16: return launch_score_mfma<16>(group, a, s);
+      case 1: return launch_score_mfma<1, B>(group, a, s);
+      case 2: return launch_score_mfma<2, B>(group, a, s);
+      case 4: return launch_score_mfma<4, B>(group, a, s);
+      case 8: return launch_score_mfma<8, B>(group, a, s);
+      case 16: return launch_score_mfma<16, B>(group, a, s);
       default: return hipErrorInvalidValue;
     }
   }
-  return launch_score_t<float>(rank, group, a, s);
+  switch (rank) {
+    case 1: return launch_score_rg<float, 1, B>(group, a, s);
+    case 2: return launch_score_rg<float, 2, B>(group, a, s);
+    case 4: return launch_score_rg<float, 4, B>(group, a, s);
+    case 8: return launch_score_rg<float, 8, B>(group, a, s);
+    case 16: return launch_score_rg<float, 16, B>(group, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_score(DType dt, int page_size, int rank, int group, bool q4, const ScoreArgs& a, hipStream_t s) {
+  if (page_size == 64) return launch_score_b<64>(dt, rank, group, q4, a, s);
+  if (page_size == 16) return launch_score_b<16>(dt, rank, group, q4, a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace lk

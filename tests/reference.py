@@ -290,3 +290,29 @@ def bf16_step_above(x: np.ndarray) -> np.ndarray:
     """The next bf16 value above |x| (bf16-representable x): |x| plus one ulp."""
     u = torch.from_numpy(np.abs(np.ascontiguousarray(x, dtype=np.float32))).to(torch.bfloat16).view(torch.int16)
     return (u + 1).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def check_all_pairs(w, dc, o, q64, lens, pairs=None, page_lse=None, e2e_lse_gate=True, share=False):
+    """check_pair on every (or the listed) (sequence, KV head) of the outputs
+    o, with the GPU's own records read back from the pool (and the shares of
+    o when ``share``)."""
+    page_lse = o["page_lse"].cpu().numpy() if page_lse is None else page_lse
+    sel, cnt = o["sel"].cpu().numpy(), o["cnt"].cpu().numpy()
+    out = o["out"].float().cpu().numpy().astype(np.float64)
+    lse = o["lse"].cpu().numpy()
+    shares = o["share"].cpu().numpy() if share else None
+    G = w.group
+    tot = PairCheck()
+    if pairs is None:
+        pairs = [(s, h) for s in range(w.batch) for h in range(w.num_kv_heads)]
+    for (s, h) in pairs:
+        K, V = host_pages(w, s, h, lens[s])
+        n_mr = lo.most_recent_page(lens[s], w.page_size)
+        own = gpu_summaries(dc, w, s, h, max(n_mr, 0))
+        hs = slice(h * G, (h + 1) * G)
+        tot.merge(check_pair(w, q64[s, hs], K, V, lens[s], sel[s, h, :cnt[s, h]], own=own,
+                                 gpu_page_lse=page_lse[s, hs], gpu_out=out[s, hs], gpu_lse=lse[s, hs],
+                                 gpu_share=None if shares is None else shares[s, h],
+                                 tag=f"seq {s} head {h} T {lens[s]}", e2e_lse_gate=e2e_lse_gate))
+        assert (sel[s, h, cnt[s, h]:] == -1).all()
+    return tot

@@ -79,17 +79,24 @@ def test_page16_record_bytes_match_table_d10(golden_dir):
     assert L.lk_summary_record_bytes(cfg(page_size=16)) == (128 + 8 * 128 + 16 * 8) * 2
 
 
-def test_page16_is_a_build_only_config():
+def test_page16_is_accepted_by_every_entry_point():
+    """16-token pages run the whole path: argument errors still come first at
+    every entry point, a workspace is sized for them (its attention splits
+    cover two pages per 32-token unit), and other page sizes are refused."""
     c16 = cfg(page_size=16)
-    # accepted by the builder (argument errors come first), refused elsewhere
     expect(L.LK_ERR_INVALID_ARG, L.lk_build_page_summary, c16, fake_cache(), None, 3, None, None, 0, 0)
     L.lk_build_page_summary(c16, fake_cache(), None, 0, None, None, 0, 0)
-    expect(L.LK_ERR_UNSUPPORTED, L.lk_score_select, c16, fake_cache(), 2, FAKE, None, None, FAKE, FAKE,
-           0x100000, 1 << 30, 0)
-    expect(L.LK_ERR_UNSUPPORTED, L.lk_decode_step, c16, fake_cache(), 2, FAKE, FAKE, FAKE, FAKE, None, None,
+    ws16 = L.lk_workspace_size(c16, 2, 64)
+    expect(L.LK_ERR_WORKSPACE, L.lk_score_select, c16, fake_cache(max_pages_per_seq=64), 2, FAKE, None, None,
+           FAKE, FAKE, 0x100000, ws16 - 1, 0)
+    expect(L.LK_ERR_INVALID_ARG, L.lk_decode_step, c16, fake_cache(), 2, FAKE, None, FAKE, FAKE, None, None,
            None, 0x100000, 1 << 30, 0)
-    expect(L.LK_ERR_UNSUPPORTED, L.lk_build_page_summary, cfg(page_size=32), fake_cache(), FAKE, 3, None, None,
-           0, 0)
+    expect(L.LK_ERR_INVALID_ARG, L.lk_sparse_decode_attn, c16, fake_cache(), 2, FAKE, None, FAKE, FAKE, None,
+           0x100000, 1 << 30, 0)
+    for bad in (32, 8, 128):
+        expect(L.LK_ERR_UNSUPPORTED, L.lk_build_page_summary, cfg(page_size=bad), fake_cache(), FAKE, 3, None,
+               None, 0, 0)
+        expect(L.LK_ERR_UNSUPPORTED, L.lk_workspace_size, cfg(page_size=bad), 1, 16)
 
 
 def test_workspace_size_scales():
@@ -119,7 +126,7 @@ def test_workspace_for_a_batch_serves_every_smaller_batch(kw, pages):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=64), L.LK_ERR_UNSUPPORTED),
-    (dict(page_size=16), L.LK_ERR_UNSUPPORTED),
+    (dict(page_size=32), L.LK_ERR_UNSUPPORTED),
     (dict(rank=3), L.LK_ERR_UNSUPPORTED),
     (dict(rank=0), L.LK_ERR_INVALID_ARG),
     (dict(num_q_heads=30), L.LK_ERR_INVALID_ARG),

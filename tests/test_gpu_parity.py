@@ -218,31 +218,8 @@ def test_build_and_score_bf16(gpu):
     dc.score_select(qd, o)
     dc.sparse_attn(qd, o["sel"], o["cnt"], o)
     torch.cuda.synchronize()
-    tot = check_all_pairs(w, dc, o, q64, T)
+    tot = ref.check_all_pairs(w, dc, o, q64, T)
     say("end to end:", tot)
-
-
-def check_all_pairs(w, dc, o, q64, lens, pairs=None, page_lse=None, e2e_lse_gate=True):
-    """ref.check_pair on every (or the listed) (sequence, KV head) of the
-    outputs o, with the GPU's own records read back from the pool."""
-    page_lse = o["page_lse"].cpu().numpy() if page_lse is None else page_lse
-    sel, cnt = o["sel"].cpu().numpy(), o["cnt"].cpu().numpy()
-    out = o["out"].float().cpu().numpy().astype(np.float64)
-    lse = o["lse"].cpu().numpy()
-    G = w.group
-    tot = ref.PairCheck()
-    if pairs is None:
-        pairs = [(s, h) for s in range(w.batch) for h in range(w.num_kv_heads)]
-    for (s, h) in pairs:
-        K, V = ref.host_pages(w, s, h, lens[s])
-        n_mr = lo.most_recent_page(lens[s], w.page_size)
-        own = ref.gpu_summaries(dc, w, s, h, max(n_mr, 0))
-        hs = slice(h * G, (h + 1) * G)
-        tot.merge(ref.check_pair(w, q64[s, hs], K, V, lens[s], sel[s, h, :cnt[s, h]], own=own,
-                                 gpu_page_lse=page_lse[s, hs], gpu_out=out[s, hs], gpu_lse=lse[s, hs],
-                                 tag=f"seq {s} head {h} T {lens[s]}", e2e_lse_gate=e2e_lse_gate))
-        assert (sel[s, h, cnt[s, h]:] == -1).all()
-    return tot
 
 
 # Accuracy bar of the fp32 builder against the fp64 oracle on separated modes
@@ -347,7 +324,7 @@ def test_decode_steps_bf16(gpu):
         o2 = dc.outputs()  # the page scores of the same step (the decode step keeps them internal)
         dc.score_select(ref.q_device(q64, w.dtype), o2)
         torch.cuda.synchronize()
-        tot = check_all_pairs(w, dc, o, q64, lens, page_lse=o2["page_lse"].cpu().numpy())
+        tot = ref.check_all_pairs(w, dc, o, q64, lens, page_lse=o2["page_lse"].cpu().numpy())
         say("  ", tot)
 
 
@@ -817,7 +794,7 @@ def test_q4_end_to_end(gpu):
     dc.score_select(qd, o)
     dc.sparse_attn(qd, o["sel"], o["cnt"], o)
     torch.cuda.synchronize()
-    tot = check_all_pairs(w, dc, o, q64, T, e2e_lse_gate=False)
+    tot = ref.check_all_pairs(w, dc, o, q64, T, e2e_lse_gate=False)
     say("int4/int8 end to end:", tot)
 
 
@@ -852,6 +829,6 @@ def test_q4_decode_steps(gpu):
         o2 = dc.outputs()
         dc.score_select(ref.q_device(q64, w.dtype), o2)
         torch.cuda.synchronize()
-        tot.merge(check_all_pairs(w, dc, o, q64, lens, pairs=list(kv), page_lse=o2["page_lse"].cpu().numpy(),
+        tot.merge(ref.check_all_pairs(w, dc, o, q64, lens, pairs=list(kv), page_lse=o2["page_lse"].cpu().numpy(),
                                   e2e_lse_gate=False))
     say("int4/int8 decode steps:", tot)
