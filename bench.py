@@ -39,6 +39,7 @@ def parse():
                    help="2: 128K x 4 (the headline); 3: one 1M-token sequence; "
                         "4: 64 sequences of 4K..256K tokens (in-stream builds in most steps)")
     p.add_argument("--no-q4", action="store_true", help="skip the int4 / int8 record run of the default line")
+    p.add_argument("--no-page16", action="store_true", help="skip the 16-token-page (r8i4) run of the default line")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="also run a plain device copy of this size (counter calibration)")
     return p.parse_args()
@@ -283,6 +284,8 @@ def main():
     result["step_frac_of_read_ceiling"] = result["achieved_GBps"] / ceil["read_GBps"]
     if with_q4:
         result["int4_records"] = q4_variant(L, w, layers, qs, kns, vns, out, lse, stream, args, ws, ws_bytes)
+    if args.workload == 2 and not args.no_page16:
+        result["page16_r8i4"] = page16_variant(L, args, stream)
     if page16 is not None:
         result["bulk_build_page16_r8i4"] = page16
 
@@ -401,6 +404,119 @@ def q4_variant(L, w, layers, qs, kns, vns, out, lse, stream, args, ws, ws_bytes)
                        "achieved_GBps": score_bytes / (score_ms * 1e-3) / 1e9,
                        "frac": score_bytes / (score_ms * 1e-3) / 8e12,
                        "traffic": recorded_traffic(TRAFFIC_PROFILE["i4"])}}
+
+
+def page16_variant(L, args, stream):
+    """The same decode step at the pages' deployed page size: 128K x 4 with
+    pages of 16 tokens and int4 basis / int8 coefficient and centroid records
+    (r = 8), on its own cache (filled from the same key model at 16 tokens,
+    bulk-built, layer copies rotated as for the default line)."""
+    import torch
+
+    from long_context_sparse_page_amd import synth
+    from long_context_sparse_page_amd.paged import DeviceCache, to_storage
+
+    B = 16
+    total = args.warmup + args.steps
+    n_layers = args.layers
+    w = synth.workload(2, steps=-(-total // n_layers) + 2, summary="i4")
+    w.page_size = B
+    d, G, hkv, hq = w.head_dim, w.group, w.num_kv_heads, w.num_q_heads
+    t0 = time.time()
+    base = DeviceCache(w)
+    base.fill_from_synth(threads=min(16, os.cpu_count() or 4))
+    base.build_all()
+    torch.cuda.synchronize()
+    fill_s = time.time() - t0
+    layers = [base]
+    for _ in range(1, n_layers):
+        c = DeviceCache.__new__(DeviceCache)
+        c.__dict__.update(base.__dict__)
+        c.k_pool, c.v_pool = base.k_pool.clone(), base.v_pool.clone()
+        c.summary_pool, c.seq_lens = base.summary_pool.clone(), base.seq_lens.clone()
+        c.block_table = base.block_table.clone()
+        c.cache = L.make_cache(c.k_pool, c.v_pool, c.summary_pool, c.block_table, c.seq_lens)
+        layers.append(c)
+    nv = 16
+    qs, kns, vns = [], [], []
+    rng = np.random.default_rng(16)
+    for i in range(nv):
+        lens = [t + 1 + i for t in w.context]
+        q = np.zeros((w.batch, hq, d), np.float32)
+        for s in range(w.batch):
+            for h in range(hkv):
+                q[s, h * G:(h + 1) * G] = synth.queries(w, i, s, h, lens[s])[0]
+        qs.append(to_storage(q, w.dtype).to("cuda"))
+        kns.append(to_storage(rng.standard_normal((w.batch, hkv, d)).astype(np.float32), w.dtype).to("cuda"))
+        vns.append(to_storage(rng.standard_normal((w.batch, hkv, d)).astype(np.float32), w.dtype).to("cuda"))
+    out = torch.empty((w.batch, hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.batch, hq), dtype=torch.float32, device="cuda")
+    sp = stream.cuda_stream
+    ws, ws_bytes = base.ws, base.ws_bytes
+
+    def step(i):
+        c = layers[i % n_layers]
+        L.lk_decode_step(c.cfg, c.cache, w.batch, qs[i % nv], kns[i % nv], vns[i % nv], out, lse, None, None,
+                         ws, ws_bytes, sp)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.warmup, total):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    lens_now = [int(x) for x in layers[0].seq_lens.cpu().tolist()]
+    rec = L.lk_summary_record_bytes(base.cfg)
+    k_pages = L.lk_page_budget(base.cfg)
+    e = 2
+    step_bytes = w.batch * (2 * hq * d * e + 2 * hkv * d * e * 2)
+    for T in lens_now:
+        n_mr = (T - 1) // B
+        step_bytes += hkv * (n_mr * (rec + 4 * G) + ((min(k_pages, n_mr + 1) - 1) * B + T - n_mr * B) * 2 * d * e)
+    page_lse = torch.empty((w.batch, hq, base.max_pages), dtype=torch.float32, device="cuda")
+
+    def score(i):
+        c = layers[i % n_layers]
+        L.lk_score_select(c.cfg, c.cache, w.batch, qs[i % nv], page_lse, None, None, None, ws, ws_bytes, sp)
+    for i in range(8):
+        score(i)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.kernel_reps):
+        score(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    score_ms = ev0.elapsed_time(ev1) / args.kernel_reps
+    score_bytes = sum(hkv * ((T - 1) // B) for T in lens_now) * (rec + 4 * G)
+
+    def dense(i):
+        c = layers[i % n_layers]
+        L.lk_dense_decode_attn(c.cfg, c.cache, w.batch, qs[i % nv], out, lse, ws, ws_bytes, sp)
+    for i in range(4):
+        dense(i)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(20):
+        dense(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    dense_ms = ev0.elapsed_time(ev1) / 20
+    res = {"workload": "128K-context decode, batch 4, pages of 16 tokens, int4 basis / int8 coefficient and "
+                       "centroid records, rank 8, budget 2048 tokens (128 pages); one step = lk_decode_step",
+           "record_bytes": rec, "ms_per_step": ms, "steps_per_s": 1e3 / ms,
+           "algorithmic_bytes_per_step": step_bytes, "achieved_GBps": step_bytes / (ms * 1e-3) / 1e9,
+           "hbm_frac": step_bytes / (ms * 1e-3) / 8e12,
+           "scorer": {"kernel": "score_q4_kernel (16-token pages)", "launch_us": score_ms * 1e3,
+                      "bytes_per_launch": score_bytes, "achieved_GBps": score_bytes / (score_ms * 1e-3) / 1e9,
+                      "frac": score_bytes / (score_ms * 1e-3) / 8e12},
+           "dense_ms": dense_ms, "speedup_over_dense": dense_ms / ms, "fill_s": fill_s}
+    del layers, base
+    torch.cuda.empty_cache()
+    return res
 
 
 def bulk_build_page16(L, w, bulk, reps, stream, ev0, ev1):

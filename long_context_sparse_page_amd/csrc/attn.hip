@@ -517,7 +517,12 @@ __global__ __launch_bounds__(kFusedThreads) void select_attn_kernel(SelectArgs s
   __shared__ int32_t s_sel[kMaxSelect], s_selp[kMaxSelect];  // fallback selection
   __shared__ int32_t s_cnt;
 
-  const int split = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
+  // 1-D grid, XCD-aware: the splits of a (sequence, KV head), which all read
+  // its page scores and block table, are logically adjacent and share an L2
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = lin % a.n_splits;
+  const int kvh = (lin / a.n_splits) % se.hkv;
+  const int seq = lin / (a.n_splits * se.hkv);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -878,7 +883,7 @@ hipError_t launch_attn(DType dt, int group, const AttnArgs& a, bool merge, hipSt
 
 template <typename T, int NPT>
 static hipError_t launch_select_attn_n(const SelectArgs& se, const AttnArgs& a, hipStream_t s) {
-  dim3 grid(a.n_splits, a.hkv, a.batch);
+  dim3 grid(a.n_splits * a.hkv * a.batch);
   dim3 block(kFusedThreads);
   switch (se.group) {
     case 1: hipLaunchKernelGGL((select_attn_kernel<T, NPT, 1>), grid, block, 0, s, se, a); break;

@@ -122,6 +122,18 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Workgroups of a launch are dispatched to the XCDs round-robin: linear id b
+// runs on XCD b % kXcds, each XCD with its own L2.  xcd_remap(b, n) is a
+// bijection of [0, n) that gives each XCD a contiguous range of logical
+// indices, so logically adjacent workgroups (which read the same lines) share
+// one L2.  Only locality depends on the dispatch order, not correctness.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+  const int q = n / kXcds, r = n % kXcds;
+  const int x = b % kXcds, local = b / kXcds;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

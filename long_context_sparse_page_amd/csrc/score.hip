@@ -611,10 +611,16 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int seq = blockIdx.z;
-  const int kvh = blockIdx.x;  // grid (KV head, page chunk, sequence), as for bf16 records
-  append_duty<bf16_t, B>(a, seq, kvh, blockIdx.y);
-  const int j0 = (blockIdx.y * kScoreWaves + wave) * NR;
+  // 1-D grid over (KV head, page chunk, sequence), KV head fastest, dealt to
+  // the XCDs in contiguous ranges: records of one page's KV heads lie side by
+  // side and share 128-byte lines, which one L2 then fetches once
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int n_chunks = (a.max_pages + kScoreWaves * NR - 1) / (kScoreWaves * NR);
+  const int kvh = lin % a.hkv;
+  const int chunk = (lin / a.hkv) % n_chunks;
+  const int seq = lin / (a.hkv * n_chunks);
+  append_duty<bf16_t, B>(a, seq, kvh, chunk);
+  const int j0 = (chunk * kScoreWaves + wave) * NR;
   if (j0 >= a.max_pages) return;
   const int col = lane & 15;
   const int kg = lane >> 4;
@@ -752,7 +758,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
 template <int R, int B>
 static hipError_t launch_score_q4(int group, const ScoreArgs& a, hipStream_t s) {
   constexpr int per_block = kScoreWaves * Q4Group<R, B>::NR;
-  dim3 grid(a.hkv, (a.max_pages + per_block - 1) / per_block, a.batch);
+  dim3 grid(a.hkv * ((a.max_pages + per_block - 1) / per_block) * a.batch);
   dim3 block(kScoreWaves * kWave);
   switch (group) {
     case 1: hipLaunchKernelGGL((score_q4_kernel<R, 1, B>), grid, block, 0, s, a); break;
