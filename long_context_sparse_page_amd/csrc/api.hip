@@ -249,7 +249,7 @@ lk_status enqueue_decode_step(const Shape& sh, const lk_config* cfg, const lk_ca
   lk::SelectArgs se{page_lse, nullptr, sel_pages, sel_count, cache->seq_lens, batch, cache->max_pages_per_seq,
                     sh.hkv, sh.G, sh.B, sh.k, 1, cache->block_table, nullptr, cache->num_phys_pages};
   const bool fused = lk::select_attn_fusable(se);
-  int n_merge = fused ? lk::select_attn_splits(sh.k) : lk::list_attn_splits(sh.k);  // the attention's splits
+  int n_merge = fused ? lk::select_attn_splits(sh.k) : lk::list_attn_splits(sh.k, sh.B);  // the attention's splits
   if (fused) {
     lk::AttnArgs aa{q, cache->k_pool, cache->v_pool, cache->block_table, cache->seq_lens, nullptr, nullptr, nullptr,
                     at<float>(ws, L.part_o), at<float>(ws, L.part_ml), out, lse_out,
@@ -264,7 +264,7 @@ lk_status enqueue_decode_step(const Shape& sh, const lk_config* cfg, const lk_ca
     se.sel_count = cnt;
     se.sel_phys = sel_phys;
     attach_chunk_lists(se, ws, L);
-    if (se.n_chunks > 0 && sh.B == 64) {
+    if (se.n_chunks > 0) {
       // chunked selection: the chunk lists, then attention whose waves merge
       // them (the selection is written only when the caller asked for it)
       se.sel_pages = sel_pages;
@@ -274,7 +274,7 @@ lk_status enqueue_decode_step(const Shape& sh, const lk_config* cfg, const lk_ca
       lk::AttnArgs aa{q, cache->k_pool, cache->v_pool, cache->block_table, cache->seq_lens, nullptr, nullptr, nullptr,
                       at<float>(ws, L.part_o), at<float>(ws, L.part_ml), out, lse_out,
                       batch, cache->max_pages_per_seq, cache->num_phys_pages, sh.hkv, sh.hq, sh.k,
-                      n_merge, 1, cfg->scale, 1};
+                      n_merge, 1, cfg->scale, 1, sh.B};
       st = hip_status(lk::launch_list_attn(sh.dt, se, aa, s), "attention launch");
       if (st != LK_OK) return st;
     } else {

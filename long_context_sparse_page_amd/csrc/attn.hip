@@ -929,9 +929,8 @@ hipError_t launch_select_attn(DType dt, const SelectArgs& se, const AttnArgs& a,
 // the earlier entry = the lower page) and picks its own entry from the lane
 // that holds it: no barrier before the K/V loads.  Wave 0 of split 0 writes
 // the selection when it is asked for.
-template <typename T, int G, int CR>
+template <typename T, int G, int CR, int B>
 __global__ __launch_bounds__(kAttnWaves * kWave) void list_attn_kernel(SelectArgs se, AttnArgs a) {
-  constexpr int B = 64;
   const int split = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -962,9 +961,13 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void list_attn_kernel(SelectArg
   const int ph0 = bt[0], phr = bt[n_mr];
   const int n_cand = n_mr > 0 ? n_mr - 1 : 0;
   const int u = split * kAttnWaves + wave;
-  const int x = u >> 1;  // this wave's selection entry
+  // this wave's selection entries: entry u >> 1 (half u & 1 of a 64-token
+  // page), or entries 2u and 2u + 1 (16-token pages)
+  const int x = B == 64 ? u >> 1 : 2 * u;
+  const int x1 = 2 * u + 1;
   int32_t* so = (split == 0 && wave == 0 && se.sel_pages) ? se.sel_pages + pair * k : nullptr;
   int pg = -1, phys = -1, cnt = 0;
+  int pg1 = -1, phys1 = -1;
   if (len <= 0) {
     if (so) {
       for (int s = lane; s < k; s += kWave) so[s] = -1;
@@ -973,6 +976,7 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void list_attn_kernel(SelectArg
   } else if (min(ktop, n_cand) == n_cand) {  // every page 0 .. n_mr
     cnt = n_mr + 1;
     if (x <= n_mr) { pg = x; phys = bt[x]; }
+    if (B == 16 && x1 <= n_mr) { pg1 = x1; phys1 = bt[x1]; }
     if (so) {
       for (int s = lane; s < k; s += kWave) so[s] = s <= n_mr ? s : -1;
       if (lane == 0) se.sel_count[pair] = cnt;
@@ -985,11 +989,13 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void list_attn_kernel(SelectArg
     cnt = n_top + 2;
     if (x == 0) { pg = 0; phys = ph0; }
     else if (x == n_top + 1) { pg = n_mr; phys = phr; }
+    if (B == 16 && x1 == n_top + 1) { pg1 = n_mr; phys1 = phr; }
     if (n_top > 0) {
-      int mp = -1, mq = -1;
-      bool have = false;
+      int mp = -1, mq = -1, mp1 = -1, mq1 = -1;
+      bool have = false, have1 = false;
       wave_take_in_order<CR>(ck, n_top, [&](int slot, int r) {
         if (slot == x - 1) { mp = cp[r]; mq = cq[r]; have = true; }
+        if (B == 16 && slot == x1 - 1) { mp1 = cp[r]; mq1 = cq[r]; have1 = true; }
         if (so) so[1 + slot] = cp[r];
       });
       const uint64_t hb = __ballot(have);
@@ -997,6 +1003,14 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void list_attn_kernel(SelectArg
         const int src = __ffsll((unsigned long long)hb) - 1;
         pg = __builtin_amdgcn_readlane(mp, src);
         phys = __builtin_amdgcn_readlane(mq, src);
+      }
+      if constexpr (B == 16) {
+        const uint64_t hb1 = __ballot(have1);
+        if (hb1) {
+          const int src = __ffsll((unsigned long long)hb1) - 1;
+          pg1 = __builtin_amdgcn_readlane(mp1, src);
+          phys1 = __builtin_amdgcn_readlane(mq1, src);
+        }
       }
     }
     if (so) {
@@ -1014,26 +1028,42 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void list_attn_kernel(SelectArg
     for (int i = 0; i < 16; ++i) o[g][i] = 0.f;
   }
   if (x < cnt && pg >= 0 && pg <= n_mr && phys >= 0 && phys < a.num_phys) {
-    const int half = u & 1;
     KV16<T> kr[kAttnTPG], vr[kAttnTPG];
-    issue_unit<T>(a, kvh, phys, half, sg, e, kr, vr);
-    const int n_tok = ((pg == n_mr) ? len - n_mr * B : B) - half * kAttnHalf;
-    if (n_tok > 0) attend_unit<T, G>(q, kr, vr, n_tok, sg, a.scale * kLog2e, m, l, o);
+    if constexpr (B == 64) {
+      const int half = u & 1;
+      issue_unit<T>(a, kvh, phys, half, sg, e, kr, vr);
+      const int n_tok = ((pg == n_mr) ? len - n_mr * B : B) - half * kAttnHalf;
+      if (n_tok > 0) attend_unit<T, G>(q, kr, vr, n_tok, sg, a.scale * kLog2e, m, l, o);
+    } else {
+      const bool has1 = pg != n_mr && x1 < cnt && pg1 >= 0 && pg1 <= n_mr && phys1 >= 0 && phys1 < a.num_phys;
+      issue_unit16<T>(a, kvh, phys, has1 ? phys1 : phys, sg, e, kr, vr);
+      int n_tok = pg == n_mr ? len - n_mr * B : B;
+      if (has1) n_tok += pg1 == n_mr ? len - n_mr * B : B;
+      attend_unit<T, G>(q, kr, vr, n_tok, sg, a.scale * kLog2e, m, l, o);
+    }
   }
   combine_write<G, kAttnWaves>(a, pair * a.n_splits + split, wave, lane, m, l, o);
 }
 
-int list_attn_splits(int k) { return (2 * k + kAttnWaves - 1) / kAttnWaves; }
+int list_attn_splits(int k, int page_size) {
+  const int units = page_size == 64 ? 2 * k : (k + 1) / 2;
+  return (units + kAttnWaves - 1) / kAttnWaves;
+}
+
+template <typename T, int G, int B>
+static hipError_t launch_list_attn_gb(const SelectArgs& se, const AttnArgs& a, hipStream_t s) {
+  const dim3 grid(a.n_splits, a.hkv, a.batch), block(kAttnWaves * kWave);
+  const int entries = se.n_chunks * (se.k - 2);
+  if (entries <= 4 * kWave) hipLaunchKernelGGL((list_attn_kernel<T, G, 4, B>), grid, block, 0, s, se, a);
+  else if (entries <= 8 * kWave) hipLaunchKernelGGL((list_attn_kernel<T, G, 8, B>), grid, block, 0, s, se, a);
+  else if (entries <= 12 * kWave) hipLaunchKernelGGL((list_attn_kernel<T, G, 12, B>), grid, block, 0, s, se, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 template <typename T, int G>
 static hipError_t launch_list_attn_g(const SelectArgs& se, const AttnArgs& a, hipStream_t s) {
-  const dim3 grid(a.n_splits, a.hkv, a.batch), block(kAttnWaves * kWave);
-  const int entries = se.n_chunks * (se.k - 2);
-  if (entries <= 4 * kWave) hipLaunchKernelGGL((list_attn_kernel<T, G, 4>), grid, block, 0, s, se, a);
-  else if (entries <= 8 * kWave) hipLaunchKernelGGL((list_attn_kernel<T, G, 8>), grid, block, 0, s, se, a);
-  else if (entries <= 12 * kWave) hipLaunchKernelGGL((list_attn_kernel<T, G, 12>), grid, block, 0, s, se, a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  return se.page_size == 64 ? launch_list_attn_gb<T, G, 64>(se, a, s) : launch_list_attn_gb<T, G, 16>(se, a, s);
 }
 
 template <typename T>
@@ -1049,7 +1079,8 @@ static hipError_t launch_list_attn_t(const SelectArgs& se, const AttnArgs& a, hi
 
 hipError_t launch_list_attn(DType dt, const SelectArgs& se, const AttnArgs& a, hipStream_t s) {
   if (se.n_chunks <= 0 || !se.cand_key || !se.cand_page || !se.cand_phys || !se.cand_cnt || se.k < 3 ||
-      se.page_size != 64 || a.page_size != 64 || se.seq_lens != a.seq_lens || a.n_splits != list_attn_splits(se.k) ||
+      (se.page_size != 64 && se.page_size != 16) || a.page_size != se.page_size || se.seq_lens != a.seq_lens ||
+      a.n_splits != list_attn_splits(se.k, se.page_size) ||
       se.hkv != a.hkv || se.batch != a.batch)
     return hipErrorInvalidValue;
   return dt == kBF16 ? launch_list_attn_t<bf16_t>(se, a, s) : launch_list_attn_t<float>(se, a, s);

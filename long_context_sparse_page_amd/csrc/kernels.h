@@ -155,9 +155,9 @@ int select_attn_splits(int k);  // attention splits of the fused launch
 hipError_t launch_select_attn(DType dt, const SelectArgs& se, const AttnArgs& a, hipStream_t s);
 // Decode step with the chunked selection: attention over the selection merged
 // from the chunk lists (launch_select_lists) by every attention wave; split 0
-// writes the selection when se.sel_pages is set.  One unit per wave,
-// a.n_splits = list_attn_splits(k).
-int list_attn_splits(int k);
+// writes the selection when se.sel_pages is set.  One 32-token unit per wave,
+// a.n_splits = list_attn_splits(k, page size).
+int list_attn_splits(int k, int page_size);
 hipError_t launch_list_attn(DType dt, const SelectArgs& se, const AttnArgs& a, hipStream_t s);
 
 }  // namespace lk

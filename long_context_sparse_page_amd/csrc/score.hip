@@ -219,8 +219,12 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_kernel(ScoreArgs a)
 // this part a scattered read of many short-lived waves, each with one batch
 // of loads in flight, streams faster than fewer waves that loop over several
 // batches.
+// Records per wave: their (r + 1) rows fill up to 5 matrix-core tiles; at
+// B = 16 a wave takes twice as many records (each covers a quarter of the
+// tokens), amortizing the wave's fixed work over more of them.
 template <int R, int B = 64> struct ScoreGroup {
-  static constexpr int NR = R >= 16 ? 2 : (R >= 8 ? 4 : (R >= 4 ? 8 : 16));  // records per group
+  static constexpr int NR = B == 64 ? (R >= 16 ? 2 : (R >= 8 ? 4 : (R >= 4 ? 8 : 16)))
+                                    : (R >= 16 ? 4 : (R >= 8 ? 8 : 16));  // records per group
   static constexpr int SLOTS = NR * (R + 1);
   static constexpr int TILES = (SLOTS + 15) / 16;
   static constexpr int CW = (R + 1) / 2;        // 32-bit words of one token's coefficients
@@ -554,7 +558,8 @@ static hipError_t launch_score_mfma(int group, const ScoreArgs& a, hipStream_t s
 // record * R + row).  The reconstruction and LSE are those of the
 // bf16 records, with the per-token coefficient scale.
 template <int R, int B = 64> struct Q4Group {
-  static constexpr int NR = R >= 16 ? 2 : (R >= 8 ? 4 : 8);  // records per wave
+  // records per wave (the centroid tile holds NR centroids and a column of ones)
+  static constexpr int NR = B == 64 ? (R >= 16 ? 2 : (R >= 8 ? 4 : 8)) : (R >= 16 ? 4 : 8);
   static constexpr int BT = NR * R / 16;                       // basis tiles
   static constexpr int SLOTS = NR * (R + 1);
   static constexpr int CSETS = B == 64 ? NR : (NR + 3) / 4;    // coefficient sets per lane (as ScoreGroup)

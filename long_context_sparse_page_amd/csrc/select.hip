@@ -33,8 +33,9 @@ constexpr int kChunkNPT = kSelChunkPages / kChunkThreads;  // pages per thread o
 constexpr int kPartThreads = 256;
 constexpr int kPartNPT = kSelChunkPages / kPartThreads;
 constexpr int kChunkedFrom = 3072;                        // tables above this many pages
-constexpr int kChunkMaxTop = 62;                          // k - 2 the lists hold
+constexpr int kChunkMaxTop = 126;                         // k - 2 the lists hold
 constexpr int kChunkMaxChunks = 12;
+constexpr int kChunkMaxEntries = 12 * kWave;              // list slots one merging wave holds
 constexpr int kChunkPairsBelow = 128;                     // fewer pairs than this
 static_assert(kChunkNPT * kChunkThreads == kSelChunkPages, "chunk tiling");
 
@@ -43,7 +44,7 @@ static_assert(kChunkNPT * kChunkThreads == kSelChunkPages, "chunk tiling");
 int select_chunk_capacity(int max_pages, int k) {
   if (max_pages <= kChunkedFrom || k < 3 || k - 2 > kChunkMaxTop) return 0;
   const int c = (max_pages + kSelChunkPages - 1) / kSelChunkPages;
-  return c <= kChunkMaxChunks ? c : 0;
+  return (c <= kChunkMaxChunks && c * (k - 2) <= kChunkMaxEntries) ? c : 0;
 }
 
 int select_chunks(int batch, int hkv, int max_pages, int k) {
