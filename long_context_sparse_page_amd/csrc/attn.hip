@@ -444,9 +444,13 @@ __device__ __forceinline__ void attn_split_block(const AttnArgs& a, int split, i
   int u = u0;
   int pg = pg_first, phys = phys_first;
   if (phys == -2) phys = (pg >= 0 && pg < a.max_pages) ? bt[pg] : -1;
+  // Every load site below issues a whole unit (an invalid page reads page 0
+  // and is not attended), so the unit's registers are always redefined there
+  // and never held across a reload.
   KV16<T> kr[kAttnTPG], vr[kAttnTPG];
-  bool loaded = false;
-  if (len > 0 && phys >= 0 && phys < a.num_phys) { issue_unit<T>(a, kvh, phys, u & 1, sg, e, kr, vr); loaded = true; }
+  bool loaded = phys >= 0 && phys < a.num_phys;
+  if (u0 < 2 * n_entries) issue_unit<T>(a, kvh, loaded ? phys : 0, u & 1, sg, e, kr, vr);
+  loaded = loaded && len > 0;
 
   int n_mr = len > 0 ? (len - 1) / B : -1;
   if (n_mr > a.max_pages - 1) n_mr = a.max_pages - 1;
@@ -458,7 +462,7 @@ __device__ __forceinline__ void attn_split_block(const AttnArgs& a, int split, i
       pg = list ? list[u >> 1] : (u >> 1);
       phys = plist ? plist[u >> 1] : ((pg >= 0 && pg < a.max_pages) ? bt[pg] : -1);
       loaded = phys >= 0 && phys < a.num_phys;
-      if (loaded) issue_unit<T>(a, kvh, phys, u & 1, sg, e, kr, vr);
+      issue_unit<T>(a, kvh, loaded ? phys : 0, u & 1, sg, e, kr, vr);
     }
     if (!loaded || pg < 0 || pg > n_mr) continue;
     const int n_tok = ((pg == n_mr) ? len - n_mr * B : B) - (u & 1) * kAttnHalf;  // tokens from the unit's start on
@@ -468,13 +472,79 @@ __device__ __forceinline__ void attn_split_block(const AttnArgs& a, int split, i
   combine_write<G, kAttnWaves>(a, ((size_t)seq * a.hkv + kvh) * a.n_splits + split, wave, lane, m, l, o);
 }
 
+// attn_split_block when every wave attends exactly one unit (the sparse
+// split count): straight-line code, the unit's K/V registers live only
+// around the one attend, so a wave holds fewer registers than the looping
+// form (which keeps the running (m, l, o) and the queries across reloads).
 template <typename T, int G, int B>
+__device__ __forceinline__ void attn_one_unit_block(const AttnArgs& a, int split, int kvh, int seq, int seq_len,
+                                                    const int32_t* list, const int32_t* plist, const int32_t* cnt_p) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int sg = lane >> 3;
+  const int e = lane & 7;
+  const int32_t* bt = a.block_table + (size_t)seq * a.max_pages;
+  const int u = split * kAttnWaves + wave;
+  const int n_entries = list ? a.k : a.max_pages;  // list entries that exist in memory
+  // list entry x -> logical page and physical page (-1 past the entries in memory)
+  auto entry = [&](int x, int& pg, int& ph) {
+    pg = -1;
+    ph = -1;
+    if (x >= n_entries) return;
+    pg = list ? list[x] : x;
+    ph = plist ? plist[x] : ((pg >= 0 && pg < a.max_pages) ? bt[pg] : -1);
+  };
+  auto valid_phys = [&](int ph) { return ph >= 0 && ph < a.num_phys; };
+  // unit u: half (u & 1) of entry u >> 1 (64-token pages), entries 2u, 2u + 1 (16)
+  int pg0, ph0, pg1 = -1, ph1 = -1;
+  entry(B == 64 ? u >> 1 : 2 * u, pg0, ph0);
+  if constexpr (B == 16) entry(2 * u + 1, pg1, ph1);
+  const int len = seq_len + a.len_add;
+  const int cnt = list ? *cnt_p : 0;
+
+  QLane<T, G> q;
+  q.load(a, seq, kvh, e);
+  float m[G], l[G], o[G][16];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[g][i] = 0.f;
+  }
+  int n_mr = len > 0 ? (len - 1) / B : -1;
+  if (n_mr > a.max_pages - 1) n_mr = a.max_pages - 1;
+  const int n_list = len <= 0 ? 0 : (list ? min(cnt, a.k) : n_mr + 1);
+  const int first = B == 64 ? u >> 1 : 2 * u;  // the unit's first list entry
+  if (first < n_list && pg0 >= 0 && pg0 <= n_mr && valid_phys(ph0)) {
+    KV16<T> kr[kAttnTPG], vr[kAttnTPG];
+    int n_tok;
+    if constexpr (B == 64) {
+      issue_unit<T>(a, kvh, ph0, u & 1, sg, e, kr, vr);
+      n_tok = ((pg0 == n_mr) ? len - n_mr * B : B) - (u & 1) * kAttnHalf;  // tokens from the unit's start on
+    } else {
+      const bool two = pg0 != n_mr && 2 * u + 1 < n_list && pg1 >= 0 && pg1 <= n_mr && valid_phys(ph1);
+      issue_unit16<T>(a, kvh, ph0, two ? ph1 : ph0, sg, e, kr, vr);
+      n_tok = pg0 == n_mr ? len - n_mr * B : B;
+      if (two) n_tok += pg1 == n_mr ? len - n_mr * B : B;
+    }
+    if (n_tok > 0) attend_unit<T, G>(q, kr, vr, n_tok, sg, a.scale * kLog2e, m, l, o);
+  }
+  combine_write<G, kAttnWaves>(a, ((size_t)seq * a.hkv + kvh) * a.n_splits + split, wave, lane, m, l, o);
+}
+
+// ONE: every wave attends one unit (pages_per_split == 1).
+template <typename T, int G, int B, bool ONE>
 __global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs a) {
   const int split = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
   const size_t pair = (size_t)seq * a.hkv + kvh;
   const int32_t* list = a.sel_pages ? a.sel_pages + pair * a.k : nullptr;
   const int32_t* plist = (list && a.sel_phys) ? a.sel_phys + pair * a.k : nullptr;
-  attn_split_block<T, G, B>(a, split, kvh, seq, a.seq_lens[seq], list, plist, list ? a.sel_count + pair : nullptr);
+  if constexpr (ONE)
+    attn_one_unit_block<T, G, B>(a, split, kvh, seq, a.seq_lens[seq], list, plist,
+                                 list ? a.sel_count + pair : nullptr);
+  else
+    attn_split_block<T, G, B>(a, split, kvh, seq, a.seq_lens[seq], list, plist, list ? a.sel_count + pair : nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -856,17 +926,19 @@ static hipError_t launch_attn_tb(int group, const AttnArgs& a, bool merge, hipSt
   dim3 grid(a.n_splits, a.hkv, a.batch);
   dim3 block(kAttnWaves * kWave);
   dim3 mgrid(a.hq, a.batch);
+  const bool one = a.pages_per_split == 1;
+#define LK_SPLIT(GG)                                                                                  \
+  if (one) hipLaunchKernelGGL((attn_split_kernel<T, GG, B, true>), grid, block, 0, s, a);             \
+  else hipLaunchKernelGGL((attn_split_kernel<T, GG, B, false>), grid, block, 0, s, a);                \
+  if (merge) hipLaunchKernelGGL((attn_merge_kernel<T, GG>), mgrid, block, 0, s, a);
   switch (group) {
-    case 1: hipLaunchKernelGGL((attn_split_kernel<T, 1, B>), grid, block, 0, s, a);
-            if (merge) hipLaunchKernelGGL((attn_merge_kernel<T, 1>), mgrid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((attn_split_kernel<T, 2, B>), grid, block, 0, s, a);
-            if (merge) hipLaunchKernelGGL((attn_merge_kernel<T, 2>), mgrid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((attn_split_kernel<T, 4, B>), grid, block, 0, s, a);
-            if (merge) hipLaunchKernelGGL((attn_merge_kernel<T, 4>), mgrid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((attn_split_kernel<T, 8, B>), grid, block, 0, s, a);
-            if (merge) hipLaunchKernelGGL((attn_merge_kernel<T, 8>), mgrid, block, 0, s, a); break;
+    case 1: LK_SPLIT(1) break;
+    case 2: LK_SPLIT(2) break;
+    case 4: LK_SPLIT(4) break;
+    case 8: LK_SPLIT(8) break;
     default: return hipErrorInvalidValue;
   }
+#undef LK_SPLIT
   return hipGetLastError();
 }
 
