@@ -54,7 +54,9 @@ __device__ __forceinline__ void load2(const float* p, float& a, float& b) {
   b = v.y;
 }
 
-template <typename T, int R>
+// DS: the decode step's launch (merge and length commit before the build);
+// the bulk build is compiled without them (fewer registers, more waves).
+template <typename T, int R, bool DS>
 __global__ __launch_bounds__(kB16Waves * kWave) void build16_kernel(BuildArgs a) {
   constexpr int B = kB16;
   constexpr int D = kHeadDim;
@@ -76,10 +78,19 @@ __global__ __launch_bounds__(kB16Waves * kWave) void build16_kernel(BuildArgs a)
   const int phys = a.phys_ids[idx];
   // decode step (idx = sequence): merge the attention partials of (idx, kvh),
   // then advance the sequence's length when its append was valid
-  const bool commit = a.commit_seq_lens && kvh == 0 && lane == 0;
-  const int len = commit ? a.commit_seq_lens[idx] : 0;
-  if (a.merge.part_o) merge_partials<T>(a, idx, kvh, lane, kWave);
-  if (commit && phys != -2) a.commit_seq_lens[idx] = len + 1;
+  if constexpr (DS) {
+    const bool commit = a.commit_seq_lens && kvh == 0 && lane == 0;
+    const int len = commit ? a.commit_seq_lens[idx] : 0;
+    if (a.merge.part_o) {
+      switch (a.merge.group) {
+        case 1: merge_partials_wave<T, 1>(a, idx, kvh, lane); break;
+        case 2: merge_partials_wave<T, 2>(a, idx, kvh, lane); break;
+        case 4: merge_partials_wave<T, 4>(a, idx, kvh, lane); break;
+        default: merge_partials_wave<T, 8>(a, idx, kvh, lane); break;
+      }
+    }
+    if (commit && phys != -2) a.commit_seq_lens[idx] = len + 1;
+  }
   if (phys < 0 || phys >= a.num_phys) return;
   const T* K = reinterpret_cast<const T*>(a.k_pool) + (((size_t)phys * a.hkv + kvh) * B) * D;
 
@@ -332,18 +343,25 @@ __global__ __launch_bounds__(kB16Waves * kWave) void build16_kernel(BuildArgs a)
   for (int y = L.mscale() + 2 + lane; y < L.bytes(); y += kWave) rec[y] = 0;
 }
 
+template <typename T, int R>
+static void launch_b16(bool ds, dim3 grid, dim3 block, hipStream_t s, const BuildArgs& a) {
+  if (ds) hipLaunchKernelGGL((build16_kernel<T, R, true>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((build16_kernel<T, R, false>), grid, block, 0, s, a);
+}
+
 template <typename T>
 static hipError_t launch_build16_t(int rank, const BuildArgs& a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
   const long long items = (long long)a.n * a.hkv;
   dim3 grid((unsigned)((items + kB16Waves - 1) / kB16Waves));
+  const bool ds = a.merge.part_o != nullptr || a.commit_seq_lens != nullptr;
   dim3 block(kB16Waves * kWave);
   switch (rank) {
-    case 1: hipLaunchKernelGGL((build16_kernel<T, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((build16_kernel<T, 2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((build16_kernel<T, 4>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((build16_kernel<T, 8>), grid, block, 0, s, a); break;
-    case 16: hipLaunchKernelGGL((build16_kernel<T, 16>), grid, block, 0, s, a); break;
+    case 1: launch_b16<T, 1>(ds, grid, block, s, a); break;
+    case 2: launch_b16<T, 2>(ds, grid, block, s, a); break;
+    case 4: launch_b16<T, 4>(ds, grid, block, s, a); break;
+    case 8: launch_b16<T, 8>(ds, grid, block, s, a); break;
+    case 16: launch_b16<T, 16>(ds, grid, block, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
