@@ -174,67 +174,86 @@ __global__ __launch_bounds__(kB16Waves * kWave) void build16_kernel(BuildArgs a)
   wave_lds_fence();
 
   // 3) cyclic Jacobi.  Round t pairs index 15 with t and (t + m) mod 15 with
-  //    (t - m) mod 15 for m = 1..7 (every pair once per 15 rounds).
+  //    (t - m) mod 15 for m = 1..7 (every pair once per 15 rounds).  The
+  //    matrices alternate between two LDS buffers; lane l owns entries
+  //    (l / 16 + 4 y, l % 16), y < 4, and their upper-triangle positions.
+  constexpr int LD = kB16Ld;
   int cur = 0;
+  const int m_pair = lane & 7;
+  const int jl = lane & (B - 1);
+  int ia[4], jb[4];
+#pragma unroll
+  for (int y = 0; y < 4; ++y) {
+    const int i = (lane >> 4) + 4 * y;
+    ia[y] = min(i, jl);
+    jb[y] = max(i, jl);
+  }
+  float* const Rw = &sRot[wave][0][0];  // [B][2]: J[i][i], J[partner][i]
+  int* const Pw = &sPart[wave][0];
   for (int sweep = 0; sweep < 12; ++sweep) {
+    const float* Ac0 = &sA[wave][cur][0][0];
     float off = 0.f, tot = 0.f;
 #pragma unroll
-    for (int y = 0; y < B * B / kWave; ++y) {
-      const int e = lane + kWave * y;
-      const float v = sA[wave][cur][e / B][e % B];
+    for (int y = 0; y < 4; ++y) {
+      const int i = (lane >> 4) + 4 * y;
+      const float v = Ac0[i * LD + jl];
       tot = fmaf(v, v, tot);
-      if (e / B != e % B) off = fmaf(v, v, off);
+      if (i != jl) off = fmaf(v, v, off);
     }
     off = group_sum<kWave>(off);
     tot = group_sum<kWave>(tot);
     if (!(off > 1e-13f * tot)) break;
     for (int t = 0; t < B - 1; ++t) {
+      const float* Ac = &sA[wave][cur][0][0];
+      float* An = &sA[wave][cur ^ 1][0][0];
+      const float* Uc = &sU[wave][cur][0][0];
+      float* Un = &sU[wave][cur ^ 1][0][0];
       if (lane < B / 2) {  // the Schur rotation of pair m = lane
-        const int m = lane;
-        int p = m == 0 ? B - 1 : (t + m) % (B - 1);
-        int q = m == 0 ? t : (t - m + (B - 1)) % (B - 1);
-        if (p > q) { const int tmp = p; p = q; q = tmp; }
-        const float app = sA[wave][cur][p][p], aqq = sA[wave][cur][q][q], apq = sA[wave][cur][p][q];
+        // (t + m) mod 15 and (t - m) mod 15 with 0 <= t, m < 15, without a division
+        const int tp = t + m_pair, tm = t - m_pair + (B - 1);
+        const int r0 = m_pair == 0 ? B - 1 : (tp >= B - 1 ? tp - (B - 1) : tp);
+        const int r1 = m_pair == 0 ? t : (tm >= B - 1 ? tm - (B - 1) : tm);
+        const int p = min(r0, r1), q = max(r0, r1);
+        const float app = Ac[p * LD + p], aqq = Ac[q * LD + q], apq = Ac[p * LD + q];
         float c = 1.f, s = 0.f, tt = 0.f;
         if (apq != 0.f) {
-          const float tau = (aqq - app) / (2.f * apq);
-          tt = (tau >= 0.f ? 1.f : -1.f) / (fabsf(tau) + sqrtf(1.f + tau * tau));
-          c = 1.f / sqrtf(1.f + tt * tt);
+          // t = sign(tau) / (|tau| + sqrt(1 + tau^2)), c = 1 / sqrt(1 + t^2), s = t c;
+          // any rotation orthogonal to rounding serves (the pair's entry is
+          // then set to zero), so the single-instruction rcp / sqrt / rsq
+          const float tau = (aqq - app) * __builtin_amdgcn_rcpf(2.f * apq);
+          tt = (tau >= 0.f ? 1.f : -1.f) * __builtin_amdgcn_rcpf(fabsf(tau) + __builtin_amdgcn_sqrtf(fmaf(tau, tau, 1.f)));
+          c = __builtin_amdgcn_rsqf(fmaf(tt, tt, 1.f));
           s = tt * c;
         }
         // J = [[c, s], [-s, c]] on (p, q): column p is (c, -s), column q is (s, c)
-        sRot[wave][p][0] = c; sRot[wave][p][1] = -s; sPart[wave][p] = q;
-        sRot[wave][q][0] = c; sRot[wave][q][1] = s;  sPart[wave][q] = p;
+        Rw[2 * p] = c; Rw[2 * p + 1] = -s; Pw[p] = q;
+        Rw[2 * q] = c; Rw[2 * q + 1] = s;  Pw[q] = p;
         // the rotated pair's diagonal, in the exact form of the Schur rotation
-        sA[wave][cur ^ 1][p][p] = app - tt * apq;
-        sA[wave][cur ^ 1][q][q] = aqq + tt * apq;
+        An[p * LD + p] = app - tt * apq;
+        An[q * LD + q] = aqq + tt * apq;
       }
       wave_lds_fence();
-      // A' = J^T A J (entry (a, b) with a <= b, mirrored), U' = U J
-      const int nxt = cur ^ 1;
+      // A' = J^T A J (entry (a, b) from the upper triangle a <= b; the
+      // diagonal was set above, the rotated pair's entry is zero), U' = U J;
+      // every index read is in 0 .. 15, so the reads are unconditional
+      const int pj = Pw[jl];
+      const float cj = Rw[2 * jl], sj = Rw[2 * jl + 1];
 #pragma unroll
-      for (int y = 0; y < B * B / kWave; ++y) {
-        const int e = lane + kWave * y;
-        const int i = e / B, j = e % B;
-        const int ia = min(i, j), jb = max(i, j);
-        const int pa = sPart[wave][ia], pb = sPart[wave][jb];
-        const float ca = sRot[wave][ia][0], sa = sRot[wave][ia][1];
-        const float cb = sRot[wave][jb][0], sb = sRot[wave][jb][1];
-        float v;
-        if (ia == jb) {
-          v = sA[wave][nxt][ia][ia];  // set by the pair's lane above
-        } else if (pa == jb) {
-          v = 0.f;                    // the rotated pair
-        } else {
-          v = ca * cb * sA[wave][cur][ia][jb] + sa * cb * sA[wave][cur][pa][jb] +
-              ca * sb * sA[wave][cur][ia][pb] + sa * sb * sA[wave][cur][pa][pb];
-        }
-        const float u = sU[wave][cur][i][j] * sRot[wave][j][0] + sU[wave][cur][i][sPart[wave][j]] * sRot[wave][j][1];
-        sU[wave][nxt][i][j] = u;
-        if (ia != jb) sA[wave][nxt][i][j] = v;
+      for (int y = 0; y < 4; ++y) {
+        const int i = (lane >> 4) + 4 * y;
+        const int pa = Pw[ia[y]], pb = Pw[jb[y]];
+        const float ca = Rw[2 * ia[y]], sa = Rw[2 * ia[y] + 1];
+        const float cb = Rw[2 * jb[y]], sb = Rw[2 * jb[y] + 1];
+        const float v = ca * cb * Ac[ia[y] * LD + jb[y]] + sa * cb * Ac[pa * LD + jb[y]] +
+                        ca * sb * Ac[ia[y] * LD + pb] + sa * sb * Ac[pa * LD + pb];
+        // one basic block for all four entries (their LDS reads overlap): the
+        // diagonal entry is stored again with the value the pair's lane set
+        const float dg = An[i * LD + jl];
+        An[i * LD + jl] = i == jl ? dg : (pa == jb[y] ? 0.f : v);
+        Un[i * LD + jl] = Uc[i * LD + jl] * cj + Uc[i * LD + pj] * sj;
       }
       wave_lds_fence();
-      cur = nxt;
+      cur ^= 1;
     }
   }
 
