@@ -151,10 +151,9 @@ lk_status lk_workspace_size(const lk_config* cfg, int32_t batch,
  * record is written in kv_dtype (round to nearest even).
  *   phys_page_ids  int32 [n_pages] device; entries < 0 are skipped.
  *   eigvals_out    optional fp32 [n_pages][Hkv][B], sorted descending, >= 0.
- * Pages must be full (all B token slots written).  At B = 16 the
- * eigendecomposition is a cyclic Jacobi iteration on the 16 x 16 Gram (the
- * page-size study of the Locks appendix, Table D.10); the record layout and
- * every rule above are the same, with B = 16. */
+ * Pages must be full (all B token slots written).  B = 16 (the page-size
+ * study of the Locks appendix, Table D.10) uses the same record layout and
+ * every rule above, with B = 16. */
 lk_status lk_build_page_summary(const lk_config* cfg, const lk_cache* cache,
                                 const int32_t* phys_page_ids, int32_t n_pages,
                                 float* eigvals_out, void* ws, size_t ws_bytes,

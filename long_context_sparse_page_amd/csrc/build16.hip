@@ -9,23 +9,23 @@
 // builder.
 //
 // The Gram is one 16 x 16 tile on the matrix cores (each fp32 entry of D as
-// three bf16 terms, six products, mirrored for exact symmetry).  A 16 x 16
-// eigenproblem suits the cyclic Jacobi method (Golub & Van Loan, Matrix
-// Computations, §8.5): the round-robin ordering pairs the 16 indices into 8
-// disjoint pairs per round (15 rounds per sweep); each round applies its 8
-// symmetric Schur rotations at once (disjoint rotations commute), with the
-// rotated diagonal pair set to a_pp - t a_pq, a_qq + t a_pq and a_pq to 0.
-// Sweeps stop once the off-diagonal energy is below 1e-13 of the total, or
-// after 12.
+// three bf16 terms, six products, mirrored for exact symmetry).  Only the
+// top r eigenpairs are needed, so the eigenproblem is solved as the 64-token
+// builder solves its own (Golub & Van Loan, Matrix Computations, ch. 8), here
+// on one wave: Householder reduction to tridiagonal form with the matrix in
+// registers (lane (row, g) holds columns 4 g .. 4 g + 3 of its row: the Gram
+// tile's own accumulator layout, by symmetry), the wanted eigenvalues of T by
+// Sturm-sequence multisection on lane segments, their eigenvectors by inverse
+// iteration with partial pivoting (re-orthogonalized within clusters of close
+// eigenvalues), and back-transformation by the 14 reflectors.  A step or a
+// pass is a few dozen instructions of one wave, so a page takes a few
+// microseconds; many waves share a CU.
 //
-// The rounds are bound by LDS latency, so the wave keeps little else in LDS
-// (about 6 KB: the 16 x 16 matrices, the centroid, a round's rotations) and
-// many waves share a CU.  The key tile is read twice, both times straight
-// into registers: in the matrix-core operand layout for the Gram (the
-// centroid of a lane's dimensions is a sum over the 16 lanes of its DPP row,
-// which hold those dimensions of the 16 tokens) and, from L2, with two
-// dimensions per lane for the basis, which is formed, signed and written from
-// registers.
+// The key tile is read twice, both times straight into registers: in the
+// matrix-core operand layout for the Gram (the centroid of a lane's
+// dimensions is a sum over the 16 lanes of its DPP row, which hold those
+// dimensions of the 16 tokens) and, from L2, with two dimensions per lane for
+// the basis, which is formed, signed and written from registers.
 
 #include "common.cuh"
 #include "kernels.h"
@@ -36,6 +36,25 @@ namespace lk {
 constexpr int kB16 = 16;
 constexpr int kB16Waves = 4;
 constexpr int kB16Ld = 17;  // padded row of the 16 x 16 matrices
+constexpr int kB16InvIters = 2;          // inverse-iteration passes per eigenvector
+constexpr float kB16ClusterTol = 1e-3f;  // eigenvalues this close (relative to lambda_1) are re-orthogonalized
+
+// Number of eigenvalues of the symmetric tridiagonal T = (d, e) below sigma:
+// the negative pivots of the LDL^T factorization of T - sigma I (Sturm
+// count); e2[i] = e[i]^2, pivots smaller than pivmin are replaced by -pivmin.
+__device__ __forceinline__ int sturm_count16(const float (&d)[kB16], const float (&e2)[kB16], float sigma,
+                                             float pivmin) {
+  float q = d[0] - sigma;
+  if (fabsf(q) < pivmin) q = -pivmin;
+  int c = q < 0.f ? 1 : 0;
+#pragma unroll
+  for (int i = 1; i < kB16; ++i) {
+    q = (d[i] - sigma) - e2[i - 1] * __builtin_amdgcn_rcpf(q);
+    if (fabsf(q) < pivmin) q = -pivmin;
+    c += q < 0.f ? 1 : 0;
+  }
+  return c;
+}
 
 __device__ __forceinline__ float b16_q_scale(float amax, float levels) { return (float)(_Float16)(amax / levels); }
 __device__ __forceinline__ int b16_q_code(float x, float s, float levels) {
@@ -61,13 +80,13 @@ __global__ __launch_bounds__(kB16Waves * kWave) void build16_kernel(BuildArgs a)
   constexpr int B = kB16;
   constexpr int D = kHeadDim;
   constexpr int KEPT = R < B ? R : B;
-  __shared__ float sA[kB16Waves][2][B][kB16Ld];   // Gram / rotated matrix (ping-pong)
-  __shared__ float sU[kB16Waves][2][B][kB16Ld];   // accumulated rotations
+  __shared__ float sA[kB16Waves][2][B][kB16Ld];   // the Gram; the reflectors (row k = reflector k)
+  __shared__ float sZ[kB16Waves][B][kB16Ld];      // eigenvector of the k-th largest eigenvalue = column k
+  __shared__ float4 sF[kB16Waves][B][KEPT];       // inverse iteration: row i of the factors of T - lambda_k I
   __shared__ float sMu[kB16Waves][D];
-  __shared__ float sRot[kB16Waves][B][2];         // per index: J[i][i], J[partner][i]
-  __shared__ int sPart[kB16Waves][B];
-  __shared__ int sOrder[kB16Waves][B];
-  __shared__ float sLam[kB16Waves][B];
+  __shared__ float sT[kB16Waves][3][B];           // T: diagonal d, subdiagonal e (e[i] couples i, i + 1), e^2
+  __shared__ float sVec[kB16Waves][2][B];         // u and w of a Householder step
+  __shared__ float sLam[kB16Waves][B];            // eigenvalues, descending
   __shared__ float sSign[kB16Waves][KEPT];
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -164,116 +183,226 @@ __global__ __launch_bounds__(kB16Waves * kWave) void build16_kernel(BuildArgs a)
         sA[wave][0][col][r] = acc[i];
       }
     }
-    // U = I
-#pragma unroll
-    for (int y = 0; y < B * B / kWave; ++y) {
-      const int e = lane + kWave * y;
-      sU[wave][0][e / B][e % B] = (e / B == e % B) ? 1.f : 0.f;
-    }
   }
   wave_lds_fence();
 
-  // 3) cyclic Jacobi.  Round t pairs index 15 with t and (t + m) mod 15 with
-  //    (t - m) mod 15 for m = 1..7 (every pair once per 15 rounds).  The
-  //    matrices alternate between two LDS buffers; lane l owns entries
-  //    (l / 16 + 4 y, l % 16), y < 4, and their upper-triangle positions.
+  // 3) eigenpairs of the Gram A.
   constexpr int LD = kB16Ld;
-  int cur = 0;
-  const int m_pair = lane & 7;
-  const int jl = lane & (B - 1);
-  int ia[4], jb[4];
+  float* const Rf = &sA[wave][1][0][0];  // reflector k = row k
+  float* const Zw = &sZ[wave][0][0];
+  float* const Td = sT[wave][0];
+  float* const Te = sT[wave][1];
+  float* const Te2 = sT[wave][2];
+  float* const Vu = sVec[wave][0];
+  float* const Vw = sVec[wave][1];
+  const int rr = lane & (B - 1), gg = lane >> 4;  // lane (row, column group)
+  // (a) Householder tridiagonalization: step k zeroes column k below the
+  //     subdiagonal with H = I - 2 u u^T (||u|| = 1, u_r = 0 for r <= k);
+  //     with p = 2 A u, K = u.p and w = p - K u, A <- A - u w^T - w u^T.
+  //     Lane (r, g) holds A[r][4 g .. 4 g + 3]; u and w reach the lanes that
+  //     hold their columns through LDS.  A zero column gives u = 0.
+  {
+    float Ar[4];
 #pragma unroll
-  for (int y = 0; y < 4; ++y) {
-    const int i = (lane >> 4) + 4 * y;
-    ia[y] = min(i, jl);
-    jb[y] = max(i, jl);
-  }
-  float* const Rw = &sRot[wave][0][0];  // [B][2]: J[i][i], J[partner][i]
-  int* const Pw = &sPart[wave][0];
-  for (int sweep = 0; sweep < 12; ++sweep) {
-    const float* Ac0 = &sA[wave][cur][0][0];
-    float off = 0.f, tot = 0.f;
+    for (int t = 0; t < 4; ++t) Ar[t] = sA[wave][0][rr][4 * gg + t];
 #pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const int i = (lane >> 4) + 4 * y;
-      const float v = Ac0[i * LD + jl];
-      tot = fmaf(v, v, tot);
-      if (i != jl) off = fmaf(v, v, off);
-    }
-    off = group_sum<kWave>(off);
-    tot = group_sum<kWave>(tot);
-    if (!(off > 1e-13f * tot)) break;
-    for (int t = 0; t < B - 1; ++t) {
-      const float* Ac = &sA[wave][cur][0][0];
-      float* An = &sA[wave][cur ^ 1][0][0];
-      const float* Uc = &sU[wave][cur][0][0];
-      float* Un = &sU[wave][cur ^ 1][0][0];
-      if (lane < B / 2) {  // the Schur rotation of pair m = lane
-        // (t + m) mod 15 and (t - m) mod 15 with 0 <= t, m < 15, without a division
-        const int tp = t + m_pair, tm = t - m_pair + (B - 1);
-        const int r0 = m_pair == 0 ? B - 1 : (tp >= B - 1 ? tp - (B - 1) : tp);
-        const int r1 = m_pair == 0 ? t : (tm >= B - 1 ? tm - (B - 1) : tm);
-        const int p = min(r0, r1), q = max(r0, r1);
-        const float app = Ac[p * LD + p], aqq = Ac[q * LD + q], apq = Ac[p * LD + q];
-        float c = 1.f, s = 0.f, tt = 0.f;
-        if (apq != 0.f) {
-          // t = sign(tau) / (|tau| + sqrt(1 + tau^2)), c = 1 / sqrt(1 + t^2), s = t c;
-          // any rotation orthogonal to rounding serves (the pair's entry is
-          // then set to zero), so the single-instruction rcp / sqrt / rsq
-          const float tau = (aqq - app) * __builtin_amdgcn_rcpf(2.f * apq);
-          tt = (tau >= 0.f ? 1.f : -1.f) * __builtin_amdgcn_rcpf(fabsf(tau) + __builtin_amdgcn_sqrtf(fmaf(tau, tau, 1.f)));
-          c = __builtin_amdgcn_rsqf(fmaf(tt, tt, 1.f));
-          s = tt * c;
-        }
-        // J = [[c, s], [-s, c]] on (p, q): column p is (c, -s), column q is (s, c)
-        Rw[2 * p] = c; Rw[2 * p + 1] = -s; Pw[p] = q;
-        Rw[2 * q] = c; Rw[2 * q + 1] = s;  Pw[q] = p;
-        // the rotated pair's diagonal, in the exact form of the Schur rotation
-        An[p * LD + p] = app - tt * apq;
-        An[q * LD + q] = aqq + tt * apq;
+    for (int k = 0; k < B - 2; ++k) {
+      const float ak = xor32_sum(xor16_sum(gg == (k >> 2) ? Ar[k & 3] : 0.f));  // A[r][k] in every group
+      const float x = rr > k ? ak : 0.f;
+      const float nrm2 = group_sum<16>(x * x);
+      const float x0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), k + 1));
+      const float nrm = __builtin_amdgcn_sqrtf(nrm2);
+      const bool nz = nrm2 > 0.f;
+      const float alpha = nz ? (x0 >= 0.f ? -nrm : nrm) : 0.f;
+      const float inv = __builtin_amdgcn_rsqf(2.f * (nrm2 + nrm * fabsf(x0)));  // 1 / ||x - alpha e_{k+1}||
+      const float u = nz ? (rr == k + 1 ? x - alpha : x) * inv : 0.f;
+      if (lane == k) Td[k] = ak;
+      if (lane == 0) Te[k] = alpha;
+      if (gg == 0) {
+        Rf[k * LD + rr] = u;
+        Vu[rr] = u;
       }
       wave_lds_fence();
-      // A' = J^T A J (entry (a, b) from the upper triangle a <= b; the
-      // diagonal was set above, the rotated pair's entry is zero), U' = U J;
-      // every index read is in 0 .. 15, so the reads are unconditional
-      const int pj = Pw[jl];
-      const float cj = Rw[2 * jl], sj = Rw[2 * jl + 1];
+      float uc[4], pp = 0.f;
 #pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        const int i = (lane >> 4) + 4 * y;
-        const int pa = Pw[ia[y]], pb = Pw[jb[y]];
-        const float ca = Rw[2 * ia[y]], sa = Rw[2 * ia[y] + 1];
-        const float cb = Rw[2 * jb[y]], sb = Rw[2 * jb[y] + 1];
-        const float v = ca * cb * Ac[ia[y] * LD + jb[y]] + sa * cb * Ac[pa * LD + jb[y]] +
-                        ca * sb * Ac[ia[y] * LD + pb] + sa * sb * Ac[pa * LD + pb];
-        // one basic block for all four entries (their LDS reads overlap): the
-        // diagonal entry is stored again with the value the pair's lane set
-        const float dg = An[i * LD + jl];
-        An[i * LD + jl] = i == jl ? dg : (pa == jb[y] ? 0.f : v);
-        Un[i * LD + jl] = Uc[i * LD + jl] * cj + Uc[i * LD + pj] * sj;
+      for (int t = 0; t < 4; ++t) {
+        uc[t] = Vu[4 * gg + t];
+        pp = fmaf(Ar[t], uc[t], pp);
       }
+      const float p = 2.f * xor32_sum(xor16_sum(pp));
+      const float K = group_sum<16>(u * p);
+      const float w = rr > k ? p - K * u : 0.f;
+      if (gg == 0) Vw[rr] = w;
       wave_lds_fence();
-      cur ^= 1;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) Ar[t] = fmaf(-u, Vw[4 * gg + t], fmaf(-w, uc[t], Ar[t]));
     }
+    // the trailing 2 x 2 block (rows and columns 14, 15: lanes (14, 3), (15, 3))
+    if (gg == 3 && rr == B - 2) Td[B - 2] = Ar[2];
+    if (gg == 3 && rr == B - 1) {
+      Td[B - 1] = Ar[3];
+      Te[B - 2] = Ar[2];
+      Te[B - 1] = 0.f;
+    }
+    wave_lds_fence();
+    if (lane < B) Te2[lane] = Te[lane] * Te[lane];
+    wave_lds_fence();
   }
+  // (b) eigenvalues of T, descending: the NK largest at once (every
+  //     eigenvalue when they are an output, else the kept ones), each on a
+  //     segment of SL = 64 / NK lanes; a pass counts the eigenvalues below SL
+  //     shifts spread over the segment's interval, which shrinks
+  //     (SL + 1)-fold.
+  float lam1, thresh;
+  {
+    float dreg[B], e2reg[B];
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      dreg[i] = Td[i];
+      e2reg[i] = Te2[i];
+    }
+    const float em = rr > 0 ? fabsf(Te[rr - 1]) : 0.f, ep = fabsf(Te[rr]);
+    const float glo = -group_max<16>(-(Td[rr] - em - ep)), ghi = group_max<16>(Td[rr] + em + ep);
+    const float tnorm = fmaxf(fabsf(glo), fabsf(ghi));
+    const float pivmin = fmaxf(tnorm * 1e-30f, 1e-30f);
+    const float tol = 2.f * 1.19209290e-7f * tnorm;
+    const int NK = a.eigvals_out ? B : KEPT;  // a power of two
+    const int SL = kWave / NK;
+    const int seg = lane / SL, sl = lane % SL;
+    const int target = B - 1 - seg;  // ascending index of the seg-th largest
+    const uint64_t segmask = SL == kWave ? ~0ull : (((1ull << SL) - 1ull) << (seg * SL));
+    float lo = glo, hi = ghi;
+    bool more = true;
+    for (int it = 0; it < 40; ++it) {
+      more = more && hi - lo > tol;
+      if (!__ballot(more)) break;
+      const float width = hi - lo;
+      const float sig = lo + width * (float)(sl + 1) * __builtin_amdgcn_rcpf((float)(SL + 1));
+      const int cnt = sturm_count16(dreg, e2reg, sig, pivmin);
+      const uint64_t below = __ballot(cnt <= target) & segmask;  // shifts at or below the eigenvalue
+      const int nl = below ? 64 - __clzll(below) - seg * SL : 0;  // highest such lane of the segment + 1
+      const float nlo = nl > 0 ? lo + width * (float)nl * __builtin_amdgcn_rcpf((float)(SL + 1)) : lo;
+      const float nhi = nl < SL ? lo + width * (float)(nl + 1) * __builtin_amdgcn_rcpf((float)(SL + 1)) : hi;
+      if (nlo == lo && nhi == hi) more = false;  // below the resolution of fp32
+      if (more) { lo = nlo; hi = nhi; }
+    }
+    if (sl == 0) sLam[wave][seg] = 0.5f * (lo + hi);
+    wave_lds_fence();
+    lam1 = sLam[wave][0];
+    thresh = fmaxf(kZeroModeRtol * lam1, kZeroModeFloor * energy);
+    if (a.eigvals_out && lane < B) a.eigvals_out[((size_t)idx * a.hkv + kvh) * B + lane] = fmaxf(sLam[wave][lane], 0.f);
 
-  // 4) eigenvalues (diagonal), descending order by rank counting (ties to the
-  //    lower index)
-  if (lane < B) {
-    const float li = sA[wave][cur][lane][lane];
-    int rank = 0;
+    // (c) inverse iteration on T: lane kk factors T - lambda_kk I once with
+    //     partial pivoting (rows i and i + 1 swap when |e_i| > |pivot|; both
+    //     choices are carried and one selected, so the chain has no branch),
+    //     then solves kB16InvIters times from a fixed varied start.
+    if (lane < KEPT) {
+      const int kk = lane;
+      const float lam = sLam[wave][kk];
+      uint32_t swm = 0u;  // bit i: rows i and i + 1 swapped
+      float ddc = dreg[0] - lam, duc = Te[0];
 #pragma unroll
-    for (int j = 0; j < B; ++j) {
-      const float lj = sA[wave][cur][j][j];
-      rank += (lj > li || (lj == li && j < lane)) ? 1 : 0;
+      for (int i = 0; i < B - 1; ++i) {
+        const float dl = Te[i];
+        const float ddn = dreg[i + 1] - lam;
+        const float dun = i + 1 < B - 1 ? Te[i + 1] : 0.f;
+        const bool keep = fabsf(ddc) >= fabsf(dl);
+        const float rk = __builtin_amdgcn_rcpf(fabsf(ddc) < pivmin ? pivmin : ddc);
+        const float rs = __builtin_amdgcn_rcpf(dl);
+        const float mk = dl * rk, ms = ddc * rs;
+        const float nk = ddn - mk * duc, ns = duc - ms * ddn;
+        sF[wave][i][kk] = make_float4(keep ? rk : rs, keep ? duc : ddn, keep ? 0.f : dun, keep ? mk : ms);
+        if (!keep) swm |= 1u << i;
+        duc = keep ? dun : -ms * dun;
+        ddc = keep ? nk : ns;
+      }
+      sF[wave][B - 1][kk] = make_float4(__builtin_amdgcn_rcpf(fabsf(ddc) < pivmin ? pivmin : ddc), 0.f, 0.f, 0.f);
+      float z[B];
+      float nrm2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        const uint32_t hsh = (uint32_t)(i * 2654435761u) ^ (uint32_t)((kk + 1) * 40503u);
+        z[i] = 0.5f + (float)((hsh >> 9) & 1023) * (1.f / 1024.f);
+        nrm2 = fmaf(z[i], z[i], nrm2);
+      }
+      float scale = __builtin_amdgcn_rsqf(nrm2);
+      for (int itr = 0; itr < kB16InvIters; ++itr) {
+        // forward: the row swaps and multipliers applied to the right-hand side
+        float zc = z[0] * scale;
+#pragma unroll
+        for (int i = 0; i < B - 1; ++i) {
+          const float zn = z[i + 1] * scale;
+          const float mlt = sF[wave][i][kk].w;
+          const bool sw = (swm >> i) & 1u;
+          z[i] = sw ? zn : zc;
+          zc = sw ? zc - mlt * zn : zn - mlt * zc;
+        }
+        // back substitution, in place
+        float x1 = zc * sF[wave][B - 1][kk].x, x2 = 0.f;
+        z[B - 1] = x1;
+        nrm2 = x1 * x1;
+#pragma unroll
+        for (int i = B - 2; i >= 0; --i) {
+          const float4 f = sF[wave][i][kk];
+          const float xv = (z[i] - f.y * x1 - f.z * x2) * f.x;
+          z[i] = xv;
+          nrm2 = fmaf(xv, xv, nrm2);
+          x2 = x1;
+          x1 = xv;
+        }
+        scale = __builtin_amdgcn_rsqf(nrm2);
+      }
+#pragma unroll
+      for (int i = 0; i < B; ++i) Zw[i * LD + kk] = z[i] * scale;
     }
-    sOrder[wave][rank] = lane;
-    sLam[wave][rank] = li;
+    wave_lds_fence();
   }
-  wave_lds_fence();
-  const float lam1 = sLam[wave][0];
-  const float thresh = fmaxf(kZeroModeRtol * lam1, kZeroModeFloor * energy);
-  if (a.eigvals_out && lane < B) a.eigvals_out[((size_t)idx * a.hkv + kvh) * B + lane] = fmaxf(sLam[wave][lane], 0.f);
+  // (d) re-orthogonalize within clusters of close eigenvalues (lane = row;
+  //     the four groups compute alike, group 0 stores)
+  {
+    const float ctol = kB16ClusterTol * fabsf(lam1);
+    for (int kk = 1; kk < KEPT; ++kk) {
+      bool touched = false;
+      float zk = Zw[rr * LD + kk];
+      for (int j = 0; j < kk; ++j) {
+        if (fabsf(sLam[wave][j] - sLam[wave][kk]) > ctol) continue;
+        const float zj = Zw[rr * LD + j];
+        zk -= group_sum<16>(zj * zk) * zj;
+        touched = true;
+      }
+      if (touched) {
+        zk *= __builtin_amdgcn_rsqf(group_sum<16>(zk * zk));
+        if (gg == 0) Zw[rr * LD + kk] = zk;
+        wave_lds_fence();
+      }
+    }
+  }
+  // (e) back-transformation y = H_0 H_1 ... H_13 z: lane (kk, b) = (lane / 4,
+  //     lane % 4) holds rows 4 b .. 4 b + 3 of eigenvector kk
+  {
+    const int kk = lane >> 2, b = lane & 3;
+    float y[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) y[t] = kk < KEPT ? Zw[(4 * b + t) * LD + kk] : 0.f;
+#pragma unroll
+    for (int k = B - 3; k >= 0; --k) {
+      float uk[4], d = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        uk[t] = Rf[k * LD + 4 * b + t];
+        d = fmaf(uk[t], y[t], d);
+      }
+      const float f = -2.f * group_sum<4>(d);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) y[t] = fmaf(f, uk[t], y[t]);
+    }
+    wave_lds_fence();
+    if (kk < KEPT) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) Zw[(4 * b + t) * LD + kk] = y[t];
+    }
+    wave_lds_fence();
+  }
 
   // 5) basis rows V[k][c] = sum_i D[i][c] U[i][idx_k] / sigma_k for this lane's
   //    dims c = 2 lane, 2 lane + 1, then the signs (largest |entry| positive,
@@ -284,18 +413,18 @@ __global__ __launch_bounds__(kB16Waves * kWave) void build16_kernel(BuildArgs a)
   float vb[KEPT][2];
 #pragma unroll
   for (int k = 0; k < KEPT; ++k) {
-    const int ik = sOrder[wave][k];
     const bool nz = lam1 > 0.f && sLam[wave][k] > thresh;
     const float inv = nz ? 1.f / sqrtf(sLam[wave][k]) : 0.f;
     float v0 = 0.f, v1 = 0.f;
 #pragma unroll
     for (int i = 0; i < B; ++i) {
-      const float uik = sU[wave][cur][i][ik];
+      const float uik = Zw[i * LD + k];
       v0 = fmaf(db[i][0], uik, v0);
       v1 = fmaf(db[i][1], uik, v1);
     }
-    v0 *= inv;
-    v1 *= inv;
+    // zero modes: no basis row (their eigenvector may be anything, even inf)
+    v0 = nz ? v0 * inv : 0.f;
+    v1 = nz ? v1 * inv : 0.f;
     // this lane's candidate: the larger |entry| of its two dims (ties: the lower)
     float best = fabsf(v0), val = v0;
     int bidx = 2 * lane;
@@ -316,7 +445,7 @@ __global__ __launch_bounds__(kB16Waves * kWave) void build16_kernel(BuildArgs a)
   auto coef_at = [&](int i, int k) -> float {
     if (k >= KEPT) return 0.f;
     const bool nz = lam1 > 0.f && sLam[wave][k] > thresh;
-    return nz ? sU[wave][cur][i][sOrder[wave][k]] * sqrtf(sLam[wave][k]) * sSign[wave][k] : 0.f;
+    return nz ? Zw[i * LD + k] * sqrtf(sLam[wave][k]) * sSign[wave][k] : 0.f;
   };
 
   // 6) record

@@ -1,6 +1,6 @@
 """Pages of 16 tokens on the GPU builder (needs an MI355X).
 
-The summaries of the Jacobi builder against the fp64 oracle (fp32 and bf16
+The summaries of the 16-token builder against the fp64 oracle (fp32 and bf16
 records, int4/int8 records), and the isotropic null of the Locks appendix
 ("Spectral tails": a rank-8 fit of 20,000 flat-spectrum B = 16 pages captures
 a median 67.8% of their variance) reproduced from the GPU builder's

@@ -85,7 +85,7 @@ def test_page16_scorer_on_oracle_records(gpu, summary, rank):
 
 @pytest.mark.parametrize("summary,rank", [("kv", 8), ("i4", 8), ("kv", 16)])
 def test_page16_end_to_end(gpu, summary, rank):
-    """GPU-built records (the Jacobi builder at 16 tokens), every matching rule."""
+    """GPU-built records (the 16-token builder), every matching rule."""
     w = page16(summary=summary, rank=rank)
     say("page16 end to end:", summary, "r", rank, w.context)
     dc = DeviceCache(w, poison=True)
