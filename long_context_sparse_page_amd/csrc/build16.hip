@@ -13,8 +13,8 @@
 // top r eigenpairs are needed, so the eigenproblem is solved as the 64-token
 // builder solves its own (Golub & Van Loan, Matrix Computations, ch. 8), here
 // on one wave: Householder reduction to tridiagonal form with the matrix in
-// registers (lane (row, g) holds columns 4 g .. 4 g + 3 of its row: the Gram
-// tile's own accumulator layout, by symmetry), the wanted eigenvalues of T by
+// registers (lane (row, g) holds columns 4 g .. 4 g + 3 of its row, read from
+// the mirrored LDS copy of the Gram), the wanted eigenvalues of T by
 // Sturm-sequence multisection on lane segments, their eigenvectors by inverse
 // iteration with partial pivoting (re-orthogonalized within clusters of close
 // eigenvalues), and back-transformation by the 14 reflectors.  A step or a
