@@ -162,6 +162,41 @@ def test_page16_decode_steps(gpu, summary):
     say("page16 decode steps:", tot)
 
 
+@pytest.mark.parametrize("group,dtype", [(1, "f32"), (2, "bf16"), (8, "f32")])
+def test_page16_decode_step_groups(gpu, group, dtype):
+    """lk_decode_step at 16 tokens for GQA groups 1, 2 and 8 (the builder
+    launch merges each (sequence, KV head)'s split partials with one wave,
+    whose lanes own different dims and heads for each group size): 18 steps
+    over a ragged batch, so both sequences complete pages and build them
+    in-stream; every matching rule at the first and the last step."""
+    w = page16(wid=0, batch=2, ctx=(16 * 40 + 9, 16 * 12 + 14), steps=18, budget=256, hq=2 * group, hkv=2,
+               dtype=dtype)
+    say("page16 decode step groups: G", group, dtype, w.context, "steps", w.steps)
+    dc = DeviceCache(w, poison=True)
+    dc.fill_from_synth()
+    dc.build_all()
+    lens = list(w.context)
+    kvs = {(s, h): synth.keys_values(w, s, h) for s in range(w.batch) for h in range(w.num_kv_heads)}
+    tot = ref.PairCheck()
+    for step in range(w.steps):
+        new_lens = [t + 1 for t in lens]
+        q64 = ref.host_queries(w, step, new_lens)
+        kn = np.stack([np.stack([kvs[(s, h)][0][lens[s]] for h in range(w.num_kv_heads)]) for s in range(w.batch)])
+        vn = np.stack([np.stack([kvs[(s, h)][1][lens[s]] for h in range(w.num_kv_heads)]) for s in range(w.batch)])
+        o = dc.outputs()
+        dc.decode_step(ref.q_device(q64, w.dtype), to_storage(kn, w.dtype).cuda(), to_storage(vn, w.dtype).cuda(), o)
+        torch.cuda.synchronize()
+        assert dc.seq_lens.cpu().tolist() == new_lens
+        lens = new_lens
+        if step not in (0, w.steps - 1):
+            continue
+        o2 = dc.outputs()
+        dc.score_select(ref.q_device(q64, w.dtype), o2)
+        torch.cuda.synchronize()
+        tot.merge(ref.check_all_pairs(w, dc, o, q64, lens, page_lse=o2["page_lse"].cpu().numpy()))
+    say("page16 decode step groups:", tot)
+
+
 def test_page16_dense_attention(gpu):
     """The same-GPU dense decode at 16 tokens against the oracle's dense attention."""
     w = page16(ctx=(16 * 300 + 11, 16 * 9 + 2))
