@@ -237,18 +237,18 @@ template <int R, int B = 64> struct ScoreGroup {
 template <int R, int B> struct GroupLoads {
   uint4 wb[ScoreGroup<R, B>::TILES][4];                    // B operand tiles
   uint32_t cw[ScoreGroup<R, B>::CSETS][ScoreGroup<R, B>::CW];  // token coefficients (bf16 pairs)
-  bool valid[ScoreGroup<R, B>::NR];                        // record present in the pool (else the page scores -inf)
+  uint32_t vbits;                                          // bit r: record r present in the pool (else the page scores -inf)
 };
 
-// Pointer of record x of the group, x lane-dependent (a select over the
-// group's uniform record pointers).
-template <int NR, typename P>
-__device__ __forceinline__ P pick_record(P const (&recp)[NR], int x) {
-  P rp = recp[0];
+// v[x] for a lane-dependent x in [LO, LO + CNT) from uniform values, by
+// masks: a select chain on x == y lets the compiler turn it into an indexed
+// load of the array, which then lives in scratch memory.
+template <int LO, int CNT, int N>
+__device__ __forceinline__ int pick_uniform(const int (&v)[N], int x) {
+  int r = 0;
 #pragma unroll
-  for (int y = 1; y < NR; ++y)
-    if (y == x) rp = recp[y];
-  return rp;
+  for (int y = LO; y < LO + CNT; ++y) r |= v[y] & -(int)(x == y);
+  return r;
 }
 
 // Every load is unconditional, so the compiler keeps them in one batch with no
@@ -256,8 +256,9 @@ __device__ __forceinline__ P pick_record(P const (&recp)[NR], int x) {
 // page 0 instead (always allocated) and its result discarded, and B columns
 // past the group's slots repeat its last slot (their products are unused).
 template <int R, int B>
-__device__ __forceinline__ void load_group(GroupLoads<R, B>& L, const bf16_t* summ, const int* phys_g, int num_phys,
-                                           int hkv, int kvh, int col, int kg, int lane) {
+__device__ __forceinline__ void load_group(GroupLoads<R, B>& L, const bf16_t* summ,
+                                           const int (&phys_g)[ScoreGroup<R, B>::NR], int num_phys, int hkv, int kvh,
+                                           int col, int kg, int lane) {
   constexpr int D = kHeadDim;
   constexpr int ROWS = R + 1;
   constexpr int NR = ScoreGroup<R, B>::NR;
@@ -266,20 +267,28 @@ __device__ __forceinline__ void load_group(GroupLoads<R, B>& L, const bf16_t* su
   constexpr int CW = ScoreGroup<R, B>::CW;
   constexpr int CSETS = ScoreGroup<R, B>::CSETS;
   constexpr size_t REC = (size_t)ROWS * D + (size_t)B * R;
+  auto rec_of = [&](int phys) {
+    return summ + ((size_t)((phys >= 0 && phys < num_phys) ? phys : 0) * hkv + kvh) * REC;
+  };
   const bf16_t* recp[NR];
+  L.vbits = 0u;
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     const int phys = phys_g[r];
-    L.valid[r] = phys >= 0 && phys < num_phys;
-    recp[r] = summ + ((size_t)(L.valid[r] ? phys : 0) * hkv + kvh) * REC;
+    L.vbits |= (phys >= 0 && phys < num_phys) ? 1u << r : 0u;
+    recp[r] = rec_of(phys);
   }
 #pragma unroll
   for (int tau = 0; tau < TILES; ++tau) {
     const int slot = min(16 * tau + col, SLOTS - 1);
     const int r = slot / ROWS, m = slot % ROWS;
     const bf16_t* rp = recp[0];
+    if constexpr (B == 64) {
 #pragma unroll
-    for (int x = 1; x < NR; ++x) if (x == r) rp = recp[x];
+      for (int x = 1; x < NR; ++x) if (x == r) rp = recp[x];
+    } else {
+      rp = rec_of(pick_uniform<0, NR>(phys_g, r));
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t)
       L.wb[tau][t] = *reinterpret_cast<const uint4*>(rp + (size_t)m * D + 32 * t + 8 * kg);
@@ -287,8 +296,8 @@ __device__ __forceinline__ void load_group(GroupLoads<R, B>& L, const bf16_t* su
 #pragma unroll
   for (int r = 0; r < CSETS; ++r) {
     const bf16_t* cp = B == 64 ? recp[r] + (size_t)ROWS * D + (size_t)lane * R
-                               : pick_record<NR>(recp, min(4 * r + (lane >> 4), NR - 1)) + (size_t)ROWS * D +
-                                     (size_t)(lane & 15) * R;
+                               : rec_of(pick_uniform<0, NR>(phys_g, min(4 * r + (lane >> 4), NR - 1))) +
+                                     (size_t)ROWS * D + (size_t)(lane & 15) * R;
     if constexpr (R % 8 == 0) {
 #pragma unroll
       for (int x = 0; x < CW; x += 4) {
@@ -314,7 +323,7 @@ __device__ __forceinline__ void load_group(GroupLoads<R, B>& L, const bf16_t* su
 // chains), and one store per head group.  coef(r, c, s) gives this lane's
 // token coefficients of record r and their scale.
 template <int R, int G, int NR, bool SCALED, typename Coef>
-__device__ __forceinline__ void group_lse(const float* P, float* Z, Coef coef, const bool (&valid)[NR], float* out,
+__device__ __forceinline__ void group_lse(const float* P, float* Z, Coef coef, uint32_t vbits, float* out,
                                           int max_pages, int g0, int j_end, int lane, float zscale) {
   constexpr int B = 64;
   constexpr int ROWS = R + 1;
@@ -368,7 +377,7 @@ __device__ __forceinline__ void group_lse(const float* P, float* Z, Coef coef, c
 #pragma unroll
       for (int t = 0; t < TPL; ++t) sum += fast_exp2(v[t] - mx);
       sum = group_sum<LPH>(sum);
-      res[rr] = valid[c0 + rr] ? (mx + fast_log2(sum)) * kLn2 : -INFINITY;
+      res[rr] = ((vbits >> (c0 + rr)) & 1u) ? (mx + fast_log2(sum)) * kLn2 : -INFINITY;
     }
     // lane hg * LPH + rr of head group hg writes record c0 + rr
     const int rsel = lane % LPH;
@@ -395,7 +404,7 @@ __device__ __forceinline__ void group_lse(const float* P, float* Z, Coef coef, c
 // a row reduction; lane 16 q + g then writes head g.  coef(p, c, s) gives the
 // lane's coefficients of pass p and their scale.
 template <int R, int G, int NR, bool SCALED, typename Coef>
-__device__ __forceinline__ void group_lse16(const float* P, Coef coef, const bool (&valid)[NR], float* out,
+__device__ __forceinline__ void group_lse16(const float* P, Coef coef, uint32_t vbits, float* out,
                                             int max_pages, int g0, int j_end, int lane, float zscale) {
   constexpr int ROWS = R + 1;
   const int q = lane >> 4, t = lane & 15;
@@ -429,10 +438,7 @@ __device__ __forceinline__ void group_lse16(const float* P, Coef coef, const boo
 #pragma unroll
     for (int g = 1; g < G; ++g)
       if (t == g) val = res[g];
-    bool ok = valid[0];
-#pragma unroll
-    for (int x = 1; x < NR; ++x)
-      if (x == rc) ok = valid[x];
+    const bool ok = (vbits >> rc) & 1u;
     const int j = g0 + r;
     if (t < G && r < NR && j < j_end) out[(size_t)t * max_pages + j] = ok ? val : -INFINITY;
   }
@@ -522,8 +528,8 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_mfma_kernel(ScoreAr
       for (int m = 0; m < R; ++m) c[m] = (m & 1) ? bf16_hi(cur.cw[r][m >> 1]) : bf16_lo(cur.cw[r][m >> 1]);
       cs = 1.f;
     };
-    if constexpr (B == 64) group_lse<R, G, NR, false>(P, Z, coef, cur.valid, out, a.max_pages, g0, j_end, lane, zscale);
-    else group_lse16<R, G, NR, false>(P, coef, cur.valid, out, a.max_pages, g0, j_end, lane, zscale);
+    if constexpr (B == 64) group_lse<R, G, NR, false>(P, Z, coef, cur.vbits, out, a.max_pages, g0, j_end, lane, zscale);
+    else group_lse16<R, G, NR, false>(P, coef, cur.vbits, out, a.max_pages, g0, j_end, lane, zscale);
   }
 }
 
@@ -571,18 +577,18 @@ __device__ __forceinline__ uint32_t bf16x2_of(float lo, float hi) {  // both exa
 __device__ __forceinline__ float ubyte_f(uint32_t x, int b) { return (float)((x >> (8 * b)) & 0xffu); }
 
 // K-step operand of 8 int4 codes (one 32-bit word, element j in nibble j) as
-// bf16 values of code + 8.
+// bf16 values of code + 136: the biased code n = code + 8 (0..15) goes into
+// the low mantissa bits of bf16 128 (0x4300 | n is exactly 128 + n), one byte
+// permute and one OR per two codes.
+constexpr float kQ4Bias = 136.f;
 __device__ __forceinline__ bf16x8_t q4_operand(uint32_t w) {
   w ^= 0x88888888u;
-  uint32_t even = w & 0x0f0f0f0fu, odd = (w >> 4) & 0x0f0f0f0fu;
-  // opaque to the compiler, so each byte below converts with one v_cvt_f32_ubyteN
-  // instead of a bit-field extract followed by a conversion
-  asm("" : "+v"(even), "+v"(odd));
-  uint4 o;
-  o.x = bf16x2_of(ubyte_f(even, 0), ubyte_f(odd, 0));
-  o.y = bf16x2_of(ubyte_f(even, 1), ubyte_f(odd, 1));
-  o.z = bf16x2_of(ubyte_f(even, 2), ubyte_f(odd, 2));
-  o.w = bf16x2_of(ubyte_f(even, 3), ubyte_f(odd, 3));
+  const uint32_t even = w & 0x0f0f0f0fu, odd = (w >> 4) & 0x0f0f0f0fu;
+  uint4 o;  // dword j: [even byte j, 0, odd byte j, 0] | 0x43004300 = elements 2 j, 2 j + 1
+  o.x = __builtin_amdgcn_perm(odd, even, 0x0c040c00u) | 0x43004300u;
+  o.y = __builtin_amdgcn_perm(odd, even, 0x0c050c01u) | 0x43004300u;
+  o.z = __builtin_amdgcn_perm(odd, even, 0x0c060c02u) | 0x43004300u;
+  o.w = __builtin_amdgcn_perm(odd, even, 0x0c070c03u) | 0x43004300u;
   return __builtin_bit_cast(bf16x8_t, o);
 }
 // K-step operand of 8 int8 codes (two 32-bit words) as bf16 values of code + 128.
@@ -649,12 +655,16 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
   int n_scored = len_raw <= 0 ? 0 : (len_raw - 1) / B;
   if (n_scored > a.max_pages - 1) n_scored = a.max_pages - 1;
   if (j0 >= n_scored) return;
-  bool valid[NR];
+  auto rec_of = [&](int phys) {
+    return summ + ((size_t)((phys >= 0 && phys < a.num_phys) ? phys : 0) * a.hkv + kvh) * REC;
+  };
+  uint32_t vbits = 0u;  // bit r: record r present in the pool
   const uint8_t* recp[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
-    valid[r] = phys_all[r] >= 0 && phys_all[r] < a.num_phys;
-    recp[r] = summ + ((size_t)(valid[r] ? phys_all[r] : 0) * a.hkv + kvh) * REC;
+    const bool valid = phys_all[r] >= 0 && phys_all[r] < a.num_phys;
+    vbits |= valid ? 1u << r : 0u;
+    recp[r] = summ + ((size_t)(valid ? phys_all[r] : 0) * a.hkv + kvh) * REC;
   }
   uint4 wb[BT];     // basis row (record, row) = column of tile tau: 32 codes
   uint32_t bsc[BT]; // its scale (fp16 bits)
@@ -674,8 +684,12 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
   {
     const int r = min(col, NR - 1);
     const uint8_t* rp = recp[0];
+    if constexpr (B == 64) {
 #pragma unroll
-    for (int x = 1; x < NR; ++x) if (x == r) rp = recp[x];
+      for (int x = 1; x < NR; ++x) if (x == r) rp = recp[x];
+    } else {
+      rp = rec_of(pick_uniform<0, NR>(phys_all, r));
+    }
     wm[0] = *reinterpret_cast<const uint4*>(rp + 32 * kg);
     wm[1] = *reinterpret_cast<const uint4*>(rp + 32 * kg + 16);
     msc = *reinterpret_cast<const uint16_t*>(rp + L.mscale());
@@ -684,7 +698,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
   uint32_t csc[CSETS];              // and their scale (fp16 bits)
 #pragma unroll
   for (int r = 0; r < CSETS; ++r) {
-    const uint8_t* rp = B == 64 ? recp[r] : pick_record<NR>(recp, min(4 * r + (lane >> 4), NR - 1));
+    const uint8_t* rp = B == 64 ? recp[r] : rec_of(pick_uniform<0, NR>(phys_all, min(4 * r + (lane >> 4), NR - 1)));
     const int tok = B == 64 ? lane : (lane & 15);
     const uint8_t* cp = rp + L.coef() + (size_t)tok * R;
     if constexpr (R == 16) {
@@ -734,7 +748,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
       if (g < G && col < NR) P[(col * ROWS) * G + g] = sc * (acc[i] - 128.f * Sg[i]);
     }
   }
-  // basis tiles: P[record * ROWS + 1 + row][g] = scale * (acc - 8 S_g)
+  // basis tiles: P[record * ROWS + 1 + row][g] = scale * (acc - 136 S_g)
 #pragma unroll
   for (int tau = 0; tau < BT; ++tau) {
     const uint32_t w[4] = {wb[tau].x, wb[tau].y, wb[tau].z, wb[tau].w};
@@ -747,7 +761,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int g = 4 * kg + i;
-      if (g < G) P[(r * ROWS + 1 + m) * G + g] = sc * (acc[i] - 8.f * Sg[i]);
+      if (g < G) P[(r * ROWS + 1 + m) * G + g] = sc * (acc[i] - kQ4Bias * Sg[i]);
     }
   }
   wave_lds_fence();
@@ -756,8 +770,8 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
     for (int m = 0; m < R; ++m) c[m] = (float)(int8_t)((cw[r][m >> 2] >> (8 * (m & 3))) & 0xffu);
     cs = half_bits_f(csc[r]);
   };
-  if constexpr (B == 64) group_lse<R, G, NR, true>(P, Z, coef, valid, out, a.max_pages, j0, j_end, lane, zscale);
-  else group_lse16<R, G, NR, true>(P, coef, valid, out, a.max_pages, j0, j_end, lane, zscale);
+  if constexpr (B == 64) group_lse<R, G, NR, true>(P, Z, coef, vbits, out, a.max_pages, j0, j_end, lane, zscale);
+  else group_lse16<R, G, NR, true>(P, coef, vbits, out, a.max_pages, j0, j_end, lane, zscale);
 }
 
 template <int R, int B>
