@@ -238,7 +238,7 @@ __device__ __forceinline__ void combine_write(const AttnArgs& a, size_t pidx, in
   const int e = lane & 7;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    float M = fmaxf(m[g], dpp<kDppRor8>(m[g]));
+    float M = vmax(m[g], dpp<kDppRor8>(m[g]));
     M = xor32_max(xor16_max(M));
     const float f = (M == -INFINITY) ? 0.f : fast_exp2(m[g] - M);
     float lg = l[g] * f;
@@ -274,7 +274,7 @@ __device__ __forceinline__ void combine_write(const AttnArgs& a, size_t pidx, in
       const int g = x / (D / 4), d4 = x % (D / 4);
       float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < NWV; ++w) M = fmaxf(M, s_m[w][g]);
+      for (int w = 0; w < NWV; ++w) M = vmax(M, s_m[w][g]);
       float4 ov = make_float4(0.f, 0.f, 0.f, 0.f);
       float lv = 0.f;
       if (M != -INFINITY) {
@@ -302,7 +302,7 @@ __device__ __forceinline__ void combine_write(const AttnArgs& a, size_t pidx, in
       const int g = x / D, d = x % D;
       float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < NWV; ++w) M = fmaxf(M, s_m[w][g]);
+      for (int w = 0; w < NWV; ++w) M = vmax(M, s_m[w][g]);
       float ov = 0.f, lv = 0.f;
       if (M != -INFINITY) {
 #pragma unroll
@@ -645,7 +645,7 @@ __global__ __launch_bounds__(kFusedThreads) void select_attn_kernel(SelectArgs s
 #pragma unroll
       for (int i = 0; i < NPT; ++i) {
         v[g][i] = page(i) < n_mr ? v[g][i] * kLog2e : -INFINITY;
-        mg[g] = fmaxf(mg[g], v[g][i]);
+        mg[g] = vmax(mg[g], v[g][i]);
       }
       sl[g] = 0.f;
 #pragma unroll
@@ -882,11 +882,11 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_merge_kernel(AttnArgs
   const float* ml = a.part_ml;
   float M = -INFINITY;
   for (int s0 = threadIdx.x; s0 < a.n_splits; s0 += kAttnWaves * kWave)
-    M = fmaxf(M, ml[((pbase + s0) * G + g) * 2]);
+    M = vmax(M, ml[((pbase + s0) * G + g) * 2]);
   M = group_max<kWave>(M);
   if (lane == 0) s_m[wave] = M;
   __syncthreads();
-  M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  M = vmax(vmax(s_m[0], s_m[1]), vmax(s_m[2], s_m[3]));
   float L = 0.f, o0 = 0.f, o1 = 0.f;
   if (M != -INFINITY) {
 #pragma unroll 4

@@ -65,10 +65,19 @@ constexpr int kDppHalfMirror = 0x141; // lane i <- 7 - i within 8
 constexpr int kDppMirror = 0x140;     // lane i <- 15 - i within 16
 constexpr int kDppRor8 = 0x128;       // lane i <- (i + 8) mod 16 within 16
 
+// Every control above reads a lane of the same row, so no lane is out of
+// bounds and the bound-control zero never applies (no old value to set up).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
 }
+
+// Maximum with NaN propagation (one v_maximum3_f32).  fmaxf drops a NaN
+// operand, so in IEEE mode the compiler first quiets every operand that is
+// not the result of arithmetic (LDS loads, DPP and permlane moves): two
+// extra instructions per maximum.  For values that are never NaN the two
+// agree, up to the sign of a zero maximum.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 // Exchange with lane ^ 16 / lane ^ 32 on the VALU (gfx950 permlane swaps):
 // swapping a value with itself leaves x in one result and its partner in the
@@ -83,11 +92,11 @@ __device__ __forceinline__ float xor32_sum(float x) {
 }
 __device__ __forceinline__ float xor16_max(float x) {
   const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  return vmax(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 __device__ __forceinline__ float xor32_max(float x) {
   const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  return vmax(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 
 // Sum / max over aligned groups of N lanes (N in {1,2,4,8,16,32,64}); every
@@ -104,10 +113,10 @@ __device__ __forceinline__ float group_sum(float x) {
 }
 template <int N>
 __device__ __forceinline__ float group_max(float x) {
-  if constexpr (N >= 2) x = fmaxf(x, dpp<kDppXor1>(x));
-  if constexpr (N >= 4) x = fmaxf(x, dpp<kDppXor2>(x));
-  if constexpr (N >= 8) x = fmaxf(x, dpp<kDppHalfMirror>(x));
-  if constexpr (N >= 16) x = fmaxf(x, dpp<kDppMirror>(x));
+  if constexpr (N >= 2) x = vmax(x, dpp<kDppXor1>(x));
+  if constexpr (N >= 4) x = vmax(x, dpp<kDppXor2>(x));
+  if constexpr (N >= 8) x = vmax(x, dpp<kDppHalfMirror>(x));
+  if constexpr (N >= 16) x = vmax(x, dpp<kDppMirror>(x));
   if constexpr (N >= 32) x = xor16_max(x);
   if constexpr (N >= 64) x = xor32_max(x);
   return x;

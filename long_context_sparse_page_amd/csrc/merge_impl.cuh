@@ -35,7 +35,7 @@ __device__ __forceinline__ void merge_partials(const BuildArgs& a, int seq, int 
       float Mc = M;
 #pragma unroll
       for (int t = 0; t < CH; ++t)
-        if (c0 + t < ns) Mc = fmaxf(Mc, ms[t]);
+        if (c0 + t < ns) Mc = vmax(Mc, ms[t]);
       if (Mc == -INFINITY) continue;
       const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mc);  // earlier chunks to the new max
       ov *= r;
@@ -109,7 +109,7 @@ __device__ __forceinline__ void merge_partials_wave(const BuildArgs& a, int seq,
       float Mc = M[u];
 #pragma unroll
       for (int t = 0; t < CH; ++t)
-        if (c0 + t < ns) Mc = fmaxf(Mc, ms[t][u]);
+        if (c0 + t < ns) Mc = vmax(Mc, ms[t][u]);
       if (Mc == -INFINITY) continue;
       const float r = M[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M[u] - Mc);  // earlier chunks to the new max
       lv[u] *= r;

@@ -189,7 +189,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_kernel(ScoreArgs a)
 #pragma unroll
       for (int t = 0; t < TPL; ++t) {
         v[t] = Z[hg * B + t0 + t];
-        mx = fmaxf(mx, v[t]);
+        mx = vmax(mx, v[t]);
       }
       mx = group_max<LPH>(mx);
       float sum = 0.f;
@@ -370,7 +370,7 @@ __device__ __forceinline__ void group_lse(const float* P, float* Z, Coef coef, u
 #pragma unroll
       for (int t = 0; t < TPL; ++t) {
         v[t] = Z[(rr * G + hg) * B + t0 + t];
-        mx = fmaxf(mx, v[t]);
+        mx = vmax(mx, v[t]);
       }
       mx = group_max<LPH>(mx);
       float sum = 0.f;

@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kPartThreads) void select_part_kernel(SelectArgs a)
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
       x[g][i] = p0 + tid + BS * i < pp.n_scored ? x[g][i] * kLog2e : -INFINITY;
-      m = fmaxf(m, x[g][i]);
+      m = vmax(m, x[g][i]);
     }
     float sl = 0.f;
 #pragma unroll
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kPartThreads) void select_part_kernel(SelectArgs a)
     const int g = tid;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_pm[g][w]);
+    for (int w = 0; w < NW; ++w) M = vmax(M, s_pm[g][w]);
     float S = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) S += s_pm[g][w] == -INFINITY ? 0.f : s_ps[g][w] * fast_exp2(s_pm[g][w] - M);

@@ -66,7 +66,7 @@ __device__ __forceinline__ float wave_max(float x) {
   const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
   const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
   const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
-  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+  return vmax(vmax(a, b), vmax(c, d));
 }
 
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t x, int ctrl_id) {
@@ -361,7 +361,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, int seq, int k
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
       x[i] = score_at(g, i);
-      m[g] = fmaxf(m[g], x[i]);
+      m[g] = vmax(m[g], x[i]);
     }
     sl[g] = 0.f;
 #pragma unroll
@@ -385,7 +385,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, int seq, int k
   for (int g = 0; g < G; ++g) {
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_pm[g * NW + w]);
+    for (int w = 0; w < NW; ++w) M = vmax(M, s_pm[g * NW + w]);
     float S = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
