@@ -72,12 +72,13 @@ __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
 }
 
-// Maximum with NaN propagation (one v_maximum3_f32).  fmaxf drops a NaN
+// Maximum (minimum) with NaN propagation (one v_maximum3_f32 / v_minimum3_f32).  fmaxf drops a NaN
 // operand, so in IEEE mode the compiler first quiets every operand that is
 // not the result of arithmetic (LDS loads, DPP and permlane moves): two
 // extra instructions per maximum.  For values that are never NaN the two
 // agree, up to the sign of a zero maximum.
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmin(float a, float b) { return __builtin_elementwise_minimum(a, b); }
 
 // Exchange with lane ^ 16 / lane ^ 32 on the VALU (gfx950 permlane swaps):
 // swapping a value with itself leaves x in one result and its partner in the

@@ -315,13 +315,24 @@ __device__ __forceinline__ void load_group(GroupLoads<R, B>& L, const bf16_t* su
   }
 }
 
+// 64-token pages: a page's logits z_i = z_c + d_i split into the centroid
+// logit z_c (row 0 of P) and the deviation d_i = s_i * sum_m c_i[m] P[m + 1]
+// (s_i = 1 unless SCALED), so LSE = z_c + log sum_i exp(d_i).  The
+// deviations of a centred page straddle zero (their coefficients sum to
+// zero), so sum_i 2^d_i needs no running maximum unless a deviation is
+// extreme: a wave whose sums leave [2^-64, 2^64] (or are not finite) takes
+// the page maxima and sums again.  In both forms the largest term that
+// matters is at least 2^-64 of the total and no term overflows, so the two
+// agree to rounding.  (At 16-token pages the maxima are always taken: the
+// two-pass form there needs more registers than the row reductions it saves.)
+__device__ __forceinline__ bool lse_sum_ok(float s) { return s >= 0x1p-64f && s <= 0x1p64f; }
+
 // Reconstruction and per-head LSE of a group of NR records whose projections
 // P[slot * G + g] (slot = record * (R + 1) + row; row 0 = centroid) are in
-// LDS, RC records at a time: every record's logits (lane = token) in one
-// pass, z_i = P[0] + s_i * sum_m c_i[m] P[m + 1] (s_i = 1 unless SCALED), one
-// transpose through LDS, then the records' LSEs side by side (independent
-// chains), and one store per head group.  coef(r, c, s) gives this lane's
-// token coefficients of record r and their scale.
+// LDS, RC records at a time: every record's deviations (lane = token) in one
+// pass, one transpose through LDS, then the records' sums side by side
+// (independent chains), and one store per head group.  coef(r, c, s) gives
+// this lane's token coefficients of record r and their scale.
 template <int R, int G, int NR, bool SCALED, typename Coef>
 __device__ __forceinline__ void group_lse(const float* P, float* Z, Coef coef, uint32_t vbits, float* out,
                                           int max_pages, int g0, int j_end, int lane, float zscale) {
@@ -339,20 +350,13 @@ __device__ __forceinline__ void group_lse(const float* P, float* Z, Coef coef, u
       float c[R], cs;
       coef(r, c, cs);
       const float* Pr = P + r * ROWS * G;
+      const float dscale = SCALED ? cs * zscale : zscale;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        float acc;
-        if constexpr (SCALED) {
-          acc = 0.f;
+        float acc = 0.f;
 #pragma unroll
-          for (int m = 0; m < R; ++m) acc = fmaf(c[m], Pr[(m + 1) * G + g], acc);
-          acc = fmaf(cs, acc, Pr[g]);
-        } else {
-          acc = Pr[g];
-#pragma unroll
-          for (int m = 0; m < R; ++m) acc = fmaf(c[m], Pr[(m + 1) * G + g], acc);
-        }
-        z[rr][g] = acc * zscale;
+        for (int m = 0; m < R; ++m) acc = fmaf(c[m], Pr[(m + 1) * G + g], acc);
+        z[rr][g] = acc * dscale;
       }
     }
 #pragma unroll
@@ -362,23 +366,36 @@ __device__ __forceinline__ void group_lse(const float* P, float* Z, Coef coef, u
     wave_lds_fence();
     const int hg = lane / LPH;
     const int t0 = (lane % LPH) * TPL;
-    float res[RC];
+    float v[RC][TPL], res[RC];
+    float lo_s = 0x1p64f, hi_s = 0x1p-64f;  // range of this head group's sums
 #pragma unroll
     for (int rr = 0; rr < RC; ++rr) {
-      float v[TPL];
-      float mx = -INFINITY;
+      float sl = 0.f;
 #pragma unroll
       for (int t = 0; t < TPL; ++t) {
-        v[t] = Z[(rr * G + hg) * B + t0 + t];
-        mx = vmax(mx, v[t]);
+        v[rr][t] = Z[(rr * G + hg) * B + t0 + t];
+        sl += fast_exp2(v[rr][t]);
       }
-      mx = group_max<LPH>(mx);
-      float sum = 0.f;
-#pragma unroll
-      for (int t = 0; t < TPL; ++t) sum += fast_exp2(v[t] - mx);
-      sum = group_sum<LPH>(sum);
-      res[rr] = ((vbits >> (c0 + rr)) & 1u) ? (mx + fast_log2(sum)) * kLn2 : -INFINITY;
+      const float sum = group_sum<LPH>(sl);
+      lo_s = vmin(lo_s, sum);
+      hi_s = vmax(hi_s, sum);
+      res[rr] = P[(c0 + rr) * ROWS * G + hg] * zscale + fast_log2(sum);
     }
+    if (__ballot(!(lse_sum_ok(lo_s) && lse_sum_ok(hi_s))) != 0ull) {  // wave-uniform: exact page maxima
+#pragma unroll
+      for (int rr = 0; rr < RC; ++rr) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < TPL; ++t) m = vmax(m, v[rr][t]);
+        m = group_max<LPH>(m);
+        float sl = 0.f;
+#pragma unroll
+        for (int t = 0; t < TPL; ++t) sl += fast_exp2(v[rr][t] - m);
+        res[rr] = P[(c0 + rr) * ROWS * G + hg] * zscale + m + fast_log2(group_sum<LPH>(sl));
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < RC; ++rr) res[rr] = ((vbits >> (c0 + rr)) & 1u) ? res[rr] * kLn2 : -INFINITY;
     // lane hg * LPH + rr of head group hg writes record c0 + rr
     const int rsel = lane % LPH;
     if constexpr (RC <= LPH) {
