@@ -40,8 +40,9 @@
  *                    centroid[d] | basis[r][d] (row m = m-th basis vector) |
  *                    coeffs[B][r] (row i = c_i) in kv_dtype; with
  *                    summary_format = LK_SUMMARY_I4 the record holds bytes:
- *                    centroid int8[d] | basis int4[r][d/2] (byte c of row m
- *                    holds dims 2c (low nibble) and 2c+1, two's complement) |
+ *                    centroid int8[d] | basis int4[r][d/2] (row m in 32-bit
+ *                    little-endian words of 8 dims: word g holds dim 8g+2j in nibble j
+ *                    and dim 8g+2j+1 in nibble j+4, j = 0..3, two's complement) |
  *                    coeffs int8[B][r] | coefficient scales fp16[B] | basis
  *                    scales fp16[r] | centroid scale fp16, zero-padded to a
  *                    multiple of 16 bytes.  A value is code * scale.

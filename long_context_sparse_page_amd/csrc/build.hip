@@ -118,9 +118,12 @@ __device__ __forceinline__ void write_q4_record(const BuildArgs& a, int phys, in
   __syncthreads();
   uint8_t* rec = reinterpret_cast<uint8_t*>(a.summary) + ((size_t)phys * a.hkv + kvh) * L.bytes();
   for (int x = tid; x < D; x += kBuildThreads) rec[x] = (uint8_t)(int8_t)q4_code(sMu[x], sMs, 127.f);
+  // basis byte 4 g + b of a row holds dims 8 g + e and 8 g + e + 2 with
+  // e = 4 (b & 1) + (b >> 1): even dims in the low half-word, odd dims in the high
   for (int x = tid; x < R * D / 2; x += kBuildThreads) {
-    const int k = x / (D / 2), c = 2 * (x % (D / 2));
-    const int lo = q4_code(basis_at(k, c), sBs[k], 7.f), hi = q4_code(basis_at(k, c + 1), sBs[k], 7.f);
+    const int k = x / (D / 2), p = x % (D / 2);
+    const int c = 8 * (p >> 2) + 4 * (p & 1) + ((p >> 1) & 1);
+    const int lo = q4_code(basis_at(k, c), sBs[k], 7.f), hi = q4_code(basis_at(k, c + 2), sBs[k], 7.f);
     rec[L.basis() + x] = (uint8_t)((lo & 0xF) | ((hi & 0xF) << 4));
   }
   for (int x = tid; x < B * R; x += kBuildThreads)

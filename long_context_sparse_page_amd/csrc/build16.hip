@@ -473,8 +473,15 @@ __global__ __launch_bounds__(kB16Waves * kWave) void build16_kernel(BuildArgs a)
   for (int k = 0; k < R; ++k) {
     const float v0 = k < KEPT ? vb[k][0] : 0.f, v1 = k < KEPT ? vb[k][1] : 0.f;
     const float bs = b16_q_scale(group_max<kWave>(fmaxf(fabsf(v0), fabsf(v1))), 7.f);
+    // this lane holds dims 2 lane, 2 lane + 1; a basis byte takes dims 8 g + e
+    // and 8 g + e + 2 (even dims in a word's low half-word, odd in its high), so
+    // lanes 4 g + x pair with lane 4 g + (x ^ 1) and write byte 4 g + (x >> 1) +
+    // 2 (x & 1): the two low codes when x is even, the two high codes when odd
     const int lo = b16_q_code(v0, bs, 7.f), hi = b16_q_code(v1, bs, 7.f);
-    rec[L.basis() + k * (D / 2) + lane] = (uint8_t)((lo & 0xF) | ((hi & 0xF) << 4));
+    const int mine = (lo & 0xF) | ((hi & 0xF) << 4);
+    const int other = __builtin_amdgcn_mov_dpp(mine, kDppXor1, 0xf, 0xf, true);
+    const int byte = (lane & 1) ? ((other >> 4) | (mine & 0xF0)) : ((mine & 0xF) | ((other & 0xF) << 4));
+    rec[L.basis() + k * (D / 2) + 4 * (lane >> 2) + ((lane >> 1) & 1) + 2 * (lane & 1)] = (uint8_t)byte;
     if (lane == k) bsc_lane = bs;
   }
   if (lane < B) {

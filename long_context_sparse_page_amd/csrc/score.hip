@@ -593,19 +593,21 @@ __device__ __forceinline__ uint32_t bf16x2_of(float lo, float hi) {  // both exa
 }
 __device__ __forceinline__ float ubyte_f(uint32_t x, int b) { return (float)((x >> (8 * b)) & 0xffu); }
 
-// K-step operand of 8 int4 codes (one 32-bit word, element j in nibble j) as
-// bf16 values of code + 136: the biased code n = code + 8 (0..15) goes into
-// the low mantissa bits of bf16 128 (0x4300 | n is exactly 128 + n), one byte
-// permute and one OR per two codes.
+// K-step operand of 8 int4 codes as bf16 values of code + 136.  The record's
+// 32-bit word for 8 dims holds the even dims in its low half-word and the odd
+// dims in its high half-word (element 2 j in nibble j, element 2 j + 1 in
+// nibble j + 4), so (w >> 4 j) & 0x000f000f puts elements 2 j and 2 j + 1 in
+// the low mantissa bits of the two halves of dword j; XOR with 0x43084308
+// then sets bf16 128's exponent and flips the sign bit of the code
+// (two's complement c becomes n = c + 8, and 0x4300 | n is exactly 128 + n).
+// One shift and one three-input bit operation per two codes.
 constexpr float kQ4Bias = 136.f;
 __device__ __forceinline__ bf16x8_t q4_operand(uint32_t w) {
-  w ^= 0x88888888u;
-  const uint32_t even = w & 0x0f0f0f0fu, odd = (w >> 4) & 0x0f0f0f0fu;
-  uint4 o;  // dword j: [even byte j, 0, odd byte j, 0] | 0x43004300 = elements 2 j, 2 j + 1
-  o.x = __builtin_amdgcn_perm(odd, even, 0x0c040c00u) | 0x43004300u;
-  o.y = __builtin_amdgcn_perm(odd, even, 0x0c050c01u) | 0x43004300u;
-  o.z = __builtin_amdgcn_perm(odd, even, 0x0c060c02u) | 0x43004300u;
-  o.w = __builtin_amdgcn_perm(odd, even, 0x0c070c03u) | 0x43004300u;
+  uint4 o;
+  o.x = (w & 0x000f000fu) ^ 0x43084308u;
+  o.y = ((w >> 4) & 0x000f000fu) ^ 0x43084308u;
+  o.z = ((w >> 8) & 0x000f000fu) ^ 0x43084308u;
+  o.w = ((w >> 12) & 0x000f000fu) ^ 0x43084308u;
   return __builtin_bit_cast(bf16x8_t, o);
 }
 // K-step operand of 8 int8 codes (two 32-bit words) as bf16 values of code + 128.

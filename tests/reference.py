@@ -68,6 +68,13 @@ def q4_offsets(d: int, B: int, r: int) -> dict:
     return o
 
 
+# int4 basis rows, per group of 8 dims (one 32-bit word): byte b holds dim
+# Q4_LO_DIMS[b] in its low nibble and Q4_HI_DIMS[b] in its high nibble, i.e.
+# the even dims in the word's low half-word and the odd dims in its high one.
+Q4_LO_DIMS = [0, 4, 1, 5]
+Q4_HI_DIMS = [2, 6, 3, 7]
+
+
 def pack_q4_records(qs: lo.QuantSummary) -> np.ndarray:
     """uint8 [n, record bytes] of quantized summaries."""
     n, r, d = qs.basis_q.shape
@@ -75,8 +82,9 @@ def pack_q4_records(qs: lo.QuantSummary) -> np.ndarray:
     o = q4_offsets(d, B, r)
     out = np.zeros((n, o["bytes"]), dtype=np.uint8)
     out[:, :d] = qs.centroid_q.astype(np.int8).view(np.uint8)
-    lo4 = qs.basis_q[:, :, 0::2] & 0xF
-    hi4 = qs.basis_q[:, :, 1::2] & 0xF
+    words = qs.basis_q.reshape(n, r, d // 8, 8)
+    lo4 = words[..., Q4_LO_DIMS] & 0xF
+    hi4 = words[..., Q4_HI_DIMS] & 0xF
     out[:, o["basis"]:o["coef"]] = (lo4 | (hi4 << 4)).astype(np.uint8).reshape(n, -1)
     out[:, o["coef"]:o["cscale"]] = qs.coeffs_q.astype(np.int8).view(np.uint8).reshape(n, -1)
     out[:, o["cscale"]:o["bscale"]] = qs.coeffs_s.astype(np.float16).view(np.uint8).reshape(n, -1)
@@ -91,10 +99,11 @@ def unpack_q4_records(buf: np.ndarray, d: int, B: int, r: int) -> lo.QuantSummar
     n = buf.shape[0]
     o = q4_offsets(d, B, r)
     mq = buf[:, :d].view(np.int8).astype(np.int64)
-    packed = buf[:, o["basis"]:o["coef"]].reshape(n, r, d // 2).astype(np.int64)
-    bq = np.zeros((n, r, d), dtype=np.int64)
-    bq[:, :, 0::2] = ((packed & 0xF) ^ 8) - 8
-    bq[:, :, 1::2] = ((packed >> 4) ^ 8) - 8
+    packed = buf[:, o["basis"]:o["coef"]].reshape(n, r, d // 8, 4).astype(np.int64)
+    bq = np.zeros((n, r, d // 8, 8), dtype=np.int64)
+    bq[..., Q4_LO_DIMS] = ((packed & 0xF) ^ 8) - 8
+    bq[..., Q4_HI_DIMS] = ((packed >> 4) ^ 8) - 8
+    bq = bq.reshape(n, r, d)
     cq = buf[:, o["coef"]:o["cscale"]].view(np.int8).reshape(n, B, r).astype(np.int64)
     f16 = lambda a, b: np.ascontiguousarray(buf[:, a:b]).view(np.float16).astype(np.float64)
     return lo.QuantSummary(centroid_q=mq, centroid_s=f16(o["mscale"], o["mscale"] + 2)[:, 0],

@@ -63,6 +63,41 @@ def test_record_bytes_and_budget():
     assert L.lk_page_budget(cfg(token_budget=256)) == 4
 
 
+def test_q4_record_packing():
+    """The int4/int8 record the tests write and read is the one include/locks.h
+    documents: int8 centroid, then each basis row in 32-bit words of 8 dims with
+    dim 8 g + 2 j in nibble j and dim 8 g + 2 j + 1 in nibble j + 4 (two's
+    complement), int8 coefficients, fp16 scales; packing round-trips."""
+    import numpy as np
+    import sys
+    sys.path.insert(0, os.path.dirname(__file__))
+    import reference as ref
+    from oracle import locks_oracle as lo
+    rng = np.random.default_rng(7)
+    n, r, d, B = 3, 8, 128, 16
+    qs = lo.QuantSummary(centroid_q=rng.integers(-127, 128, (n, d)), centroid_s=rng.uniform(0.5, 2, n),
+                         basis_q=rng.integers(-7, 8, (n, r, d)), basis_s=rng.uniform(0.5, 2, (n, r)),
+                         coeffs_q=rng.integers(-127, 128, (n, B, r)), coeffs_s=rng.uniform(0.5, 2, (n, B)),
+                         eigvals=np.zeros((n, B)), r_eff=np.full(n, r))
+    qs.centroid_s, qs.basis_s, qs.coeffs_s = (lo.fp16_round(x) for x in (qs.centroid_s, qs.basis_s, qs.coeffs_s))
+    buf = ref.pack_q4_records(qs)
+    assert buf.shape == (n, L.lk_summary_record_bytes(cfg(page_size=16, summary_format=L.LK_SUMMARY_I4)))
+    o = ref.q4_offsets(d, B, r)
+    assert (buf[:, :d].view(np.int8) == qs.centroid_q).all()
+    w = buf[:, o["basis"]:o["coef"]].reshape(n, r, d // 8, 4).astype(np.uint32)
+    word = w[..., 0] | (w[..., 1] << 8) | (w[..., 2] << 16) | (w[..., 3] << 24)
+    dims = qs.basis_q.reshape(n, r, d // 8, 8)
+    for j in range(4):
+        assert (((word >> (4 * j)) & 0xF) == (dims[..., 2 * j] & 0xF)).all()
+        assert (((word >> (16 + 4 * j)) & 0xF) == (dims[..., 2 * j + 1] & 0xF)).all()
+    u = ref.unpack_q4_records(buf, d, B, r)
+    for a, b in [(u.centroid_q, qs.centroid_q), (u.basis_q, qs.basis_q), (u.coeffs_q, qs.coeffs_q),
+                 (u.centroid_s, qs.centroid_s), (u.basis_s, qs.basis_s), (u.coeffs_s, qs.coeffs_s)]:
+        assert (a == b).all()
+    text = open(HEADER).read()
+    assert "dim 8g+2j in nibble j" in text and "8g+2j+1 in nibble j+4" in text
+
+
 def test_page16_record_bytes_match_table_d10(golden_dir):
     """Quantized records at B = 16 hold Table D.10's logical payload (Locks App.
     D, "State accounting") plus the fp16 scales (B + r + 1 of them), padded to
