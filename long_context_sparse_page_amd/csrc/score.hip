@@ -416,23 +416,26 @@ __device__ __forceinline__ void group_lse(const float* P, float* Z, Coef coef, u
   }
 }
 
-// The same at B = 16: lane 16 q + t holds token t of record 4 p + q in pass p,
-// so each record's logits sit on one row of 16 lanes and its per-head LSE is
-// a row reduction; lane 16 q + g then writes head g.  coef(p, c, s) gives the
-// lane's coefficients of pass p and their scale.
+// The same at B = 16: lane 16 q + t holds token t of record 4 p + q in pass p
+// and forms its G logits; one transpose through LDS (Z[(q * G + g) * 16 + t])
+// then gives each (record, head) pair of the pass 16 / G lanes with G tokens
+// each, so a pair's LSE is G - 1 local steps and log2(16 / G) lane steps
+// instead of four lane steps per head; the first lane of a pair writes it.
+// coef(p, c, s) gives the lane's coefficients of pass p and their scale.
 template <int R, int G, int NR, bool SCALED, typename Coef>
-__device__ __forceinline__ void group_lse16(const float* P, Coef coef, uint32_t vbits, float* out,
+__device__ __forceinline__ void group_lse16(const float* P, float* Z, Coef coef, uint32_t vbits, float* out,
                                             int max_pages, int g0, int j_end, int lane, float zscale) {
   constexpr int ROWS = R + 1;
+  constexpr int LPP = 16 / G;  // lanes per (record, head) pair after the transpose
   const int q = lane >> 4, t = lane & 15;
+  const int pr = lane / LPP;             // pair of this lane: record 4 p + pr / G, head pr % G
+  const int t0 = (lane % LPP) * G;       // its first token
 #pragma unroll
   for (int p = 0; p < (NR + 3) / 4; ++p) {
-    const int r = 4 * p + q;
-    const int rc = min(r, NR - 1);
+    const int rc = min(4 * p + q, NR - 1);
     float c[R], cs;
     coef(p, c, cs);
     const float* Pr = P + rc * ROWS * G;
-    float res[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float acc;
@@ -446,18 +449,27 @@ __device__ __forceinline__ void group_lse16(const float* P, Coef coef, uint32_t 
 #pragma unroll
         for (int m = 0; m < R; ++m) acc = fmaf(c[m], Pr[(m + 1) * G + g], acc);
       }
-      const float z = acc * zscale;
-      const float mx = group_max<16>(z);
-      const float sum = group_sum<16>(fast_exp2(z - mx));
-      res[g] = (mx + fast_log2(sum)) * kLn2;
+      Z[(q * G + g) * 16 + t] = acc * zscale;
     }
-    float val = res[0];
+    wave_lds_fence();
+    float v[G];
+    float mx = -INFINITY;
 #pragma unroll
-    for (int g = 1; g < G; ++g)
-      if (t == g) val = res[g];
-    const bool ok = (vbits >> rc) & 1u;
+    for (int i = 0; i < G; ++i) {
+      v[i] = Z[pr * 16 + t0 + i];
+      mx = vmax(mx, v[i]);
+    }
+    mx = group_max<LPP>(mx);
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < G; ++i) sum += fast_exp2(v[i] - mx);
+    sum = group_sum<LPP>(sum);
+    const int r = 4 * p + pr / G, g = pr % G;
     const int j = g0 + r;
-    if (t < G && r < NR && j < j_end) out[(size_t)t * max_pages + j] = ok ? val : -INFINITY;
+    if (lane % LPP == 0 && r < NR && j < j_end)
+      out[(size_t)g * max_pages + j] = ((vbits >> r) & 1u) ? (mx + fast_log2(sum)) * kLn2 : -INFINITY;
+    if (4 * (p + 1) < NR) wave_lds_fence();  // Z is rewritten by the next pass
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -472,7 +484,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_mfma_kernel(ScoreAr
 
   __shared__ float sP[kScoreWaves][SLOTS * G];
   constexpr int RC = (16 / G) < NR ? (16 / G) : NR;  // records per LDS transpose (RC * G <= 16)
-  __shared__ float sZ[kScoreWaves][B == 64 ? RC * G * B : 1];
+  __shared__ float sZ[kScoreWaves][B == 64 ? RC * G * B : 4 * G * 16];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform: scalar table loads
@@ -546,7 +558,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_mfma_kernel(ScoreAr
       cs = 1.f;
     };
     if constexpr (B == 64) group_lse<R, G, NR, false>(P, Z, coef, cur.vbits, out, a.max_pages, g0, j_end, lane, zscale);
-    else group_lse16<R, G, NR, false>(P, coef, cur.vbits, out, a.max_pages, g0, j_end, lane, zscale);
+    else group_lse16<R, G, NR, false>(P, Z, coef, cur.vbits, out, a.max_pages, g0, j_end, lane, zscale);
   }
 }
 
@@ -637,7 +649,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
 
   __shared__ float sP[kScoreWaves][SLOTS * G];
   constexpr int RC = (16 / G) < NR ? (16 / G) : NR;
-  __shared__ float sZ[kScoreWaves][B == 64 ? RC * G * B : 1];
+  __shared__ float sZ[kScoreWaves][B == 64 ? RC * G * B : 4 * G * 16];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -790,7 +802,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
     cs = half_bits_f(csc[r]);
   };
   if constexpr (B == 64) group_lse<R, G, NR, true>(P, Z, coef, vbits, out, a.max_pages, j0, j_end, lane, zscale);
-  else group_lse16<R, G, NR, true>(P, coef, vbits, out, a.max_pages, j0, j_end, lane, zscale);
+  else group_lse16<R, G, NR, true>(P, Z, coef, vbits, out, a.max_pages, j0, j_end, lane, zscale);
 }
 
 template <int R, int B>
