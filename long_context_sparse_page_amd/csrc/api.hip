@@ -249,12 +249,12 @@ lk_status enqueue_decode_step(const Shape& sh, const lk_config* cfg, const lk_ca
   lk::SelectArgs se{page_lse, nullptr, sel_pages, sel_count, cache->seq_lens, batch, cache->max_pages_per_seq,
                     sh.hkv, sh.G, sh.B, sh.k, 1, cache->block_table, nullptr, cache->num_phys_pages};
   const bool fused = lk::select_attn_fusable(se);
-  int n_merge = fused ? lk::select_attn_splits(sh.k) : lk::list_attn_splits(sh.k, sh.B);  // the attention's splits
+  int n_merge = fused ? lk::select_attn_splits(sh.k, sh.B) : lk::list_attn_splits(sh.k, sh.B);  // the attention's splits
   if (fused) {
     lk::AttnArgs aa{q, cache->k_pool, cache->v_pool, cache->block_table, cache->seq_lens, nullptr, nullptr, nullptr,
                     at<float>(ws, L.part_o), at<float>(ws, L.part_ml), out, lse_out,
                     batch, cache->max_pages_per_seq, cache->num_phys_pages, sh.hkv, sh.hq, sh.k,
-                    n_merge, 1, cfg->scale, 1};
+                    n_merge, 1, cfg->scale, 1, sh.B};
     st = hip_status(lk::launch_select_attn(sh.dt, se, aa, s), "selection + attention launch");
     if (st != LK_OK) return st;
   } else {

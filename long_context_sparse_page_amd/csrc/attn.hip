@@ -551,37 +551,42 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs
 // Decode step: selection and attention in one launch.
 //
 // Workgroup = 8 waves per (split, KV head, sequence); wave w of split s
-// attends unit 8 s + w of the selection list (half page (8 s + w) & 1 of list
-// entry (8 s + w) >> 1).  Every workgroup of a (sequence, KV head) computes
-// that pair's selection itself (the same selection as select_block: the
-// sink, the most recent page and the top k - 2 candidates by m_bar, ties to
-// the lower page index, in page order), with three barriers:
+// attends unit u = 8 s + w of the selection list: half u & 1 of list entry
+// u >> 1 (64-token pages), or list entries 2u and 2u + 1 (16-token pages).
+// Every workgroup of a (sequence, KV head) computes that pair's selection
+// itself (the same selection as select_block: the sink, the most recent page
+// and the top k - 2 candidates by m_bar, ties to the lower page index, in
+// page order), with three barriers:
 //  1. per-head normalizers (thread t holds pages (8 NPT (t / 64) + 64 i)
 //     + t % 64, i < NPT: each wave owns a contiguous page range);
 //  2. ranking keys; each thread's largest key goes to LDS;
 //  3. every wave finds the same pivot (the (k-2)-th largest of the maxima of
-//     groups of 8 threads; at least k-2 keys reach it) and appends its keys
+//     groups of 8 threads when there are enough groups, else of the
+//     threads' maxima; at least k-2 keys reach it) and appends its keys
 //     >= pivot to its own LDS list, in page order.
 // Then every wave reads the concatenated lists (page order), finds the exact
-// cut by bisection on ballot counts (up to 2 keys per lane) and takes its own
-// unit's page from the lane that holds it: no further barrier before the
-// K/V loads.  More than 128 keys at the pivot (massive ties) fall back to
+// cut by bisection on ballot counts (CR keys per lane) and takes its unit's
+// pages from the lanes that hold them: no further barrier before the K/V
+// loads.  More than CR * 64 keys at the pivot (massive ties) fall back to
 // select_block over LDS.
 constexpr int kFusedWaves = 8;
 constexpr int kFusedThreads = kFusedWaves * kWave;
-constexpr int kFusedCap = 2 * kWave;  // list entries the exact cut holds in registers
 
-template <typename T, int NPT, int G>
+template <typename T, int NPT, int G, int B, int CR>
 __global__ __launch_bounds__(kFusedThreads) void select_attn_kernel(SelectArgs se, AttnArgs a) {
-  constexpr int B = 64;
   constexpr int BS = kFusedThreads;
   constexpr int NW = kFusedWaves;
   constexpr int TR = BS / kWave;  // threads per pivot group
+  constexpr int CAP = CR * kWave;  // list entries the exact cut holds in registers
+  // 2^(s2 - m) of every page stays in registers from the normalizer pass to
+  // the keys when it fits; else the keys take it again
+  constexpr bool kKeepE = G * NPT <= 48;
+  static_assert(B == 64 || B == 16, "page size");
   __shared__ float s_pm[G][NW], s_ps[G][NW];
   __shared__ uint32_t s_tmax[BS];
-  __shared__ uint32_t s_ck[NW][kFusedCap];
-  __shared__ int32_t s_cp[NW][kFusedCap];
-  __shared__ int32_t s_cph[NW][kFusedCap];
+  __shared__ uint32_t s_ck[NW][CAP];
+  __shared__ int32_t s_cp[NW][CAP];
+  __shared__ int32_t s_cph[NW][CAP];
   __shared__ int32_t s_wc[NW];
   __shared__ int32_t s_fix[2];
   __shared__ int32_t s_sel[kMaxSelect], s_selp[kMaxSelect];  // fallback selection
@@ -626,19 +631,24 @@ __global__ __launch_bounds__(kFusedThreads) void select_attn_kernel(SelectArgs s
   const int n_cand = n_mr > 0 ? n_mr - 1 : 0;
   const int n_top = min(k - 2, n_cand);
   const int unit = split * NW + wave;  // this wave's unit of the selection list
-  const int x = unit >> 1;             // its list entry
-  int cnt = 0, pg = -1, phys = -1;
+  // its list entries: x (and x1 at 16-token pages)
+  const int x = B == 64 ? unit >> 1 : 2 * unit;
+  const int x1 = 2 * unit + 1;
+  int cnt = 0, pg = -1, phys = -1, pg1 = -1, phys1 = -1;
   int mode = 0;  // 0: no page or every page, 1: fixed pages + list in registers, 2: fallback in LDS
-  uint32_t ck[2] = {0u, 0u};
-  int cpg[2] = {-1, -1}, cph[2] = {-1, -1}, slot[2] = {0, 0};
-  bool taken[2] = {false, false};
+  uint32_t ck[CR];
+  int cpg[CR], cph[CR], slot[CR];
+  bool taken[CR];
+#pragma unroll
+  for (int r = 0; r < CR; ++r) { ck[r] = 0u; cpg[r] = -1; cph[r] = -1; slot[r] = 0; taken[r] = false; }
 
   if (len > 0 && n_top == n_cand) {  // every page 0 .. n_mr is selected
     cnt = n_mr + 1;
     if (x <= n_mr) { pg = x; phys = bt[x]; }
+    if (B == 16 && x1 <= n_mr) { pg1 = x1; phys1 = bt[x1]; }
   } else if (len > 0) {
     // 1) per-head normalizers M_g, S_g (scores in log2 units)
-    float mg[G], sl[G], E[G][NPT];
+    float mg[G], sl[G], E[G][kKeepE ? NPT : 1];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       mg[g] = -INFINITY;
@@ -650,8 +660,9 @@ __global__ __launch_bounds__(kFusedThreads) void select_attn_kernel(SelectArgs s
       sl[g] = 0.f;
 #pragma unroll
       for (int i = 0; i < NPT; ++i) {
-        E[g][i] = mg[g] == -INFINITY ? 0.f : fast_exp2(v[g][i] - mg[g]);
-        sl[g] += E[g][i];
+        const float ex = mg[g] == -INFINITY ? 0.f : fast_exp2(v[g][i] - mg[g]);
+        if constexpr (kKeepE) E[g][i] = ex;
+        sl[g] += ex;
       }
     }
 #pragma unroll
@@ -693,7 +704,11 @@ __global__ __launch_bounds__(kFusedThreads) void select_attn_kernel(SelectArgs s
       if (j < 1 || j >= n_mr) continue;
       float xg[G], eg[G];
 #pragma unroll
-      for (int g = 0; g < G; ++g) { xg[g] = v[g][i]; eg[g] = E[g][i]; }
+      for (int g = 0; g < G; ++g) {
+        xg[g] = v[g][i];
+        if constexpr (kKeepE) eg[g] = E[g][i];
+        else eg[g] = mg[g] == -INFINITY ? 0.f : fast_exp2(v[g][i] - mg[g]);
+      }
       float mb;
       key[i] = order_key(share_log2<G>(xg, eg, scale, Mg, log2S, invG, log2G, mb));
       tmax = max(tmax, key[i]);
@@ -728,7 +743,7 @@ __global__ __launch_bounds__(kFusedThreads) void select_attn_kernel(SelectArgs s
         const bool c = key[i] >= piv && key[i] != 0u;
         const uint64_t bm = __ballot(c);
         const int pos = wc + lanes_below(bm);
-        if (c && pos < kFusedCap) {
+        if (c && pos < CAP) {
           s_ck[wave][pos] = key[i];
           s_cp[wave][pos] = page(i);
           s_cph[wave][pos] = ph[i];
@@ -742,11 +757,11 @@ __global__ __launch_bounds__(kFusedThreads) void select_attn_kernel(SelectArgs s
 #pragma unroll
       for (int w = 0; w < NW; ++w) off[w + 1] = off[w] + s_wc[w];
       const int C = off[NW];
-      if (C <= kFusedCap) {
+      if (C <= CAP) {
         // exact cut over the concatenated lists (entry lane + 64 r)
         mode = 1;
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
+        for (int r = 0; r < CR; ++r) {
           const int en = lane + kWave * r;
           if (en < C) {
             int w = 0, base = 0;
@@ -758,14 +773,14 @@ __global__ __launch_bounds__(kFusedThreads) void select_attn_kernel(SelectArgs s
             cph[r] = s_cph[w][en - base];
           }
         }
-        const uint32_t t = wave_nth_largest<2>(ck, n_top);
+        const uint32_t t = wave_nth_largest<CR>(ck, n_top);
         int n_gt = 0;
 #pragma unroll
-        for (int r = 0; r < 2; ++r) n_gt += __popcll(__ballot(ck[r] > t));
+        for (int r = 0; r < CR; ++r) n_gt += __popcll(__ballot(ck[r] > t));
         const int take_eq = n_top - n_gt;
         int eq_before = 0, out_before = 0;
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
+        for (int r = 0; r < CR; ++r) {
           const bool eq = ck[r] == t;
           const uint64_t be = __ballot(eq);
           taken[r] = ck[r] > t || (eq && eq_before + lanes_below(be) < take_eq);
@@ -774,23 +789,29 @@ __global__ __launch_bounds__(kFusedThreads) void select_attn_kernel(SelectArgs s
           slot[r] = 1 + out_before + lanes_below(bs);
           out_before += __popcll(bs);
         }
-        if (x == 0) {
-          pg = 0;
-          phys = s_fix[0];
-        } else if (x <= n_top) {
+        // list entry xx: the sink, a taken candidate (from the lane that
+        // holds it) or the most recent page
+        auto entry = [&](int xx, int& p, int& f) {
+          if (xx == 0) {
+            p = 0;
+            f = s_fix[0];
+          } else if (xx <= n_top) {
 #pragma unroll
-          for (int r = 0; r < 2; ++r) {
-            const uint64_t mm = __ballot(taken[r] && slot[r] == x);
-            if (mm) {
-              const int src = __ffsll((unsigned long long)mm) - 1;
-              pg = __builtin_amdgcn_readlane(cpg[r], src);
-              phys = __builtin_amdgcn_readlane(cph[r], src);
+            for (int r = 0; r < CR; ++r) {
+              const uint64_t mm = __ballot(taken[r] && slot[r] == xx);
+              if (mm) {
+                const int src = __ffsll((unsigned long long)mm) - 1;
+                p = __builtin_amdgcn_readlane(cpg[r], src);
+                f = __builtin_amdgcn_readlane(cph[r], src);
+              }
             }
+          } else if (xx == n_top + 1) {
+            p = n_mr;
+            f = s_fix[1];
           }
-        } else if (x == n_top + 1) {
-          pg = n_mr;
-          phys = s_fix[1];
-        }
+        };
+        entry(x, pg, phys);
+        if constexpr (B == 16) entry(x1, pg1, phys1);
       } else {
         // massive ties at the pivot: the general selection over LDS
         mode = 2;
@@ -798,11 +819,13 @@ __global__ __launch_bounds__(kFusedThreads) void select_attn_kernel(SelectArgs s
         __syncthreads();
         cnt = s_cnt;
         if (x < cnt) { pg = s_sel[x]; phys = s_selp[x]; }
+        if (B == 16 && x1 < cnt) { pg1 = s_sel[x1]; phys1 = s_selp[x1]; }
       }
     } else {  // k = 2: the sink and the most recent page
       mode = 1;
       if (x == 0) { pg = 0; phys = s_fix[0]; }
       else if (x == 1) { pg = n_mr; phys = s_fix[1]; }
+      if (B == 16 && x1 == 1) { pg1 = n_mr; phys1 = s_fix[1]; }
     }
   }
 
@@ -824,7 +847,7 @@ __global__ __launch_bounds__(kFusedThreads) void select_attn_kernel(SelectArgs s
     } else {
       if (wave == 0) {
 #pragma unroll
-        for (int r = 0; r < 2; ++r)
+        for (int r = 0; r < CR; ++r)
           if (taken[r]) {
             so[slot[r]] = cpg[r];
             if (sp) sp[slot[r]] = valid_phys(cph[r]);
@@ -853,11 +876,21 @@ __global__ __launch_bounds__(kFusedThreads) void select_attn_kernel(SelectArgs s
     for (int i = 0; i < 16; ++i) o[g][i] = 0.f;
   }
   if (x < cnt && pg >= 0 && pg <= n_mr && phys >= 0 && phys < a.num_phys) {
-    const int half = unit & 1;
     KV16<T> kr[kAttnTPG], vr[kAttnTPG];
-    issue_unit<T>(a, kvh, phys, half, sg, e, kr, vr);
-    const int n_tok = ((pg == n_mr) ? len - n_mr * B : B) - half * kAttnHalf;
-    if (n_tok > 0) attend_unit<T, G>(q, kr, vr, n_tok, sg, a.scale * kLog2e, m, l, o);
+    if constexpr (B == 64) {
+      const int half = unit & 1;
+      issue_unit<T>(a, kvh, phys, half, sg, e, kr, vr);
+      const int n_tok = ((pg == n_mr) ? len - n_mr * B : B) - half * kAttnHalf;
+      if (n_tok > 0) attend_unit<T, G>(q, kr, vr, n_tok, sg, a.scale * kLog2e, m, l, o);
+    } else {
+      // the unit's first page whole (or its filled part when it is the most
+      // recent page, the last entry), then the second when present
+      const bool has1 = pg != n_mr && x1 < cnt && pg1 >= 0 && pg1 <= n_mr && phys1 >= 0 && phys1 < a.num_phys;
+      issue_unit16<T>(a, kvh, phys, has1 ? phys1 : phys, sg, e, kr, vr);
+      int n_tok = pg == n_mr ? len - n_mr * B : B;
+      if (has1) n_tok += pg1 == n_mr ? len - n_mr * B : B;
+      attend_unit<T, G>(q, kr, vr, n_tok, sg, a.scale * kLog2e, m, l, o);
+    }
   }
   combine_write<G, NW>(a, pair * a.n_splits + split, wave, lane, m, l, o);
 }
@@ -953,41 +986,70 @@ hipError_t launch_attn(DType dt, int group, const AttnArgs& a, bool merge, hipSt
   return dt == kBF16 ? launch_attn_t<bf16_t>(group, a, merge, s) : launch_attn_t<float>(group, a, merge, s);
 }
 
-template <typename T, int NPT>
+template <typename T, int NPT, int B, int CR>
 static hipError_t launch_select_attn_n(const SelectArgs& se, const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.n_splits * a.hkv * a.batch);
   dim3 block(kFusedThreads);
   switch (se.group) {
-    case 1: hipLaunchKernelGGL((select_attn_kernel<T, NPT, 1>), grid, block, 0, s, se, a); break;
-    case 2: hipLaunchKernelGGL((select_attn_kernel<T, NPT, 2>), grid, block, 0, s, se, a); break;
-    case 4: hipLaunchKernelGGL((select_attn_kernel<T, NPT, 4>), grid, block, 0, s, se, a); break;
+    case 1: hipLaunchKernelGGL((select_attn_kernel<T, NPT, 1, B, CR>), grid, block, 0, s, se, a); break;
+    case 2: hipLaunchKernelGGL((select_attn_kernel<T, NPT, 2, B, CR>), grid, block, 0, s, se, a); break;
+    case 4: hipLaunchKernelGGL((select_attn_kernel<T, NPT, 4, B, CR>), grid, block, 0, s, se, a); break;
     default: return hipErrorInvalidValue;  // G = 8 keeps the two launches (registers)
   }
   return hipGetLastError();
 }
 
-template <typename T>
-static hipError_t launch_select_attn_t(const SelectArgs& se, const AttnArgs& a, hipStream_t s) {
+// Tiers of pages per thread: 64-token pages up to 3,072 pages per sequence,
+// 16-token pages up to 8,704.
+constexpr int kFusedMaxPages64 = kFusedThreads * 6;
+constexpr int kFusedMaxPages16 = kFusedThreads * 17;
+
+template <typename T, int B, int CR>
+static hipError_t launch_select_attn_b(const SelectArgs& se, const AttnArgs& a, hipStream_t s) {
   const int n = se.max_pages;
-  if (n <= kFusedThreads * 2) return launch_select_attn_n<T, 2>(se, a, s);
-  if (n <= kFusedThreads * 4) return launch_select_attn_n<T, 4>(se, a, s);
-  if (n <= kFusedThreads * 5) return launch_select_attn_n<T, 5>(se, a, s);
-  if (n <= kFusedThreads * 6) return launch_select_attn_n<T, 6>(se, a, s);
+  if constexpr (B == 64) {
+    if (n <= kFusedThreads * 2) return launch_select_attn_n<T, 2, B, CR>(se, a, s);
+    if (n <= kFusedThreads * 4) return launch_select_attn_n<T, 4, B, CR>(se, a, s);
+    if (n <= kFusedThreads * 5) return launch_select_attn_n<T, 5, B, CR>(se, a, s);
+    if (n <= kFusedThreads * 6) return launch_select_attn_n<T, 6, B, CR>(se, a, s);
+  } else {
+    if (n <= kFusedThreads * 6) return launch_select_attn_n<T, 6, B, CR>(se, a, s);
+    if (n <= kFusedThreads * 12) return launch_select_attn_n<T, 12, B, CR>(se, a, s);
+    if (n <= kFusedThreads * 17) return launch_select_attn_n<T, 17, B, CR>(se, a, s);
+  }
   return hipErrorNotSupported;
 }
 
-bool select_attn_fusable(const SelectArgs& se) {
-  return se.max_pages <= kFusedThreads * 6 && se.k <= kMaxSelect && se.group <= 4 && se.page_size == 64 &&
-         se.share_out == nullptr;
+// List entries per lane of the exact cut: twice the candidates kept, rounded
+// up to lanes (the keys at or above the pivot are typically a few more than
+// k - 2); 64-token pages keep two (more keys at the pivot take the fallback).
+static int fused_list_regs(const SelectArgs& se) {
+  if (se.page_size == 64) return 2;
+  return 2 * (se.k - 2) <= 2 * kWave ? 2 : (2 * (se.k - 2) <= 4 * kWave ? 4 : 0);
 }
 
-int select_attn_splits(int k) { return (2 * k + kFusedWaves - 1) / kFusedWaves; }
+bool select_attn_fusable(const SelectArgs& se) {
+  if (se.group > 4 || se.share_out != nullptr || se.k > kMaxSelect) return false;
+  if (se.page_size == 64) return se.max_pages <= kFusedMaxPages64;
+  return se.page_size == 16 && se.max_pages <= kFusedMaxPages16 && fused_list_regs(se) > 0;
+}
+
+int select_attn_splits(int k, int page_size) {
+  const int units = page_size == 64 ? 2 * k : (k + 1) / 2;
+  return (units + kFusedWaves - 1) / kFusedWaves;
+}
 
 hipError_t launch_select_attn(DType dt, const SelectArgs& se, const AttnArgs& a, hipStream_t s) {
   if (!select_attn_fusable(se)) return hipErrorNotSupported;
-  if (se.seq_lens != a.seq_lens || a.n_splits != select_attn_splits(se.k) || a.page_size != 64)
+  if (se.seq_lens != a.seq_lens || a.page_size != se.page_size ||
+      a.n_splits != select_attn_splits(se.k, se.page_size))
     return hipErrorInvalidValue;
-  return dt == kBF16 ? launch_select_attn_t<bf16_t>(se, a, s) : launch_select_attn_t<float>(se, a, s);
+  const bool bf = dt == kBF16;
+  if (se.page_size == 64)
+    return bf ? launch_select_attn_b<bf16_t, 64, 2>(se, a, s) : launch_select_attn_b<float, 64, 2>(se, a, s);
+  if (fused_list_regs(se) == 2)
+    return bf ? launch_select_attn_b<bf16_t, 16, 2>(se, a, s) : launch_select_attn_b<float, 16, 2>(se, a, s);
+  return bf ? launch_select_attn_b<bf16_t, 16, 4>(se, a, s) : launch_select_attn_b<float, 16, 4>(se, a, s);
 }
 
 

@@ -149,9 +149,10 @@ hipError_t launch_build(DType dt, int rank, const BuildArgs& a, hipStream_t s);
 // and length commit set) wave (seq, kvh) first merges and commits as above
 hipError_t launch_build16(DType dt, int rank, const BuildArgs& a, hipStream_t s);
 // Decode step: selection (se) and attention splits (a) in one launch, for
-// tables of up to 3072 pages per sequence (select_attn_fusable).
+// tables of up to 3,072 pages per sequence at 64-token pages and 8,704 at
+// 16-token pages, G <= 4 (select_attn_fusable).
 bool select_attn_fusable(const SelectArgs& se);
-int select_attn_splits(int k);  // attention splits of the fused launch
+int select_attn_splits(int k, int page_size);  // attention splits of the fused launch
 hipError_t launch_select_attn(DType dt, const SelectArgs& se, const AttnArgs& a, hipStream_t s);
 // Decode step with the chunked selection: attention over the selection merged
 // from the chunk lists (launch_select_lists) by every attention wave; split 0

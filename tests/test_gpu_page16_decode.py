@@ -227,15 +227,18 @@ def test_page16_dense_attention(gpu):
     say("page16 dense: max rel L2", worst)
 
 
-@pytest.mark.parametrize("summary,budget", [("kv", 512), ("i4", 1024)])
-def test_page16_chunked_selection(gpu, summary, budget):
-    """A wide 16-token table (5,000 pages) with one (sequence, KV head) pair:
-    the chunked selection with its merge launch, then the split attention,
-    in lk_score_select and in the decode step."""
+@pytest.mark.parametrize("summary,budget,cap", [("kv", 512, 5000), ("i4", 1024, 5000), ("kv", 2048, 5000),
+                                                ("i4", 2048, 9000)])
+def test_page16_chunked_selection(gpu, summary, budget, cap):
+    """A wide 16-token table (5,000 or 9,000 pages) with one (sequence, KV
+    head) pair: the chunked selection with its merge launch, then the split
+    attention, in lk_score_select; the decode step selects and attends in one
+    launch up to 8,704 pages (lists of 128 or 256 entries at budgets of 32 and
+    128 pages), and beyond through the chunk lists."""
     T = 16 * 4500 + 6
     w = page16(wid=1, batch=1, ctx=(T,), budget=budget, summary=summary, hq=4, hkv=1, steps=1)
-    say("page16 chunked selection:", summary, "T", T, "budget", budget)
-    dc = DeviceCache(w, poison=True, capacity_pages=[5000])
+    say("page16 chunked selection:", summary, "T", T, "budget", budget, "table", cap)
+    dc = DeviceCache(w, poison=True, capacity_pages=[cap])
     dc.fill_from_synth()
     dc.build_all()
     q64 = ref.host_queries(w, 0, [T])
