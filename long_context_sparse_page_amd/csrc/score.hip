@@ -255,6 +255,12 @@ __device__ __forceinline__ int pick_uniform(const int (&v)[N], int x) {
   return r;
 }
 
+// The physical page of record r of a wave's group for a lane-dependent r, at
+// 16-token pages: lane x < NR of `mine` holds record x's page (clamped into
+// the pool), and the cross-lane permute reads it from lane r: one
+// instruction in place of a compare-and-select per record.
+__device__ __forceinline__ int lane_page(int mine, int r) { return __builtin_amdgcn_ds_bpermute(r << 2, mine); }
+
 // Every load is unconditional, so the compiler keeps them in one batch with no
 // wait in between: a record that is not in the pool is read from physical
 // page 0 instead (always allocated) and its result discarded, and B columns
@@ -592,12 +598,12 @@ static hipError_t launch_score_mfma(int group, const ScoreArgs& a, hipStream_t s
 // the same mapping).  Codes are converted biased (int4 + 8, int8 + 128: plain
 // byte-to-float conversions) and the bias is removed from the products,
 // sum_c q_c code_c = sum_c q_c (code_c + bias) - bias * S_g with S_g = sum_c q_c.
-// Tiles: one tile of the NR centroids, whose column NR is a column of ones
-// (its products are the S_g), then NR * R / 16 tiles of basis rows (column =
-// record * R + row).  The reconstruction and LSE are those of the
+// Tiles: one tile of the NR centroids, and beside it the product of the
+// queries with an all-ones operand (every column holds the S_g), then
+// NR * R / 16 tiles of basis rows (column = record * R + row).  The reconstruction and LSE are those of the
 // bf16 records, with the per-token coefficient scale.
 template <int R, int B = 64> struct Q4Group {
-  // records per wave (the centroid tile holds NR centroids and a column of ones)
+  // records per wave (the centroid tile holds the NR centroids)
   static constexpr int NR = B == 64 ? (R >= 16 ? 2 : (R >= 8 ? 4 : 8)) : (R >= 16 ? 4 : 8);
   static constexpr int BT = NR * R / 16;                       // basis tiles
   static constexpr int SLOTS = NR * (R + 1);
@@ -678,7 +684,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
   // once (as for bf16 records).
   int phys_all[NR];
 #pragma unroll
-  for (int x = 0; x < NR; ++x) phys_all[x] = bt[min(j0 + x, a.max_pages - 1)];
+  for (int x = 0; x < NR; ++x) phys_all[x] = __builtin_amdgcn_readfirstlane(bt[min(j0 + x, a.max_pages - 1)]);
   const int len_raw = a.seq_lens[seq] + a.len_add;
   uint4 qw[4];  // query min(col, G - 1), dims 32 kg .. 32 kg + 31
   {
@@ -690,9 +696,15 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
   int n_scored = len_raw <= 0 ? 0 : (len_raw - 1) / B;
   if (n_scored > a.max_pages - 1) n_scored = a.max_pages - 1;
   if (j0 >= n_scored) return;
-  auto rec_of = [&](int phys) {
-    return summ + ((size_t)((phys >= 0 && phys < a.num_phys) ? phys : 0) * a.hkv + kvh) * REC;
-  };
+  // 16-token pages: lane x < NR holds record x's physical page (clamped)
+  int mine = 0;
+  if constexpr (B == 16) {
+    mine = bt[min(j0 + min(lane, NR - 1), a.max_pages - 1)];
+    mine = (mine >= 0 && mine < a.num_phys) ? mine : 0;
+  }
+  const uint8_t* summ_h = summ + (size_t)kvh * REC;
+  const size_t rec_stride = (size_t)a.hkv * REC;
+  auto rec_of_lane = [&](int r) { return summ_h + (size_t)(uint32_t)lane_page(mine, r) * rec_stride; };
   uint32_t vbits = 0u;  // bit r: record r present in the pool
   const uint8_t* recp[NR];
 #pragma unroll
@@ -723,7 +735,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
 #pragma unroll
       for (int x = 1; x < NR; ++x) if (x == r) rp = recp[x];
     } else {
-      rp = rec_of(pick_uniform<0, NR>(phys_all, r));
+      rp = rec_of_lane(r);
     }
     wm[0] = *reinterpret_cast<const uint4*>(rp + 32 * kg);
     wm[1] = *reinterpret_cast<const uint4*>(rp + 32 * kg + 16);
@@ -733,7 +745,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
   uint32_t csc[CSETS];              // and their scale (fp16 bits)
 #pragma unroll
   for (int r = 0; r < CSETS; ++r) {
-    const uint8_t* rp = B == 64 ? recp[r] : rec_of(pick_uniform<0, NR>(phys_all, min(4 * r + (lane >> 4), NR - 1)));
+    const uint8_t* rp = B == 64 ? recp[r] : rec_of_lane(min(4 * r + (lane >> 4), NR - 1));
     const int tok = B == 64 ? lane : (lane & 15);
     const uint8_t* cp = rp + L.coef() + (size_t)tok * R;
     if constexpr (R == 16) {
@@ -758,24 +770,21 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_q4_kernel(ScoreArgs
 #pragma unroll
   for (int t = 0; t < 4; ++t) qa[t] = __builtin_bit_cast(bf16x8_t, qw[t]);
 
-  // centroid tile first: columns 0 .. NR-1 are the centroids, column NR is a
-  // column of ones, whose products are S_g = sum of query g over all dims
+  // centroid tile first: columns 0 .. NR-1 are the centroids; a second
+  // product with an all-ones operand holds S_g = sum of query g over all dims
+  // in every column
   float Sg[4];  // S of the queries whose products this lane holds (rows 4 kg + i)
   {
     const uint32_t w[8] = {wm[0].x, wm[0].y, wm[0].z, wm[0].w, wm[1].x, wm[1].y, wm[1].z, wm[1].w};
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, accs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      bf16x8_t op = q8_operand(w[2 * t], w[2 * t + 1]);
-      if (col == NR) op = __builtin_bit_cast(bf16x8_t, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], op, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], q8_operand(w[2 * t], w[2 * t + 1]), acc, 0, 0, 0);
+      accs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[t], ones, accs, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float s0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc[i]), NR));       // rows i
-      const float s1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc[i]), 16 + NR));  // rows 4 + i
-      Sg[i] = kg ? s1 : s0;
-    }
+    for (int i = 0; i < 4; ++i) Sg[i] = accs[i];
     const float sc = half_bits_f(msc);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
