@@ -562,8 +562,9 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_split_kernel(AttnArgs
 //  2. ranking keys; each thread's largest key goes to LDS;
 //  3. every wave finds the same pivot (the (k-2)-th largest of the maxima of
 //     groups of 8 threads when there are enough groups, else of the
-//     threads' maxima; at least k-2 keys reach it) and appends its keys
-//     >= pivot to its own LDS list, in page order.
+//     threads' maxima, with the key bits below 16 left clear; at least k-2
+//     keys reach it) and appends its keys >= pivot to its own LDS list, in
+//     page order.
 // Then every wave reads the concatenated lists (page order), finds the exact
 // cut by bisection on ballot counts (CR keys per lane) and takes its unit's
 // pages from the lanes that hold them: no further barrier before the K/V
@@ -578,9 +579,6 @@ __global__ __launch_bounds__(kFusedThreads) void select_attn_kernel(SelectArgs s
   constexpr int NW = kFusedWaves;
   constexpr int TR = BS / kWave;  // threads per pivot group
   constexpr int CAP = CR * kWave;  // list entries the exact cut holds in registers
-  // 2^(s2 - m) of every page stays in registers from the normalizer pass to
-  // the keys when it fits; else the keys take it again
-  constexpr bool kKeepE = G * NPT <= 48;
   static_assert(B == 64 || B == 16, "page size");
   __shared__ float s_pm[G][NW], s_ps[G][NW];
   __shared__ uint32_t s_tmax[BS];
@@ -591,6 +589,7 @@ __global__ __launch_bounds__(kFusedThreads) void select_attn_kernel(SelectArgs s
   __shared__ int32_t s_fix[2];
   __shared__ int32_t s_sel[kMaxSelect], s_selp[kMaxSelect];  // fallback selection
   __shared__ int32_t s_cnt;
+  __shared__ uint32_t s_piv;
 
   // 1-D grid, XCD-aware: the splits of a (sequence, KV head), which all read
   // its page scores and block table, are logically adjacent and share an L2
@@ -635,20 +634,16 @@ __global__ __launch_bounds__(kFusedThreads) void select_attn_kernel(SelectArgs s
   const int x = B == 64 ? unit >> 1 : 2 * unit;
   const int x1 = 2 * unit + 1;
   int cnt = 0, pg = -1, phys = -1, pg1 = -1, phys1 = -1;
-  int mode = 0;  // 0: no page or every page, 1: fixed pages + list in registers, 2: fallback in LDS
-  uint32_t ck[CR];
-  int cpg[CR], cph[CR], slot[CR];
-  bool taken[CR];
-#pragma unroll
-  for (int r = 0; r < CR; ++r) { ck[r] = 0u; cpg[r] = -1; cph[r] = -1; slot[r] = 0; taken[r] = false; }
+  int mode = 0;  // 0: no page or every page, 1: the selection in LDS (s_sel / s_selp), 2: k = 2
 
   if (len > 0 && n_top == n_cand) {  // every page 0 .. n_mr is selected
     cnt = n_mr + 1;
     if (x <= n_mr) { pg = x; phys = bt[x]; }
     if (B == 16 && x1 <= n_mr) { pg1 = x1; phys1 = bt[x1]; }
   } else if (len > 0) {
-    // 1) per-head normalizers M_g, S_g (scores in log2 units)
-    float mg[G], sl[G], E[G][kKeepE ? NPT : 1];
+    // 1) per-head normalizers M_g, S_g (scores in log2 units); v then holds
+    //    2^(s2 - m_g) (m_g: this thread's maximum of head g)
+    float mg[G], sl[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       mg[g] = -INFINITY;
@@ -660,9 +655,8 @@ __global__ __launch_bounds__(kFusedThreads) void select_attn_kernel(SelectArgs s
       sl[g] = 0.f;
 #pragma unroll
       for (int i = 0; i < NPT; ++i) {
-        const float ex = mg[g] == -INFINITY ? 0.f : fast_exp2(v[g][i] - mg[g]);
-        if constexpr (kKeepE) E[g][i] = ex;
-        sl[g] += ex;
+        v[g][i] = mg[g] == -INFINITY ? 0.f : fast_exp2(v[g][i] - mg[g]);
+        sl[g] += v[g][i];
       }
     }
 #pragma unroll
@@ -702,24 +696,32 @@ __global__ __launch_bounds__(kFusedThreads) void select_attn_kernel(SelectArgs s
       if (j == 0) s_fix[0] = ph[i];
       if (j == n_mr) s_fix[1] = ph[i];
       if (j < 1 || j >= n_mr) continue;
-      float xg[G], eg[G];
+      // m_bar_j; a share below 2^-120 is taken in the log domain from the
+      // page's scores, read again (rare)
+      float mb = 0.f;
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        xg[g] = v[g][i];
-        if constexpr (kKeepE) eg[g] = E[g][i];
-        else eg[g] = mg[g] == -INFINITY ? 0.f : fast_exp2(v[g][i] - mg[g]);
+      for (int g = 0; g < G; ++g) mb = fmaf(v[g][i], scale[g], mb);
+      mb *= invG;
+      float lm;
+      if (mb >= 0x1p-120f) {
+        lm = fast_log2(mb);
+      } else {
+        float xg[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) xg[g] = lse[(size_t)g * se.max_pages + j] * kLog2e;
+        lm = share_log2_small<G>(xg, Mg, log2S, log2G, mb);
       }
-      float mb;
-      key[i] = order_key(share_log2<G>(xg, eg, scale, Mg, log2S, invG, log2G, mb));
+      key[i] = order_key(lm);
       tmax = max(tmax, key[i]);
     }
     s_tmax[tid] = tmax;
     __syncthreads();
     cnt = n_top + 2;
     if (n_top > 0) {
-      // 3) pivot, found by every wave alike
-      uint32_t piv;
-      {
+      // 3) pivot, by wave 0 (the bisections below run on one wave: their
+      //    ballot counts use the CU's one scalar unit)
+      if (wave == 0) {
+        uint32_t piv;
         uint32_t gm[1] = {0u};
 #pragma unroll
         for (int r = 0; r < TR; ++r) gm[0] = max(gm[0], s_tmax[lane * TR + r]);
@@ -735,8 +737,11 @@ __global__ __launch_bounds__(kFusedThreads) void select_attn_kernel(SelectArgs s
           }
           piv = nz >= n_top ? wave_nth_largest<TR>(tv, n_top) : 1u;
         }
+        if (lane == 0) s_piv = piv;
       }
-      //    this wave's keys >= pivot, in page order, to its own list
+      __syncthreads();
+      const uint32_t piv = s_piv;
+      //    every wave's keys >= pivot, in page order, to its own list
       int wc = 0;
 #pragma unroll
       for (int i = 0; i < NPT; ++i) {
@@ -752,77 +757,58 @@ __global__ __launch_bounds__(kFusedThreads) void select_attn_kernel(SelectArgs s
       }
       if (lane == 0) s_wc[wave] = wc;
       __syncthreads();
-      int off[NW + 1];
-      off[0] = 0;
+      int C = 0;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) off[w + 1] = off[w] + s_wc[w];
-      const int C = off[NW];
+      for (int w = 0; w < NW; ++w) C += s_wc[w];
+      mode = 1;
       if (C <= CAP) {
-        // exact cut over the concatenated lists (entry lane + 64 r)
-        mode = 1;
+        // 4) exact cut over the concatenated lists (entry lane + 64 r) by
+        //    wave 0, which writes the selection to LDS in page order
+        if (wave == 0) {
+          int off[NW + 1];
+          off[0] = 0;
 #pragma unroll
-        for (int r = 0; r < CR; ++r) {
-          const int en = lane + kWave * r;
-          if (en < C) {
-            int w = 0, base = 0;
+          for (int w = 0; w < NW; ++w) off[w + 1] = off[w] + s_wc[w];
+          uint32_t ck[CR];
+          int cpg[CR], cph[CR];
 #pragma unroll
-            for (int ww = 1; ww < NW; ++ww)
-              if (en >= off[ww]) { w = ww; base = off[ww]; }
-            ck[r] = s_ck[w][en - base];
-            cpg[r] = s_cp[w][en - base];
-            cph[r] = s_cph[w][en - base];
-          }
-        }
-        const uint32_t t = wave_nth_largest<CR>(ck, n_top);
-        int n_gt = 0;
+          for (int r = 0; r < CR; ++r) {
+            const int en = lane + kWave * r;
+            ck[r] = 0u;
+            cpg[r] = -1;
+            cph[r] = -1;
+            if (en < C) {
+              int w = 0, base = 0;
 #pragma unroll
-        for (int r = 0; r < CR; ++r) n_gt += __popcll(__ballot(ck[r] > t));
-        const int take_eq = n_top - n_gt;
-        int eq_before = 0, out_before = 0;
-#pragma unroll
-        for (int r = 0; r < CR; ++r) {
-          const bool eq = ck[r] == t;
-          const uint64_t be = __ballot(eq);
-          taken[r] = ck[r] > t || (eq && eq_before + lanes_below(be) < take_eq);
-          eq_before += __popcll(be);
-          const uint64_t bs = __ballot(taken[r]);
-          slot[r] = 1 + out_before + lanes_below(bs);
-          out_before += __popcll(bs);
-        }
-        // list entry xx: the sink, a taken candidate (from the lane that
-        // holds it) or the most recent page
-        auto entry = [&](int xx, int& p, int& f) {
-          if (xx == 0) {
-            p = 0;
-            f = s_fix[0];
-          } else if (xx <= n_top) {
-#pragma unroll
-            for (int r = 0; r < CR; ++r) {
-              const uint64_t mm = __ballot(taken[r] && slot[r] == xx);
-              if (mm) {
-                const int src = __ffsll((unsigned long long)mm) - 1;
-                p = __builtin_amdgcn_readlane(cpg[r], src);
-                f = __builtin_amdgcn_readlane(cph[r], src);
-              }
+              for (int ww = 1; ww < NW; ++ww)
+                if (en >= off[ww]) { w = ww; base = off[ww]; }
+              ck[r] = s_ck[w][en - base];
+              cpg[r] = s_cp[w][en - base];
+              cph[r] = s_cph[w][en - base];
             }
-          } else if (xx == n_top + 1) {
-            p = n_mr;
-            f = s_fix[1];
           }
-        };
-        entry(x, pg, phys);
-        if constexpr (B == 16) entry(x1, pg1, phys1);
+          wave_take_in_order<CR>(ck, n_top, [&](int sl, int r) {
+            s_sel[1 + sl] = cpg[r];
+            s_selp[1 + sl] = cph[r];
+          });
+          if (lane == 0) {
+            s_sel[0] = 0;
+            s_selp[0] = s_fix[0];
+            s_sel[n_top + 1] = n_mr;
+            s_selp[n_top + 1] = s_fix[1];
+          }
+        }
       } else {
         // massive ties at the pivot: the general selection over LDS
-        mode = 2;
         select_block<BS, NPT, G>(se, seq, kvh, seq_len, s_sel, &s_cnt, s_selp);
         __syncthreads();
         cnt = s_cnt;
-        if (x < cnt) { pg = s_sel[x]; phys = s_selp[x]; }
-        if (B == 16 && x1 < cnt) { pg1 = s_sel[x1]; phys1 = s_selp[x1]; }
       }
+      __syncthreads();
+      if (x < cnt) { pg = s_sel[x]; phys = s_selp[x]; }
+      if (B == 16 && x1 < cnt) { pg1 = s_sel[x1]; phys1 = s_selp[x1]; }
     } else {  // k = 2: the sink and the most recent page
-      mode = 1;
+      mode = 2;
       if (x == 0) { pg = 0; phys = s_fix[0]; }
       else if (x == 1) { pg = n_mr; phys = s_fix[1]; }
       if (B == 16 && x1 == 1) { pg1 = n_mr; phys1 = s_fix[1]; }
@@ -833,35 +819,14 @@ __global__ __launch_bounds__(kFusedThreads) void select_attn_kernel(SelectArgs s
   if (split == 0 && se.sel_pages) {
     int32_t* so = se.sel_pages + pair * k;
     int32_t* sp = se.sel_phys ? se.sel_phys + pair * k : nullptr;
-    if (mode == 0) {
-      for (int sl0 = tid; sl0 < k; sl0 += BS) {
-        const bool in = sl0 < cnt;
-        so[sl0] = in ? sl0 : -1;
-        if (sp) sp[sl0] = in ? valid_phys(bt[sl0]) : -1;
-      }
-    } else if (mode == 2) {
-      for (int sl0 = tid; sl0 < k; sl0 += BS) {
-        so[sl0] = s_sel[sl0];
-        if (sp) sp[sl0] = s_selp[sl0];
-      }
-    } else {
-      if (wave == 0) {
-#pragma unroll
-        for (int r = 0; r < CR; ++r)
-          if (taken[r]) {
-            so[slot[r]] = cpg[r];
-            if (sp) sp[slot[r]] = valid_phys(cph[r]);
-          }
-      }
-      if (tid == 0) {
-        so[0] = 0;
-        so[cnt - 1] = n_mr;
-        if (sp) { sp[0] = valid_phys(s_fix[0]); sp[cnt - 1] = valid_phys(s_fix[1]); }
-      }
-      for (int sl0 = cnt + tid; sl0 < k; sl0 += BS) {
-        so[sl0] = -1;
-        if (sp) sp[sl0] = -1;
-      }
+    for (int sl0 = tid; sl0 < k; sl0 += BS) {
+      const bool in = sl0 < cnt;
+      int pv = -1, fv = -1;
+      if (in && mode == 0) { pv = sl0; fv = valid_phys(bt[sl0]); }
+      if (in && mode == 1) { pv = s_sel[sl0]; fv = valid_phys(s_selp[sl0]); }
+      if (in && mode == 2) { pv = sl0 == 0 ? 0 : n_mr; fv = valid_phys(s_fix[sl0 == 0 ? 0 : 1]); }
+      so[sl0] = pv;
+      if (sp) sp[sl0] = fv;
     }
     if (tid == 0) se.sel_count[pair] = cnt;
   }

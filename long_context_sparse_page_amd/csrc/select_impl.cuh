@@ -96,9 +96,10 @@ __device__ __forceinline__ void wave_minmax_u32(uint32_t& mx, uint32_t& mn) {
 // with #{x >= t} >= n.  Needs at least n nonzero values.  Bits above the
 // highest bit where the largest and smallest nonzero values differ are common
 // to the answer; the rest are set greedily from the top, one ballot count per
-// bit.
+// bit.  With lowbit > 0 the bits below it are left clear: t is then a lower
+// bound of the n-th largest value (still #{x >= t} >= n), in fewer steps.
 template <int R>
-__device__ __forceinline__ uint32_t wave_nth_largest(const uint32_t (&x)[R], int n) {
+__device__ __forceinline__ uint32_t wave_nth_largest(const uint32_t (&x)[R], int n, int lowbit = 0) {
   uint32_t mx = 0u, mn = 0xffffffffu;
 #pragma unroll
   for (int r = 0; r < R; ++r)
@@ -109,7 +110,7 @@ __device__ __forceinline__ uint32_t wave_nth_largest(const uint32_t (&x)[R], int
   if (diff) {
     const int hb = 31 - __clz(diff);
     t = mx & ~((hb == 31) ? 0xffffffffu : ((2u << hb) - 1u));
-    for (int bit = hb; bit >= 0; --bit) {
+    for (int bit = hb; bit >= lowbit; --bit) {
       const uint32_t c = t | (1u << bit);
       int cnt = 0;
 #pragma unroll
@@ -225,20 +226,12 @@ __device__ __forceinline__ void select_from_list(const uint32_t* s_ckey, const i
   }
 }
 
-// log2 m_bar_j of one page from its G scores in log2 units x[g], with
-// e[g] = 2^(x[g] - m_g) (m_g: the thread's running maximum of head g) and
-// scale[g] = 2^(m_g - M_g) / S_g; m_bar_j itself is returned in mb.  A share
-// below 2^-120 is evaluated in the log domain,
+// log2 m_bar_j of a page whose share is below 2^-120, from its G scores in
+// log2 units (see share_log2), evaluated in the log domain:
 // log2 m_bar = log2 sum_g 2^(x[g] - M_g - log2 S_g) - log2 G.
 template <int G>
-__device__ __forceinline__ float share_log2(const float (&x)[G], const float (&e)[G], const float (&scale)[G],
-                                           const float (&Mg)[G], const float (&log2S)[G], float invG, float log2G,
-                                           float& mb) {
-  mb = 0.f;
-#pragma unroll
-  for (int g = 0; g < G; ++g) mb = fmaf(e[g], scale[g], mb);
-  mb *= invG;
-  if (mb >= 0x1p-120f) return fast_log2(mb);
+__device__ __forceinline__ float share_log2_small(const float (&x)[G], const float (&Mg)[G], const float (&log2S)[G],
+                                                 float log2G, float& mb) {
   float d[G], mx = -INFINITY;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -254,6 +247,23 @@ __device__ __forceinline__ float share_log2(const float (&x)[G], const float (&e
   }
   mb = fast_exp2(lm);
   return lm;
+}
+
+// log2 m_bar_j of one page from its G scores in log2 units x[g], with
+// e[g] = 2^(x[g] - m_g) (m_g: the thread's running maximum of head g) and
+// scale[g] = 2^(m_g - M_g) / S_g; m_bar_j itself is returned in mb.  A share
+// below 2^-120 is evaluated in the log domain,
+// log2 m_bar = log2 sum_g 2^(x[g] - M_g - log2 S_g) - log2 G.
+template <int G>
+__device__ __forceinline__ float share_log2(const float (&x)[G], const float (&e)[G], const float (&scale)[G],
+                                           const float (&Mg)[G], const float (&log2S)[G], float invG, float log2G,
+                                           float& mb) {
+  mb = 0.f;
+#pragma unroll
+  for (int g = 0; g < G; ++g) mb = fmaf(e[g], scale[g], mb);
+  mb *= invG;
+  if (mb >= 0x1p-120f) return fast_log2(mb);
+  return share_log2_small<G>(x, Mg, log2S, log2G, mb);
 }
 
 // One workgroup of BS threads selects for (seq, kvh); sel / cnt_out / selp
