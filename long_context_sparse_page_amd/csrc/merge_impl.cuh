@@ -68,7 +68,7 @@ __device__ __forceinline__ void merge_partials_wave(const BuildArgs& a, int seq,
   constexpr int D = kHeadDim;
   constexpr int W = G == 1 ? 2 : 4;         // dims per lane and head
   constexpr int HPL = G == 1 ? 1 : G / 2;  // heads per lane
-  constexpr int CH = G <= 2 ? 8 : (G == 4 ? 4 : 2);
+  constexpr int CH = G <= 4 ? 8 : 4;  // splits per round trip (one for the fused launch's 8 at G <= 4)
   static_assert(HPL * W * kWave == G * D, "every output owned by one lane");
   const int ns = a.merge.n_splits;
   const int hsub = G == 1 ? 0 : lane / 32;
