@@ -35,6 +35,7 @@ namespace lk {
 
 constexpr int kB16 = 16;
 constexpr int kB16Waves = 4;
+constexpr int kB16StepThreads = 512;  // decode-step launch: one merged output per thread for G <= 4
 constexpr int kB16Ld = 17;  // padded row of the 16 x 16 matrices
 constexpr int kB16InvIters = 2;          // inverse-iteration passes per eigenvector
 constexpr float kB16ClusterTol = 1e-3f;  // eigenvalues this close (relative to lambda_1) are re-orthogonalized
@@ -73,10 +74,14 @@ __device__ __forceinline__ void load2(const float* p, float& a, float& b) {
   b = v.y;
 }
 
-// DS: the decode step's launch (merge and length commit before the build);
-// the bulk build is compiled without them (fewer registers, more waves).
+// DS: the decode step's launch, one workgroup of kB16StepThreads threads per
+// (sequence, KV head): all threads merge the pair's attention partials (one
+// output each), thread 0 of KV head 0 commits the length, and wave 0 then
+// builds the page the step's append completed, if any.  The bulk build is
+// compiled without them (one (page, KV head) per wave; fewer registers, more
+// waves).
 template <typename T, int R, bool DS>
-__global__ __launch_bounds__(kB16Waves * kWave) void build16_kernel(BuildArgs a) {
+__global__ __launch_bounds__(DS ? kB16StepThreads : kB16Waves * kWave) void build16_kernel(BuildArgs a) {
   constexpr int B = kB16;
   constexpr int D = kHeadDim;
   constexpr int KEPT = R < B ? R : B;
@@ -90,25 +95,25 @@ __global__ __launch_bounds__(kB16Waves * kWave) void build16_kernel(BuildArgs a)
   __shared__ float sSign[kB16Waves][KEPT];
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int item = blockIdx.x * kB16Waves + wave;  // (page, KV head) pair
-  if (item >= a.n * a.hkv) return;
-  const int idx = item / a.hkv, kvh = item % a.hkv;
-  const int phys = a.phys_ids[idx];
-  // decode step (idx = sequence): merge the attention partials of (idx, kvh),
-  // then advance the sequence's length when its append was valid
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  int idx, kvh;
   if constexpr (DS) {
-    const bool commit = a.commit_seq_lens && kvh == 0 && lane == 0;
+    idx = blockIdx.x / a.hkv;  // idx = sequence
+    kvh = blockIdx.x % a.hkv;
+  } else {
+    const int item = blockIdx.x * kB16Waves + wv;  // (page, KV head) pair
+    if (item >= a.n * a.hkv) return;
+    idx = item / a.hkv;
+    kvh = item % a.hkv;
+  }
+  const int wave = DS ? 0 : wv;  // this wave's slot of the LDS arrays
+  const int phys = a.phys_ids[idx];
+  if constexpr (DS) {
+    const bool commit = a.commit_seq_lens && kvh == 0 && threadIdx.x == 0;
     const int len = commit ? a.commit_seq_lens[idx] : 0;
-    if (a.merge.part_o) {
-      switch (a.merge.group) {
-        case 1: merge_partials_wave<T, 1>(a, idx, kvh, lane); break;
-        case 2: merge_partials_wave<T, 2>(a, idx, kvh, lane); break;
-        case 4: merge_partials_wave<T, 4>(a, idx, kvh, lane); break;
-        default: merge_partials_wave<T, 8>(a, idx, kvh, lane); break;
-      }
-    }
+    if (a.merge.part_o) merge_partials<T>(a, idx, kvh, threadIdx.x, blockDim.x);
     if (commit && phys != -2) a.commit_seq_lens[idx] = len + 1;
+    if (wv != 0) return;
   }
   if (phys < 0 || phys >= a.num_phys) return;
   const T* K = reinterpret_cast<const T*>(a.k_pool) + (((size_t)phys * a.hkv + kvh) * B) * D;
@@ -507,10 +512,10 @@ static void launch_b16(bool ds, dim3 grid, dim3 block, hipStream_t s, const Buil
 template <typename T>
 static hipError_t launch_build16_t(int rank, const BuildArgs& a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
-  const long long items = (long long)a.n * a.hkv;
-  dim3 grid((unsigned)((items + kB16Waves - 1) / kB16Waves));
   const bool ds = a.merge.part_o != nullptr || a.commit_seq_lens != nullptr;
-  dim3 block(kB16Waves * kWave);
+  const long long items = (long long)a.n * a.hkv;
+  dim3 grid((unsigned)(ds ? items : (items + kB16Waves - 1) / kB16Waves));
+  dim3 block(ds ? kB16StepThreads : kB16Waves * kWave);
   switch (rank) {
     case 1: launch_b16<T, 1>(ds, grid, block, s, a); break;
     case 2: launch_b16<T, 2>(ds, grid, block, s, a); break;

@@ -169,8 +169,9 @@ def test_page16_decode_steps(gpu, summary):
 @pytest.mark.parametrize("group,dtype", [(1, "f32"), (2, "bf16"), (8, "f32")])
 def test_page16_decode_step_groups(gpu, group, dtype):
     """lk_decode_step at 16 tokens for GQA groups 1, 2 and 8 (the builder
-    launch merges each (sequence, KV head)'s split partials with one wave,
-    whose lanes own different dims and heads for each group size): 18 steps
+    launch merges each (sequence, KV head)'s split partials with one thread
+    per output, so a group of 1 leaves most threads idle and a group of 8
+    gives each thread two outputs): 18 steps
     over a ragged batch, so both sequences complete pages and build them
     in-stream; every matching rule at the first and the last step."""
     w = page16(wid=0, batch=2, ctx=(16 * 40 + 9, 16 * 12 + 14), steps=18, budget=256, hq=2 * group, hkv=2,
