@@ -62,14 +62,15 @@ def upload_oracle_records(dc, w, T):
     return summ
 
 
-@pytest.mark.parametrize("summary,rank,group", [("kv", 8, 4), ("i4", 8, 4), ("kv", 4, 4), ("i4", 16, 4),
-                                                ("kv", 8, 1), ("i4", 8, 1), ("kv", 16, 8), ("i4", 8, 8),
-                                                ("i4", 4, 2)])
-def test_page16_scorer_on_oracle_records(gpu, summary, rank, group):
+@pytest.mark.parametrize("summary,rank,group,hkv", [("kv", 8, 4, 8), ("i4", 8, 4, 8), ("kv", 4, 4, 8),
+                                                    ("i4", 16, 4, 8), ("kv", 8, 1, 8), ("i4", 8, 1, 8),
+                                                    ("kv", 16, 8, 2), ("i4", 8, 8, 2), ("i4", 4, 2, 4),
+                                                    ("i4", 8, 4, 3)])
+def test_page16_scorer_on_oracle_records(gpu, summary, rank, group, hkv):
     """Scorer isolation: the oracle's own records in the pool; page LSE within
     1e-3, shares, the selection at the 1e-4 band and attention over it, for
-    GQA groups 1, 2, 4 and 8."""
-    hkv = {1: 8, 2: 4, 4: 8, 8: 2}[group]
+    GQA groups 1, 2, 4 and 8 and KV head counts 8, 4, 3 and 2 (3: the int4/int8
+    scorer's grid split by division instead of a mask)."""
     w = page16(summary=summary, rank=rank, hq=group * hkv, hkv=hkv)
     say("page16 scorer on oracle records:", summary, "r", rank, "G", group, w.context)
     dc = DeviceCache(w, poison=True)

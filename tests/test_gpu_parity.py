@@ -775,12 +775,14 @@ def test_q4_score_select_on_oracle_records(gpu, rank):
     assert worst < 1e-4
 
 
-@pytest.mark.parametrize("summary,group", [("kv", 1), ("kv", 2), ("kv", 8), ("i4", 1), ("i4", 2), ("i4", 8)])
-def test_score_select_on_oracle_records_groups(gpu, summary, group):
+@pytest.mark.parametrize("summary,group,hkv", [("kv", 1, 8), ("kv", 2, 4), ("kv", 8, 2), ("i4", 1, 8), ("i4", 2, 4),
+                                               ("i4", 8, 2), ("i4", 4, 3), ("kv", 4, 3)])
+def test_score_select_on_oracle_records_groups(gpu, summary, group, hkv):
     """The matrix-core scorers (bf16 and int4/int8 records, 64-token pages) at
-    GQA groups 1, 2 and 8 on the oracle's own records: page LSE within 1e-3
-    (measured < 1e-4 expected), shares and the selection at the 1e-4 band."""
-    hkv = {1: 8, 2: 4, 8: 2}[group]
+    GQA groups 1, 2, 4 and 8 and KV head counts 8, 4, 3 and 2 (3: the int4/int8
+    scorer's grid split by division instead of a mask) on the oracle's own
+    records: page LSE within 1e-3 (measured < 1e-4 expected), shares and the
+    selection at the 1e-4 band."""
     w = small_bf16(hq=group * hkv, hkv=hkv)
     if summary == "i4":
         w.summary = "i4"
