@@ -364,21 +364,33 @@ __global__ __launch_bounds__(DS ? kB16StepThreads : kB16Waves * kWave) void buil
   }
   // (d) re-orthogonalize within clusters of close eigenvalues (lane = row;
   //     the four groups compute alike, group 0 stores)
+  //     All pairs are tested at once across the lanes, so a page without
+  //     close pairs (the usual case) spends one LDS round trip here, not a
+  //     chain of them.
   {
     const float ctol = kB16ClusterTol * fabsf(lam1);
-    for (int kk = 1; kk < KEPT; ++kk) {
-      bool touched = false;
-      float zk = Zw[rr * LD + kk];
-      for (int j = 0; j < kk; ++j) {
-        if (fabsf(sLam[wave][j] - sLam[wave][kk]) > ctol) continue;
-        const float zj = Zw[rr * LD + j];
-        zk -= group_sum<16>(zj * zk) * zj;
-        touched = true;
-      }
-      if (touched) {
-        zk *= __builtin_amdgcn_rsqf(group_sum<16>(zk * zk));
-        if (gg == 0) Zw[rr * LD + kk] = zk;
-        wave_lds_fence();
+    // pairs (j, kk), j < kk < KEPT, as x = 16 kk + j, one per lane and pass
+    bool close = false;
+#pragma unroll
+    for (int t = 0; t < (16 * KEPT + kWave - 1) / kWave; ++t) {
+      const int x = t * kWave + lane, kk = x >> 4, j = x & 15;
+      if (j < kk && kk < KEPT) close |= fabsf(sLam[wave][j] - sLam[wave][kk]) <= ctol;
+    }
+    if (__builtin_amdgcn_ballot_w64(close) != 0) {
+      for (int kk = 1; kk < KEPT; ++kk) {
+        bool touched = false;
+        float zk = Zw[rr * LD + kk];
+        for (int j = 0; j < kk; ++j) {
+          if (fabsf(sLam[wave][j] - sLam[wave][kk]) > ctol) continue;
+          const float zj = Zw[rr * LD + j];
+          zk -= group_sum<16>(zj * zk) * zj;
+          touched = true;
+        }
+        if (touched) {
+          zk *= __builtin_amdgcn_rsqf(group_sum<16>(zk * zk));
+          if (gg == 0) Zw[rr * LD + kk] = zk;
+          wave_lds_fence();
+        }
       }
     }
   }
@@ -416,35 +428,88 @@ __global__ __launch_bounds__(DS ? kB16StepThreads : kB16Waves * kWave) void buil
 #pragma unroll
   for (int i = 0; i < B; ++i) { db[i][0] -= mu0; db[i][1] -= mu1; }
   float vb[KEPT][2];
+  if constexpr (KEPT <= 8) {
+    // products one vector at a time, then the signs four vectors at a time with
+    // independent cross-lane reductions and no LDS: the largest magnitude over
+    // the wave, the lowest dim holding it (a maximum of minus the dim), then
+    // that entry's sign from its lane
 #pragma unroll
-  for (int k = 0; k < KEPT; ++k) {
-    const bool nz = lam1 > 0.f && sLam[wave][k] > thresh;
-    const float inv = nz ? 1.f / sqrtf(sLam[wave][k]) : 0.f;
-    float v0 = 0.f, v1 = 0.f;
+    for (int k = 0; k < KEPT; ++k) {
+      const bool nz = lam1 > 0.f && sLam[wave][k] > thresh;
+      const float inv = nz ? 1.f / sqrtf(sLam[wave][k]) : 0.f;
+      float v0 = 0.f, v1 = 0.f;
 #pragma unroll
-    for (int i = 0; i < B; ++i) {
-      const float uik = Zw[i * LD + k];
-      v0 = fmaf(db[i][0], uik, v0);
-      v1 = fmaf(db[i][1], uik, v1);
+      for (int i = 0; i < B; ++i) {
+        const float uik = Zw[i * LD + k];
+        v0 = fmaf(db[i][0], uik, v0);
+        v1 = fmaf(db[i][1], uik, v1);
+      }
+      // zero modes: no basis row (their eigenvector may be anything, even inf)
+      vb[k][0] = nz ? v0 * inv : 0.f;
+      vb[k][1] = nz ? v1 * inv : 0.f;
+      wave_lds_fence();  // one vector's loads and products at a time (registers)
     }
-    // zero modes: no basis row (their eigenvector may be anything, even inf)
-    v0 = nz ? v0 * inv : 0.f;
-    v1 = nz ? v1 * inv : 0.f;
-    // this lane's candidate: the larger |entry| of its two dims (ties: the lower)
-    float best = fabsf(v0), val = v0;
-    int bidx = 2 * lane;
-    if (fabsf(v1) > best) { best = fabsf(v1); val = v1; bidx = 2 * lane + 1; }
+    constexpr int SG = 4;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float b2 = __shfl_xor(best, o);
-      const float v2 = __shfl_xor(val, o);
-      const int i2 = __shfl_xor(bidx, o);
-      if (b2 > best || (b2 == best && i2 < bidx)) { best = b2; val = v2; bidx = i2; }
+    for (int k0 = 0; k0 < KEPT; k0 += SG) {
+      float amax[SG], cand[SG];
+#pragma unroll
+      for (int c = 0; c < SG; ++c)
+        if (k0 + c < KEPT) amax[c] = group_max<kWave>(fmaxf(fabsf(vb[k0 + c][0]), fabsf(vb[k0 + c][1])));
+#pragma unroll
+      for (int c = 0; c < SG; ++c)
+        if (k0 + c < KEPT) {
+          const float* v = vb[k0 + c];
+          cand[c] = group_max<kWave>(fabsf(v[0]) == amax[c] ? -(float)(2 * lane)
+                                     : (fabsf(v[1]) == amax[c] ? -(float)(2 * lane + 1) : -1024.f));
+        }
+#pragma unroll
+      for (int c = 0; c < SG; ++c)
+        if (k0 + c < KEPT) {
+          const int k = k0 + c;
+          const int dim = __builtin_amdgcn_readfirstlane((int)(-cand[c]));
+          const float at =
+              __int_as_float(__builtin_amdgcn_readlane(__float_as_int((dim & 1) ? vb[k][1] : vb[k][0]), dim >> 1));
+          const float sg = at < 0.f ? -1.f : 1.f;
+          vb[k][0] *= sg;
+          vb[k][1] *= sg;
+          if (lane == 0) sSign[wave][k] = sg;
+        }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    const float sg = val < 0.f ? -1.f : 1.f;
-    vb[k][0] = v0 * sg;
-    vb[k][1] = v1 * sg;
-    if (lane == 0) sSign[wave][k] = sg;
+  } else {
+    // 16 vectors: products and sign one vector at a time (the sign by
+    // shuffles), which holds fewer registers
+#pragma unroll
+    for (int k = 0; k < KEPT; ++k) {
+      const bool nz = lam1 > 0.f && sLam[wave][k] > thresh;
+      const float inv = nz ? 1.f / sqrtf(sLam[wave][k]) : 0.f;
+      float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        const float uik = Zw[i * LD + k];
+        v0 = fmaf(db[i][0], uik, v0);
+        v1 = fmaf(db[i][1], uik, v1);
+      }
+      // zero modes: no basis row (their eigenvector may be anything, even inf)
+      v0 = nz ? v0 * inv : 0.f;
+      v1 = nz ? v1 * inv : 0.f;
+      // this lane's candidate: the larger |entry| of its two dims (ties: the lower)
+      float best = fabsf(v0), val = v0;
+      int bidx = 2 * lane;
+      if (fabsf(v1) > best) { best = fabsf(v1); val = v1; bidx = 2 * lane + 1; }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const float b2 = __shfl_xor(best, o);
+        const float v2 = __shfl_xor(val, o);
+        const int i2 = __shfl_xor(bidx, o);
+        if (b2 > best || (b2 == best && i2 < bidx)) { best = b2; val = v2; bidx = i2; }
+      }
+      const float sg = val < 0.f ? -1.f : 1.f;
+      vb[k][0] = v0 * sg;
+      vb[k][1] = v1 * sg;
+      if (lane == 0) sSign[wave][k] = sg;
+    }
   }
   wave_lds_fence();
   auto coef_at = [&](int i, int k) -> float {
