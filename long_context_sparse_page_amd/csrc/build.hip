@@ -137,7 +137,7 @@ __device__ __forceinline__ void write_q4_record(const BuildArgs& a, int phys, in
 }
 
 template <typename T, int R>
-__global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
+__global__ __launch_bounds__(kMergeThreads) __attribute__((amdgpu_waves_per_eu(3))) void build_kernel(BuildArgs a) {
   constexpr int B = 64;
   constexpr int D = kHeadDim;
   constexpr int KEPT = R < B ? R : B;
@@ -518,8 +518,20 @@ __global__ __launch_bounds__(kMergeThreads) void build_kernel(BuildArgs a) {
     for (int i = 0; i < B; ++i) sZ[i][kk] = z[i] * scale;
   }
   __syncthreads();
-  // re-orthogonalize within clusters of close eigenvalues (wave 0, lane = row)
+  // re-orthogonalize within clusters of close eigenvalues (wave 0, lane =
+  // row); all pairs (j, kk), j < kk, are first tested across the lanes (x =
+  // 16 kk + j, one per lane and pass), so a page without close pairs (the
+  // usual case) spends one LDS round trip here, not a chain of them
+  bool close = false;
   if (wave == 0) {
+    const float ctol = kClusterTol * fabsf(sLam[0]);
+#pragma unroll
+    for (int t = 0; t < (16 * KEPT + kWave - 1) / kWave; ++t) {
+      const int x = t * kWave + lane, kk = x >> 4, j = x & 15;
+      if (j < kk && kk < KEPT) close |= fabsf(sLam[j] - sLam[kk]) <= ctol;
+    }
+  }
+  if (wave == 0 && __builtin_amdgcn_ballot_w64(close) != 0) {
     const float ctol = kClusterTol * fabsf(sLam[0]);
     for (int kk = 1; kk < KEPT; ++kk) {
       bool touched = false;
