@@ -146,7 +146,8 @@ hipError_t launch_select_lists(const SelectArgs& a, hipStream_t s);
 hipError_t launch_attn(DType dt, int group, const AttnArgs& a, bool merge, hipStream_t s);
 hipError_t launch_build(DType dt, int rank, const BuildArgs& a, hipStream_t s);
 // Pages of 16 tokens: one wave per (page, KV head); in the decode step (merge
-// and length commit set) wave (seq, kvh) first merges and commits as above
+// and length commit set) one 512-thread workgroup per (seq, kvh) merges and
+// commits as above, then its wave 0 builds
 hipError_t launch_build16(DType dt, int rank, const BuildArgs& a, hipStream_t s);
 // Decode step: selection (se) and attention splits (a) in one launch, for
 // tables of up to 3,072 pages per sequence at 64-token pages and 8,704 at
