@@ -10,11 +10,11 @@ namespace lk {
 // Decode step: combine the attention split partials of (seq, kvh) for its G
 // heads, o = sum_s e^{m_s - M} o_s / sum_s e^{m_s - M} l_s and
 // lse = M + log sum_s e^{m_s - M} l_s (max in log2 units).
-// Threads t0, t0 + nt, ... of the caller take one (head, dim) output each.
-template <typename T>
-__device__ __forceinline__ void merge_partials(const BuildArgs& a, int seq, int kvh, int t0, int nt) {
+// Threads t0, t0 + nt, ... of the caller take one (head, dim) output each;
+// the partials of CH splits are loaded together (one round trip).
+template <typename T, int CH>
+__device__ __forceinline__ void merge_partials_ch(const BuildArgs& a, int seq, int kvh, int t0, int nt) {
   constexpr int D = kHeadDim;
-  constexpr int CH = 16;  // splits whose partials are loaded together (one round trip)
   const int G = a.merge.group;
   const int ns = a.merge.n_splits;
   const float* ml = a.merge.part_ml + ((size_t)seq * a.hkv + kvh) * ns * G * 2;
@@ -56,6 +56,14 @@ __device__ __forceinline__ void merge_partials(const BuildArgs& a, int seq, int 
       a.merge.lse_out[(size_t)seq * a.merge.hq + h] =
           lv > 0.f ? (M + __builtin_amdgcn_logf(lv)) * kLn2 : -INFINITY;
   }
+}
+
+// Eight splits (the fused launch's count) in one batch without the clamped
+// duplicate loads a batch of 16 would issue; more splits in batches of 16.
+template <typename T>
+__device__ __forceinline__ void merge_partials(const BuildArgs& a, int seq, int kvh, int t0, int nt) {
+  if (a.merge.n_splits <= 8) merge_partials_ch<T, 8>(a, seq, kvh, t0, nt);
+  else merge_partials_ch<T, 16>(a, seq, kvh, t0, nt);
 }
 
 }  // namespace lk
